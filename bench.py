@@ -1,0 +1,209 @@
+"""Benchmark of the KDA forward on one MI355X.
+
+A step is one chunked-prefill forward of the prefill workload (B=4, T=4096,
+H=HV=16, K=V=128, chunk 64, bf16 q/k/v, fp32 gate inputs and state, safe
+gate): gate, cumulative decay, intra-chunk solve and inter-chunk propagation,
+all in one launch of the fused chunk kernel.  The recurrent decode row is
+timed in the same run on the decode workload (B=256, HV=32, 256 single-token
+steps over a 512 MiB fp32 state) and reported in the "decode" object.
+
+Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
+HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
+bytes per launch / mean launch time (HIP events on the launch stream) against
+the 8 TB/s HBM peak; `mfma_frac` adds algorithmic FLOPs against the 2.5166
+PFLOP/s dense bf16 MFMA peak.  `cpu_baseline` times the fp64 CPU oracle on all
+host cores over a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+
+
+def chunk_bytes(w):
+    """Algorithmic HBM bytes of one chunked forward: every input read once
+    (q, k once per query/key head), o written once, final (and initial) state."""
+    qk = 2 * w.B * w.T * w.H * w.K * (2 if w.dtype == "bf16" else 4)
+    v = w.B * w.T * w.HV * w.V * (2 if w.dtype == "bf16" else 4)
+    g = w.B * w.T * w.HV * w.K * 4
+    beta = w.B * w.T * w.HV * 4
+    o = w.B * w.T * w.HV * w.V * 4
+    state = w.B * w.HV * w.K * w.V * 4 * (2 if w.s0_std > 0 else 1)
+    return qk + v + g + beta + o + state
+
+
+def chunk_flops(w, C=64):
+    """Dense FLOPs of the chunkwise algorithm: 2 (3 C K + 2 C V + 3 K V) per
+    token and value head (A_qk, R, w, u, U, Q S, A U, state update)."""
+    return 2 * (3 * C * w.K + 2 * C * w.V + 3 * w.K * w.V) * w.B * w.T * w.HV
+
+
+def decode_bytes(w):
+    """Per step: the fp32 state read and written once, plus q, k, v, g_raw,
+    beta and o for one token."""
+    e = 2 if w.dtype == "bf16" else 4
+    return (2 * w.B * w.HV * w.K * w.V * 4 + 2 * w.B * w.H * w.K * e + w.B * w.HV * w.V * e
+            + w.B * w.HV * w.K * 4 + w.B * w.HV * 4 + w.B * w.HV * w.V * 4)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "gva", "long", "tiny"])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kimi_delta_attention_02_amd as kda
+    from kimi_delta_attention_02_amd import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    d = synth.make_inputs(w)
+    g = {n: (t.to(dev) if t is not None else None) for n, t in d.items()}
+    o = torch.empty((w.B, w.T, w.HV, w.V), dtype=torch.float32, device=dev)
+    S = torch.empty((w.B, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.chunk_fwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"],
+                      gate=w.gate, lower_bound=w.lower_bound, chunk_size=w.chunk,
+                      initial_state=g["S0"], o=o, final_state=S)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    tokens = w.B * w.T
+    nbytes = chunk_bytes(w)
+    flops = chunk_flops(w, w.chunk)
+    launch_ms = sum(per) / len(per)
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    result = {
+        "metric": "KDA fwd tokens/s (chunked prefill, decode) + % of MFMA / HBM roofline",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1), v,g_raw N(0,1), beta=sigmoid(N(0,1)))",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HV": w.HV, "K": w.K,
+                   "V": w.V, "chunk": w.chunk, "gate": w.gate, "global_batch": w.B,
+                   "seq_len": w.T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunk_fwd_kernel<128, bf16>", "bytes_per_launch": nbytes,
+                     "launch_ms": launch_ms},
+        "mfma": {"algorithmic_flops": flops,
+                 "achieved_tflops": flops / (launch_ms * 1e-3) / 1e12,
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": flops / (launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "wall_s_timed": t_wall,
+    }
+    del o, S, g
+
+    if not args.no_decode:
+        wd = synth.WORKLOADS["decode"]
+        dd = synth.make_inputs(wd)
+        st = dd["S0"].to(dev)
+        qs, ks, vs = (dd[n].transpose(0, 1).contiguous().to(dev) for n in ("q", "k", "v"))
+        gs = dd["g_raw"].transpose(0, 1).contiguous().to(dev)
+        bs = dd["beta"].transpose(0, 1).contiguous().to(dev)
+        A_log, dtb = dd["A_log"].to(dev), dd["dt_bias"].to(dev)
+        od = torch.empty((wd.steps, wd.B, wd.HV, wd.V), dtype=torch.float32, device=dev)
+
+        def dstep(t):
+            kda.recurrent_step(qs[t], ks[t], vs[t], gs[t], bs[t], A_log, dtb, st, gate=wd.gate,
+                               lower_bound=wd.lower_bound, o=od[t])
+
+        for t in range(min(8, wd.steps)):
+            dstep(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(wd.steps):
+            dstep(t)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1)
+        per_step_ms = dms / wd.steps
+        dgbs = decode_bytes(wd) / (per_step_ms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": wd.name, "B": wd.B, "HV": wd.HV, "K": wd.K, "V": wd.V, "steps": wd.steps,
+            "value": wd.B * wd.steps / (dms * 1e-3), "unit": "tokens/s",
+            "ms_per_token_step": per_step_ms,
+            "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dgbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "decode_step_kernel<128, 128, bf16>",
+                         "bytes_per_launch": decode_bytes(wd)},
+        }
+        del qs, ks, vs, gs, bs, od, st
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 1024 * 1024 // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = 4 * n
+
+    if not args.no_cpu:
+        import oracle
+
+        cores = os.cpu_count() or 1
+        npf = lambda x: None if x is None else x.float().numpy()
+        # bounded sample: whole (sequence, head) pairs, at most ~64 x 4096 token-heads
+        # (a few seconds to tens of seconds of fp64 work), at least one per core
+        pairs = [(b, hv) for b in range(w.B) for hv in range(w.HV)]
+        heads = pairs[:max(1, cores, (64 * 4096) // max(1, w.T))]
+        t0 = time.perf_counter()
+        oracle.default().kda_fwd_heads(npf(d["q"]), npf(d["k"]), npf(d["v"]), npf(d["g_raw"]),
+                                       npf(d["beta"]), npf(d["A_log"]), npf(d["dt_bias"]), w.gate,
+                                       w.lower_bound, npf(d["S0"]), heads, threads=cores)
+        dt = time.perf_counter() - t0
+        token_heads = len(heads) * w.T
+        result["cpu_baseline"] = {
+            "value": token_heads / dt / w.HV, "unit": "tokens/s", "cores": min(cores, len(heads)),
+            "kind": "oracle",
+            "sample": "%d (sequence, value head) pairs x %d tokens of the %s workload, fp64 naive "
+                      "recurrence, one pair per thread; tokens/s = token-heads/s / HV"
+                      % (len(heads), w.T, w.name),
+            "seconds": dt}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

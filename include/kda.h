@@ -1,0 +1,147 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The operation (from the "K3 notes" pages, section "KDA 递归核心", subsection
+ * "逐步公式"): for every sequence b and value head hv, with state
+ * S[K][V] (key rows, value columns), for each token t in order
+ *
+ *     S_dec = exp(g_t) (.) S_{t-1}            per-key-channel decay of row kappa
+ *     r_t   = v_t - k_t . S_dec               delta-rule residual
+ *     S_t   = S_dec + (beta_t k_t) outer r_t  rank-1 write
+ *     o_t   = (1/sqrt(K)) q_t . S_t           read (includes token t's own write)
+ *
+ * g_t is the gate ("K3 notes", section "Gate 激活"): with
+ * input = g_raw + dt_bias[hv][kappa] and rate = exp(A_log[hv]),
+ *     KDA_GATE_SAFE     : g = lower_bound * sigmoid(rate * input)   in [lower_bound, 0]
+ *     KDA_GATE_STANDARD : g = -rate * softplus(input)               in (-inf, 0]
+ *     KDA_GATE_NONE     : g = g_raw  (the caller passes the log-decay itself)
+ * GVA: value head hv reads query/key head h = hv / (HV / H) (q and k are
+ * shared by HV/H consecutive value heads, as repeat_interleave would do).
+ *
+ * Two schedules of the same recurrence ("DeltaNet family" page, sections on
+ * the fused recurrent kernel and on chunkwise KDA): kda_chunk_fwd processes a
+ * whole sequence chunk by chunk (intra-chunk dependencies resolved by a
+ * lower-triangular solve, the state carried between chunks); kda_recurrent_step
+ * advances the state by one token.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major memory
+ *    with the shapes given below, aligned to 16 bytes.  The caller owns every
+ *    buffer; the library allocates nothing and keeps no global state.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
+ *    default stream).  Nothing synchronises the host.  Input buffers must stay
+ *    valid, and outputs unread, until the stream reaches the enqueued work.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    non-KDA_OK status means nothing was enqueued (except KDA_ERR_HIP, which
+ *    reports a failed launch).  No entry point aborts or throws.
+ *  - The read scale is fixed at 1/sqrt(K).
+ *  - Outputs must not overlap inputs, except where stated.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, HV % H != 0, ... */
+  KDA_ERR_UNSUPPORTED = 2, /* valid but not built: head size, chunk size */
+  KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  KDA_ERR_HIP = 4          /* a kernel launch failed */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum { KDA_GATE_STANDARD = 0, KDA_GATE_SAFE = 1, KDA_GATE_NONE = 2 } kda_gate_kind;
+
+typedef struct ihipStream_t* kda_stream_t; /* the same type as hipStream_t */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+/*
+ * kda_gate -- gate activation ("K3 notes", "Gate 激活": two-gate table and the
+ * kda_gate_reference panel), optionally followed by the chunk-local inclusive
+ * prefix sum of the log-decay ("DeltaNet family" page, chunkwise pipeline:
+ * the cumulative log-decay whose differences give D_{j+1:i}).
+ *
+ *   g_raw   [B, T, HV, K] float32
+ *   A_log   [HV] float32                 rate = exp(A_log[hv])
+ *   dt_bias [HV, K] float32 or NULL      NULL means zero bias
+ *   gate, lower_bound                    lower_bound < 0 required for KDA_GATE_SAFE
+ *   chunk_size  0: g_out = g;  C > 0: g_out[t] = sum of g over the tokens of
+ *               t's chunk up to and including t (chunks of C tokens from t = 0)
+ *   g_out   [B, T, HV, K] float32 (may alias g_raw)
+ * Any K >= 1 is accepted.  B or T equal to 0 is a no-op.
+ */
+kda_status kda_gate(const float* g_raw, const float* A_log, const float* dt_bias,
+                    kda_gate_kind gate, float lower_bound, int B, int T, int HV, int K,
+                    int chunk_size, float* g_out, kda_stream_t stream);
+
+/*
+ * kda_chunk_fwd -- chunkwise-parallel forward over whole sequences ("DeltaNet
+ * family" page, "Chunkwise KDA": temporary errors, causal triangular solve,
+ * chunk-end state, chunk outputs), gate computed in-kernel from g_raw.
+ *
+ *   q, k          [B, T, H, K]   float32 or bfloat16 (qkv_dtype)
+ *   v             [B, T, HV, V]  same dtype as q and k
+ *   g_raw         [B, T, HV, K]  float32
+ *   beta          [B, T, HV]     float32
+ *   A_log         [HV]           float32
+ *   dt_bias       [HV, K]        float32 or NULL
+ *   initial_state [B, HV, K, V]  float32, or NULL for zeros
+ *   o             [B, T, HV, V]  float32 output
+ *   final_state   [B, HV, K, V]  float32 output, or NULL; may alias initial_state
+ *   chunk_size    16, 32 or 64 (tokens per chunk; the result does not depend on it
+ *                 beyond rounding)
+ *   workspace     device scratch of kda_chunk_fwd_workspace_bytes(...) bytes, or
+ *                 NULL when that size is 0
+ * Supported head sizes: K == V in {16, 32, 64, 128}; HV % H == 0.  T may be any
+ * length >= 0 (a ragged last chunk is handled in-kernel); T == 0 copies the
+ * initial state (or zeros) to final_state.
+ * Arithmetic: fp32 inputs run fp32 matrix products; bf16 inputs run bf16 MFMA
+ * products with fp32 accumulation and split (hi + lo) operands where precision
+ * needs them; the state is fp32 throughout.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int chunk_size,
+                                     kda_dtype qkv_dtype);
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                         const float* g_raw, const float* beta, const float* A_log,
+                         const float* dt_bias, kda_gate_kind gate, float lower_bound,
+                         const float* initial_state, float* o, float* final_state, int B, int T,
+                         int H, int HV, int K, int V, int chunk_size, void* workspace,
+                         size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_recurrent_step -- one decode token for every sequence ("DeltaNet family"
+ * page, fused recurrent mode: decay, key prediction, residual, rank-1 write,
+ * query read), the state updated in place in HBM.
+ *
+ *   q, k    [B, H, K]        float32 or bfloat16 (qkv_dtype)
+ *   v       [B, HV, V]       same dtype
+ *   g_raw   [B, HV, K]       float32
+ *   beta    [B, HV]          float32
+ *   A_log   [HV], dt_bias [HV, K] or NULL, gate, lower_bound: as kda_gate
+ *   state   [B, HV, K, V]    float32, read and overwritten with the new state
+ *   o       [B, HV, V]       float32 output
+ * Supported: K, V in {16, 32, 64, 128}; HV % H == 0.
+ */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                              const float* g_raw, const float* beta, const float* A_log,
+                              const float* dt_bias, kda_gate_kind gate, float lower_bound,
+                              float* state, float* o, int B, int H, int HV, int K, int V,
+                              kda_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,149 @@
+"""Kimi Delta Attention forward on MI355X (gfx950): thin Python binding.
+
+Every function marshals torch tensors (device memory, the current HIP stream)
+into the C ABI of ``include/kda.h`` and nothing else: each step of the
+computation runs in the HIP kernels of ``libkda.so``.
+
+* :func:`gate`           -- gate activation (+ optional chunk-local cumulative sum)
+* :func:`chunk_fwd`      -- chunkwise forward over whole sequences
+* :func:`recurrent_step` -- one decode token, state updated in place
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+__all__ = ["gate", "chunk_fwd", "recurrent_step", "chunk_fwd_workspace_bytes", "KDAError"]
+
+KDAError = _lib.KDAError
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _qkv_dtype(q):
+    if q.dtype == torch.float32:
+        return _lib.KDA_F32
+    if q.dtype == torch.bfloat16:
+        return _lib.KDA_BF16
+    raise TypeError("q, k, v must be float32 or bfloat16, got %s" % q.dtype)
+
+
+def gate(g_raw, A_log, dt_bias=None, *, gate="safe", lower_bound=-5.0, chunk_size=0, out=None):
+    """Gate activation of g_raw [B, T, HV, K] (float32); with chunk_size > 0 the
+    chunk-local inclusive cumulative sum of the log-decay.  Returns float32."""
+    lib = _lib.load()
+    dev = g_raw.device
+    B, T, HV, K = g_raw.shape
+    _need(g_raw, "g_raw", torch.float32, (B, T, HV, K), dev)
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, (HV,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
+    if out is None:
+        out = torch.empty_like(g_raw)
+    _need(out, "out", torch.float32, (B, T, HV, K), dev)
+    st = lib.kda_gate(_ptr(g_raw), _ptr(A_log), _ptr(dt_bias), _lib.GATES[gate], float(lower_bound),
+                      B, T, HV, K, int(chunk_size), _ptr(out), _stream(dev))
+    _lib.check("kda_gate", st)
+    return out
+
+
+def chunk_fwd_workspace_bytes(B, T, H, HV, K, V, chunk_size=64, dtype=torch.bfloat16):
+    d = _lib.KDA_BF16 if dtype == torch.bfloat16 else _lib.KDA_F32
+    return int(_lib.load().kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, chunk_size, d))
+
+
+def chunk_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_bound=-5.0,
+              chunk_size=64, initial_state=None, output_final_state=True, o=None,
+              final_state=None, workspace=None):
+    """Chunkwise KDA forward.
+
+    q, k [B, T, H, K] and v [B, T, HV, V] (float32 or bfloat16, one dtype);
+    g_raw [B, T, HV, K], beta [B, T, HV], A_log [HV], dt_bias [HV, K] or None,
+    initial_state [B, HV, K, V] or None (float32).  Returns (o, final_state)
+    with o [B, T, HV, V] float32 and final_state [B, HV, K, V] float32 (None
+    when output_final_state is False).
+    """
+    lib = _lib.load()
+    dev = q.device
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dt = q.dtype
+    qkv = _qkv_dtype(q)
+    _need(q, "q", dt, (B, T, H, K), dev)
+    _need(k, "k", dt, (B, T, H, K), dev)
+    _need(v, "v", dt, (B, T, HV, V), dev)
+    _need(g_raw, "g_raw", torch.float32, (B, T, HV, K), dev)
+    _need(beta, "beta", torch.float32, (B, T, HV), dev)
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, (HV,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (B, HV, K, V), dev)
+    if o is None:
+        o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (B, HV, K, V), dev)
+    need = int(lib.kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, chunk_size, qkv))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta), _ptr(A_log),
+                           _ptr(dt_bias), _lib.GATES[gate], float(lower_bound), _ptr(initial_state),
+                           _ptr(o), _ptr(final_state), B, T, H, HV, K, V, int(chunk_size),
+                           _ptr(workspace), ws_bytes, _stream(dev))
+    _lib.check("kda_chunk_fwd", st)
+    return o, final_state
+
+
+def recurrent_step(q, k, v, g_raw, beta, A_log, dt_bias, state, *, gate="safe", lower_bound=-5.0,
+                   o=None):
+    """One decode token: q, k [B, H, K], v [B, HV, V], g_raw [B, HV, K], beta
+    [B, HV]; state [B, HV, K, V] float32 is updated in place.  Returns o
+    [B, HV, V] float32."""
+    lib = _lib.load()
+    dev = q.device
+    B, H, K = q.shape
+    HV, V = v.shape[1], v.shape[2]
+    dt = q.dtype
+    qkv = _qkv_dtype(q)
+    _need(q, "q", dt, (B, H, K), dev)
+    _need(k, "k", dt, (B, H, K), dev)
+    _need(v, "v", dt, (B, HV, V), dev)
+    _need(g_raw, "g_raw", torch.float32, (B, HV, K), dev)
+    _need(beta, "beta", torch.float32, (B, HV), dev)
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, (HV,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
+    _need(state, "state", torch.float32, (B, HV, K, V), dev)
+    if o is None:
+        o = torch.empty((B, HV, V), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, HV, V), dev)
+    st = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta),
+                                _ptr(A_log), _ptr(dt_bias), _lib.GATES[gate], float(lower_bound),
+                                _ptr(state), _ptr(o), B, H, HV, K, V, _stream(dev))
+    _lib.check("kda_recurrent_step", st)
+    return o

@@ -1,0 +1,124 @@
+// Host side of the C ABI declared in include/kda.h: argument validation,
+// then one asynchronous kernel launch on the caller's stream.  Validation runs
+// entirely on the host and returns before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+hipError_t launch_gate(const float* g_raw, const float* A_log, const float* dt_bias, int kind,
+                       float lower_bound, int B, int T, int HV, int K, int chunk, float* g_out,
+                       hipStream_t stream);
+hipError_t launch_decode(const void* q, const void* k, const void* v, int bf16,
+                         const float* g_raw, const float* beta, const float* A_log,
+                         const float* dt_bias, int kind, float lower_bound, float* state,
+                         float* o, int B, int H, int HV, int K, int V, hipStream_t stream);
+hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
+                        const float* beta, const float* A_log, const float* dt_bias, int kind,
+                        float lower_bound, const float* S0, float* o, float* S_out, int B, int T,
+                        int H, int HV, int K, hipStream_t stream);
+}  // namespace kda
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_size_ok(int n) { return n == 16 || n == 32 || n == 64 || n == 128; }
+
+// Gate arguments shared by every entry point.
+kda_status check_gate(kda_gate_kind gate, float lower_bound, const float* A_log) {
+  if (gate != KDA_GATE_STANDARD && gate != KDA_GATE_SAFE && gate != KDA_GATE_NONE)
+    return KDA_ERR_INVALID_ARG;
+  if (gate != KDA_GATE_NONE && !A_log) return KDA_ERR_INVALID_ARG;
+  if (gate == KDA_GATE_SAFE && !(lower_bound < 0.0f && isfinite(lower_bound)))
+    return KDA_ERR_INVALID_ARG;
+  return KDA_OK;
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head or chunk size not built";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
+  }
+  return "unknown kda_status";
+}
+
+int kda_version(void) { return 10000; }
+
+kda_status kda_gate(const float* g_raw, const float* A_log, const float* dt_bias,
+                    kda_gate_kind gate, float lower_bound, int B, int T, int HV, int K,
+                    int chunk_size, float* g_out, kda_stream_t stream) {
+  kda_status st = check_gate(gate, lower_bound, A_log);
+  if (st != KDA_OK) return st;
+  if (B < 0 || T < 0 || HV < 1 || K < 1 || chunk_size < 0) return KDA_ERR_INVALID_ARG;
+  if (B == 0 || T == 0) return KDA_OK;
+  if (!g_raw || !g_out) return KDA_ERR_INVALID_ARG;
+  return from_hip(kda::launch_gate(g_raw, A_log, dt_bias, (int)gate, lower_bound, B, T, HV, K,
+                                   chunk_size, g_out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int chunk_size,
+                                     kda_dtype qkv_dtype) {
+  (void)B, (void)T, (void)H, (void)HV, (void)K, (void)V, (void)chunk_size, (void)qkv_dtype;
+  return 0;  // the fused kernel keeps every intermediate on chip
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                         const float* g_raw, const float* beta, const float* A_log,
+                         const float* dt_bias, kda_gate_kind gate, float lower_bound,
+                         const float* initial_state, float* o, float* final_state, int B, int T,
+                         int H, int HV, int K, int V, int chunk_size, void* workspace,
+                         size_t workspace_bytes, kda_stream_t stream) {
+  kda_status st = check_gate(gate, lower_bound, A_log);
+  if (st != KDA_OK) return st;
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0) return KDA_ERR_INVALID_ARG;
+  if ((long)B * HV > (1L << 28)) return KDA_ERR_INVALID_ARG;
+  if (!head_size_ok(K) || V != K) return KDA_ERR_UNSUPPORTED;
+  if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+  // empty tensors may come with null data pointers: required only when there are tokens
+  if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, g_raw, o, initial_state, final_state, dt_bias};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+  size_t need = kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, chunk_size, qkv_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (B == 0) return KDA_OK;
+  return from_hip(kda::launch_chunk(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log, dt_bias,
+                                    (int)gate, lower_bound, initial_state, o, final_state, B, T, H,
+                                    HV, K, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                              const float* g_raw, const float* beta, const float* A_log,
+                              const float* dt_bias, kda_gate_kind gate, float lower_bound,
+                              float* state, float* o, int B, int H, int HV, int K, int V,
+                              kda_stream_t stream) {
+  kda_status st = check_gate(gate, lower_bound, A_log);
+  if (st != KDA_OK) return st;
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (B < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0) return KDA_ERR_INVALID_ARG;
+  if ((long)B * HV > (1L << 28)) return KDA_ERR_INVALID_ARG;
+  if (!head_size_ok(K) || !head_size_ok(V)) return KDA_ERR_UNSUPPORTED;
+  if (B > 0 && (!q || !k || !v || !g_raw || !beta || !state || !o)) return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, g_raw, state, o, dt_bias};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+  if (B == 0) return KDA_OK;
+  return from_hip(kda::launch_decode(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log, dt_bias,
+                                     (int)gate, lower_bound, state, o, B, H, HV, K, V,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

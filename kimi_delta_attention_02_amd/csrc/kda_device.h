@@ -1,0 +1,93 @@
+// Device-side helpers shared by the KDA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): about 16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  __bf16 h = static_cast<__bf16>(x);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = f32_to_bf16_bits(x - static_cast<float>(h));
+}
+
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// log(1 + e) for e in [0, 1]; a short series where 1 + e would round.
+__device__ __forceinline__ float log1p_small(float e) {
+  if (e < 0.0009765625f) return e * (1.0f - e * (0.5f - e * (1.0f / 3.0f)));
+  return __builtin_amdgcn_logf(1.0f + e) * kLn2;
+}
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^-|x|); NaN propagates
+// through e, and softplus(+inf) = +inf.
+__device__ __forceinline__ float softplus_f(float x) {
+  float e = exp_f(-fabsf(x));
+  return fmaxf(x, 0.0f) + log1p_small(e);
+}
+
+// Gate activation: log-decay g for one element ("K3 notes", "Gate 激活").
+//   safe     : g = L * sigmoid(rate * (g_raw + bias))
+//   standard : g = -rate * softplus(g_raw + bias)
+//   none     : g = g_raw
+__device__ __forceinline__ float gate_log_decay(float graw, float bias, float rate, int kind,
+                                                float L) {
+  if (kind == KDA_GATE_SAFE) {
+    float z = rate * (graw + bias);
+    float e = __builtin_amdgcn_exp2f(-z * kLog2e);  // +inf for very negative z -> sigmoid 0
+    return L * __builtin_amdgcn_rcpf(1.0f + e);
+  }
+  if (kind == KDA_GATE_STANDARD) return -rate * softplus_f(graw + bias);
+  return graw;
+}
+
+// ------------------------------------------------------------ load helpers
+
+template <typename T>
+struct In;  // element type of q / k / v
+
+template <>
+struct In<float> {
+  static __device__ __forceinline__ float at(const float* p, long i) { return p[i]; }
+  // four consecutive elements
+  static __device__ __forceinline__ void load4(const float* p, long i, float out[4]) {
+    float4 v = *reinterpret_cast<const float4*>(p + i);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+};
+
+template <>
+struct In<uint16_t> {  // bfloat16 bits
+  static __device__ __forceinline__ float at(const uint16_t* p, long i) {
+    return bf16_bits_to_f32(p[i]);
+  }
+  static __device__ __forceinline__ void load4(const uint16_t* p, long i, float out[4]) {
+    uint2 v = *reinterpret_cast<const uint2*>(p + i);
+    out[0] = __uint_as_float(v.x << 16);
+    out[1] = __uint_as_float(v.x & 0xffff0000u);
+    out[2] = __uint_as_float(v.y << 16);
+    out[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+};
+
+}  // namespace kda

@@ -1,0 +1,53 @@
+"""GPU parity at the full sizes of the five synthetic workloads, in the launch
+configuration the benchmark times.  The oracle recomputes a sample of
+(sequence, value head) pairs over their whole length; every output of those
+pairs and their final states are compared."""
+import pytest
+import torch
+
+import kda_testlib as L
+from kimi_delta_attention_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _chunked(name, nheads):
+    w = synth.WORKLOADS[name]
+    d = synth.make_inputs(w)
+    print("%s: B=%d T=%d H=%d HV=%d K=%d" % (name, w.B, w.T, w.H, w.HV, w.K), flush=True)
+    o, S = L.run_chunk(d, w.gate, w.lower_bound, w.chunk)
+    heads = L.sample_heads(w.B, w.HV, nheads, seed=w.seed)
+    ref = L.oracle_heads(d, w.gate, w.lower_bound, heads)
+    tol = L.TOL_F32 if w.dtype == "f32" else L.TOL_BF16
+    L.compare_heads(o, S, ref, tol, name)
+
+
+def test_workload_tiny_chunked_all_heads():
+    _chunked("tiny", 2)
+
+
+@pytest.mark.timeout(300)
+def test_workload_prefill():
+    _chunked("prefill", 8)
+
+
+@pytest.mark.timeout(300)
+def test_workload_gva():
+    _chunked("gva", 6)
+
+
+@pytest.mark.timeout(600)
+def test_workload_long():
+    _chunked("long", 4)
+
+
+@pytest.mark.timeout(600)
+def test_workload_decode():
+    """256 single-token steps over B=256, HV=32 with a 512 MiB fp32 state."""
+    w = synth.WORKLOADS["decode"]
+    d = synth.make_inputs(w)
+    print("decode: B=%d steps=%d HV=%d K=%d" % (w.B, w.steps, w.HV, w.K), flush=True)
+    o, S = L.run_decode(d, w.gate, w.lower_bound, d["S0"])
+    heads = L.sample_heads(w.B, w.HV, 16, seed=w.seed)
+    ref = L.oracle_heads(d, w.gate, w.lower_bound, heads)
+    L.compare_heads(o, S, ref, L.TOL_F32, "decode")
