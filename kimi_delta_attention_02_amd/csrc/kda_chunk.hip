@@ -61,6 +61,7 @@ struct ChunkParams {
 
 constexpr int kTok = 16;     // tokens per block
 constexpr int kCat = 40;     // row stride of [hi t0..15 | lo t0..15] operands (+8 pad)
+constexpr int kRS = 20;      // row stride of the fp32 R tile (16-byte rows, conflict-free stores)
 constexpr float kGammaMin = 7.888609052210118e-31f;  // 2^-100
 constexpr float kGammaMax = 1.2676506002282294e30f;  // 2^100 (only a positive log-decay can get here)
 
@@ -79,10 +80,11 @@ struct SmemBF16 {
   uint16_t aqk[kTok * kCat];                    // A          [i][hi j | lo j]
   uint16_t akk[kTok * kCat];                    // (I+R)^-1   [i][hi j | lo j]
   uint16_t ebT[BV * kCat];                      // Ebar^T     [v][hi t | lo t]
-  uint16_t uT[BV * kCat];                       // U^T        [v][hi t | lo t]
-  float r[kTok * 17 > (K / 16) * BV ? kTok * 17 : (K / 16) * BV];
+  uint16_t uT[4][kTok * kCat];                  // U^T per wave, own column block [v][hi t | lo t]
+  float r[kTok * kRS > (K / 16) * BV ? kTok * kRS : (K / 16) * BV];
   float gam[K];
   float beta[kTok];
+  int flag[4];
 };
 
 template <int K, int BV>
@@ -92,10 +94,11 @@ struct SmemF32 {
   float keT[K * 17];  // [c][t]
   float st[BV * LD];  // [v][c]
   float aqk[kTok * 17], akk[kTok * 17];
-  float ebT[BV * 17], uT[BV * 17];
-  float r[kTok * 17 > (K / 16) * BV ? kTok * 17 : (K / 16) * BV];
+  float ebT[BV * 17], uT[4][kTok * 17];
+  float r[kTok * kRS > (K / 16) * BV ? kTok * kRS : (K / 16) * BV];
   float gam[K];
   float beta[kTok];
+  int flag[4];
 };
 
 // ------------------------------------------------------------ MFMA tiles
@@ -169,7 +172,7 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo_half, uint16_t hi_half) {
 
 // ----------------------------------------------------------------- kernel
 
-template <int K, typename T>
+template <int K, typename T, int GK>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int V = K;
@@ -195,8 +198,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   const int h = hv / (HV / H);
   const int v0 = vt * BV;
   const float scale = 1.0f / __builtin_sqrtf((float)K);
-  const float rate = p.kind != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
-  const float* bias = (p.dt_bias && p.kind != KDA_GATE_NONE) ? p.dt_bias + (long)hv * K : nullptr;
+  const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
+  const float* bias = (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias + (long)hv * K : nullptr;
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
@@ -239,66 +242,102 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   };
   write_state_operand();
 
+  // ---- inputs of the next block, prefetched into registers one block ahead
+  typedef typename In<T>::Raw4 Raw4;
+  typedef typename In<T>::Raw1 Raw1;
+  const int tp = tid & 7, c0 = (tid >> 3) * 4;  // prep thread: token pair, channel quad
+  const int cbw = w - 2;                        // waves 2.. own value column block cbw
+  const bool prep_thread = tid < 2 * K;
+  const bool ebar_wave = w >= 2 && cbw < NCB;
+  float bias4[4] = {0.f, 0.f, 0.f, 0.f};  // dt_bias of the prep thread's channels
+  if (bias && prep_thread) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bias4[c] = bias[c0 + c];
+  }
+  float4 pg[2];
+  Raw4 pq[2], pk[2];
+  Raw1 pv[4];
+  float pbeta = 0.0f;
+  // Loads past the end of the sequence read the last token instead (always a
+  // valid address) and are replaced by padding values where they are used.
+  auto fetch = [&](int tb) {
+    if (prep_thread) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int t = min(tb + 2 * tp + j, T_ - 1);
+        const long row = b * T_ + t;
+        pg[j] = *reinterpret_cast<const float4*>(p.g_raw + (row * HV + hv) * K + c0);
+        pq[j] = In<T>::raw4(qg, (row * H + h) * K + c0);
+        pk[j] = In<T>::raw4(kg, (row * H + h) * K + c0);
+      }
+    }
+    if (tid < kTok) {
+      const float bt = p.beta[(b * T_ + min(tb + tid, T_ - 1)) * HV + hv];
+      pbeta = tb + tid < T_ ? bt : 0.0f;
+    }
+  };
+  auto fetch_v = [&](int tb) {
+    if (ebar_wave) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb + 4 * (lane >> 4) + r;
+        const Raw1 x = vg[((b * T_ + min(t, T_ - 1)) * HV + hv) * V + v0 + 16 * cbw + (lane & 15)];
+        pv[r] = t < T_ ? x : In<T>::zero1();
+      }
+    }
+  };
+  if (T_ > 0) {
+    fetch(0);
+    fetch_v(0);
+  }
+
   for (int t0 = 0; t0 < T_; t0 += kTok) {
     // ------------------------------------------------------------ prep
-    // thread (tp, cq): tokens 2tp, 2tp+1 of the block, channels 4cq .. 4cq+3
+    // thread (tp, cq): tokens 2tp, 2tp+1 of the block, channels c0 .. c0+3
     bool overflow = false;
-    if (tid < 2 * K) {
-      const int tp = tid & 7, c0 = (tid >> 3) * 4;
+    if (prep_thread) {
       float al[2][4], qv[2][4], kv[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int t = t0 + 2 * tp + j;
-        if (t < T_) {
-          const long row = (b * T_ + t);
-          const float4 g4 = *reinterpret_cast<const float4*>(p.g_raw + (row * HV + hv) * K + c0);
-          const float gr[4] = {g4.x, g4.y, g4.z, g4.w};
+        const bool valid = t0 + 2 * tp + j < T_;  // padding: no decay, no write, no read
+        const float gr[4] = {pg[j].x, pg[j].y, pg[j].z, pg[j].w};
+        In<T>::unpack4(pq[j], qv[j]);
+        In<T>::unpack4(pk[j], kv[j]);
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            al[j][c] = exp_f(gate_log_decay(gr[c], bias ? bias[c0 + c] : 0.0f, rate, p.kind,
-                                            p.lower_bound));
-          In<T>::load4(qg, (row * H + h) * K + c0, qv[j]);
-          In<T>::load4(kg, (row * H + h) * K + c0, kv[j]);
-        } else {  // padding past the end: no decay, no write, no read
-#pragma unroll
-          for (int c = 0; c < 4; ++c) al[j][c] = 1.0f, qv[j][c] = 0.0f, kv[j][c] = 0.0f;
+        for (int c = 0; c < 4; ++c) {
+          const float a = exp_f(gate_log_decay_k<GK>(gr[c], bias4[c], rate, p.lower_bound));
+          al[j][c] = valid ? a : 1.0f;
+          qv[j][c] = valid ? qv[j][c] : 0.0f;
+          kv[j][c] = valid ? kv[j][c] : 0.0f;
         }
       }
-      float E0[4], E1[4], S0f[4], S1f[4], gam[4];
+      float E0[4], E1[4], S0f[4], S1f[4], ig[4];
+      uint16_t ke_h0[4], ke_l0[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        // inclusive product over the pairs of lanes 0..tp (8-lane segment)
+        // prefix products over the token pairs of an 8-lane segment (DPP row shifts)
         const float pair = al[0][c] * al[1][c];
-        float x = pair;
-#pragma unroll
-        for (int d = 1; d < 8; d <<= 1) {
-          const float y = __shfl_up(x, d, 8);
-          if (tp >= d) x *= y;
-        }
-        float ex = __shfl_up(x, 1, 8);
+        float x = pair, y;
+        y = row_shr<1>(x); if (tp >= 1) x *= y;
+        y = row_shr<2>(x); if (tp >= 2) x *= y;
+        y = row_shr<4>(x); if (tp >= 4) x *= y;
+        float ex = row_shr<1>(x);
         if (tp == 0) ex = 1.0f;
         E0[c] = ex * al[0][c];
         E1[c] = x;
-        gam[c] = __shfl(x, 7, 8);
-        // product over the pairs of lanes tp..7, then exclusive of lane tp
+        // suffix products, exclusive of the lane's own pair
         float z = pair;
-#pragma unroll
-        for (int d = 1; d < 8; d <<= 1) {
-          const float y = __shfl_down(z, d, 8);
-          if (tp + d < 8) z *= y;
-        }
-        float sx = __shfl_down(z, 1, 8);
+        y = row_shl<1>(z); if (tp < 7) z *= y;
+        y = row_shl<2>(z); if (tp < 6) z *= y;
+        y = row_shl<4>(z); if (tp < 4) z *= y;
+        float sx = row_shl<1>(z);
         if (tp == 7) sx = 1.0f;
         S1f[c] = sx;
         S0f[c] = al[1][c] * sx;
-        overflow |= !(gam[c] >= kGammaMin && gam[c] <= kGammaMax);
-      }
-      float ig[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ig[c] = __builtin_amdgcn_rcpf(gam[c]);
-      if (tp == 0) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sm.gam[c0 + c] = gam[c];
+        const float gam = x * sx;  // decay over the whole block
+        overflow |= !(gam >= kGammaMin && gam <= kGammaMax);
+        ig[c] = __builtin_amdgcn_rcpf(gam);
+        if (tp == 0) sm.gam[c0 + c] = gam;
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -325,29 +364,38 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
             sm.keT[(c0 + c) * 17 + t] = ke[c];
           }
         } else {
-          uint16_t h4[4], l4[4];
-          auto put = [&](uint16_t* dh, uint16_t* dl, const float* x) {
+          auto put = [&](uint16_t* dh, uint16_t* dl, const float* x, uint16_t* h4, uint16_t* l4) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) split_bf16(x[c], h4[c], l4[c]);
             *reinterpret_cast<uint2*>(dh + t * LD + c0) = uint2{pack2(h4[0], h4[1]), pack2(h4[2], h4[3])};
-            if (dl)
-              *reinterpret_cast<uint2*>(dl + t * LD + c0) = uint2{pack2(l4[0], l4[1]), pack2(l4[2], l4[3])};
+            *reinterpret_cast<uint2*>(dl + t * LD + c0) = uint2{pack2(l4[0], l4[1]), pack2(l4[2], l4[3])};
           };
-          put(sm.qr_hi, sm.qr_lo, qr);
-          put(sm.qh_hi, sm.qh_lo, qh);
-          put(sm.kr_hi, sm.kr_lo, kr);
-          put(sm.kh_hi, sm.kh_lo, kh);
-          put(sm.ke_hi, sm.ke_lo, ke);
+          uint16_t h4[4], l4[4];
+          put(sm.qr_hi, sm.qr_lo, qr, h4, l4);
+          put(sm.qh_hi, sm.qh_lo, qh, h4, l4);
+          put(sm.kr_hi, sm.kr_lo, kr, h4, l4);
+          put(sm.kh_hi, sm.kh_lo, kh, h4, l4);
+          put(sm.ke_hi, sm.ke_lo, ke, h4, l4);
+          // (k Suf)^T: the lane's two tokens are adjacent, one 32-bit store per channel
+          if (j == 0) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {  // h4 / l4 hold the split of ke
-            sm.keT[(c0 + c) * kCat + t] = h4[c];
-            sm.keT[(c0 + c) * kCat + 16 + t] = l4[c];
+            for (int c = 0; c < 4; ++c) ke_h0[c] = h4[c], ke_l0[c] = l4[c];
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              *reinterpret_cast<uint32_t*>(sm.keT + (c0 + c) * kCat + t - 1) = pack2(ke_h0[c], h4[c]);
+              *reinterpret_cast<uint32_t*>(sm.keT + (c0 + c) * kCat + 16 + t - 1) = pack2(ke_l0[c], l4[c]);
+            }
           }
         }
       }
     }
-    if (tid < kTok) sm.beta[tid] = (t0 + tid < T_) ? p.beta[(b * T_ + t0 + tid) * HV + hv] : 0.0f;
-    const int fallback = __syncthreads_or(overflow ? 1 : 0);
+    if (tid < kTok) sm.beta[tid] = pbeta;
+    const bool ov_wave = __any(overflow);
+    if (lane == 0) sm.flag[w] = ov_wave ? 1 : 0;
+    if (t0 + kTok < T_) fetch(t0 + kTok);  // next block's inputs travel while this one computes
+    __syncthreads();
+    const int fallback = sm.flag[0] | sm.flag[1] | sm.flag[2] | sm.flag[3];
 
     if (fallback) {
       // ---------------- token-by-token recurrence for this block (exact, slow)
@@ -364,8 +412,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int c = 16 * kb + 4 * (lane >> 4) + r;
-            const float a = exp_f(gate_log_decay(p.g_raw[(row * HV + hv) * K + c],
-                                                 bias ? bias[c] : 0.0f, rate, p.kind, p.lower_bound));
+            const float a = exp_f(gate_log_decay_k<GK>(p.g_raw[(row * HV + hv) * K + c],
+                                                       bias ? bias[c] : 0.0f, rate, p.lower_bound));
             kk[i][r] = In<T>::at(kg, (row * H + h) * K + c);
             qq[i][r] = In<T>::at(qg, (row * H + h) * K + c);
             sacc[i][r] *= a;
@@ -410,14 +458,15 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
         }
         __syncthreads();
       }
+      if (t0 + kTok < T_) fetch_v(t0 + kTok);
       write_state_operand();
       __syncthreads();
       continue;
     }
 
-    // ------------------------------------------------- B: A, R, K_hat S, Q_hat S
+    // -------------------------------------------------------------- B
+    // wave 0: A;  wave 1: R, then (I + R)^{-1};  waves 2..: K_hat S, Q_hat S, Ebar
     f32x4 qs = {0.f, 0.f, 0.f, 0.f};
-    const int cbw = w - 2;  // value column block of waves 2, 3
     if (w == 0) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (F32) mma_f32<K>(acc, sm.qr, LD, sm.ke, LD, lane);
@@ -444,9 +493,55 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * (lane >> 4) + r;
-        sm.r[i * 17 + j] = j < i ? sm.beta[i] * acc[r] : 0.0f;
+        sm.r[i * kRS + j] = j < i ? sm.beta[i] * acc[r] : 0.0f;
       }
-    } else if (cbw < NCB) {
+      // The same wave reads R back: LDS requests of one wave complete in
+      // order; the fences keep the compiler from reordering around them.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (lane < 16) {
+        // (I + R)^{-1}, column c = lane, by forward substitution in fp32:
+        // X[i] = delta_ic - sum_{m<i} R[i][m] X[m], four partial sums per row
+        const int c = lane;
+        // all 40 row segments of the strict lower triangle are read up front
+        // (broadcast reads), so LDS latency is paid once, not per row
+        float4 Rr[40];
+        {
+          int n = 0;
+#pragma unroll
+          for (int i = 1; i < kTok; ++i)
+#pragma unroll
+            for (int m4 = 0; m4 < i; m4 += 4) Rr[n++] = *reinterpret_cast<const float4*>(&sm.r[i * kRS + m4]);
+        }
+        float X[kTok];
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < kTok; ++i) {
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m4 = 0; m4 < i; m4 += 4) {
+            const float4 rr = Rr[n++];
+            const float rv[4] = {rr.x, rr.y, rr.z, rr.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (m4 + u < i) part[u] += rv[u] * X[m4 + u];
+          }
+          X[i] = ((i == c) ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
+        }
+#pragma unroll
+        for (int i = 0; i < kTok; ++i) {
+          if constexpr (F32) {
+            sm.akk[i * 17 + c] = X[i];
+          } else {
+            uint16_t hi, lo;
+            split_bf16(X[i], hi, lo);
+            sm.akk[i * kCat + c] = hi;
+            sm.akk[i * kCat + 16 + c] = lo;
+          }
+        }
+      }
+    } else if (ebar_wave) {
       f32x4 pk = {0.f, 0.f, 0.f, 0.f};
       if constexpr (F32) {
         mma_f32<K>(pk, sm.kh, LD, sm.st + cbw * 16 * LD, LD, lane);
@@ -461,8 +556,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * (lane >> 4) + r;
-        const float vv = (t0 + t < T_) ? In<T>::at(vg, ((b * T_ + t0 + t) * HV + hv) * V + v0 + vcol) : 0.0f;
-        const float e = sm.beta[t] * (vv - pk[r]);
+        const float e = sm.beta[t] * (In<T>::widen(pv[r]) - pk[r]);
         if constexpr (F32) {
           sm.ebT[vcol * 17 + t] = e;
         } else {
@@ -472,60 +566,41 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
           sm.ebT[vcol * kCat + 16 + t] = lo;
         }
       }
+      if (t0 + kTok < T_) fetch_v(t0 + kTok);
     }
     __syncthreads();
 
-    // ------------------------------------------- B2: (I + R)^{-1}, fp32 substitution
-    if (w == 1 && lane < 16) {
-      const int c = lane;
-      float X[kTok];
-#pragma unroll
-      for (int i = 0; i < kTok; ++i) {
-        float s = (i == c) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int m = 0; m < i; ++m) s -= sm.r[i * 17 + m] * X[m];
-        X[i] = s;
-      }
-#pragma unroll
-      for (int i = 0; i < kTok; ++i) {
-        if constexpr (F32) {
-          sm.akk[i * 17 + c] = X[i];
-        } else {
-          uint16_t hi, lo;
-          split_bf16(X[i], hi, lo);
-          sm.akk[i * kCat + c] = hi;
-          sm.akk[i * kCat + 16 + c] = lo;
-        }
-      }
-    }
-    __syncthreads();
-
-    // ------------------------------------------------------- C: U = (I+R)^-1 Ebar
-    if (w >= 2 && cbw < NCB) {
+    // -------------------------------------------------------------- D
+    // Every wave owns one value column block (cb = w % NCB): it resolves
+    // U = (I + R)^{-1} Ebar for that block itself (a private copy, so no
+    // further barrier), then waves 2.. form the outputs and every wave updates
+    // its own state blocks.
+    const int cbo = w % NCB;
+    {
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (F32) mma_f32<kTok>(u, sm.akk, 17, sm.ebT + cbw * 16 * 17, 17, lane);
-      else mma_tok_bf16(u, sm.akk, sm.ebT + cbw * 16 * kCat, lane);
-      const int vcol = 16 * cbw + (lane & 15);
+      if constexpr (F32) mma_f32<kTok>(u, sm.akk, 17, sm.ebT + cbo * 16 * 17, 17, lane);
+      else mma_tok_bf16(u, sm.akk, sm.ebT + cbo * 16 * kCat, lane);
+      const int vl = lane & 15;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 4 * (lane >> 4) + r;
         if constexpr (F32) {
-          sm.uT[vcol * 17 + t] = u[r];
+          sm.uT[w][vl * 17 + t] = u[r];
         } else {
           uint16_t hi, lo;
           split_bf16(u[r], hi, lo);
-          sm.uT[vcol * kCat + t] = hi;
-          sm.uT[vcol * kCat + 16 + t] = lo;
+          sm.uT[w][vl * kCat + t] = hi;
+          sm.uT[w][vl * kCat + 16 + t] = lo;
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __syncthreads();
-
-    // ------------------------------------------- D: outputs and the state update
-    if (w >= 2 && cbw < NCB) {
+    if (ebar_wave) {
       f32x4 ov = qs * scale;
-      if constexpr (F32) mma_f32<kTok>(ov, sm.aqk, 17, sm.uT + cbw * 16 * 17, 17, lane);
-      else mma_tok_bf16(ov, sm.aqk, sm.uT + cbw * 16 * kCat, lane);
+      if constexpr (F32) mma_f32<kTok>(ov, sm.aqk, 17, sm.uT[w], 17, lane);
+      else mma_tok_bf16(ov, sm.aqk, sm.uT[w], lane);
       const int vcol = 16 * cbw + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -537,12 +612,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
     for (int i = 0; i < BPW; ++i) {
       const int blk = w + 4 * i;
       if (blk >= NBLK) continue;
-      const int kb = blk / NCB, cb = blk % NCB;
+      const int kb = blk / NCB;
       f32x4 acc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = sacc[i][r] * sm.gam[16 * kb + 4 * (lane >> 4) + r];
-      if constexpr (F32) mma_f32<kTok>(acc, sm.keT + 16 * kb * 17, 17, sm.uT + cb * 16 * 17, 17, lane);
-      else mma_tok_bf16(acc, sm.keT + 16 * kb * kCat, sm.uT + cb * 16 * kCat, lane);
+      if constexpr (F32) mma_f32<kTok>(acc, sm.keT + 16 * kb * 17, 17, sm.uT[w], 17, lane);
+      else mma_tok_bf16(acc, sm.keT + 16 * kb * kCat, sm.uT[w], lane);
       sacc[i] = acc;
     }
     write_state_operand();
@@ -564,7 +639,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   }
 }
 
-template <int K, typename T>
+template <int K, typename T, int GK>
 static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   constexpr int BV = K < 32 ? K : 32;
   constexpr int NVT = K / BV;
@@ -576,14 +651,14 @@ static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   if (lds < 84 * 1024) lds = 84 * 1024;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int nheads = p.B * p.HV;
   const long blocks = (long)((nheads + 7) / 8) * 8 * NVT;
-  hipLaunchKernelGGL((chunk_fwd_kernel<K, T>), dim3((unsigned)blocks), dim3(256), lds, stream, p);
+  hipLaunchKernelGGL((chunk_fwd_kernel<K, T, GK>), dim3((unsigned)blocks), dim3(256), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -592,12 +667,20 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
                         float lower_bound, const float* S0, float* o, float* S_out, int B, int T,
                         int H, int HV, int K, hipStream_t stream) {
   ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, B, T, H, HV, kind, lower_bound};
-#define KDA_CHUNK_CASE(KK)                                                  \
-  if (K == KK)                                                              \
-    return bf16 ? launch_chunk_kt<KK, uint16_t>(p, stream)                  \
-                : launch_chunk_kt<KK, float>(p, stream);
+#define KDA_CHUNK_GATE(KK, TT)                                                   \
+  switch (kind) {                                                                \
+    case KDA_GATE_SAFE: return launch_chunk_kt<KK, TT, KDA_GATE_SAFE>(p, stream);         \
+    case KDA_GATE_STANDARD: return launch_chunk_kt<KK, TT, KDA_GATE_STANDARD>(p, stream); \
+    default: return launch_chunk_kt<KK, TT, KDA_GATE_NONE>(p, stream);                    \
+  }
+#define KDA_CHUNK_CASE(KK)                                  \
+  if (K == KK) {                                            \
+    if (bf16) { KDA_CHUNK_GATE(KK, uint16_t) }              \
+    else { KDA_CHUNK_GATE(KK, float) }                      \
+  }
   KDA_CHUNK_CASE(16) KDA_CHUNK_CASE(32) KDA_CHUNK_CASE(64) KDA_CHUNK_CASE(128)
 #undef KDA_CHUNK_CASE
+#undef KDA_CHUNK_GATE
   return hipErrorInvalidValue;
 }
 

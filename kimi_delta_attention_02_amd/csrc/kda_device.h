@@ -61,6 +61,32 @@ __device__ __forceinline__ float gate_log_decay(float graw, float bias, float ra
   return graw;
 }
 
+// DPP lane shifts inside rows of 16 lanes (lanes whose source falls outside
+// the row keep 0); VALU-speed alternatives to LDS-routed shuffles.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {  // lane p reads lane p - N
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x110 + N, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {  // lane p reads lane p + N
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               0x100 + N, 0xF, 0xF, false));
+}
+
+// The same gate with its kind fixed at compile time (no branch per element).
+template <int GK>
+__device__ __forceinline__ float gate_log_decay_k(float graw, float bias, float rate, float L) {
+  if constexpr (GK == KDA_GATE_SAFE) {
+    const float z = rate * (graw + bias);
+    return L * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+  } else if constexpr (GK == KDA_GATE_STANDARD) {
+    return -rate * softplus_f(graw + bias);
+  } else {
+    return graw;
+  }
+}
+
 // ------------------------------------------------------------ load helpers
 
 template <typename T>
@@ -68,6 +94,16 @@ struct In;  // element type of q / k / v
 
 template <>
 struct In<float> {
+  typedef float4 Raw4;  // four elements as loaded, before widening
+  typedef float Raw1;
+  static __device__ __forceinline__ Raw4 raw4(const float* p, long i) {
+    return *reinterpret_cast<const float4*>(p + i);
+  }
+  static __device__ __forceinline__ void unpack4(Raw4 v, float out[4]) {
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+  static __device__ __forceinline__ float widen(Raw1 v) { return v; }
+  static __device__ __forceinline__ Raw1 zero1() { return 0.0f; }
   static __device__ __forceinline__ float at(const float* p, long i) { return p[i]; }
   // four consecutive elements
   static __device__ __forceinline__ void load4(const float* p, long i, float out[4]) {
@@ -78,6 +114,19 @@ struct In<float> {
 
 template <>
 struct In<uint16_t> {  // bfloat16 bits
+  typedef uint2 Raw4;
+  typedef uint16_t Raw1;
+  static __device__ __forceinline__ Raw4 raw4(const uint16_t* p, long i) {
+    return *reinterpret_cast<const uint2*>(p + i);
+  }
+  static __device__ __forceinline__ void unpack4(Raw4 v, float out[4]) {
+    out[0] = __uint_as_float(v.x << 16);
+    out[1] = __uint_as_float(v.x & 0xffff0000u);
+    out[2] = __uint_as_float(v.y << 16);
+    out[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ float widen(Raw1 v) { return bf16_bits_to_f32(v); }
+  static __device__ __forceinline__ Raw1 zero1() { return 0; }
   static __device__ __forceinline__ float at(const uint16_t* p, long i) {
     return bf16_bits_to_f32(p[i]);
   }
