@@ -7,29 +7,33 @@
 // channel), gamma = E_{n-1} and Suf_j = prod_{m>j} alpha_m = gamma / E_j:
 //
 //   temporary errors   Ebar_i = beta_i (v_i - (k_i * E_i) . S)
-//   coupling           R_ij   = beta_i sum_c k_ic k_jc E_ic / E_jc        (j < i)
+//   coupling           R_ij   = beta_i sum_c (k_ic E_ic) (k_jc / E_jc)    (j < i)
 //   resolved errors    U      = (I + R)^{-1} Ebar        (causal triangular solve)
 //   outputs            O_i    = s (q_i * E_i) . S + sum_{j<=i} A_ij U_j,
-//                      A_ij   = s sum_c q_ic k_jc E_ic / E_jc             (j <= i)
+//                      A_ij   = s sum_c (q_ic E_ic) (k_jc / E_jc)         (j <= i)
 //   block-end state    S'     = diag(gamma) S + (k * Suf)^T U
 //
-// with s = 1/sqrt(K).  The ratio E_i / E_j is factored as (x_i E_i / gamma) .
-// (y_j Suf_j): both factors stay finite as long as gamma >= 2^-100 in every
-// channel (at most 69 nats of decay inside 16 tokens; the safe gate with
-// lower bound -5 never exceeds 80 nats, and real data far less).  A block
-// that breaks the bound is run token by token instead (same recurrence, no
-// factorisation), so every input is handled exactly.
+// with s = 1/sqrt(K).  Every factor is bounded: E and Suf lie in [gamma, 1]
+// and k / E in [|k|, |k| / gamma], finite as long as gamma >= 2^-100 in every
+// channel (69 nats of decay inside 16 tokens; the safe gate with lower bound
+// -5 stays under 80 nats, and real data far less).  A block that breaks the
+// bound is run token by token instead (the recurrence itself, no
+// factorisation), so every input is handled exactly.  Across blocks the state
+// carries the coupling between earlier and later tokens, which makes the
+// 16-token blocks the diagonal blocks of the chunk's triangular system.
 //
-// Schedule.  One workgroup (4 wavefronts) owns one (sequence b, value head hv,
-// 32-wide value tile) and walks the sequence in 16-token blocks, keeping its
-// K x 32 slice of the fp32 state in registers (MFMA accumulator layout) for
-// the whole sequence.  The four value tiles of one head are placed on the same
-// XCD so that their shared q, k, g_raw reads hit that XCD's L2.  Per block:
-//   prep   all threads: gate, cumulative products, scaled operands -> LDS
-//   B      wave 0: A (MFMA); wave 1: R (MFMA); waves 2..: K_hat S, Q_hat S, Ebar
-//   B2     wave 1: (I + R)^{-1} by forward substitution (fp32)
-//   C      waves 2..: U = (I + R)^{-1} Ebar
-//   D      waves 2..: O;  all waves: state update of their own state blocks
+// Schedule.  One workgroup owns one (sequence b, value head hv, 32-wide value
+// tile); the four value tiles of a head share blockIdx % 8 and so an XCD (and
+// its L2, which serves their common q, k, g_raw reads).  Its eight wavefronts
+// form a three-stage pipeline over 16-token blocks, one barrier per step:
+//   waves 0-3  prep of block n+2: gate, cumulative products, scaled operands,
+//              with the block's HBM inputs prefetched into registers a step ahead
+//   wave 4     A for block n+1 (MFMA)
+//   wave 5     R for block n+1 (MFMA), then (I + R)^{-1} by fp32 substitution
+//   waves 6-7  the state chain of block n, one 16-wide value column block each:
+//              K_hat S, Q_hat S, Ebar, U, O and the state update, with that
+//              column block of the fp32 state held in registers for the whole
+//              sequence (no other wave touches it, so the chain needs no barrier)
 // bf16 inputs use bf16 MFMA with fp32 accumulation.  Every operand of these
 // products is derived (scaled by decay factors, the state, or a solve result),
 // and a single bf16 rounding of them costs far more than the 1e-2 error budget
@@ -59,46 +63,61 @@ struct ChunkParams {
   float lower_bound;
 };
 
-constexpr int kTok = 16;     // tokens per block
-constexpr int kCat = 40;     // row stride of [hi t0..15 | lo t0..15] operands (+8 pad)
-constexpr int kRS = 20;      // row stride of the fp32 R tile (16-byte rows, conflict-free stores)
+constexpr int kTok = 16;      // tokens per block
+constexpr int kCat = 40;      // row stride of [hi t0..15 | lo t0..15] operands (+8 pad)
+constexpr int kRS = 20;       // row stride of the fp32 R tile (16-byte rows, conflict-free stores)
+constexpr int kThreads = 512;  // eight wavefronts
+constexpr int kPrepWaves = 4, kAqkWave = 4, kInvWave = 5, kChainWave0 = 6;
 constexpr float kGammaMin = 7.888609052210118e-31f;  // 2^-100
 constexpr float kGammaMax = 1.2676506002282294e30f;  // 2^100 (only a positive log-decay can get here)
 
 // ------------------------------------------------------------------ LDS
-
-template <int K, int BV>
-struct SmemBF16 {
-  static constexpr int LD = K + 8;  // row stride of [16][K] and [BV][K] operands
-  uint16_t qr_hi[kTok * LD], qr_lo[kTok * LD];  // q E / gamma      rows of A
-  uint16_t qh_hi[kTok * LD], qh_lo[kTok * LD];  // q E              Q_hat S
-  uint16_t kr_hi[kTok * LD], kr_lo[kTok * LD];  // k E / gamma      rows of R
-  uint16_t kh_hi[kTok * LD], kh_lo[kTok * LD];  // k E              K_hat S
-  uint16_t ke_hi[kTok * LD], ke_lo[kTok * LD];  // k Suf            columns of A and R
-  uint16_t keT[K * kCat];                       // (k Suf)^T  [c][hi t | lo t]
-  uint16_t st_hi[BV * LD], st_lo[BV * LD];      // S^T        [v][c]
-  uint16_t aqk[kTok * kCat];                    // A          [i][hi j | lo j]
-  uint16_t akk[kTok * kCat];                    // (I+R)^-1   [i][hi j | lo j]
-  uint16_t ebT[BV * kCat];                      // Ebar^T     [v][hi t | lo t]
-  uint16_t uT[4][kTok * kCat];                  // U^T per wave, own column block [v][hi t | lo t]
-  float r[kTok * kRS > (K / 16) * BV ? kTok * kRS : (K / 16) * BV];
-  float gam[K];
-  float beta[kTok];
-  int flag[4];
+// ROWS x K operand with the key axis contiguous (bf16: hi and lo words).
+template <bool F32, int ROWS, int K>
+struct alignas(16) RowOp;
+template <int ROWS, int K>
+struct alignas(16) RowOp<false, ROWS, K> {
+  static constexpr int LD = K + 8;
+  uint16_t hi[ROWS * LD], lo[ROWS * LD];
+};
+template <int ROWS, int K>
+struct alignas(16) RowOp<true, ROWS, K> {
+  static constexpr int LD = K + 1;
+  float f[ROWS * LD];
 };
 
-template <int K, int BV>
-struct SmemF32 {
-  static constexpr int LD = K + 1;
-  float qr[kTok * LD], qh[kTok * LD], kr[kTok * LD], kh[kTok * LD], ke[kTok * LD];
-  float keT[K * 17];  // [c][t]
-  float st[BV * LD];  // [v][c]
-  float aqk[kTok * 17], akk[kTok * 17];
-  float ebT[BV * 17], uT[4][kTok * 17];
-  float r[kTok * kRS > (K / 16) * BV ? kTok * kRS : (K / 16) * BV];
-  float gam[K];
+// ROWS x 16-token operand with the token axis contiguous: bf16 rows are
+// [hi t0..15 | lo t0..15].
+template <bool F32, int ROWS>
+struct alignas(16) TokOp;
+template <int ROWS>
+struct alignas(16) TokOp<false, ROWS> {
+  uint16_t c[ROWS * kCat];
+};
+template <int ROWS>
+struct alignas(16) TokOp<true, ROWS> {
+  float c[ROWS * 17 + 3];
+};
+
+// Operands of one 16-token block, written by the prep stage.
+template <bool F32, int K>
+struct alignas(16) BlockOps {
+  RowOp<F32, kTok, K> qh, kh, ki;  // q E, k E, k / E  (rows = tokens)
+  TokOp<F32, K> keT;               // (k Suf)^T        (rows = key channels)
+  float gam[K];                    // gamma per key channel
   float beta[kTok];
-  int flag[4];
+  int flag[4];                     // per prep wave: a channel broke the gamma bound
+};
+
+template <bool F32, int K, int BV>
+struct alignas(16) Smem {
+  BlockOps<F32, K> blk[3];
+  TokOp<F32, kTok> aqk[2], akk[2];  // A and (I + R)^{-1} of the next two blocks
+  float r[kTok * kRS];
+  struct alignas(16) Chain {         // private to one chain wave
+    RowOp<F32, 16, K> st;            // S^T of its column block  [v][c]
+    TokOp<F32, 16> eb, u;            // Ebar^T, U^T              [v][t]
+  } chain[BV / 16];
 };
 
 // ------------------------------------------------------------ MFMA tiles
@@ -170,23 +189,105 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo_half, uint16_t hi_half) {
   return (uint32_t)lo_half | ((uint32_t)hi_half << 16);
 }
 
+// Retain factor exp(g) for the token-by-token path, kept out of line: that
+// rare path then does not raise the register allocation of the main one.
+template <int GK>
+__device__ __noinline__ float slow_path_alpha(float graw, float bias, float rate, float L) {
+  return exp_f(gate_log_decay_k<GK>(graw, bias, rate, L));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  // One wavefront's LDS requests complete in order; the fences keep the
+  // compiler from moving its LDS accesses across this point.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// four consecutive key-axis values of one row
+template <bool F32, int ROWS, int K>
+__device__ __forceinline__ void put4(RowOp<F32, ROWS, K>& op, int row, int c0, const float x[4]) {
+  constexpr int LD = RowOp<F32, ROWS, K>::LD;
+  if constexpr (F32) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) op.f[row * LD + c0 + c] = x[c];
+  } else {
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) split_bf16(x[c], h[c], l[c]);
+    *reinterpret_cast<uint2*>(op.hi + row * LD + c0) = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+    *reinterpret_cast<uint2*>(op.lo + row * LD + c0) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+  }
+}
+
+// one value at (row, token t)
+template <bool F32, int ROWS>
+__device__ __forceinline__ void put_tok(TokOp<F32, ROWS>& op, int row, int t, float x) {
+  if constexpr (F32) {
+    op.c[row * 17 + t] = x;
+  } else {
+    uint16_t h, l;
+    split_bf16(x, h, l);
+    op.c[row * kCat + t] = h;
+    op.c[row * kCat + 16 + t] = l;
+  }
+}
+
+// two adjacent tokens t (even) and t + 1 of one row
+template <bool F32, int ROWS>
+__device__ __forceinline__ void put_tok2(TokOp<F32, ROWS>& op, int row, int t, float x0, float x1) {
+  if constexpr (F32) {
+    op.c[row * 17 + t] = x0;
+    op.c[row * 17 + t + 1] = x1;
+  } else {
+    uint16_t h0, l0, h1, l1;
+    split_bf16(x0, h0, l0);
+    split_bf16(x1, h1, l1);
+    *reinterpret_cast<uint32_t*>(op.c + row * kCat + t) = pack2(h0, h1);
+    *reinterpret_cast<uint32_t*>(op.c + row * kCat + 16 + t) = pack2(l0, l1);
+  }
+}
+
+// acc += A[arow0 .. +16) x B[brow0 .. +16)^T over the key axis
+template <bool F32, int K, int RA, int RB>
+__device__ __forceinline__ void kprod(f32x4& acc, const RowOp<F32, RA, K>& A, int arow0,
+                                      const RowOp<F32, RB, K>& B, int brow0, int lane) {
+  constexpr int LD = RowOp<F32, RA, K>::LD;
+  if constexpr (F32)
+    mma_f32<K>(acc, A.f + arow0 * LD, LD, B.f + brow0 * LD, LD, lane);
+  else
+    mma_kappa_bf16<K, 3>(acc, A.hi + arow0 * LD, A.lo + arow0 * LD, B.hi + brow0 * LD,
+                         B.lo + brow0 * LD, LD, lane);
+}
+
+// acc += A[arow0 .. +16) (16 tokens) x B (16 tokens x 16, given by its columns)
+template <bool F32, int RA, int RB>
+__device__ __forceinline__ void tprod(f32x4& acc, const TokOp<F32, RA>& A, int arow0,
+                                      const TokOp<F32, RB>& B, int lane) {
+  if constexpr (F32)
+    mma_f32<kTok>(acc, A.c + arow0 * 17, 17, B.c, 17, lane);
+  else
+    mma_tok_bf16(acc, A.c + arow0 * kCat, B.c, lane);
+}
+
 // ----------------------------------------------------------------- kernel
 
 template <int K, typename T, int GK>
-__global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
+__global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int V = K;
   constexpr int BV = V < 32 ? V : 32;
   constexpr int NCB = BV / 16, NKB = K / 16, NVT = V / BV;
-  constexpr int NBLK = NKB * NCB;
-  constexpr int BPW = (NBLK + 3) / 4;
-  using Smem = typename std::conditional<F32, SmemF32<K, BV>, SmemBF16<K, BV>>::type;
-  constexpr int LD = Smem::LD;
+  using SM = Smem<F32, K, BV>;
+  using Ops = BlockOps<F32, K>;
+  typedef typename In<T>::Raw4 Raw4;
+  typedef typename In<T>::Raw1 Raw1;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T_ = p.T, HV = p.HV, H = p.H;
+  const int NT = (T_ + kTok - 1) / kTok;
 
   // workgroup -> (head, value tile): the NVT tiles of a head share blockIdx % 8
   const int nheads = p.B * HV;
@@ -204,436 +305,304 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkParams p) {
   const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
 
-  // ---- state slice: blocks blk = w + 4 i, (kb, cb) = (blk / NCB, blk % NCB)
-  f32x4 sacc[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int blk = w + 4 * i;
-    if (blk < NBLK && p.S0) {
-      const int kb = blk / NCB, cb = blk % NCB;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 16 * kb + 4 * (lane >> 4) + r;
-        sacc[i][r] = p.S0[((long)hd * K + c) * V + v0 + 16 * cb + (lane & 15)];
-      }
+  // Each role runs its own loop over the pipeline steps; every loop executes
+  // the same NT + 2 barriers, and registers are allocated per role.
+  if (w < kPrepWaves) {
+    // ---- prep threads: token pair tp (tokens 2tp, 2tp+1), key channels c0 .. c0+3
+    const bool prep_thread = tid < 2 * K;
+    const int tp = tid & 7, c0 = (tid >> 3) * 4;
+    float bias4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias && prep_thread) {
+  #pragma unroll
+      for (int c = 0; c < 4; ++c) bias4[c] = bias[c0 + c];
     }
-  }
-
-  // S^T operand for the next block's products with the state
-  auto write_state_operand = [&]() {
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int blk = w + 4 * i;
-      if (blk >= NBLK) continue;
-      const int kb = blk / NCB, cb = blk % NCB;
-      const int vcol = 16 * cb + (lane & 15), c0 = 16 * kb + 4 * (lane >> 4);
-      if constexpr (F32) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.st[vcol * LD + c0 + r] = sacc[i][r];
-      } else {
-        uint16_t hi[4], lo[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) split_bf16(sacc[i][r], hi[r], lo[r]);
-        *reinterpret_cast<uint2*>(sm.st_hi + vcol * LD + c0) = uint2{pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
-        *reinterpret_cast<uint2*>(sm.st_lo + vcol * LD + c0) = uint2{pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
-      }
-    }
-  };
-  write_state_operand();
-
-  // ---- inputs of the next block, prefetched into registers one block ahead
-  typedef typename In<T>::Raw4 Raw4;
-  typedef typename In<T>::Raw1 Raw1;
-  const int tp = tid & 7, c0 = (tid >> 3) * 4;  // prep thread: token pair, channel quad
-  const int cbw = w - 2;                        // waves 2.. own value column block cbw
-  const bool prep_thread = tid < 2 * K;
-  const bool ebar_wave = w >= 2 && cbw < NCB;
-  float bias4[4] = {0.f, 0.f, 0.f, 0.f};  // dt_bias of the prep thread's channels
-  if (bias && prep_thread) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) bias4[c] = bias[c0 + c];
-  }
-  float4 pg[2];
-  Raw4 pq[2], pk[2];
-  Raw1 pv[4];
-  float pbeta = 0.0f;
-  // Loads past the end of the sequence read the last token instead (always a
-  // valid address) and are replaced by padding values where they are used.
-  auto fetch = [&](int tb) {
-    if (prep_thread) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int t = min(tb + 2 * tp + j, T_ - 1);
-        const long row = b * T_ + t;
-        pg[j] = *reinterpret_cast<const float4*>(p.g_raw + (row * HV + hv) * K + c0);
-        pq[j] = In<T>::raw4(qg, (row * H + h) * K + c0);
-        pk[j] = In<T>::raw4(kg, (row * H + h) * K + c0);
-      }
-    }
-    if (tid < kTok) {
-      const float bt = p.beta[(b * T_ + min(tb + tid, T_ - 1)) * HV + hv];
-      pbeta = tb + tid < T_ ? bt : 0.0f;
-    }
-  };
-  auto fetch_v = [&](int tb) {
-    if (ebar_wave) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tb + 4 * (lane >> 4) + r;
-        const Raw1 x = vg[((b * T_ + min(t, T_ - 1)) * HV + hv) * V + v0 + 16 * cbw + (lane & 15)];
-        pv[r] = t < T_ ? x : In<T>::zero1();
-      }
-    }
-  };
-  if (T_ > 0) {
-    fetch(0);
-    fetch_v(0);
-  }
-
-  for (int t0 = 0; t0 < T_; t0 += kTok) {
-    // ------------------------------------------------------------ prep
-    // thread (tp, cq): tokens 2tp, 2tp+1 of the block, channels c0 .. c0+3
-    bool overflow = false;
-    if (prep_thread) {
-      float al[2][4], qv[2][4], kv[2][4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bool valid = t0 + 2 * tp + j < T_;  // padding: no decay, no write, no read
-        const float gr[4] = {pg[j].x, pg[j].y, pg[j].z, pg[j].w};
-        In<T>::unpack4(pq[j], qv[j]);
-        In<T>::unpack4(pk[j], kv[j]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float a = exp_f(gate_log_decay_k<GK>(gr[c], bias4[c], rate, p.lower_bound));
-          al[j][c] = valid ? a : 1.0f;
-          qv[j][c] = valid ? qv[j][c] : 0.0f;
-          kv[j][c] = valid ? kv[j][c] : 0.0f;
+    float4 pg[2];
+    Raw4 pq[2], pk[2];
+    float pbeta = 0.0f;
+    // Loads past the end of the sequence read the last token instead (always a
+    // valid address) and are replaced by padding values where they are used.
+    auto fetch = [&](int blk) {
+      const int tb = blk * kTok;
+      if (prep_thread) {
+  #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const long row = b * T_ + min(tb + 2 * tp + j, T_ - 1);
+          pg[j] = *reinterpret_cast<const float4*>(p.g_raw + (row * HV + hv) * K + c0);
+          pq[j] = In<T>::raw4(qg, (row * H + h) * K + c0);
+          pk[j] = In<T>::raw4(kg, (row * H + h) * K + c0);
         }
       }
-      float E0[4], E1[4], S0f[4], S1f[4], ig[4];
-      uint16_t ke_h0[4], ke_l0[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // prefix products over the token pairs of an 8-lane segment (DPP row shifts)
-        const float pair = al[0][c] * al[1][c];
-        float x = pair, y;
-        y = row_shr<1>(x); if (tp >= 1) x *= y;
-        y = row_shr<2>(x); if (tp >= 2) x *= y;
-        y = row_shr<4>(x); if (tp >= 4) x *= y;
-        float ex = row_shr<1>(x);
-        if (tp == 0) ex = 1.0f;
-        E0[c] = ex * al[0][c];
-        E1[c] = x;
-        // suffix products, exclusive of the lane's own pair
-        float z = pair;
-        y = row_shl<1>(z); if (tp < 7) z *= y;
-        y = row_shl<2>(z); if (tp < 6) z *= y;
-        y = row_shl<4>(z); if (tp < 4) z *= y;
-        float sx = row_shl<1>(z);
-        if (tp == 7) sx = 1.0f;
-        S1f[c] = sx;
-        S0f[c] = al[1][c] * sx;
-        const float gam = x * sx;  // decay over the whole block
-        overflow |= !(gam >= kGammaMin && gam <= kGammaMax);
-        ig[c] = __builtin_amdgcn_rcpf(gam);
-        if (tp == 0) sm.gam[c0 + c] = gam;
+      if (tid < kTok) {
+        const float bt = p.beta[(b * T_ + min(tb + tid, T_ - 1)) * HV + hv];
+        pbeta = tb + tid < T_ ? bt : 0.0f;
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int t = 2 * tp + j;
-        const float* E = j ? E1 : E0;
-        const float* Sf = j ? S1f : S0f;
-        float qr[4], qh[4], kr[4], kh[4], ke[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          qh[c] = qv[j][c] * E[c];
-          kh[c] = kv[j][c] * E[c];
-          qr[c] = qh[c] * ig[c];
-          kr[c] = kh[c] * ig[c];
-          ke[c] = kv[j][c] * Sf[c];
-        }
-        if constexpr (F32) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            sm.qr[t * LD + c0 + c] = qr[c];
-            sm.qh[t * LD + c0 + c] = qh[c];
-            sm.kr[t * LD + c0 + c] = kr[c];
-            sm.kh[t * LD + c0 + c] = kh[c];
-            sm.ke[t * LD + c0 + c] = ke[c];
-            sm.keT[(c0 + c) * 17 + t] = ke[c];
-          }
-        } else {
-          auto put = [&](uint16_t* dh, uint16_t* dl, const float* x, uint16_t* h4, uint16_t* l4) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) split_bf16(x[c], h4[c], l4[c]);
-            *reinterpret_cast<uint2*>(dh + t * LD + c0) = uint2{pack2(h4[0], h4[1]), pack2(h4[2], h4[3])};
-            *reinterpret_cast<uint2*>(dl + t * LD + c0) = uint2{pack2(l4[0], l4[1]), pack2(l4[2], l4[3])};
-          };
-          uint16_t h4[4], l4[4];
-          put(sm.qr_hi, sm.qr_lo, qr, h4, l4);
-          put(sm.qh_hi, sm.qh_lo, qh, h4, l4);
-          put(sm.kr_hi, sm.kr_lo, kr, h4, l4);
-          put(sm.kh_hi, sm.kh_lo, kh, h4, l4);
-          put(sm.ke_hi, sm.ke_lo, ke, h4, l4);
-          // (k Suf)^T: the lane's two tokens are adjacent, one 32-bit store per channel
-          if (j == 0) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) ke_h0[c] = h4[c], ke_l0[c] = l4[c];
-          } else {
-#pragma unroll
+    };
+    if (NT > 0) fetch(0);
+    for (int it = 0; it < NT + 2; ++it) {
+      if (it < NT) {
+        Ops& B = sm.blk[it % 3];
+        bool overflow = false;
+        if (prep_thread) {
+          const int t0 = it * kTok;
+          float al[2][4], qv[2][4], kv[2][4];
+  #pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const bool valid = t0 + 2 * tp + j < T_;  // padding: no decay, no write, no read
+            const float gr[4] = {pg[j].x, pg[j].y, pg[j].z, pg[j].w};
+            In<T>::unpack4(pq[j], qv[j]);
+            In<T>::unpack4(pk[j], kv[j]);
+  #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              *reinterpret_cast<uint32_t*>(sm.keT + (c0 + c) * kCat + t - 1) = pack2(ke_h0[c], h4[c]);
-              *reinterpret_cast<uint32_t*>(sm.keT + (c0 + c) * kCat + 16 + t - 1) = pack2(ke_l0[c], l4[c]);
+              const float a = exp_f(gate_log_decay_k<GK>(gr[c], bias4[c], rate, p.lower_bound));
+              al[j][c] = valid ? a : 1.0f;
+              qv[j][c] = valid ? qv[j][c] : 0.0f;
+              kv[j][c] = valid ? kv[j][c] : 0.0f;
+            }
+          }
+          if (tid < kTok) B.beta[tid] = pbeta;
+          if (it + 1 < NT) fetch(it + 1);  // the next block's inputs travel meanwhile
+          float E[2][4], Sf[2][4], ig[4];
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            // prefix products over the token pairs of an 8-lane segment (DPP row shifts)
+            const float pair = al[0][c] * al[1][c];
+            float x = pair, y;
+            y = row_shr<1>(x); if (tp >= 1) x *= y;
+            y = row_shr<2>(x); if (tp >= 2) x *= y;
+            y = row_shr<4>(x); if (tp >= 4) x *= y;
+            float ex = row_shr<1>(x);
+            if (tp == 0) ex = 1.0f;
+            E[0][c] = ex * al[0][c];
+            E[1][c] = x;
+            // suffix products, exclusive of the lane's own pair
+            float z = pair;
+            y = row_shl<1>(z); if (tp < 7) z *= y;
+            y = row_shl<2>(z); if (tp < 6) z *= y;
+            y = row_shl<4>(z); if (tp < 4) z *= y;
+            float sx = row_shl<1>(z);
+            if (tp == 7) sx = 1.0f;
+            Sf[1][c] = sx;
+            Sf[0][c] = al[1][c] * sx;
+            const float gam = x * sx;  // decay over the whole block
+            overflow |= !(gam >= kGammaMin && gam <= kGammaMax);
+            ig[c] = __builtin_amdgcn_rcpf(gam);
+            if (tp == 0) B.gam[c0 + c] = gam;
+          }
+          float ke[2][4];
+  #pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int t = 2 * tp + j;
+            float qh[4], kh[4], ki[4];
+  #pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              qh[c] = qv[j][c] * E[j][c];
+              kh[c] = kv[j][c] * E[j][c];
+              ke[j][c] = kv[j][c] * Sf[j][c];
+              ki[c] = ke[j][c] * ig[c];  // k / E = k Suf / gamma
+            }
+            put4(B.qh, t, c0, qh);
+            put4(B.kh, t, c0, kh);
+            put4(B.ki, t, c0, ki);
+          }
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) put_tok2(B.keT, c0 + c, 2 * tp, ke[0][c], ke[1][c]);
+        }
+        const bool ov = __any(overflow);
+        if (lane == 0) B.flag[w] = ov ? 1 : 0;
+      }
+      __syncthreads();
+    }
+  } else if (w == kAqkWave || w == kInvWave) {
+    for (int it = 0; it < NT + 2; ++it) {
+      const int ti = it - 1;
+      if (ti >= 0 && ti < NT) {
+        const Ops& B = sm.blk[ti % 3];
+        if (!(B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3])) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const int j = lane & 15;
+          if (w == kAqkWave) {
+            kprod(acc, B.qh, 0, B.ki, 0, lane);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 4 * (lane >> 4) + r;
+              put_tok(sm.aqk[ti & 1], i, j, j <= i ? scale * acc[r] : 0.0f);
+            }
+          } else {
+            kprod(acc, B.kh, 0, B.ki, 0, lane);
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 4 * (lane >> 4) + r;
+              sm.r[i * kRS + j] = j < i ? B.beta[i] * acc[r] : 0.0f;
+            }
+            wave_lds_sync();
+            if (lane < 16) {
+              // (I + R)^{-1}, column c = lane, by forward substitution in fp32:
+              // X[i] = delta_ic - sum_{m<i} R[i][m] X[m], four partial sums per row.
+              // Rows are read (as broadcast reads) in groups of four, one group
+              // ahead of the arithmetic, so LDS latency overlaps the FMAs.
+              const int c = lane;
+              float4 Rg[2][16];  // a group of rows 4g..4g+3 holds at most 15 row segments
+              auto load_group = [&](int g, float4* dst) {
+                int n = 0;
+  #pragma unroll
+                for (int i = 4 * g; i < 4 * g + 4; ++i)
+  #pragma unroll
+                  for (int m4 = 0; m4 < i; m4 += 4)
+                    dst[n++] = *reinterpret_cast<const float4*>(&sm.r[i * kRS + m4]);
+              };
+              load_group(0, Rg[0]);
+              float X[kTok];
+  #pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                if (g + 1 < 4) load_group(g + 1, Rg[(g + 1) & 1]);
+                int n = 0;
+  #pragma unroll
+                for (int i = 4 * g; i < 4 * g + 4; ++i) {
+                  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+                  for (int m4 = 0; m4 < i; m4 += 4) {
+                    const float4 rr = Rg[g & 1][n++];
+                    const float rv[4] = {rr.x, rr.y, rr.z, rr.w};
+  #pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                      if (m4 + u < i) part[u] += rv[u] * X[m4 + u];
+                  }
+                  X[i] = ((i == c) ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
+                }
+              }
+  #pragma unroll
+              for (int i = 0; i < kTok; ++i) put_tok(sm.akk[ti & 1], i, c, X[i]);
             }
           }
         }
       }
-    }
-    if (tid < kTok) sm.beta[tid] = pbeta;
-    const bool ov_wave = __any(overflow);
-    if (lane == 0) sm.flag[w] = ov_wave ? 1 : 0;
-    if (t0 + kTok < T_) fetch(t0 + kTok);  // next block's inputs travel while this one computes
-    __syncthreads();
-    const int fallback = sm.flag[0] | sm.flag[1] | sm.flag[2] | sm.flag[3];
-
-    if (fallback) {
-      // ---------------- token-by-token recurrence for this block (exact, slow)
-      for (int tt = 0; tt < kTok && t0 + tt < T_; ++tt) {
-        const long row = b * T_ + t0 + tt;
-        const float bt = sm.beta[tt];
-        float kk[BPW][4], qq[BPW][4];
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-          const int blk = w + 4 * i;
-          if (blk >= NBLK) continue;
-          const int kb = blk / NCB, cb = blk % NCB;
-          float part = 0.0f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int c = 16 * kb + 4 * (lane >> 4) + r;
-            const float a = exp_f(gate_log_decay_k<GK>(p.g_raw[(row * HV + hv) * K + c],
-                                                       bias ? bias[c] : 0.0f, rate, p.lower_bound));
-            kk[i][r] = In<T>::at(kg, (row * H + h) * K + c);
-            qq[i][r] = In<T>::at(qg, (row * H + h) * K + c);
-            sacc[i][r] *= a;
-            part += kk[i][r] * sacc[i][r];
-          }
-          part += __shfl_xor(part, 16);
-          part += __shfl_xor(part, 32);
-          if (lane < 16) sm.r[kb * BV + 16 * cb + lane] = part;
-        }
-        __syncthreads();
-        float opart[BPW];
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-          const int blk = w + 4 * i;
-          opart[i] = 0.0f;
-          if (blk >= NBLK) continue;
-          const int cb = blk % NCB, col = 16 * cb + (lane & 15);
-          float pr = 0.0f;
-          for (int kb2 = 0; kb2 < NKB; ++kb2) pr += sm.r[kb2 * BV + col];
-          const float rr = bt * (In<T>::at(vg, (row * HV + hv) * V + v0 + col) - pr);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sacc[i][r] += kk[i][r] * rr;
-            opart[i] += qq[i][r] * sacc[i][r];
-          }
-          opart[i] += __shfl_xor(opart[i], 16);
-          opart[i] += __shfl_xor(opart[i], 32);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < BPW; ++i) {
-          const int blk = w + 4 * i;
-          if (blk >= NBLK) continue;
-          const int kb = blk / NCB, cb = blk % NCB;
-          if (lane < 16) sm.r[kb * BV + 16 * cb + lane] = opart[i];
-        }
-        __syncthreads();
-        if (tid < BV) {
-          float ov = 0.0f;
-          for (int kb2 = 0; kb2 < NKB; ++kb2) ov += sm.r[kb2 * BV + tid];
-          p.o[(row * HV + hv) * V + v0 + tid] = scale * ov;
-        }
-        __syncthreads();
-      }
-      if (t0 + kTok < T_) fetch_v(t0 + kTok);
-      write_state_operand();
       __syncthreads();
-      continue;
     }
-
-    // -------------------------------------------------------------- B
-    // wave 0: A;  wave 1: R, then (I + R)^{-1};  waves 2..: K_hat S, Q_hat S, Ebar
-    f32x4 qs = {0.f, 0.f, 0.f, 0.f};
-    if (w == 0) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (F32) mma_f32<K>(acc, sm.qr, LD, sm.ke, LD, lane);
-      else mma_kappa_bf16<K, 3>(acc, sm.qr_hi, sm.qr_lo, sm.ke_hi, sm.ke_lo, LD, lane);
-      const int j = lane & 15;
-#pragma unroll
+  } else {
+    // ---- chain waves: value column block cb, state rows 16 kb + 4 (lane/16) + r
+    const int cb = w - kChainWave0;
+    const bool chain = cb >= 0 && cb < NCB;
+    const int vcol = v0 + 16 * cb + (lane & 15);
+    f32x4 sacc[NKB];
+    Raw1 pv[4];
+    auto fetch_v = [&](int blk) {
+  #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 4 * (lane >> 4) + r;
-        const float a = j <= i ? scale * acc[r] : 0.0f;
-        if constexpr (F32) {
-          sm.aqk[i * 17 + j] = a;
-        } else {
-          uint16_t hi, lo;
-          split_bf16(a, hi, lo);
-          sm.aqk[i * kCat + j] = hi;
-          sm.aqk[i * kCat + 16 + j] = lo;
+        const int t = blk * kTok + 4 * (lane >> 4) + r;
+        const Raw1 x = vg[((b * T_ + min(t, T_ - 1)) * HV + hv) * V + vcol];
+        pv[r] = t < T_ ? x : In<T>::zero1();
+      }
+    };
+    auto write_state_operand = [&](typename SM::Chain& C) {
+  #pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float x[4] = {sacc[kb][0], sacc[kb][1], sacc[kb][2], sacc[kb][3]};
+        put4(C.st, lane & 15, 16 * kb + 4 * (lane >> 4), x);
+      }
+    };
+    if (chain) {
+  #pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * kb + 4 * (lane >> 4) + r;
+          sacc[kb][r] = p.S0 ? p.S0[((long)hd * K + c) * V + vcol] : 0.0f;
         }
       }
-    } else if (w == 1) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (F32) mma_f32<K>(acc, sm.kr, LD, sm.ke, LD, lane);
-      else mma_kappa_bf16<K, 3>(acc, sm.kr_hi, sm.kr_lo, sm.ke_hi, sm.ke_lo, LD, lane);
-      const int j = lane & 15;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * (lane >> 4) + r;
-        sm.r[i * kRS + j] = j < i ? sm.beta[i] * acc[r] : 0.0f;
-      }
-      // The same wave reads R back: LDS requests of one wave complete in
-      // order; the fences keep the compiler from reordering around them.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (lane < 16) {
-        // (I + R)^{-1}, column c = lane, by forward substitution in fp32:
-        // X[i] = delta_ic - sum_{m<i} R[i][m] X[m], four partial sums per row
-        const int c = lane;
-        // all 40 row segments of the strict lower triangle are read up front
-        // (broadcast reads), so LDS latency is paid once, not per row
-        float4 Rr[40];
-        {
-          int n = 0;
-#pragma unroll
-          for (int i = 1; i < kTok; ++i)
-#pragma unroll
-            for (int m4 = 0; m4 < i; m4 += 4) Rr[n++] = *reinterpret_cast<const float4*>(&sm.r[i * kRS + m4]);
-        }
-        float X[kTok];
-        int n = 0;
-#pragma unroll
-        for (int i = 0; i < kTok; ++i) {
-          float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m4 = 0; m4 < i; m4 += 4) {
-            const float4 rr = Rr[n++];
-            const float rv[4] = {rr.x, rr.y, rr.z, rr.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (m4 + u < i) part[u] += rv[u] * X[m4 + u];
+      write_state_operand(sm.chain[cb]);
+      wave_lds_sync();
+      if (NT > 0) fetch_v(0);
+    }
+    for (int it = 0; it < NT + 2; ++it) {
+      const int tc = it - 2;
+      if (tc >= 0 && chain) {
+        const Ops& B = sm.blk[tc % 3];
+        typename SM::Chain& C = sm.chain[cb];
+        const int t0 = tc * kTok;
+        if (B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3]) {
+          // ---- token-by-token recurrence (exact, slow path); the wave owns all
+          // key rows of its columns, so both reductions stay in the wavefront
+          for (int tt = 0; tt < kTok && t0 + tt < T_; ++tt) {
+            const long row = b * T_ + t0 + tt;
+            const float* grow = p.g_raw + (row * HV + hv) * K;
+            const T* krow = kg + (row * H + h) * K;
+            const T* qrow = qg + (row * H + h) * K;
+            float part = 0.0f;
+  #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int c = 16 * kb + 4 * (lane >> 4) + r;
+                sacc[kb][r] *= slow_path_alpha<GK>(grow[c], bias ? bias[c] : 0.0f, rate, p.lower_bound);
+                part += In<T>::at(krow, c) * sacc[kb][r];
+              }
+              // one key block at a time: keeps this rare path's registers bounded
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            const float rr = p.beta[row * HV + hv] * (In<T>::at(vg, (row * HV + hv) * V + vcol) - part);
+            float op = 0.0f;
+  #pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int c = 16 * kb + 4 * (lane >> 4) + r;
+                sacc[kb][r] += In<T>::at(krow, c) * rr;
+                op += In<T>::at(qrow, c) * sacc[kb][r];
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            op += __shfl_xor(op, 16);
+            op += __shfl_xor(op, 32);
+            if (lane < 16) p.o[(row * HV + hv) * V + vcol] = scale * op;
           }
-          X[i] = ((i == c) ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
-        }
-#pragma unroll
-        for (int i = 0; i < kTok; ++i) {
-          if constexpr (F32) {
-            sm.akk[i * 17 + c] = X[i];
-          } else {
-            uint16_t hi, lo;
-            split_bf16(X[i], hi, lo);
-            sm.akk[i * kCat + c] = hi;
-            sm.akk[i * kCat + 16 + c] = lo;
+          if (tc + 1 < NT) fetch_v(tc + 1);
+        } else {
+          f32x4 pk = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+          kprod(pk, B.kh, 0, C.st, 0, lane);
+          kprod(qs, B.qh, 0, C.st, 0, lane);
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 4 * (lane >> 4) + r;
+            put_tok(C.eb, lane & 15, t, B.beta[t] * (In<T>::widen(pv[r]) - pk[r]));
+          }
+          if (tc + 1 < NT) fetch_v(tc + 1);
+          wave_lds_sync();
+          f32x4 u = {0.f, 0.f, 0.f, 0.f};
+          tprod(u, sm.akk[tc & 1], 0, C.eb, lane);
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) put_tok(C.u, lane & 15, 4 * (lane >> 4) + r, u[r]);
+          wave_lds_sync();
+          f32x4 ov = qs * scale;
+          tprod(ov, sm.aqk[tc & 1], 0, C.u, lane);
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * (lane >> 4) + r;
+            if (t < T_) p.o[((b * T_ + t) * HV + hv) * V + vcol] = ov[r];
+          }
+  #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            f32x4 acc;
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = sacc[kb][r] * B.gam[16 * kb + 4 * (lane >> 4) + r];
+            tprod(acc, B.keT, 16 * kb, C.u, lane);
+            sacc[kb] = acc;
           }
         }
+        write_state_operand(C);
+        wave_lds_sync();
       }
-    } else if (ebar_wave) {
-      f32x4 pk = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (F32) {
-        mma_f32<K>(pk, sm.kh, LD, sm.st + cbw * 16 * LD, LD, lane);
-        mma_f32<K>(qs, sm.qh, LD, sm.st + cbw * 16 * LD, LD, lane);
-      } else {
-        mma_kappa_bf16<K, 3>(pk, sm.kh_hi, sm.kh_lo, sm.st_hi + cbw * 16 * LD,
-                             sm.st_lo + cbw * 16 * LD, LD, lane);
-        mma_kappa_bf16<K, 3>(qs, sm.qh_hi, sm.qh_lo, sm.st_hi + cbw * 16 * LD,
-                             sm.st_lo + cbw * 16 * LD, LD, lane);
-      }
-      const int vcol = 16 * cbw + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * (lane >> 4) + r;
-        const float e = sm.beta[t] * (In<T>::widen(pv[r]) - pk[r]);
-        if constexpr (F32) {
-          sm.ebT[vcol * 17 + t] = e;
-        } else {
-          uint16_t hi, lo;
-          split_bf16(e, hi, lo);
-          sm.ebT[vcol * kCat + t] = hi;
-          sm.ebT[vcol * kCat + 16 + t] = lo;
+      __syncthreads();
+    }
+    if (chain && p.S_out) {
+  #pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * kb + 4 * (lane >> 4) + r;
+          p.S_out[((long)hd * K + c) * V + vcol] = sacc[kb][r];
         }
-      }
-      if (t0 + kTok < T_) fetch_v(t0 + kTok);
-    }
-    __syncthreads();
-
-    // -------------------------------------------------------------- D
-    // Every wave owns one value column block (cb = w % NCB): it resolves
-    // U = (I + R)^{-1} Ebar for that block itself (a private copy, so no
-    // further barrier), then waves 2.. form the outputs and every wave updates
-    // its own state blocks.
-    const int cbo = w % NCB;
-    {
-      f32x4 u = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (F32) mma_f32<kTok>(u, sm.akk, 17, sm.ebT + cbo * 16 * 17, 17, lane);
-      else mma_tok_bf16(u, sm.akk, sm.ebT + cbo * 16 * kCat, lane);
-      const int vl = lane & 15;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * (lane >> 4) + r;
-        if constexpr (F32) {
-          sm.uT[w][vl * 17 + t] = u[r];
-        } else {
-          uint16_t hi, lo;
-          split_bf16(u[r], hi, lo);
-          sm.uT[w][vl * kCat + t] = hi;
-          sm.uT[w][vl * kCat + 16 + t] = lo;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    if (ebar_wave) {
-      f32x4 ov = qs * scale;
-      if constexpr (F32) mma_f32<kTok>(ov, sm.aqk, 17, sm.uT[w], 17, lane);
-      else mma_tok_bf16(ov, sm.aqk, sm.uT[w], lane);
-      const int vcol = 16 * cbw + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * (lane >> 4) + r;
-        if (t0 + t < T_) p.o[((b * T_ + t0 + t) * HV + hv) * V + v0 + vcol] = ov[r];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int blk = w + 4 * i;
-      if (blk >= NBLK) continue;
-      const int kb = blk / NCB;
-      f32x4 acc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = sacc[i][r] * sm.gam[16 * kb + 4 * (lane >> 4) + r];
-      if constexpr (F32) mma_f32<kTok>(acc, sm.keT + 16 * kb * 17, 17, sm.uT[w], 17, lane);
-      else mma_tok_bf16(acc, sm.keT + 16 * kb * kCat, sm.uT[w], lane);
-      sacc[i] = acc;
-    }
-    write_state_operand();
-    __syncthreads();
-  }
-
-  if (p.S_out) {
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int blk = w + 4 * i;
-      if (blk >= NBLK) continue;
-      const int kb = blk / NCB, cb = blk % NCB;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 16 * kb + 4 * (lane >> 4) + r;
-        p.S_out[((long)hd * K + c) * V + v0 + 16 * cb + (lane & 15)] = sacc[i][r];
       }
     }
   }
@@ -643,11 +612,10 @@ template <int K, typename T, int GK>
 static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   constexpr int BV = K < 32 ? K : 32;
   constexpr int NVT = K / BV;
-  using Smem = typename std::conditional<std::is_same<T, float>::value, SmemF32<K, BV>,
-                                         SmemBF16<K, BV>>::type;
+  using SM = Smem<std::is_same<T, float>::value, K, BV>;
   // More than half of the CU's 160 KiB of LDS per workgroup keeps one
   // workgroup per CU, so the B*HV*NVT workgroups spread over all CUs.
-  size_t lds = sizeof(Smem);
+  size_t lds = sizeof(SM);
   if (lds < 84 * 1024) lds = 84 * 1024;
   static bool configured = false;
   if (!configured) {
@@ -658,7 +626,8 @@ static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   }
   const int nheads = p.B * p.HV;
   const long blocks = (long)((nheads + 7) / 8) * 8 * NVT;
-  hipLaunchKernelGGL((chunk_fwd_kernel<K, T, GK>), dim3((unsigned)blocks), dim3(256), lds, stream, p);
+  hipLaunchKernelGGL((chunk_fwd_kernel<K, T, GK>), dim3((unsigned)blocks), dim3(kThreads), lds,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -667,16 +636,16 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
                         float lower_bound, const float* S0, float* o, float* S_out, int B, int T,
                         int H, int HV, int K, hipStream_t stream) {
   ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, B, T, H, HV, kind, lower_bound};
-#define KDA_CHUNK_GATE(KK, TT)                                                   \
-  switch (kind) {                                                                \
+#define KDA_CHUNK_GATE(KK, TT)                                                            \
+  switch (kind) {                                                                         \
     case KDA_GATE_SAFE: return launch_chunk_kt<KK, TT, KDA_GATE_SAFE>(p, stream);         \
     case KDA_GATE_STANDARD: return launch_chunk_kt<KK, TT, KDA_GATE_STANDARD>(p, stream); \
     default: return launch_chunk_kt<KK, TT, KDA_GATE_NONE>(p, stream);                    \
   }
-#define KDA_CHUNK_CASE(KK)                                  \
-  if (K == KK) {                                            \
-    if (bf16) { KDA_CHUNK_GATE(KK, uint16_t) }              \
-    else { KDA_CHUNK_GATE(KK, float) }                      \
+#define KDA_CHUNK_CASE(KK)                     \
+  if (K == KK) {                               \
+    if (bf16) { KDA_CHUNK_GATE(KK, uint16_t) } \
+    else { KDA_CHUNK_GATE(KK, float) }         \
   }
   KDA_CHUNK_CASE(16) KDA_CHUNK_CASE(32) KDA_CHUNK_CASE(64) KDA_CHUNK_CASE(128)
 #undef KDA_CHUNK_CASE
