@@ -260,6 +260,66 @@ __device__ __forceinline__ void kprod(f32x4& acc, const RowOp<F32, RA, K>& A, in
                          B.lo + brow0 * LD, LD, lane);
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 16x16x16 bf16 MFMA: the B operand layout (lane l holds k = 4 (l/16) .. +3 of
+// column l % 16) equals the accumulator layout, so a product's result can feed
+// the next product over the token axis straight from registers.
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split4(const float x[4], bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const __bf16 h = static_cast<__bf16>(x[r]);
+    hi[r] = h;
+    lo[r] = static_cast<__bf16>(x[r] - static_cast<float>(h));
+  }
+}
+
+// acc += A (16 x 16 tokens, rows [hi | lo] at `row`) * B (accumulator layout,
+// given as hi and lo words): hi*hi + hi*lo + lo*hi.
+__device__ __forceinline__ void tprod_reg(f32x4& acc, const uint16_t* Acat, bf16x4 bh, bf16x4 bl,
+                                          int lane) {
+  const uint16_t* a = Acat + (lane & 15) * kCat + 4 * (lane >> 4);
+  const bf16x4 ah = *reinterpret_cast<const bf16x4*>(a);
+  const bf16x4 al = *reinterpret_cast<const bf16x4*>(a + 16);
+  acc = mfma16(ah, bh, acc);
+  acc = mfma16(ah, bl, acc);
+  acc = mfma16(al, bh, acc);
+}
+
+// acc1 += A1 x B^T and acc2 += A2 x B^T over the key axis, B's fragments read once
+template <bool F32, int K, int RB>
+__device__ __forceinline__ void kprod2(f32x4& acc1, f32x4& acc2, const RowOp<F32, kTok, K>& A1,
+                                       const RowOp<F32, kTok, K>& A2, const RowOp<F32, RB, K>& B,
+                                       int lane) {
+  constexpr int LD = RowOp<F32, kTok, K>::LD;
+  if constexpr (F32 || K % 32 != 0) {
+    kprod(acc1, A1, 0, B, 0, lane);
+    kprod(acc2, A2, 0, B, 0, lane);
+  } else {
+    const int row = lane & 15, kq = (lane >> 4) * 8;
+#pragma unroll
+    for (int s = 0; s < K; s += 32) {
+      const int o = row * LD + s + kq;
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(B.hi + o);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(B.lo + o);
+      const bf16x8 a1h = *reinterpret_cast<const bf16x8*>(A1.hi + o);
+      const bf16x8 a1l = *reinterpret_cast<const bf16x8*>(A1.lo + o);
+      const bf16x8 a2h = *reinterpret_cast<const bf16x8*>(A2.hi + o);
+      const bf16x8 a2l = *reinterpret_cast<const bf16x8*>(A2.lo + o);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, bh, acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h, bh, acc2, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, bl, acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h, bl, acc2, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1l, bh, acc1, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2l, bh, acc2, 0, 0, 0);
+    }
+  }
+}
+
 // acc += A[arow0 .. +16) (16 tokens) x B (16 tokens x 16, given by its columns)
 template <bool F32, int RA, int RB>
 __device__ __forceinline__ void tprod(f32x4& acc, const TokOp<F32, RA>& A, int arow0,
@@ -318,7 +378,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     }
     float4 pg[2];
     Raw4 pq[2], pk[2];
-    float pbeta = 0.0f;
     // Loads past the end of the sequence read the last token instead (always a
     // valid address) and are replaced by padding values where they are used.
     auto fetch = [&](int blk) {
@@ -332,22 +391,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           pk[j] = In<T>::raw4(kg, (row * H + h) * K + c0);
         }
       }
-      if (tid < kTok) {
-        const float bt = p.beta[(b * T_ + min(tb + tid, T_ - 1)) * HV + hv];
-        pbeta = tb + tid < T_ ? bt : 0.0f;
-      }
     };
     if (NT > 0) fetch(0);
     for (int it = 0; it < NT + 2; ++it) {
       if (it < NT) {
         Ops& B = sm.blk[it % 3];
         bool overflow = false;
-        if (prep_thread) {
+        // Full blocks (all but possibly the last) skip the padding selects.
+        auto prep_block = [&](auto full) {
+          constexpr bool kFull = decltype(full)::value;
           const int t0 = it * kTok;
           float al[2][4], qv[2][4], kv[2][4];
   #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const bool valid = t0 + 2 * tp + j < T_;  // padding: no decay, no write, no read
+            const bool valid = kFull || t0 + 2 * tp + j < T_;  // padding: no decay, no write, no read
             const float gr[4] = {pg[j].x, pg[j].y, pg[j].z, pg[j].w};
             In<T>::unpack4(pq[j], qv[j]);
             In<T>::unpack4(pk[j], kv[j]);
@@ -359,7 +416,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               kv[j][c] = valid ? kv[j][c] : 0.0f;
             }
           }
-          if (tid < kTok) B.beta[tid] = pbeta;
           if (it + 1 < NT) fetch(it + 1);  // the next block's inputs travel meanwhile
           float E[2][4], Sf[2][4], ig[4];
   #pragma unroll
@@ -406,6 +462,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           }
   #pragma unroll
           for (int c = 0; c < 4; ++c) put_tok2(B.keT, c0 + c, 2 * tp, ke[0][c], ke[1][c]);
+        };
+        if (prep_thread) {
+          if ((it + 1) * kTok <= T_) prep_block(std::true_type{});
+          else prep_block(std::false_type{});
         }
         const bool ov = __any(overflow);
         if (lane == 0) B.flag[w] = ov ? 1 : 0;
@@ -413,7 +473,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       __syncthreads();
     }
   } else if (w == kAqkWave || w == kInvWave) {
+    // The A wave also carries beta (16 scattered loads per block) into the
+    // buffer the prep waves fill this step, fetched one step ahead.
+    float pbeta = 0.0f;
+    auto fetch_beta = [&](int blk) {
+      const int t = blk * kTok + lane;
+      const float bt = p.beta[(b * T_ + min(t, T_ - 1)) * HV + hv];
+      pbeta = t < T_ ? bt : 0.0f;
+    };
+    if (w == kAqkWave && lane < kTok && NT > 0) fetch_beta(0);
     for (int it = 0; it < NT + 2; ++it) {
+      if (w == kAqkWave && lane < kTok && it < NT) {
+        sm.blk[it % 3].beta[lane] = pbeta;
+        if (it + 1 < NT) fetch_beta(it + 1);
+      }
       const int ti = it - 1;
       if (ti >= 0 && ti < NT) {
         const Ops& B = sm.blk[ti % 3];
@@ -560,34 +633,52 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           if (tc + 1 < NT) fetch_v(tc + 1);
         } else {
           f32x4 pk = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
-          kprod(pk, B.kh, 0, C.st, 0, lane);
-          kprod(qs, B.qh, 0, C.st, 0, lane);
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 4 * (lane >> 4) + r;
-            put_tok(C.eb, lane & 15, t, B.beta[t] * (In<T>::widen(pv[r]) - pk[r]));
-          }
+          kprod2(pk, qs, B.kh, B.qh, C.st, lane);  // K_hat S and Q_hat S
+          const int g = lane >> 4;
+          const float4 bt4 = *reinterpret_cast<const float4*>(&B.beta[4 * g]);
+          const float e[4] = {bt4.x * (In<T>::widen(pv[0]) - pk[0]),
+                              bt4.y * (In<T>::widen(pv[1]) - pk[1]),
+                              bt4.z * (In<T>::widen(pv[2]) - pk[2]),
+                              bt4.w * (In<T>::widen(pv[3]) - pk[3])};
           if (tc + 1 < NT) fetch_v(tc + 1);
-          wave_lds_sync();
           f32x4 u = {0.f, 0.f, 0.f, 0.f};
-          tprod(u, sm.akk[tc & 1], 0, C.eb, lane);
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) put_tok(C.u, lane & 15, 4 * (lane >> 4) + r, u[r]);
-          wave_lds_sync();
           f32x4 ov = qs * scale;
-          tprod(ov, sm.aqk[tc & 1], 0, C.u, lane);
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 4 * (lane >> 4) + r;
-            if (t < T_) p.o[((b * T_ + t) * HV + hv) * V + vcol] = ov[r];
+          if constexpr (F32) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) put_tok(C.eb, lane & 15, 4 * g + r, e[r]);
+            wave_lds_sync();
+            tprod(u, sm.akk[tc & 1], 0, C.eb, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) put_tok(C.u, lane & 15, 4 * g + r, u[r]);
+            wave_lds_sync();
+            tprod(ov, sm.aqk[tc & 1], 0, C.u, lane);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+              const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * kb + 4 * g]);
+              f32x4 acc = sacc[kb] * f32x4{gm.x, gm.y, gm.z, gm.w};
+              tprod(acc, B.keT, 16 * kb, C.u, lane);
+              sacc[kb] = acc;
+            }
+          } else {
+            // Ebar, U stay in registers: accumulator layout = B operand layout
+            bf16x4 eh, el, uh, ul;
+            split4(e, eh, el);
+            tprod_reg(u, sm.akk[tc & 1].c, eh, el, lane);  // U = (I + R)^{-1} Ebar
+            const float uu[4] = {u[0], u[1], u[2], u[3]};
+            split4(uu, uh, ul);
+            tprod_reg(ov, sm.aqk[tc & 1].c, uh, ul, lane);  // O = s Q_hat S + A U
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {               // S = gamma S + (k Suf)^T U
+              const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * kb + 4 * g]);
+              f32x4 acc = sacc[kb] * f32x4{gm.x, gm.y, gm.z, gm.w};
+              tprod_reg(acc, B.keT.c + 16 * kb * kCat, uh, ul, lane);
+              sacc[kb] = acc;
+            }
           }
-  #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            f32x4 acc;
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = sacc[kb][r] * B.gam[16 * kb + 4 * (lane >> 4) + r];
-            tprod(acc, B.keT, 16 * kb, C.u, lane);
-            sacc[kb] = acc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * g + r;
+            if (t < T_) p.o[((b * T_ + t) * HV + hv) * V + vcol] = ov[r];
           }
         }
         write_state_operand(C);
