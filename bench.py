@@ -55,6 +55,24 @@ def decode_bytes(w):
             + w.B * w.HV * w.K * 4 + w.B * w.HV * 4 + w.B * w.HV * w.V * 4)
 
 
+def measured_traffic(key):
+    """HBM bytes per launch from the counter passes summarised in
+    profiles/traffic.json, or None when the kernel sources changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[key]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest()[:16] != rec["source_sha256_16"]:
+            return None
+        return rec["traffic_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,7 +142,8 @@ def main():
                    "V": w.V, "chunk": w.chunk, "gate": w.gate, "global_batch": w.B,
                    "seq_len": w.T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("chunk") if args.workload == "prefill" else None,
                      "kernel": "chunk_fwd_kernel<128, bf16>", "bytes_per_launch": nbytes,
                      "launch_ms": launch_ms},
         "mfma": {"algorithmic_flops": flops,
@@ -166,7 +185,7 @@ def main():
             "value": wd.B * wd.steps / (dms * 1e-3), "unit": "tokens/s",
             "ms_per_token_step": per_step_ms,
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dgbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": dgbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
                          "kernel": "decode_step_kernel<128, 128, bf16>",
                          "bytes_per_launch": decode_bytes(wd)},
         }
