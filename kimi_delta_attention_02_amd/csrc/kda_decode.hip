@@ -7,14 +7,17 @@
 // owning a tile of the state for the whole step.
 //
 // The step is bound by HBM: the fp32 state [K, V] of every (b, hv) is read once
-// and written once.  One wavefront owns a K x TV column tile (TV = min(V, 32)):
-// lane l holds column quad cq = l % NQ (16-byte loads, NQ lanes cover one
-// 128-byte row segment) and rows kappa = rg + RG * i of row group rg = l / NQ,
-// so every load instruction reads RG full row segments.  All RPL row loads are
-// issued before any arithmetic.  The two reductions over kappa (prediction
-// k.S_dec and read q.S_new) stay inside the wavefront: lanes of one column quad
-// differ only in the rg bits, so log2(RG) butterfly shuffles finish each sum;
-// no LDS and no barrier.
+// and written once.  A K x TV column tile (TV = min(V, 32)) is split by rows
+// over WT wavefronts (four for K = 128), so each lane keeps only RPL = 4
+// 16-byte rows in flight: many short streams reach a higher fraction of HBM
+// bandwidth than few long ones on this part.  In a wavefront, lane l holds
+// column quad cq = l % NQ (NQ lanes cover one 128-byte row segment) and rows
+// row0 + RG * i of row group rg = l / NQ, so every load instruction reads RG
+// full row segments; all loads are issued before any arithmetic.  The two
+// reductions over kappa (prediction k.S_dec and read q.S_new) run as
+// log2(RG) butterfly shuffles inside each wavefront, then one LDS exchange
+// across the WT wavefronts of the tile.  The decay factors exp(g) and the key
+// and query rows are computed once per workgroup into LDS.
 #include "kda_device.h"
 
 namespace kda {
@@ -33,101 +36,134 @@ struct DecodeParams {
   float lower_bound;
 };
 
-template <int K, int V, typename T>
+template <int K, int V>
+struct DecodeTiling {
+  static constexpr int TV = V < 64 ? V : 64;     // columns of a tile
+  static constexpr int NQ = TV / 4;              // column quads per row segment
+  static constexpr int RG = 64 / NQ;             // row groups per wavefront
+  static constexpr int WT = K / RG < 4 ? K / RG : 4;  // wavefronts splitting a tile's rows
+  static constexpr int RPL = K / (WT * RG);      // rows per lane
+  static constexpr int NVT = V / TV;             // tiles per (b, hv)
+  static constexpr int TPW = 4 / WT;             // tiles per workgroup of 4 wavefronts
+  static_assert(RPL >= 1 && K % (WT * RG) == 0, "head size too small for this tiling");
+};
+
+template <int K, int V, typename T, int GK>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
-  constexpr int TV = V < 32 ? V : 32;  // columns per wavefront
-  constexpr int NQ = TV / 4;           // column quads per row segment
-  constexpr int RG = 64 / NQ;          // row groups
-  constexpr int RPL = K / RG;          // rows per lane
-  static_assert(RPL >= 1 && K % RG == 0, "head size too small for this tiling");
-  constexpr int NVT = V / TV;
+  using D = DecodeTiling<K, V>;
+  constexpr int TV = D::TV, NQ = D::NQ, RG = D::RG, WT = D::WT, RPL = D::RPL, NVT = D::NVT,
+                TPW = D::TPW;
+  __shared__ float s_al[TPW][K], s_k[TPW][K], s_q[TPW][K];
+  __shared__ f32x4 s_red[2][4][NQ];  // per wavefront partial sums of the two reductions
 
-  const int lane = threadIdx.x & 63;
-  const long wave = (long)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  const long nwaves = (long)p.B * p.HV * NVT;
-  if (wave >= nwaves) return;
-  const int vt = (int)(wave % NVT);
-  const long bh = wave / NVT;  // b * HV + hv
-  const int hv = (int)(bh % p.HV);
-  const long b = bh / p.HV;
-  const int h = hv / (p.HV / p.H);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const long nheads = (long)p.B * p.HV;
+  const long tile0 = (long)blockIdx.x * TPW;
+  const long ntiles = nheads * NVT;
 
-  const int cq = lane % NQ;
-  const int rg = lane / NQ;
+  // decay factors and key/query rows of each tile's (b, hv), once per workgroup
+  for (int e = tid; e < TPW * K; e += 256) {
+    const int ts = e / K, r = e % K;
+    const long tile = tile0 + ts;
+    if (tile < ntiles) {
+      const long bh = tile / NVT;
+      const int hv = (int)(bh % p.HV);
+      const long b = bh / p.HV;
+      const int h = hv / (p.HV / p.H);
+      const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
+      const float bias = (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[(long)hv * K + r] : 0.0f;
+      s_al[ts][r] = exp_f(gate_log_decay_k<GK>(p.g_raw[bh * K + r], bias, rate, p.lower_bound));
+      s_k[ts][r] = In<T>::at(static_cast<const T*>(p.k), (b * p.H + h) * K + r);
+      s_q[ts][r] = In<T>::at(static_cast<const T*>(p.q), (b * p.H + h) * K + r);
+    }
+  }
+
+  const int ts = w / WT, rq = w % WT;  // tile slot, row quarter
+  const long tile = tile0 + ts;
+  const bool active = tile < ntiles;
+  const long bh = tile / NVT;          // b * HV + hv
+  const int vt = (int)(tile % NVT);
+  const int cq = lane % NQ, rg = lane / NQ;
   const int col = vt * TV + cq * 4;
-
+  const int row0 = rq * (K / WT) + rg;
   float* S = p.state + bh * (long)K * V;
   f32x4 s[RPL];
+  float vv[4] = {0.f, 0.f, 0.f, 0.f};
+  float bt = 0.0f;
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < RPL; ++i)
-    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (long)(rg + RG * i) * V + col));
-
-  const T* q = static_cast<const T*>(p.q) + (b * p.H + h) * K;
-  const T* kk = static_cast<const T*>(p.k) + (b * p.H + h) * K;
-  const float* gr = p.g_raw + bh * K;
-  const float rate = p.kind != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
-  const float* bias = (p.dt_bias && p.kind != KDA_GATE_NONE) ? p.dt_bias + (long)hv * K : nullptr;
-  float kr[RPL], qr[RPL], al[RPL];
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    const int r = rg + RG * i;
-    kr[i] = In<T>::at(kk, r);
-    qr[i] = In<T>::at(q, r);
-    al[i] = exp_f(gate_log_decay(gr[r], bias ? bias[r] : 0.0f, rate, p.kind, p.lower_bound));
+    for (int i = 0; i < RPL; ++i)
+      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (long)(row0 + RG * i) * V + col));
+    In<T>::load4(static_cast<const T*>(p.v), bh * V + col, vv);
+    bt = p.beta[bh];
   }
-  float vv[4];
-  In<T>::load4(static_cast<const T*>(p.v), bh * V + col, vv);
-  const float bt = p.beta[bh];
+  __syncthreads();
 
-  // decay, then prediction p = k . S_dec
+  // decay, then prediction p = k . S_dec: in-wave butterfly, then across the WT waves
   f32x4 pr = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    s[i] *= al[i];
-    pr += kr[i] * s[i];
+    for (int i = 0; i < RPL; ++i) {
+      const int r = row0 + RG * i;
+      s[i] *= s_al[ts][r];
+      pr += s_k[ts][r] * s[i];
+    }
   }
 #pragma unroll
   for (int m = NQ; m < 64; m <<= 1)
 #pragma unroll
     for (int c = 0; c < 4; ++c) pr[c] += __shfl_xor(pr[c], m);
+  if (rg == 0) s_red[0][w][cq] = pr;
+  __syncthreads();
+  pr = s_red[0][ts * WT][cq];
+#pragma unroll
+  for (int j = 1; j < WT; ++j) pr += s_red[0][ts * WT + j][cq];
 
   // residual, rank-1 write, read q . S_new
-  f32x4 r;
+  f32x4 rv;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) r[c] = bt * (vv[c] - pr[c]);
+  for (int c = 0; c < 4; ++c) rv[c] = bt * (vv[c] - pr[c]);
   f32x4 ov = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    s[i] += kr[i] * r;
-    ov += qr[i] * s[i];
+    for (int i = 0; i < RPL; ++i) {
+      const int r = row0 + RG * i;
+      s[i] += s_k[ts][r] * rv;
+      ov += s_q[ts][r] * s[i];
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (long)(row0 + RG * i) * V + col));
   }
 #pragma unroll
   for (int m = NQ; m < 64; m <<= 1)
 #pragma unroll
     for (int c = 0; c < 4; ++c) ov[c] += __shfl_xor(ov[c], m);
-
+  if (rg == 0) s_red[1][w][cq] = ov;
+  __syncthreads();
+  if (active && rq == 0 && rg == 0) {
+    f32x4 o = s_red[1][ts * WT][cq];
 #pragma unroll
-  for (int i = 0; i < RPL; ++i)
-    __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (long)(rg + RG * i) * V + col));
-  if (rg == 0) {
+    for (int j = 1; j < WT; ++j) o += s_red[1][ts * WT + j][cq];
     const float scale = 1.0f / __builtin_sqrtf((float)K);
-    *reinterpret_cast<f32x4*>(p.o + bh * V + col) = ov * scale;
+    *reinterpret_cast<f32x4*>(p.o + bh * V + col) = o * scale;
   }
 }
 
-template <int K, int V, typename T>
+template <int K, int V, typename T, int GK>
 static hipError_t launch_decode_kv(const DecodeParams& p, hipStream_t stream) {
-  constexpr int TV = V < 32 ? V : 32;
-  long waves = (long)p.B * p.HV * (V / TV);
-  long blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((decode_step_kernel<K, V, T>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  using D = DecodeTiling<K, V>;
+  const long tiles = (long)p.B * p.HV * D::NVT;
+  const long blocks = (tiles + D::TPW - 1) / D::TPW;
+  hipLaunchKernelGGL((decode_step_kernel<K, V, T, GK>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int GK>
 static hipError_t launch_decode_t(const DecodeParams& p, int K, int V, hipStream_t stream) {
 #define KDA_DEC_CASE(KK, VV) \
-  if (K == KK && V == VV) return launch_decode_kv<KK, VV, T>(p, stream);
+  if (K == KK && V == VV) return launch_decode_kv<KK, VV, T, GK>(p, stream);
 #define KDA_DEC_ROW(KK) KDA_DEC_CASE(KK, 16) KDA_DEC_CASE(KK, 32) KDA_DEC_CASE(KK, 64) KDA_DEC_CASE(KK, 128)
   KDA_DEC_ROW(16) KDA_DEC_ROW(32) KDA_DEC_ROW(64) KDA_DEC_ROW(128)
 #undef KDA_DEC_ROW
@@ -135,12 +171,21 @@ static hipError_t launch_decode_t(const DecodeParams& p, int K, int V, hipStream
   return hipErrorInvalidValue;
 }
 
+template <typename T>
+static hipError_t launch_decode_g(const DecodeParams& p, int K, int V, hipStream_t stream) {
+  switch (p.kind) {
+    case KDA_GATE_SAFE: return launch_decode_t<T, KDA_GATE_SAFE>(p, K, V, stream);
+    case KDA_GATE_STANDARD: return launch_decode_t<T, KDA_GATE_STANDARD>(p, K, V, stream);
+    default: return launch_decode_t<T, KDA_GATE_NONE>(p, K, V, stream);
+  }
+}
+
 hipError_t launch_decode(const void* q, const void* k, const void* v, int bf16,
                          const float* g_raw, const float* beta, const float* A_log,
                          const float* dt_bias, int kind, float lower_bound, float* state,
                          float* o, int B, int H, int HV, int K, int V, hipStream_t stream) {
   DecodeParams p{q, k, v, g_raw, beta, A_log, dt_bias, state, o, B, H, HV, kind, lower_bound};
-  return bf16 ? launch_decode_t<uint16_t>(p, K, V, stream) : launch_decode_t<float>(p, K, V, stream);
+  return bf16 ? launch_decode_g<uint16_t>(p, K, V, stream) : launch_decode_g<float>(p, K, V, stream);
 }
 
 }  // namespace kda
