@@ -100,18 +100,19 @@ struct alignas(16) TokOp<true, ROWS> {
 };
 
 // Operands of one 16-token block, written by the prep stage.
-template <bool F32, int K>
+template <bool F32, int K, int BV>
 struct alignas(16) BlockOps {
   RowOp<F32, kTok, K> qh, kh, ki;  // q E, k E, k / E  (rows = tokens)
   TokOp<F32, K> keT;               // (k Suf)^T        (rows = key channels)
   float gam[K];                    // gamma per key channel
   float beta[kTok];
   int flag[4];                     // per prep wave: a channel broke the gamma bound
+  alignas(16) typename std::conditional<F32, float, uint16_t>::type vT[BV][kTok];  // v tile, [column][t]
 };
 
 template <bool F32, int K, int BV>
 struct alignas(16) Smem {
-  BlockOps<F32, K> blk[3];
+  BlockOps<F32, K, BV> blk[3];
   TokOp<F32, kTok> aqk[2], akk[2];  // A and (I + R)^{-1} of the next two blocks
   float r[kTok * kRS];
   struct alignas(16) Chain {         // private to one chain wave
@@ -339,9 +340,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   constexpr int BV = V < 32 ? V : 32;
   constexpr int NCB = BV / 16, NKB = K / 16, NVT = V / BV;
   using SM = Smem<F32, K, BV>;
-  using Ops = BlockOps<F32, K>;
+  using Ops = BlockOps<F32, K, BV>;
   typedef typename In<T>::Raw4 Raw4;
-  typedef typename In<T>::Raw1 Raw1;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
 
@@ -370,6 +370,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   if (w < kPrepWaves) {
     // ---- prep threads: token pair tp (tokens 2tp, 2tp+1), key channels c0 .. c0+3
     const bool prep_thread = tid < 2 * K;
+    // v of the workgroup's value tile: thread -> token vtt, columns vc4 .. vc4+3
+    constexpr int kVThreads = kTok * BV / 4;
+    const bool v_thread = tid < kVThreads;
+    const int vtt = tid / (BV / 4), vc4 = (tid % (BV / 4)) * 4;
     const int tp = tid & 7, c0 = (tid >> 3) * 4;
     float bias4[4] = {0.f, 0.f, 0.f, 0.f};
     if (bias && prep_thread) {
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       for (int c = 0; c < 4; ++c) bias4[c] = bias[c0 + c];
     }
     float4 pg[2];
-    Raw4 pq[2], pk[2];
+    Raw4 pq[2], pk[2], pvv;
     // Loads past the end of the sequence read the last token instead (always a
     // valid address) and are replaced by padding values where they are used.
     auto fetch = [&](int blk) {
@@ -392,7 +396,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
         }
       }
     };
-    if (NT > 0) fetch(0);
+    auto fetch_v = [&](int blk) {
+      const long row = b * T_ + min(blk * kTok + vtt, T_ - 1);
+      pvv = In<T>::raw4(vg, (row * HV + hv) * V + v0 + vc4);
+    };
+    if (NT > 0) {
+      fetch(0);
+      if (v_thread) fetch_v(0);
+    }
     for (int it = 0; it < NT + 2; ++it) {
       if (it < NT) {
         Ops& B = sm.blk[it % 3];
@@ -463,6 +474,21 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   #pragma unroll
           for (int c = 0; c < 4; ++c) put_tok2(B.keT, c0 + c, 2 * tp, ke[0][c], ke[1][c]);
         };
+        if (v_thread) {  // v tile, transposed for the chain waves (padding rows: 0)
+          const bool valid = it * kTok + vtt < T_;
+          if constexpr (F32) {
+            const float vx[4] = {pvv.x, pvv.y, pvv.z, pvv.w};
+  #pragma unroll
+            for (int c = 0; c < 4; ++c) B.vT[vc4 + c][vtt] = valid ? vx[c] : 0.0f;
+          } else {
+            const uint32_t lo = valid ? pvv.x : 0u, hi = valid ? pvv.y : 0u;
+            B.vT[vc4 + 0][vtt] = (uint16_t)(lo & 0xffffu);
+            B.vT[vc4 + 1][vtt] = (uint16_t)(lo >> 16);
+            B.vT[vc4 + 2][vtt] = (uint16_t)(hi & 0xffffu);
+            B.vT[vc4 + 3][vtt] = (uint16_t)(hi >> 16);
+          }
+          if (it + 1 < NT) fetch_v(it + 1);
+        }
         if (prep_thread) {
           if ((it + 1) * kTok <= T_) prep_block(std::true_type{});
           else prep_block(std::false_type{});
@@ -557,15 +583,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     const bool chain = cb >= 0 && cb < NCB;
     const int vcol = v0 + 16 * cb + (lane & 15);
     f32x4 sacc[NKB];
-    Raw1 pv[4];
-    auto fetch_v = [&](int blk) {
-  #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = blk * kTok + 4 * (lane >> 4) + r;
-        const Raw1 x = vg[((b * T_ + min(t, T_ - 1)) * HV + hv) * V + vcol];
-        pv[r] = t < T_ ? x : In<T>::zero1();
-      }
-    };
     auto write_state_operand = [&](typename SM::Chain& C) {
   #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -584,7 +601,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       }
       write_state_operand(sm.chain[cb]);
       wave_lds_sync();
-      if (NT > 0) fetch_v(0);
     }
     for (int it = 0; it < NT + 2; ++it) {
       const int tc = it - 2;
@@ -630,17 +646,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             op += __shfl_xor(op, 32);
             if (lane < 16) p.o[(row * HV + hv) * V + vcol] = scale * op;
           }
-          if (tc + 1 < NT) fetch_v(tc + 1);
         } else {
           f32x4 pk = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
           kprod2(pk, qs, B.kh, B.qh, C.st, lane);  // K_hat S and Q_hat S
           const int g = lane >> 4;
           const float4 bt4 = *reinterpret_cast<const float4*>(&B.beta[4 * g]);
-          const float e[4] = {bt4.x * (In<T>::widen(pv[0]) - pk[0]),
-                              bt4.y * (In<T>::widen(pv[1]) - pk[1]),
-                              bt4.z * (In<T>::widen(pv[2]) - pk[2]),
-                              bt4.w * (In<T>::widen(pv[3]) - pk[3])};
-          if (tc + 1 < NT) fetch_v(tc + 1);
+          float vv[4];  // v of tokens 4g .. 4g+3 in this lane's column (padding: 0)
+          if constexpr (F32) {
+            const float4 x = *reinterpret_cast<const float4*>(&B.vT[16 * cb + (lane & 15)][4 * g]);
+            vv[0] = x.x; vv[1] = x.y; vv[2] = x.z; vv[3] = x.w;
+          } else {
+            In<T>::unpack4(*reinterpret_cast<const uint2*>(&B.vT[16 * cb + (lane & 15)][4 * g]), vv);
+          }
+          const float e[4] = {bt4.x * (vv[0] - pk[0]), bt4.y * (vv[1] - pk[1]),
+                              bt4.z * (vv[2] - pk[2]), bt4.w * (vv[3] - pk[3])};
           f32x4 u = {0.f, 0.f, 0.f, 0.f};
           f32x4 ov = qs * scale;
           if constexpr (F32) {
