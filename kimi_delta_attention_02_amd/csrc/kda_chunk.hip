@@ -370,10 +370,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   if (w < kPrepWaves) {
     // ---- prep threads: token pair tp (tokens 2tp, 2tp+1), key channels c0 .. c0+3
     const bool prep_thread = tid < 2 * K;
-    // v of the workgroup's value tile: thread -> token vtt, columns vc4 .. vc4+3
-    constexpr int kVThreads = kTok * BV / 4;
-    const bool v_thread = tid < kVThreads;
-    const int vtt = tid / (BV / 4), vc4 = (tid % (BV / 4)) * 4;
+    // v of the workgroup's value tile, spread over all prep threads:
+    // thread -> token vtt, columns vc .. vc + VPT - 1
+    constexpr int VPT = kTok * BV / (64 * kPrepWaves);
+    static_assert(VPT == 1 || VPT == 2, "value tile / prep thread split");
+    typedef typename std::conditional<VPT * sizeof(T) == 2, uint16_t,
+            typename std::conditional<VPT * sizeof(T) == 4, uint32_t, uint2>::type>::type VRaw;
+    const int vtt = tid / (BV / VPT), vc = (tid % (BV / VPT)) * VPT;
+    VRaw pvv;
     const int tp = tid & 7, c0 = (tid >> 3) * 4;
     float bias4[4] = {0.f, 0.f, 0.f, 0.f};
     if (bias && prep_thread) {
@@ -381,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       for (int c = 0; c < 4; ++c) bias4[c] = bias[c0 + c];
     }
     float4 pg[2];
-    Raw4 pq[2], pk[2], pvv;
+    Raw4 pq[2], pk[2];
     // Loads past the end of the sequence read the last token instead (always a
     // valid address) and are replaced by padding values where they are used.
     auto fetch = [&](int blk) {
@@ -398,11 +402,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     };
     auto fetch_v = [&](int blk) {
       const long row = b * T_ + min(blk * kTok + vtt, T_ - 1);
-      pvv = In<T>::raw4(vg, (row * HV + hv) * V + v0 + vc4);
+      pvv = *reinterpret_cast<const VRaw*>(vg + (row * HV + hv) * V + v0 + vc);
     };
     if (NT > 0) {
       fetch(0);
-      if (v_thread) fetch_v(0);
+      fetch_v(0);
     }
     for (int it = 0; it < NT + 2; ++it) {
       if (it < NT) {
@@ -474,18 +478,18 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   #pragma unroll
           for (int c = 0; c < 4; ++c) put_tok2(B.keT, c0 + c, 2 * tp, ke[0][c], ke[1][c]);
         };
-        if (v_thread) {  // v tile, transposed for the chain waves (padding rows: 0)
-          const bool valid = it * kTok + vtt < T_;
-          if constexpr (F32) {
-            const float vx[4] = {pvv.x, pvv.y, pvv.z, pvv.w};
-  #pragma unroll
-            for (int c = 0; c < 4; ++c) B.vT[vc4 + c][vtt] = valid ? vx[c] : 0.0f;
+        {  // v tile, transposed for the chain waves (padding rows: 0)
+          const VRaw x = it * kTok + vtt < T_ ? pvv : VRaw{};
+          if constexpr (F32 && VPT == 1) {
+            B.vT[vc][vtt] = __uint_as_float(x);
+          } else if constexpr (F32) {
+            B.vT[vc][vtt] = __uint_as_float(x.x);
+            B.vT[vc + 1][vtt] = __uint_as_float(x.y);
+          } else if constexpr (VPT == 1) {
+            B.vT[vc][vtt] = x;
           } else {
-            const uint32_t lo = valid ? pvv.x : 0u, hi = valid ? pvv.y : 0u;
-            B.vT[vc4 + 0][vtt] = (uint16_t)(lo & 0xffffu);
-            B.vT[vc4 + 1][vtt] = (uint16_t)(lo >> 16);
-            B.vT[vc4 + 2][vtt] = (uint16_t)(hi & 0xffffu);
-            B.vT[vc4 + 3][vtt] = (uint16_t)(hi >> 16);
+            B.vT[vc][vtt] = (uint16_t)(x & 0xffffu);
+            B.vT[vc + 1][vtt] = (uint16_t)(x >> 16);
           }
           if (it + 1 < NT) fetch_v(it + 1);
         }
