@@ -110,15 +110,34 @@ struct alignas(16) BlockOps {
   alignas(16) typename std::conditional<F32, float, uint16_t>::type vT[BV][kTok];  // v tile, [column][t]
 };
 
+// Per chain wave: scratch of the fp32-input path (Ebar^T, U^T  [v][t]).
+template <bool F32>
+struct ChainScratch {
+  TokOp<true, 16> eb, u;
+};
+template <>
+struct ChainScratch<false> {};
+
+// bf16 inputs: U of one column block handed from the chain to the output
+// wave, per lane the hi and lo words of its four accumulator-layout values.
+template <bool F32, int NCB>
+struct UHandoff {
+  uint4 u[NCB][2][64];  // [column block][block parity][lane]
+};
+template <int NCB>
+struct UHandoff<true, NCB> {};
+
 template <bool F32, int K, int BV>
 struct alignas(16) Smem {
   BlockOps<F32, K, BV> blk[3];
-  TokOp<F32, kTok> aqk[2], akk[2];  // A and (I + R)^{-1} of the next two blocks
+  TokOp<F32, kTok> akk[2];           // (I + R)^{-1} of the next two blocks
+  TokOp<F32, kTok> aqk[F32 ? 2 : 1];  // A (fp32 inputs; bf16 keeps it in registers)
   float r[kTok * kRS];
-  struct alignas(16) Chain {         // private to one chain wave
-    RowOp<F32, 16, K> st;            // S^T of its column block  [v][c]
-    TokOp<F32, 16> eb, u;            // Ebar^T, U^T              [v][t]
+  struct alignas(16) Chain {
+    RowOp<F32, 16, K> st[2];         // S^T of its column block [v][c], by block parity
+    ChainScratch<F32> f;
   } chain[BV / 16];
+  UHandoff<F32, BV / 16> uo;
 };
 
 // ------------------------------------------------------------ MFMA tiles
@@ -366,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   const T* vg = static_cast<const T*>(p.v);
 
   // Each role runs its own loop over the pipeline steps; every loop executes
-  // the same NT + 2 barriers, and registers are allocated per role.
+  // the same NT + 3 barriers, and registers are allocated per role.
   if (w < kPrepWaves) {
     // ---- prep threads: token pair tp (tokens 2tp, 2tp+1), key channels c0 .. c0+3
     const bool prep_thread = tid < 2 * K;
@@ -400,15 +419,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
         }
       }
     };
+    float pbeta = 0.0f;
     auto fetch_v = [&](int blk) {
       const long row = b * T_ + min(blk * kTok + vtt, T_ - 1);
       pvv = *reinterpret_cast<const VRaw*>(vg + (row * HV + hv) * V + v0 + vc);
+      if (tid < kTok) pbeta = p.beta[(b * T_ + min(blk * kTok + tid, T_ - 1)) * HV + hv];
     };
     if (NT > 0) {
       fetch(0);
       fetch_v(0);
     }
-    for (int it = 0; it < NT + 2; ++it) {
+    for (int it = 0; it < NT + 3; ++it) {
       if (it < NT) {
         Ops& B = sm.blk[it % 3];
         bool overflow = false;
@@ -491,6 +512,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             B.vT[vc][vtt] = (uint16_t)(x & 0xffffu);
             B.vT[vc + 1][vtt] = (uint16_t)(x >> 16);
           }
+          if (tid < kTok) B.beta[tid] = it * kTok + tid < T_ ? pbeta : 0.0f;
           if (it + 1 < NT) fetch_v(it + 1);
         }
         if (prep_thread) {
@@ -503,32 +525,78 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       __syncthreads();
     }
   } else if (w == kAqkWave || w == kInvWave) {
-    // The A wave also carries beta (16 scattered loads per block) into the
-    // buffer the prep waves fill this step, fetched one step ahead.
-    float pbeta = 0.0f;
-    auto fetch_beta = [&](int blk) {
-      const int t = blk * kTok + lane;
-      const float bt = p.beta[(b * T_ + min(t, T_ - 1)) * HV + hv];
-      pbeta = t < T_ ? bt : 0.0f;
-    };
-    if (w == kAqkWave && lane < kTok && NT > 0) fetch_beta(0);
-    for (int it = 0; it < NT + 2; ++it) {
-      if (w == kAqkWave && lane < kTok && it < NT) {
-        sm.blk[it % 3].beta[lane] = pbeta;
-        if (it + 1 < NT) fetch_beta(it + 1);
-      }
+    // bf16 inputs: the A wave also forms the outputs, one step behind the
+    // chain: O = s Q_hat S + A U for the block whose U the chain produced last
+    // step.  A is computed as A^T = (k / E)(q E)^T, whose accumulator layout is
+    // A's MFMA operand layout, and stays in registers; Q_hat S reads the
+    // chain's LDS copy of the state; U arrives from the chain through LDS.
+    bf16x4 ah_n = {}, al_n = {}, ah_o = {}, al_o = {};  // A of blocks it-2 (n), it-3 (o)
+    bool skip_n = true, skip_o = true;  // block absent or run token by token
+    f32x4 qsv[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) qsv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < NT + 3; ++it) {
       const int ti = it - 1;
-      if (ti >= 0 && ti < NT) {
+      if constexpr (!F32) {
+        if (w == kAqkWave) {
+          const int g = lane >> 4;
+          if (!skip_o) {  // O of block it - 3
+            const int t0 = (it - 3) * kTok;
+            float* orow = p.o + ((b * T_ + t0 + 4 * g) * HV + hv) * (long)V + v0 + (lane & 15);
+  #pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              const uint4 uu = sm.uo.u[cb][(it - 3) & 1][lane];
+              const bf16x4 uh = __builtin_bit_cast(bf16x4, uint2{uu.x, uu.y});
+              const bf16x4 ul = __builtin_bit_cast(bf16x4, uint2{uu.z, uu.w});
+              f32x4 acc = qsv[cb];
+              acc = mfma16(ah_o, uh, acc);
+              acc = mfma16(ah_o, ul, acc);
+              acc = mfma16(al_o, uh, acc);
+  #pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (t0 + 4 * g + r < T_) orow[(long)r * HV * V + 16 * cb] = acc[r];
+            }
+          }
+          ah_o = ah_n;
+          al_o = al_n;
+          skip_o = skip_n;
+          if (!skip_o) {  // s Q_hat S of block it - 2
+            const Ops& B2 = sm.blk[(it - 2) % 3];
+  #pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+              kprod(acc, B2.qh, 0, sm.chain[cb].st[(it - 2) & 1], 0, lane);
+              qsv[cb] = acc * scale;
+            }
+          }
+          skip_n = true;
+          if (ti >= 0 && ti < NT) {  // A of block it - 1
+            const Ops& B = sm.blk[ti % 3];
+            skip_n = (B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3]) != 0;
+            if (!skip_n) {
+              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+              kprod(acc, B.ki, 0, B.qh, 0, lane);  // lane l, r: A[l % 16][4 g + r] / s
+              float a[4];
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) a[r] = 4 * g + r <= (lane & 15) ? scale * acc[r] : 0.0f;
+              split4(a, ah_n, al_n);
+            }
+          }
+        }
+      }
+      if (ti >= 0 && ti < NT && (F32 || w == kInvWave)) {
         const Ops& B = sm.blk[ti % 3];
         if (!(B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3])) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           const int j = lane & 15;
           if (w == kAqkWave) {
-            kprod(acc, B.qh, 0, B.ki, 0, lane);
+            if constexpr (F32) {
+              kprod(acc, B.qh, 0, B.ki, 0, lane);
   #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 4 * (lane >> 4) + r;
-              put_tok(sm.aqk[ti & 1], i, j, j <= i ? scale * acc[r] : 0.0f);
+              for (int r = 0; r < 4; ++r) {
+                const int i = 4 * (lane >> 4) + r;
+                put_tok(sm.aqk[ti & 1], i, j, j <= i ? scale * acc[r] : 0.0f);
+              }
             }
           } else {
             kprod(acc, B.kh, 0, B.ki, 0, lane);
@@ -587,11 +655,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     const bool chain = cb >= 0 && cb < NCB;
     const int vcol = v0 + 16 * cb + (lane & 15);
     f32x4 sacc[NKB];
-    auto write_state_operand = [&](typename SM::Chain& C) {
+    auto write_state_operand = [&](RowOp<F32, 16, K>& st) {
   #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const float x[4] = {sacc[kb][0], sacc[kb][1], sacc[kb][2], sacc[kb][3]};
-        put4(C.st, lane & 15, 16 * kb + 4 * (lane >> 4), x);
+        put4(st, lane & 15, 16 * kb + 4 * (lane >> 4), x);
       }
     };
     if (chain) {
@@ -603,12 +671,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           sacc[kb][r] = p.S0 ? p.S0[((long)hd * K + c) * V + vcol] : 0.0f;
         }
       }
-      write_state_operand(sm.chain[cb]);
+      write_state_operand(sm.chain[cb].st[0]);
       wave_lds_sync();
     }
-    for (int it = 0; it < NT + 2; ++it) {
+    for (int it = 0; it < NT + 3; ++it) {
       const int tc = it - 2;
-      if (tc >= 0 && chain) {
+      if (tc >= 0 && tc < NT && chain) {
         const Ops& B = sm.blk[tc % 3];
         typename SM::Chain& C = sm.chain[cb];
         const int t0 = tc * kTok;
@@ -652,7 +720,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           }
         } else {
           f32x4 pk = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
-          kprod2(pk, qs, B.kh, B.qh, C.st, lane);  // K_hat S and Q_hat S
+          if constexpr (F32)
+            kprod2(pk, qs, B.kh, B.qh, C.st[tc & 1], lane);  // K_hat S and Q_hat S
+          else
+            kprod(pk, B.kh, 0, C.st[tc & 1], 0, lane);        // K_hat S
           const int g = lane >> 4;
           const float4 bt4 = *reinterpret_cast<const float4*>(&B.beta[4 * g]);
           float vv[4];  // v of tokens 4g .. 4g+3 in this lane's column (padding: 0)
@@ -665,22 +736,27 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           const float e[4] = {bt4.x * (vv[0] - pk[0]), bt4.y * (vv[1] - pk[1]),
                               bt4.z * (vv[2] - pk[2]), bt4.w * (vv[3] - pk[3])};
           f32x4 u = {0.f, 0.f, 0.f, 0.f};
-          f32x4 ov = qs * scale;
           if constexpr (F32) {
+            f32x4 ov = qs * scale;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) put_tok(C.eb, lane & 15, 4 * g + r, e[r]);
+            for (int r = 0; r < 4; ++r) put_tok(C.f.eb, lane & 15, 4 * g + r, e[r]);
             wave_lds_sync();
-            tprod(u, sm.akk[tc & 1], 0, C.eb, lane);
+            tprod(u, sm.akk[tc & 1], 0, C.f.eb, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) put_tok(C.u, lane & 15, 4 * g + r, u[r]);
+            for (int r = 0; r < 4; ++r) put_tok(C.f.u, lane & 15, 4 * g + r, u[r]);
             wave_lds_sync();
-            tprod(ov, sm.aqk[tc & 1], 0, C.u, lane);
+            tprod(ov, sm.aqk[tc & 1], 0, C.f.u, lane);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
               const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * kb + 4 * g]);
               f32x4 acc = sacc[kb] * f32x4{gm.x, gm.y, gm.z, gm.w};
-              tprod(acc, B.keT, 16 * kb, C.u, lane);
+              tprod(acc, B.keT, 16 * kb, C.f.u, lane);
               sacc[kb] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = t0 + 4 * g + r;
+              if (t < T_) p.o[((b * T_ + t) * HV + hv) * V + vcol] = ov[r];
             }
           } else {
             // Ebar, U stay in registers: accumulator layout = B operand layout
@@ -689,7 +765,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             tprod_reg(u, sm.akk[tc & 1].c, eh, el, lane);  // U = (I + R)^{-1} Ebar
             const float uu[4] = {u[0], u[1], u[2], u[3]};
             split4(uu, uh, ul);
-            tprod_reg(ov, sm.aqk[tc & 1].c, uh, ul, lane);  // O = s Q_hat S + A U
+            {  // U to the output wave
+              const uint2 h2 = __builtin_bit_cast(uint2, uh), l2 = __builtin_bit_cast(uint2, ul);
+              sm.uo.u[cb][tc & 1][lane] = uint4{h2.x, h2.y, l2.x, l2.y};
+            }
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {               // S = gamma S + (k Suf)^T U
               const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * kb + 4 * g]);
@@ -698,13 +777,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               sacc[kb] = acc;
             }
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 4 * g + r;
-            if (t < T_) p.o[((b * T_ + t) * HV + hv) * V + vcol] = ov[r];
-          }
         }
-        write_state_operand(C);
+        write_state_operand(C.st[(tc + 1) & 1]);
         wave_lds_sync();
       }
       __syncthreads();
