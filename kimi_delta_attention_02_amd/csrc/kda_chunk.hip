@@ -132,7 +132,9 @@ struct alignas(16) Smem {
   BlockOps<F32, K, BV> blk[3];
   TokOp<F32, kTok> akk[2];           // (I + R)^{-1} of the next two blocks
   TokOp<F32, kTok> aqk[F32 ? 2 : 1];  // A (fp32 inputs; bf16 keeps it in registers)
-  float r[kTok * kRS];
+  alignas(16) float r[kTok * kRS];
+  alignas(16) float xd[kTok * kRS];  // inverse of I + R's diagonal 8 x 8 blocks (zero elsewhere)
+  alignas(16) float pt[kTok * kRS];
   struct alignas(16) Chain {
     RowOp<F32, 16, K> st[2];         // S^T of its column block [v][c], by block parity
     ChainScratch<F32> f;
@@ -535,6 +537,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     f32x4 qsv[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) qsv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (w == kInvWave)  // the off-diagonal blocks of xd stay zero
+      for (int e = lane; e < kTok * kRS; e += 64) sm.xd[e] = 0.0f;
     for (int it = 0; it < NT + 3; ++it) {
       const int ti = it - 1;
       if constexpr (!F32) {
@@ -606,43 +610,53 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               sm.r[i * kRS + j] = j < i ? B.beta[i] * acc[r] : 0.0f;
             }
             wave_lds_sync();
-            if (lane < 16) {
-              // (I + R)^{-1}, column c = lane, by forward substitution in fp32:
-              // X[i] = delta_ic - sum_{m<i} R[i][m] X[m], four partial sums per row.
-              // Rows are read (as broadcast reads) in groups of four, one group
-              // ahead of the arithmetic, so LDS latency overlaps the FMAs.
-              const int c = lane;
-              float4 Rg[2][16];  // a group of rows 4g..4g+3 holds at most 15 row segments
-              auto load_group = [&](int g, float4* dst) {
-                int n = 0;
+            // (I + R)^{-1} in fp32.  With X_d the inverse of I + R's two 8 x 8
+            // diagonal blocks and N = R's lower-left 8 x 8 block,
+            // (I + R)^{-1} = X_d - X_d N X_d, since (X_d N)^2 = 0.
+            {  // X_d by forward substitution, one column c per lane (lanes >= 16 repeat)
+              const int c = lane & 15, bo = c & 8;  // bo: first row of c's diagonal block
+              float X[8];
   #pragma unroll
-                for (int i = 4 * g; i < 4 * g + 4; ++i)
+              for (int ii = 0; ii < 8; ++ii) {
+                const float* rrow = &sm.r[(bo + ii) * kRS + bo];
+                float part[2] = {0.f, 0.f};
   #pragma unroll
-                  for (int m4 = 0; m4 < i; m4 += 4)
-                    dst[n++] = *reinterpret_cast<const float4*>(&sm.r[i * kRS + m4]);
-              };
-              load_group(0, Rg[0]);
-              float X[kTok];
-  #pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                if (g + 1 < 4) load_group(g + 1, Rg[(g + 1) & 1]);
-                int n = 0;
-  #pragma unroll
-                for (int i = 4 * g; i < 4 * g + 4; ++i) {
-                  float part[4] = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-                  for (int m4 = 0; m4 < i; m4 += 4) {
-                    const float4 rr = Rg[g & 1][n++];
-                    const float rv[4] = {rr.x, rr.y, rr.z, rr.w};
-  #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                      if (m4 + u < i) part[u] += rv[u] * X[m4 + u];
-                  }
-                  X[i] = ((i == c) ? 1.0f : 0.0f) - ((part[0] + part[1]) + (part[2] + part[3]));
-                }
+                for (int m = 0; m < ii; ++m) part[m & 1] += rrow[m] * X[m];
+                X[ii] = ((ii == (c & 7)) ? 1.0f : 0.0f) - (part[0] + part[1]);
               }
+              if (lane < 16) {
   #pragma unroll
-              for (int i = 0; i < kTok; ++i) put_tok(sm.akk[ti & 1], i, c, X[i]);
+                for (int ii = 0; ii < 8; ++ii) sm.xd[(bo + ii) * kRS + c] = X[ii];
+              }
+            }
+            wave_lds_sync();
+            {  // Y = X^T = Y_d - Y_d P, P = N^T Y_d, on the 16x16x4 fp32 MFMA
+              const int row = lane & 15, kk = lane >> 4;
+              f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+              for (int s4 = 8; s4 < 16; s4 += 4) {  // N^T is zero outside k = 8..15, rows 0..7
+                const float a = row < 8 ? sm.r[(s4 + kk) * kRS + row] : 0.0f;
+                pacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sm.xd[row * kRS + s4 + kk], pacc, 0, 0, 0);
+              }
+              *reinterpret_cast<f32x4*>(&sm.pt[row * kRS + 4 * kk]) = pacc;  // P^T, [column][row]
+              wave_lds_sync();
+              const float4 yd = *reinterpret_cast<const float4*>(&sm.xd[row * kRS + 4 * kk]);
+              f32x4 y = {yd.x, yd.y, yd.z, yd.w};
+  #pragma unroll
+              for (int s4 = 0; s4 < 8; s4 += 4)  // P is zero outside rows 0..7
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(-sm.xd[(s4 + kk) * kRS + row],
+                                                         sm.pt[row * kRS + s4 + kk], y, 0, 0, 0);
+              // lane l, r: Y[4 kk + r][row] = X[row][4 kk + r], X's MFMA operand layout
+              if constexpr (F32) {
+  #pragma unroll
+                for (int r = 0; r < 4; ++r) sm.akk[ti & 1].c[row * 17 + 4 * kk + r] = y[r];
+              } else {
+                const float yy[4] = {y[0], y[1], y[2], y[3]};
+                bf16x4 yh, yl;
+                split4(yy, yh, yl);
+                *reinterpret_cast<bf16x4*>(&sm.akk[ti & 1].c[row * kCat + 4 * kk]) = yh;
+                *reinterpret_cast<bf16x4*>(&sm.akk[ti & 1].c[row * kCat + 16 + 4 * kk]) = yl;
+              }
             }
           }
         }
