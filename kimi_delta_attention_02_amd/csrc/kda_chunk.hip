@@ -207,10 +207,6 @@ __device__ __forceinline__ void mma_f32(f32x4& acc, const float* A, int lda, con
                                                0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2(uint16_t lo_half, uint16_t hi_half) {
-  return (uint32_t)lo_half | ((uint32_t)hi_half << 16);
-}
-
 // Retain factor exp(g) for the token-by-token path, kept out of line: that
 // rare path then does not raise the register allocation of the main one.
 template <int GK>
@@ -234,11 +230,11 @@ __device__ __forceinline__ void put4(RowOp<F32, ROWS, K>& op, int row, int c0, c
 #pragma unroll
     for (int c = 0; c < 4; ++c) op.f[row * LD + c0 + c] = x[c];
   } else {
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) split_bf16(x[c], h[c], l[c]);
-    *reinterpret_cast<uint2*>(op.hi + row * LD + c0) = uint2{pack2(h[0], h[1]), pack2(h[2], h[3])};
-    *reinterpret_cast<uint2*>(op.lo + row * LD + c0) = uint2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+    uint2 h, l;
+    split2_bf16(x[0], x[1], h.x, l.x);
+    split2_bf16(x[2], x[3], h.y, l.y);
+    *reinterpret_cast<uint2*>(op.hi + row * LD + c0) = h;
+    *reinterpret_cast<uint2*>(op.lo + row * LD + c0) = l;
   }
 }
 
@@ -262,11 +258,10 @@ __device__ __forceinline__ void put_tok2(TokOp<F32, ROWS>& op, int row, int t, f
     op.c[row * 17 + t] = x0;
     op.c[row * 17 + t + 1] = x1;
   } else {
-    uint16_t h0, l0, h1, l1;
-    split_bf16(x0, h0, l0);
-    split_bf16(x1, h1, l1);
-    *reinterpret_cast<uint32_t*>(op.c + row * kCat + t) = pack2(h0, h1);
-    *reinterpret_cast<uint32_t*>(op.c + row * kCat + 16 + t) = pack2(l0, l1);
+    uint32_t h, l;
+    split2_bf16(x0, x1, h, l);
+    *reinterpret_cast<uint32_t*>(op.c + row * kCat + t) = h;
+    *reinterpret_cast<uint32_t*>(op.c + row * kCat + 16 + t) = l;
   }
 }
 
@@ -292,12 +287,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 
 __device__ __forceinline__ void split4(const float x[4], bf16x4& hi, bf16x4& lo) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const __bf16 h = static_cast<__bf16>(x[r]);
-    hi[r] = h;
-    lo[r] = static_cast<__bf16>(x[r] - static_cast<float>(h));
-  }
+  uint2 h, l;
+  split2_bf16(x[0], x[1], h.x, l.x);
+  split2_bf16(x[2], x[3], h.y, l.y);
+  hi = __builtin_bit_cast(bf16x4, h);
+  lo = __builtin_bit_cast(bf16x4, l);
 }
 
 // acc += A (16 x 16 tokens, rows [hi | lo] at `row`) * B (accumulator layout,
@@ -405,8 +399,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   #pragma unroll
       for (int c = 0; c < 4; ++c) bias4[c] = bias[c0 + c];
     }
+    const GateConsts gc = gate_consts(rate, p.lower_bound);
     float4 pg[2];
     Raw4 pq[2], pk[2];
+    // Per-thread row-0 pointers of this sequence; token t adds t times the row stride.
+    const float* g_base = p.g_raw + (b * T_ * HV + hv) * (long)K + c0;
+    const T* q_base = qg + (b * T_ * H + h) * (long)K + c0;
+    const T* k_base = kg + (b * T_ * H + h) * (long)K + c0;
+    const T* v_base = vg + (b * T_ * HV + hv) * (long)V + v0 + vc;
+    const float* beta_base = p.beta + b * T_ * HV + hv;
     // Loads past the end of the sequence read the last token instead (always a
     // valid address) and are replaced by padding values where they are used.
     auto fetch = [&](int blk) {
@@ -414,18 +415,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       if (prep_thread) {
   #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const long row = b * T_ + min(tb + 2 * tp + j, T_ - 1);
-          pg[j] = *reinterpret_cast<const float4*>(p.g_raw + (row * HV + hv) * K + c0);
-          pq[j] = In<T>::raw4(qg, (row * H + h) * K + c0);
-          pk[j] = In<T>::raw4(kg, (row * H + h) * K + c0);
+          const long t = min(tb + 2 * tp + j, T_ - 1);
+          pg[j] = *reinterpret_cast<const float4*>(g_base + t * (HV * K));
+          pq[j] = In<T>::raw4(q_base, t * (H * K));
+          pk[j] = In<T>::raw4(k_base, t * (H * K));
         }
       }
     };
     float pbeta = 0.0f;
     auto fetch_v = [&](int blk) {
-      const long row = b * T_ + min(blk * kTok + vtt, T_ - 1);
-      pvv = *reinterpret_cast<const VRaw*>(vg + (row * HV + hv) * V + v0 + vc);
-      if (tid < kTok) pbeta = p.beta[(b * T_ + min(blk * kTok + tid, T_ - 1)) * HV + hv];
+      pvv = *reinterpret_cast<const VRaw*>(v_base + (long)min(blk * kTok + vtt, T_ - 1) * (HV * V));
+      if (tid < kTok) pbeta = beta_base[(long)min(blk * kTok + tid, T_ - 1) * HV];
     };
     if (NT > 0) {
       fetch(0);
@@ -439,49 +439,58 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
         auto prep_block = [&](auto full) {
           constexpr bool kFull = decltype(full)::value;
           const int t0 = it * kTok;
+          const float4 g_in[2] = {pg[0], pg[1]};
+          const Raw4 q_in[2] = {pq[0], pq[1]}, k_in[2] = {pk[0], pk[1]};
+          if (it + 1 < NT) fetch(it + 1);  // the next block's inputs travel during this step
           float al[2][4], qv[2][4], kv[2][4];
   #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const bool valid = kFull || t0 + 2 * tp + j < T_;  // padding: no decay, no write, no read
-            const float gr[4] = {pg[j].x, pg[j].y, pg[j].z, pg[j].w};
-            In<T>::unpack4(pq[j], qv[j]);
-            In<T>::unpack4(pk[j], kv[j]);
+            const float gr[4] = {g_in[j].x, g_in[j].y, g_in[j].z, g_in[j].w};
+            In<T>::unpack4(q_in[j], qv[j]);
+            In<T>::unpack4(k_in[j], kv[j]);
   #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const float a = exp_f(gate_log_decay_k<GK>(gr[c], bias4[c], rate, p.lower_bound));
+              const float a = gate_alpha<GK>(gr[c], bias4[c], gc);
               al[j][c] = valid ? a : 1.0f;
               qv[j][c] = valid ? qv[j][c] : 0.0f;
               kv[j][c] = valid ? kv[j][c] : 0.0f;
             }
           }
-          if (it + 1 < NT) fetch(it + 1);  // the next block's inputs travel meanwhile
-          float E[2][4], Sf[2][4], ig[4];
+          // Products over the token pairs of an 8-lane segment by DPP row shifts,
+          // each shift applied to the four channels together: inclusive prefix
+          // x and suffix z of the pair products.
+          float x[4], z[4], y;
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) x[c] = z[c] = al[0][c] * al[1][c];
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) { y = row_shr<1>(x[c]); if (tp >= 1) x[c] *= y; }
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) { y = row_shl<1>(z[c]); if (tp < 7) z[c] *= y; }
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) { y = row_shr<2>(x[c]); if (tp >= 2) x[c] *= y; }
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) { y = row_shl<2>(z[c]); if (tp < 6) z[c] *= y; }
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) { y = row_shr<4>(x[c]); if (tp >= 4) x[c] *= y; }
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) { y = row_shl<4>(z[c]); if (tp < 4) z[c] *= y; }
+          float E[2][4], Sf[2][4], ig[4], gam[4];
   #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            // prefix products over the token pairs of an 8-lane segment (DPP row shifts)
-            const float pair = al[0][c] * al[1][c];
-            float x = pair, y;
-            y = row_shr<1>(x); if (tp >= 1) x *= y;
-            y = row_shr<2>(x); if (tp >= 2) x *= y;
-            y = row_shr<4>(x); if (tp >= 4) x *= y;
-            float ex = row_shr<1>(x);
+            float ex = row_shr<1>(x[c]);  // exclusive prefix
             if (tp == 0) ex = 1.0f;
-            E[0][c] = ex * al[0][c];
-            E[1][c] = x;
-            // suffix products, exclusive of the lane's own pair
-            float z = pair;
-            y = row_shl<1>(z); if (tp < 7) z *= y;
-            y = row_shl<2>(z); if (tp < 6) z *= y;
-            y = row_shl<4>(z); if (tp < 4) z *= y;
-            float sx = row_shl<1>(z);
+            float sx = row_shl<1>(z[c]);  // exclusive suffix
             if (tp == 7) sx = 1.0f;
+            E[0][c] = ex * al[0][c];
+            E[1][c] = x[c];
             Sf[1][c] = sx;
             Sf[0][c] = al[1][c] * sx;
-            const float gam = x * sx;  // decay over the whole block
-            overflow |= !(gam >= kGammaMin && gam <= kGammaMax);
-            ig[c] = __builtin_amdgcn_rcpf(gam);
-            if (tp == 0) B.gam[c0 + c] = gam;
+            gam[c] = x[c] * sx;  // decay over the whole block
+            overflow |= !(gam[c] >= kGammaMin && gam[c] <= kGammaMax);
+            ig[c] = __builtin_amdgcn_rcpf(gam[c]);
           }
+          if (tp == 0) *reinterpret_cast<float4*>(&B.gam[c0]) = float4{gam[0], gam[1], gam[2], gam[3]};
           float ke[2][4];
   #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -666,6 +675,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   } else {
     // ---- chain waves: value column block cb, state rows 16 kb + 4 (lane/16) + r
     const int cb = w - kChainWave0;
+    // The chain is the pipeline's critical path and shares its SIMD with a
+    // VALU-heavy prep wave: its instructions win the issue arbitration.
+    __builtin_amdgcn_s_setprio(2);
     const bool chain = cb >= 0 && cb < NCB;
     const int vcol = v0 + 16 * cb + (lane & 15);
     f32x4 sacc[NKB];
@@ -733,12 +745,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             if (lane < 16) p.o[(row * HV + hv) * V + vcol] = scale * op;
           }
         } else {
+          const int g = lane >> 4;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {  // diag(gamma) S first: needs nothing below
+            const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * kb + 4 * g]);
+            sacc[kb] *= f32x4{gm.x, gm.y, gm.z, gm.w};
+          }
           f32x4 pk = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
           if constexpr (F32)
             kprod2(pk, qs, B.kh, B.qh, C.st[tc & 1], lane);  // K_hat S and Q_hat S
           else
             kprod(pk, B.kh, 0, C.st[tc & 1], 0, lane);        // K_hat S
-          const int g = lane >> 4;
           const float4 bt4 = *reinterpret_cast<const float4*>(&B.beta[4 * g]);
           float vv[4];  // v of tokens 4g .. 4g+3 in this lane's column (padding: 0)
           if constexpr (F32) {
@@ -761,12 +778,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             wave_lds_sync();
             tprod(ov, sm.aqk[tc & 1], 0, C.f.u, lane);
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-              const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * kb + 4 * g]);
-              f32x4 acc = sacc[kb] * f32x4{gm.x, gm.y, gm.z, gm.w};
-              tprod(acc, B.keT, 16 * kb, C.f.u, lane);
-              sacc[kb] = acc;
-            }
+            for (int kb = 0; kb < NKB; ++kb) tprod(sacc[kb], B.keT, 16 * kb, C.f.u, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int t = t0 + 4 * g + r;
@@ -784,12 +796,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               sm.uo.u[cb][tc & 1][lane] = uint4{h2.x, h2.y, l2.x, l2.y};
             }
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {               // S = gamma S + (k Suf)^T U
-              const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * kb + 4 * g]);
-              f32x4 acc = sacc[kb] * f32x4{gm.x, gm.y, gm.z, gm.w};
-              tprod_reg(acc, B.keT.c + 16 * kb * kCat, uh, ul, lane);
-              sacc[kb] = acc;
-            }
+            for (int kb = 0; kb < NKB; ++kb)  // S = gamma S + (k Suf)^T U
+              tprod_reg(sacc[kb], B.keT.c + 16 * kb * kCat, uh, ul, lane);
           }
         }
         write_state_operand(C.st[(tc + 1) & 1]);

@@ -31,6 +31,27 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16_bits(x - static_cast<float>(h));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// The same split for two values at once, packed: hi = the bf16 pair of x0, x1
+// (round to nearest even) and lo = the bf16 pair of the remainders x - hi.
+// The remainders come from v_dot2c_f32_bf16 as x + hi . m with m = (-1, 0)
+// or (0, -1): the products are exact and x - hi is representable, so the one
+// rounding of the dot product is exact.  The masks live in scalar registers
+// behind an empty asm, which keeps the compiler from encoding (-1, 0) as the
+// inline constant -1.0 (the hardware reads that constant as the f32 bit
+// pattern 0xbf800000, i.e. the pair (0, -1)).
+__device__ __forceinline__ void split2_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  uint32_t m0 = 0x0000bf80u, m1 = 0xbf800000u;
+  asm("" : "+s"(m0), "+s"(m1));
+  const bf16x2 h = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+  const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m0), x0, false);
+  const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m1), x1, false);
+  const bf16x2 l = {static_cast<__bf16>(l0), static_cast<__bf16>(l1)};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
 // log(1 + e) for e in [0, 1]; a short series where 1 + e would round.
@@ -84,6 +105,29 @@ __device__ __forceinline__ float gate_log_decay_k(float graw, float bias, float 
     return -rate * softplus_f(graw + bias);
   } else {
     return graw;
+  }
+}
+
+// Retain factor alpha = exp(g) of the same gate, with the per-head constants
+// folded into cr = -rate log2(e) and cl = L log2(e):
+//   safe     : alpha = 2^(cl / (1 + 2^(cr (g_raw + bias))))
+//   standard : alpha = 2^(cr softplus(g_raw + bias))
+//   none     : alpha = 2^(g_raw log2(e))
+struct GateConsts {
+  float cr, cl;
+};
+__device__ __forceinline__ GateConsts gate_consts(float rate, float L) {
+  return GateConsts{-rate * kLog2e, L * kLog2e};
+}
+template <int GK>
+__device__ __forceinline__ float gate_alpha(float graw, float bias, GateConsts gc) {
+  if constexpr (GK == KDA_GATE_SAFE) {
+    return __builtin_amdgcn_exp2f(
+        gc.cl * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gc.cr * (graw + bias))));
+  } else if constexpr (GK == KDA_GATE_STANDARD) {
+    return __builtin_amdgcn_exp2f(gc.cr * softplus_f(graw + bias));
+  } else {
+    return __builtin_amdgcn_exp2f(graw * kLog2e);
   }
 }
 
