@@ -5,7 +5,9 @@ H=HV=16, K=V=128, chunk 64, bf16 q/k/v, fp32 gate inputs and state, safe
 gate): gate, cumulative decay, intra-chunk solve and inter-chunk propagation,
 all in one launch of the fused chunk kernel.  The recurrent decode row is
 timed in the same run on the decode workload (B=256, HV=32, 256 single-token
-steps over a 512 MiB fp32 state) and reported in the "decode" object.
+steps over a 512 MiB fp32 state) and reported in the "decode" object; the
+fused multi-token recurrent forward runs the same 256 tokens as 16-token calls
+and as one 256-token call ("recurrent" object).
 
 Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
 HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
@@ -53,6 +55,15 @@ def decode_bytes(w):
     e = 2 if w.dtype == "bf16" else 4
     return (2 * w.B * w.HV * w.K * w.V * 4 + 2 * w.B * w.H * w.K * e + w.B * w.HV * w.V * e
             + w.B * w.HV * w.K * 4 + w.B * w.HV * 4 + w.B * w.HV * w.V * 4)
+
+
+def recurrent_bytes(w, tokens):
+    """One multi-token call: the fp32 state read and written once, plus q, k,
+    v, g_raw, beta and o of every token of the call."""
+    e = 2 if w.dtype == "bf16" else 4
+    per_token = (2 * w.B * w.H * w.K * e + w.B * w.HV * w.V * e + w.B * w.HV * w.K * 4
+                 + w.B * w.HV * 4 + w.B * w.HV * w.V * 4)
+    return 2 * w.B * w.HV * w.K * w.V * 4 + tokens * per_token
 
 
 def measured_traffic(key):
@@ -190,6 +201,47 @@ def main():
                          "bytes_per_launch": decode_bytes(wd)},
         }
         del qs, ks, vs, gs, bs, od, st
+
+        # The fused multi-token recurrent forward on the same workload: the 256
+        # tokens as 16 calls of 16 tokens (state handed from call to call, so
+        # read and written once per call) and as one call of 256 tokens.
+        gd = {n: dd[n].to(dev) for n in ("q", "k", "v", "g_raw", "beta")}
+        st = dd["S0"].to(dev)
+        rec = {"workload": wd.name, "B": wd.B, "HV": wd.HV, "K": wd.K, "V": wd.V,
+               "tokens": wd.steps, "kernel": "recurrent_fwd_kernel<128, 128, bf16>"}
+        for per_call in (16, wd.steps):
+            calls = wd.steps // per_call
+            chunks = [{n: gd[n][:, c * per_call:(c + 1) * per_call].contiguous() for n in gd}
+                      for c in range(calls)]
+            outs = [torch.empty((wd.B, per_call, wd.HV, wd.V), dtype=torch.float32, device=dev)
+                    for _ in range(calls)]
+
+            def rcall(c):
+                x = chunks[c]
+                kda.recurrent_fwd(x["q"], x["k"], x["v"], x["g_raw"], x["beta"], A_log, dtb,
+                                  gate=wd.gate, lower_bound=wd.lower_bound, initial_state=st,
+                                  final_state=st, o=outs[c])
+
+            rcall(0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for c in range(calls):
+                rcall(c)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rms_ = e0.elapsed_time(e1)
+            nbytes = recurrent_bytes(wd, per_call)
+            gbs = nbytes * calls / (rms_ * 1e-3) / 1e9
+            rec["calls_of_%d" % per_call] = {
+                "calls": calls, "value": wd.B * wd.steps / (rms_ * 1e-3), "unit": "tokens/s",
+                "ms_per_call": rms_ / calls,
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                             "bytes_per_launch": nbytes}}
+            del chunks, outs
+        result["recurrent"] = rec
+        del gd, st
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4

@@ -21,8 +21,9 @@
  * Two schedules of the same recurrence ("DeltaNet family" page, sections on
  * the fused recurrent kernel and on chunkwise KDA): kda_chunk_fwd processes a
  * whole sequence chunk by chunk (intra-chunk dependencies resolved by a
- * lower-triangular solve, the state carried between chunks); kda_recurrent_step
- * advances the state by one token.
+ * lower-triangular solve, the state carried between chunks); kda_recurrent_fwd
+ * runs the tokens of a call one by one with the state kept on chip, and
+ * kda_recurrent_step advances a state held in HBM by one token.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers to contiguous row-major memory
@@ -139,6 +140,33 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, kda_d
                               const float* dt_bias, kda_gate_kind gate, float lower_bound,
                               float* state, float* o, int B, int H, int HV, int K, int V,
                               kda_stream_t stream);
+
+/*
+ * kda_recurrent_fwd -- the fused recurrent schedule over T tokens per call
+ * ("DeltaNet family" page, fused recurrent mode, which loops over time with the
+ * state on chip): per (sequence, value head, value tile) the state tile is read
+ * from initial_state once, advanced through the T tokens in registers, and
+ * written to final_state once.  Meant for short prefills and multi-token
+ * (speculative) decode, where the chunked path's fixed cost does not pay off;
+ * the result equals T calls of kda_recurrent_step up to rounding.
+ *
+ *   q, k          [B, T, H, K]   float32 or bfloat16 (qkv_dtype)
+ *   v             [B, T, HV, V]  same dtype
+ *   g_raw         [B, T, HV, K]  float32
+ *   beta          [B, T, HV]     float32
+ *   A_log, dt_bias, gate, lower_bound: as kda_gate
+ *   initial_state [B, HV, K, V]  float32, or NULL for zeros
+ *   o             [B, T, HV, V]  float32 output
+ *   final_state   [B, HV, K, V]  float32 output, or NULL; may alias initial_state
+ * Supported: K, V in {16, 32, 64, 128} (independently); HV % H == 0; any
+ * T >= 0 (T == 0 copies the initial state, or zeros, to final_state).
+ * Arithmetic is fp32 throughout (bf16 inputs are widened exactly).
+ */
+kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                             const float* g_raw, const float* beta, const float* A_log,
+                             const float* dt_bias, kda_gate_kind gate, float lower_bound,
+                             const float* initial_state, float* o, float* final_state, int B,
+                             int T, int H, int HV, int K, int V, kda_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,7 @@ computation runs in the HIP kernels of ``libkda.so``.
 
 * :func:`gate`           -- gate activation (+ optional chunk-local cumulative sum)
 * :func:`chunk_fwd`      -- chunkwise forward over whole sequences
+* :func:`recurrent_fwd`  -- T tokens per call with the state kept on chip
 * :func:`recurrent_step` -- one decode token, state updated in place
 """
 from __future__ import annotations
@@ -14,7 +15,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["gate", "chunk_fwd", "recurrent_step", "chunk_fwd_workspace_bytes", "KDAError"]
+__all__ = ["gate", "chunk_fwd", "recurrent_fwd", "recurrent_step", "chunk_fwd_workspace_bytes",
+           "KDAError"]
 
 KDAError = _lib.KDAError
 
@@ -115,6 +117,49 @@ def chunk_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_b
                            _ptr(o), _ptr(final_state), B, T, H, HV, K, V, int(chunk_size),
                            _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check("kda_chunk_fwd", st)
+    return o, final_state
+
+
+def _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias, initial_state):
+    dev = q.device
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    dt = q.dtype
+    _need(q, "q", dt, (B, T, H, K), dev)
+    _need(k, "k", dt, (B, T, H, K), dev)
+    _need(v, "v", dt, (B, T, HV, V), dev)
+    _need(g_raw, "g_raw", torch.float32, (B, T, HV, K), dev)
+    _need(beta, "beta", torch.float32, (B, T, HV), dev)
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, (HV,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (B, HV, K, V), dev)
+    return dev, B, T, H, HV, K, V
+
+
+def recurrent_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_bound=-5.0,
+                  initial_state=None, output_final_state=True, o=None, final_state=None):
+    """Fused recurrent forward over the T tokens of a call, the state kept on
+    chip.  Arguments and returns as :func:`chunk_fwd` (no chunk size); K and V
+    may differ.  ``final_state`` may be the ``initial_state`` tensor itself."""
+    lib = _lib.load()
+    qkv = _qkv_dtype(q)
+    dev, B, T, H, HV, K, V = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
+                                                  initial_state)
+    if o is None:
+        o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (B, HV, K, V), dev)
+    st = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta),
+                               _ptr(A_log), _ptr(dt_bias), _lib.GATES[gate], float(lower_bound),
+                               _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, HV, K, V,
+                               _stream(dev))
+    _lib.check("kda_recurrent_fwd", st)
     return o, final_state
 
 

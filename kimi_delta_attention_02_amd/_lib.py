@@ -27,6 +27,8 @@ SIGNATURES = {
                                _vp, _vp] + [_c_int] * 7 + [_vp, ctypes.c_size_t, _vp]),
     "kda_recurrent_step": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_float,
                                     _vp, _vp] + [_c_int] * 5 + [_vp]),
+    "kda_recurrent_fwd": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_float,
+                                   _vp, _vp, _vp] + [_c_int] * 6 + [_vp]),
 }
 
 _lib = None

@@ -15,6 +15,11 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, int bf16,
                          const float* g_raw, const float* beta, const float* A_log,
                          const float* dt_bias, int kind, float lower_bound, float* state,
                          float* o, int B, int H, int HV, int K, int V, hipStream_t stream);
+hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf16,
+                            const float* g_raw, const float* beta, const float* A_log,
+                            const float* dt_bias, int kind, float lower_bound, const float* S0,
+                            float* o, float* S_out, int B, int T, int H, int HV, int K, int V,
+                            hipStream_t stream);
 hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
                         float lower_bound, const float* S0, float* o, float* S_out, int B, int T,
@@ -119,6 +124,28 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, kda_d
   return from_hip(kda::launch_decode(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log, dt_bias,
                                      (int)gate, lower_bound, state, o, B, H, HV, K, V,
                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                             const float* g_raw, const float* beta, const float* A_log,
+                             const float* dt_bias, kda_gate_kind gate, float lower_bound,
+                             const float* initial_state, float* o, float* final_state, int B,
+                             int T, int H, int HV, int K, int V, kda_stream_t stream) {
+  kda_status st = check_gate(gate, lower_bound, A_log);
+  if (st != KDA_OK) return st;
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0) return KDA_ERR_INVALID_ARG;
+  if ((long)B * HV > (1L << 28)) return KDA_ERR_INVALID_ARG;
+  if (!head_size_ok(K) || !head_size_ok(V)) return KDA_ERR_UNSUPPORTED;
+  if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, g_raw, o, initial_state, final_state, dt_bias};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+  if (B == 0) return KDA_OK;
+  return from_hip(kda::launch_recurrent(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log,
+                                        dt_bias, (int)gate, lower_bound, initial_state, o,
+                                        final_state, B, T, H, HV, K, V,
+                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -150,6 +150,216 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused recurrent forward over T tokens per call: the same per-token step with
+// the state tile held in registers across all tokens, read from the initial
+// state once and written to the final state once ("DeltaNet family" page, the
+// fused recurrent kernel: one program per (sequence, head, value tile) looping
+// over time).  Per token: exp(g), k and q rows of the next token are formed in
+// a second LDS buffer while the current token runs, so each token costs two
+// barriers (after the prediction partials and after the read partials); the
+// HBM inputs of a token are loaded one token ahead.
+
+struct RecurrentParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g_raw;
+  const float* beta;
+  const float* A_log;
+  const float* dt_bias;
+  const float* S0;
+  float* S_out;
+  float* o;
+  int B, T, H, HV, kind;
+  float lower_bound;
+};
+
+template <int K, int V, typename T, int GK>
+__global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecurrentParams p) {
+  using D = DecodeTiling<K, V>;
+  constexpr int TV = D::TV, NQ = D::NQ, RG = D::RG, WT = D::WT, RPL = D::RPL, NVT = D::NVT,
+                TPW = D::TPW;
+  static_assert(TPW * K <= 256, "one decay/key/query element per thread");
+  __shared__ float s_al[2][TPW][K], s_k[2][TPW][K], s_q[2][TPW][K];
+  __shared__ f32x4 s_red[2][4][NQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int T_ = p.T, HV = p.HV, H = p.H;
+  const long nheads = (long)p.B * HV;
+  const long tile0 = (long)blockIdx.x * TPW;
+  const long ntiles = nheads * NVT;
+
+  // ---- the decay / key / query element of this thread: tile slot gts, row gr
+  const bool gthread = tid < TPW * K;
+  const int gts = tid / K, gr = tid % K;
+  const bool gactive = gthread && tile0 + gts < ntiles;
+  const long gbh = gactive ? (tile0 + gts) / NVT : 0;  // b * HV + hv
+  const int ghv = (int)(gbh % HV);
+  const long gb = gbh / HV;
+  const int gh = ghv / (HV / H);
+  const GateConsts gc = gate_consts(GK != KDA_GATE_NONE ? exp_f(p.A_log[ghv]) : 1.0f, p.lower_bound);
+  const float gbias = (p.dt_bias && GK != KDA_GATE_NONE && gactive) ? p.dt_bias[(long)ghv * K + gr] : 0.0f;
+  const float* g_ptr = p.g_raw + (gb * T_ * HV + ghv) * (long)K + gr;
+  const T* k_ptr = static_cast<const T*>(p.k) + (gb * T_ * H + gh) * (long)K + gr;
+  const T* q_ptr = static_cast<const T*>(p.q) + (gb * T_ * H + gh) * (long)K + gr;
+  float pg = 0.0f;
+  typename In<T>::Raw1 pk = In<T>::zero1(), pq = In<T>::zero1();
+  auto fetch_g = [&](int t) {
+    if (gactive) {
+      pg = g_ptr[(long)t * HV * K];
+      pk = k_ptr[(long)t * H * K];
+      pq = q_ptr[(long)t * H * K];
+    }
+  };
+  auto put_g = [&](int buf) {
+    if (gthread) {
+      s_al[buf][gts][gr] = gactive ? gate_alpha<GK>(pg, gbias, gc) : 1.0f;
+      s_k[buf][gts][gr] = gactive ? In<T>::widen(pk) : 0.0f;
+      s_q[buf][gts][gr] = gactive ? In<T>::widen(pq) : 0.0f;
+    }
+  };
+
+  // ---- the state tile of this thread (layout of the decode step)
+  const int ts = w / WT, rq = w % WT;
+  const long tile = tile0 + ts;
+  const bool active = tile < ntiles;
+  const long bh = active ? tile / NVT : 0;
+  const int vt = (int)(tile % NVT);
+  const int cq = lane % NQ, rg = lane / NQ;
+  const int col = vt * TV + cq * 4;
+  const int row0 = rq * (K / WT) + rg;
+  const long b = bh / HV;
+  const int hv = (int)(bh % HV);
+  f32x4 s[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (active && p.S0) {
+    const float* S = p.S0 + bh * (long)K * V;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (long)(row0 + RG * i) * V + col));
+  }
+  const T* v_ptr = static_cast<const T*>(p.v) + (b * T_ * HV + hv) * (long)V + col;
+  const float* beta_ptr = p.beta + b * T_ * HV + hv;
+  float* o_ptr = p.o + (b * T_ * HV + hv) * (long)V + col;
+  float pv[4] = {0.f, 0.f, 0.f, 0.f}, pb = 0.0f;
+  auto fetch_v = [&](int t) {
+    if (active) {
+      In<T>::load4(v_ptr, (long)t * HV * V, pv);
+      pb = beta_ptr[(long)t * HV];
+    }
+  };
+  const float scale = 1.0f / __builtin_sqrtf((float)K);
+
+  if (T_ > 0) {
+    fetch_g(0);
+    fetch_v(0);
+    put_g(0);
+    if (T_ > 1) fetch_g(1);
+  }
+  __syncthreads();
+  for (int t = 0; t < T_; ++t) {
+    const int buf = t & 1;
+    const float vv[4] = {pv[0], pv[1], pv[2], pv[3]};
+    const float bt = pb;
+    if (t + 1 < T_) fetch_v(t + 1);
+
+    // decay, then the prediction k . S_dec: in-wave butterfly, then across the WT waves
+    f32x4 pr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int r = row0 + RG * i;
+      s[i] *= s_al[buf][ts][r];
+      pr += s_k[buf][ts][r] * s[i];
+    }
+#pragma unroll
+    for (int m = NQ; m < 64; m <<= 1)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pr[c] += __shfl_xor(pr[c], m);
+    if (rg == 0) s_red[0][w][cq] = pr;
+    __syncthreads();
+
+    // residual, rank-1 write, read q . S_new
+    pr = s_red[0][ts * WT][cq];
+#pragma unroll
+    for (int j = 1; j < WT; ++j) pr += s_red[0][ts * WT + j][cq];
+    f32x4 rv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rv[c] = bt * (vv[c] - pr[c]);
+    f32x4 ov = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int r = row0 + RG * i;
+      s[i] += s_k[buf][ts][r] * rv;
+      ov += s_q[buf][ts][r] * s[i];
+    }
+#pragma unroll
+    for (int m = NQ; m < 64; m <<= 1)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ov[c] += __shfl_xor(ov[c], m);
+    if (rg == 0) s_red[1][w][cq] = ov;
+    if (t + 1 < T_) {  // the next token's rows; that buffer was last read before the last barrier
+      put_g(buf ^ 1);
+      if (t + 2 < T_) fetch_g(t + 2);
+    }
+    __syncthreads();
+    if (active && rq == 0 && rg == 0) {
+      f32x4 o = s_red[1][ts * WT][cq];
+#pragma unroll
+      for (int j = 1; j < WT; ++j) o += s_red[1][ts * WT + j][cq];
+      *reinterpret_cast<f32x4*>(o_ptr + (long)t * HV * V) = o * scale;
+    }
+  }
+  if (active && p.S_out) {
+    float* S = p.S_out + bh * (long)K * V;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (long)(row0 + RG * i) * V + col));
+  }
+}
+
+template <int K, int V, typename T, int GK>
+static hipError_t launch_recurrent_kv(const RecurrentParams& p, hipStream_t stream) {
+  using D = DecodeTiling<K, V>;
+  const long tiles = (long)p.B * p.HV * D::NVT;
+  const long blocks = (tiles + D::TPW - 1) / D::TPW;
+  hipLaunchKernelGGL((recurrent_fwd_kernel<K, V, T, GK>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int GK>
+static hipError_t launch_recurrent_t(const RecurrentParams& p, int K, int V, hipStream_t stream) {
+#define KDA_REC_CASE(KK, VV) \
+  if (K == KK && V == VV) return launch_recurrent_kv<KK, VV, T, GK>(p, stream);
+#define KDA_REC_ROW(KK) KDA_REC_CASE(KK, 16) KDA_REC_CASE(KK, 32) KDA_REC_CASE(KK, 64) KDA_REC_CASE(KK, 128)
+  KDA_REC_ROW(16) KDA_REC_ROW(32) KDA_REC_ROW(64) KDA_REC_ROW(128)
+#undef KDA_REC_ROW
+#undef KDA_REC_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t launch_recurrent_g(const RecurrentParams& p, int K, int V, hipStream_t stream) {
+  switch (p.kind) {
+    case KDA_GATE_SAFE: return launch_recurrent_t<T, KDA_GATE_SAFE>(p, K, V, stream);
+    case KDA_GATE_STANDARD: return launch_recurrent_t<T, KDA_GATE_STANDARD>(p, K, V, stream);
+    default: return launch_recurrent_t<T, KDA_GATE_NONE>(p, K, V, stream);
+  }
+}
+
+hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf16,
+                            const float* g_raw, const float* beta, const float* A_log,
+                            const float* dt_bias, int kind, float lower_bound, const float* S0,
+                            float* o, float* S_out, int B, int T, int H, int HV, int K, int V,
+                            hipStream_t stream) {
+  RecurrentParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, S_out, o, B, T, H, HV, kind,
+                    lower_bound};
+  return bf16 ? launch_recurrent_g<uint16_t>(p, K, V, stream)
+              : launch_recurrent_g<float>(p, K, V, stream);
+}
+
 template <int K, int V, typename T, int GK>
 static hipError_t launch_decode_kv(const DecodeParams& p, hipStream_t stream) {
   using D = DecodeTiling<K, V>;

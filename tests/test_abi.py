@@ -38,7 +38,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["kda_status_string", "kda_version", "kda_gate",
                                   "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-                                  "kda_recurrent_step"])
+                                  "kda_recurrent_step", "kda_recurrent_fwd"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -123,6 +123,32 @@ def test_gate_none_needs_no_A_log(lib):
 ])
 def test_recurrent_step_validation(lib, kw, status):
     assert _step(lib, **kw) == status
+
+
+def _rec(lib, **kw):
+    a = dict(q=P, k=P, v=P, dt=_lib.KDA_BF16, g=P, beta=P, A=P, bias=None, gate=1, L=-5.0,
+             S0=None, o=P, S=P, B=2, T=16, H=2, HV=4, K=128, V=64)
+    a.update(kw)
+    return lib.kda_recurrent_fwd(a["q"], a["k"], a["v"], a["dt"], a["g"], a["beta"], a["A"],
+                                 a["bias"], a["gate"], a["L"], a["S0"], a["o"], a["S"], a["B"],
+                                 a["T"], a["H"], a["HV"], a["K"], a["V"], None)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(HV=3), _lib.KDA_ERR_INVALID_ARG),
+    (dict(v=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(o=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(S0=P + 8), _lib.KDA_ERR_INVALID_ARG),       # misaligned initial state
+    (dict(T=-2), _lib.KDA_ERR_INVALID_ARG),
+    (dict(A=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(K=24), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(V=256), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(gate=2, A=None, B=0), _lib.KDA_OK),
+    (dict(B=0), _lib.KDA_OK),
+])
+def test_recurrent_fwd_validation(lib, kw, status):
+    assert _rec(lib, **kw) == status
 
 
 @needs_no_gpu
