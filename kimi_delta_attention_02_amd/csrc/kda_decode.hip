@@ -7,17 +7,18 @@
 // owning a tile of the state for the whole step.
 //
 // The step is bound by HBM: the fp32 state [K, V] of every (b, hv) is read once
-// and written once.  A K x TV column tile (TV = min(V, 32)) is split by rows
-// over WT wavefronts (four for K = 128), so each lane keeps only RPL = 4
-// 16-byte rows in flight: many short streams reach a higher fraction of HBM
-// bandwidth than few long ones on this part.  In a wavefront, lane l holds
-// column quad cq = l % NQ (NQ lanes cover one 128-byte row segment) and rows
-// row0 + RG * i of row group rg = l / NQ, so every load instruction reads RG
-// full row segments; all loads are issued before any arithmetic.  The two
-// reductions over kappa (prediction k.S_dec and read q.S_new) run as
-// log2(RG) butterfly shuffles inside each wavefront, then one LDS exchange
-// across the WT wavefronts of the tile.  The decay factors exp(g) and the key
-// and query rows are computed once per workgroup into LDS.
+// and written once.  A K x TV column tile (TV = min(V, 64)) is split by rows
+// over WT wavefronts (four for K = 128), so each lane keeps only RPL 16-byte
+// rows in flight: many short streams reach a higher fraction of HBM bandwidth
+// than few long ones on this part.  In a wavefront, lane l holds column quad
+// cq = l % NQ (NQ lanes cover one row segment of the tile) and rows row0 + RG i
+// of row group rg = l / NQ, so every load instruction reads RG full row
+// segments; all loads are issued before any arithmetic.  The two reductions
+// over kappa (prediction k.S_dec and read q.S_new) run as log2(RG) butterfly
+// steps inside each wavefront (row swaps for the 16- and 32-lane distances),
+// then one LDS exchange across the WT wavefronts of the tile.  The decay
+// factors exp(g) and the key and query rows are computed once per workgroup
+// into LDS.
 #include "kda_device.h"
 
 namespace kda {
@@ -35,6 +36,19 @@ struct DecodeParams {
   int B, H, HV, kind;
   float lower_bound;
 };
+
+// Sum over the lanes of a wavefront that share l % NQ (the row groups), for
+// the four components at once.
+template <int NQ>
+__device__ __forceinline__ f32x4 sum_row_groups(f32x4 v) {
+  if constexpr (NQ < 64) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = xor_sum<NQ>(v[c]);
+    return sum_row_groups<2 * NQ>(v);
+  } else {
+    return v;
+  }
+}
 
 template <int K, int V>
 struct DecodeTiling {
@@ -109,10 +123,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
       pr += s_k[ts][r] * s[i];
     }
   }
-#pragma unroll
-  for (int m = NQ; m < 64; m <<= 1)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) pr[c] += __shfl_xor(pr[c], m);
+  pr = sum_row_groups<NQ>(pr);
   if (rg == 0) s_red[0][w][cq] = pr;
   __syncthreads();
   pr = s_red[0][ts * WT][cq];
@@ -135,10 +146,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
     for (int i = 0; i < RPL; ++i)
       __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (long)(row0 + RG * i) * V + col));
   }
-#pragma unroll
-  for (int m = NQ; m < 64; m <<= 1)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ov[c] += __shfl_xor(ov[c], m);
+  ov = sum_row_groups<NQ>(ov);
   if (rg == 0) s_red[1][w][cq] = ov;
   __syncthreads();
   if (active && rq == 0 && rg == 0) {
@@ -273,10 +281,7 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecurrentParams p) {
       s[i] *= s_al[buf][ts][r];
       pr += s_k[buf][ts][r] * s[i];
     }
-#pragma unroll
-    for (int m = NQ; m < 64; m <<= 1)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) pr[c] += __shfl_xor(pr[c], m);
+    pr = sum_row_groups<NQ>(pr);
     if (rg == 0) s_red[0][w][cq] = pr;
     __syncthreads();
 
@@ -294,10 +299,7 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecurrentParams p) {
       s[i] += s_k[buf][ts][r] * rv;
       ov += s_q[buf][ts][r] * s[i];
     }
-#pragma unroll
-    for (int m = NQ; m < 64; m <<= 1)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ov[c] += __shfl_xor(ov[c], m);
+    ov = sum_row_groups<NQ>(ov);
     if (rg == 0) s_red[1][w][cq] = ov;
     if (t + 1 < T_) {  // the next token's rows; that buffer was last read before the last barrier
       put_g(buf ^ 1);

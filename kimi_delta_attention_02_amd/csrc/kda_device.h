@@ -95,6 +95,28 @@ __device__ __forceinline__ float row_shl(float x) {  // lane p reads lane p + N
                                                                0x100 + N, 0xF, 0xF, false));
 }
 
+// x + x[lane ^ M] in every lane.  For M = 16 and 32 this uses the gfx950 row
+// swaps (VALU, no LDS round trip): v_permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even rows of its second, and
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second, so with x in both operands the two results add up to x plus its
+// partner in every lane.  They are written in asm because the compiler at hand
+// reads both results of the builtin from one register.  The nop gives the two
+// wait states the compiler itself places between a VALU write and the swap.
+template <int M>
+__device__ __forceinline__ float xor_sum(float x) {
+  if constexpr (M == 16 || M == 32) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    if constexpr (M == 16)
+      asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    else
+      asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  } else {
+    return x + __shfl_xor(x, M);
+  }
+}
+
 // The same gate with its kind fixed at compile time (no branch per element).
 template <int GK>
 __device__ __forceinline__ float gate_log_decay_k(float graw, float bias, float rate, float L) {
