@@ -7,7 +7,8 @@ all in one launch of the fused chunk kernel.  The recurrent decode row is
 timed in the same run on the decode workload (B=256, HV=32, 256 single-token
 steps over a 512 MiB fp32 state) and reported in the "decode" object; the
 fused multi-token recurrent forward runs the same 256 tokens as 16-token calls
-and as one 256-token call ("recurrent" object).
+and as one 256-token call ("recurrent" object), and the chunked forward runs the
+prefill shape with one gate per (token, value head) ("head_gate" object).
 
 Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
 HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
@@ -36,7 +37,7 @@ def chunk_bytes(w):
     (q, k once per query/key head), o written once, final (and initial) state."""
     qk = 2 * w.B * w.T * w.H * w.K * (2 if w.dtype == "bf16" else 4)
     v = w.B * w.T * w.HV * w.V * (2 if w.dtype == "bf16" else 4)
-    g = w.B * w.T * w.HV * w.K * 4
+    g = w.B * w.T * w.HV * (1 if w.per_head_gate else w.K) * 4
     beta = w.B * w.T * w.HV * 4
     o = w.B * w.T * w.HV * w.V * 4
     state = w.B * w.HV * w.K * w.V * 4 * (2 if w.s0_std > 0 else 1)
@@ -164,6 +165,40 @@ def main():
         "wall_s_timed": t_wall,
     }
     del o, S, g
+
+    # The same chunked forward with one gate per (token, value head) (the
+    # Gated DeltaNet form) on the prefill shape.
+    wh = synth.WORKLOADS["prefill_head_gate"]
+    dh = synth.make_inputs(wh)
+    gh = {n: (t.to(dev) if t is not None else None) for n, t in dh.items()}
+    oh = torch.empty((wh.B, wh.T, wh.HV, wh.V), dtype=torch.float32, device=dev)
+    Sh = torch.empty((wh.B, wh.HV, wh.K, wh.V), dtype=torch.float32, device=dev)
+
+    def hstep():
+        kda.chunk_fwd(gh["q"], gh["k"], gh["v"], gh["g_raw"], gh["beta"], gh["A_log"],
+                      gh["dt_bias"], gate=wh.gate, lower_bound=wh.lower_bound,
+                      chunk_size=wh.chunk, initial_state=gh["S0"], o=oh, final_state=Sh)
+
+    for _ in range(args.warmup):
+        hstep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        hstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    hms = e0.elapsed_time(e1) / args.steps
+    hbytes = chunk_bytes(wh)
+    hgbs = hbytes / (hms * 1e-3) / 1e9
+    result["head_gate"] = {
+        "workload": wh.name, "B": wh.B, "T": wh.T, "H": wh.H, "HV": wh.HV, "K": wh.K,
+        "gate": wh.gate + ", one per (token, value head)", "value": wh.B * wh.T / (hms * 1e-3),
+        "unit": "tokens/s", "ms_per_step": hms,
+        "roofline": {"bound": "hbm", "achieved": hgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hgbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": hbytes,
+                     "kernel": "chunk_fwd_kernel<128, bf16, per-head gate>"}}
+    del gh, oh, Sh
 
     if not args.no_decode:
         wd = synth.WORKLOADS["decode"]

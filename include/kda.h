@@ -18,6 +18,14 @@
  * GVA: value head hv reads query/key head h = hv / (HV / H) (q and k are
  * shared by HV/H consecutive value heads, as repeat_interleave would do).
  *
+ * Per-head gates: KDA_GATE_PER_HEAD may be OR-ed into any gate kind.  The gate
+ * is then one scalar per (token, value head), shared by all key channels: the
+ * scalar retain gate of Gated DeltaNet ("DeltaNet family" page, "Gated
+ * DeltaNet"), of which KDA's channel-wise gate is the generalisation.  g_raw
+ * loses its K axis ([..., HV] instead of [..., HV, K]) and dt_bias is [HV];
+ * the same activation formulas apply.  DeltaNet itself is KDA_GATE_NONE with
+ * g_raw = 0.
+ *
  * Two schedules of the same recurrence ("DeltaNet family" page, sections on
  * the fused recurrent kernel and on chunkwise KDA): kda_chunk_fwd processes a
  * whole sequence chunk by chunk (intra-chunk dependencies resolved by a
@@ -27,7 +35,8 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers to contiguous row-major memory
- *    with the shapes given below, aligned to 16 bytes.  The caller owns every
+ *    with the shapes given below, aligned to 16 bytes (4 bytes suffice for
+ *    g_raw and dt_bias with KDA_GATE_PER_HEAD).  The caller owns every
  *    buffer; the library allocates nothing and keeps no global state.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
  *    default stream).  Nothing synchronises the host.  Input buffers must stay
@@ -57,7 +66,12 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
-typedef enum { KDA_GATE_STANDARD = 0, KDA_GATE_SAFE = 1, KDA_GATE_NONE = 2 } kda_gate_kind;
+typedef enum {
+  KDA_GATE_STANDARD = 0,
+  KDA_GATE_SAFE = 1,
+  KDA_GATE_NONE = 2,
+  KDA_GATE_PER_HEAD = 16 /* flag, OR-ed into one of the three kinds above */
+} kda_gate_kind;
 
 typedef struct ihipStream_t* kda_stream_t; /* the same type as hipStream_t */
 
@@ -73,14 +87,15 @@ int kda_version(void);
  * prefix sum of the log-decay ("DeltaNet family" page, chunkwise pipeline:
  * the cumulative log-decay whose differences give D_{j+1:i}).
  *
- *   g_raw   [B, T, HV, K] float32
+ *   g_raw   [B, T, HV, K] float32 ([B, T, HV] with KDA_GATE_PER_HEAD)
  *   A_log   [HV] float32                 rate = exp(A_log[hv])
- *   dt_bias [HV, K] float32 or NULL      NULL means zero bias
+ *   dt_bias [HV, K] float32 or NULL      NULL means zero bias ([HV] per head)
  *   gate, lower_bound                    lower_bound < 0 required for KDA_GATE_SAFE
  *   chunk_size  0: g_out = g;  C > 0: g_out[t] = sum of g over the tokens of
  *               t's chunk up to and including t (chunks of C tokens from t = 0)
- *   g_out   [B, T, HV, K] float32 (may alias g_raw)
- * Any K >= 1 is accepted.  B or T equal to 0 is a no-op.
+ *   g_out   the shape of g_raw, float32 (may alias g_raw)
+ * Any K >= 1 is accepted (K is ignored with KDA_GATE_PER_HEAD).  B or T equal
+ * to 0 is a no-op.
  */
 kda_status kda_gate(const float* g_raw, const float* A_log, const float* dt_bias,
                     kda_gate_kind gate, float lower_bound, int B, int T, int HV, int K,
@@ -93,10 +108,10 @@ kda_status kda_gate(const float* g_raw, const float* A_log, const float* dt_bias
  *
  *   q, k          [B, T, H, K]   float32 or bfloat16 (qkv_dtype)
  *   v             [B, T, HV, V]  same dtype as q and k
- *   g_raw         [B, T, HV, K]  float32
+ *   g_raw         [B, T, HV, K]  float32 ([B, T, HV] with KDA_GATE_PER_HEAD)
  *   beta          [B, T, HV]     float32
  *   A_log         [HV]           float32
- *   dt_bias       [HV, K]        float32 or NULL
+ *   dt_bias       [HV, K]        float32 or NULL ([HV] with KDA_GATE_PER_HEAD)
  *   initial_state [B, HV, K, V]  float32, or NULL for zeros
  *   o             [B, T, HV, V]  float32 output
  *   final_state   [B, HV, K, V]  float32 output, or NULL; may alias initial_state
@@ -128,7 +143,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
  *
  *   q, k    [B, H, K]        float32 or bfloat16 (qkv_dtype)
  *   v       [B, HV, V]       same dtype
- *   g_raw   [B, HV, K]       float32
+ *   g_raw   [B, HV, K]       float32 ([B, HV] with KDA_GATE_PER_HEAD)
  *   beta    [B, HV]          float32
  *   A_log   [HV], dt_bias [HV, K] or NULL, gate, lower_bound: as kda_gate
  *   state   [B, HV, K, V]    float32, read and overwritten with the new state
@@ -152,7 +167,7 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, kda_d
  *
  *   q, k          [B, T, H, K]   float32 or bfloat16 (qkv_dtype)
  *   v             [B, T, HV, V]  same dtype
- *   g_raw         [B, T, HV, K]  float32
+ *   g_raw         [B, T, HV, K]  float32 ([B, T, HV] with KDA_GATE_PER_HEAD)
  *   beta          [B, T, HV]     float32
  *   A_log, dt_bias, gate, lower_bound: as kda_gate
  *   initial_state [B, HV, K, V]  float32, or NULL for zeros

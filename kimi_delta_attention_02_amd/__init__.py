@@ -4,6 +4,10 @@ Every function marshals torch tensors (device memory, the current HIP stream)
 into the C ABI of ``include/kda.h`` and nothing else: each step of the
 computation runs in the HIP kernels of ``libkda.so``.
 
+Gates are per key channel (g_raw with a trailing K axis, dt_bias [HV, K]) or,
+when g_raw has no K axis, one scalar per (token, value head) as in Gated
+DeltaNet (dt_bias [HV]); the binding passes KDA_GATE_PER_HEAD for the latter.
+
 * :func:`gate`           -- gate activation (+ optional chunk-local cumulative sum)
 * :func:`chunk_fwd`      -- chunkwise forward over whole sequences
 * :func:`recurrent_fwd`  -- T tokens per call with the state kept on chip
@@ -40,6 +44,21 @@ def _need(t, name, dtype, shape, device):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
+def _gate_code(gate, per_head):
+    return _lib.GATES[gate] | (_lib.KDA_GATE_PER_HEAD if per_head else 0)
+
+
+def _check_gate_inputs(g_raw, dt_bias, A_log, lead, HV, K, dev):
+    """g_raw is lead + (HV, K) (per channel) or lead + (HV,) (per head)."""
+    per_head = g_raw.dim() == len(lead) + 1
+    _need(g_raw, "g_raw", torch.float32, tuple(lead) + ((HV,) if per_head else (HV, K)), dev)
+    if A_log is not None:
+        _need(A_log, "A_log", torch.float32, (HV,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (HV,) if per_head else (HV, K), dev)
+    return per_head
+
+
 def _qkv_dtype(q):
     if q.dtype == torch.float32:
         return _lib.KDA_F32
@@ -49,21 +68,21 @@ def _qkv_dtype(q):
 
 
 def gate(g_raw, A_log, dt_bias=None, *, gate="safe", lower_bound=-5.0, chunk_size=0, out=None):
-    """Gate activation of g_raw [B, T, HV, K] (float32); with chunk_size > 0 the
-    chunk-local inclusive cumulative sum of the log-decay.  Returns float32."""
+    """Gate activation of g_raw [B, T, HV, K] or, per head, [B, T, HV]
+    (float32); with chunk_size > 0 the chunk-local inclusive cumulative sum of
+    the log-decay.  Returns float32 of g_raw's shape."""
     lib = _lib.load()
     dev = g_raw.device
-    B, T, HV, K = g_raw.shape
-    _need(g_raw, "g_raw", torch.float32, (B, T, HV, K), dev)
-    if A_log is not None:
-        _need(A_log, "A_log", torch.float32, (HV,), dev)
-    if dt_bias is not None:
-        _need(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
+    if g_raw.dim() == 3:
+        (B, T, HV), K = g_raw.shape, 1
+    else:
+        B, T, HV, K = g_raw.shape
+    per_head = _check_gate_inputs(g_raw, dt_bias, A_log, (B, T), HV, K, dev)
     if out is None:
         out = torch.empty_like(g_raw)
-    _need(out, "out", torch.float32, (B, T, HV, K), dev)
-    st = lib.kda_gate(_ptr(g_raw), _ptr(A_log), _ptr(dt_bias), _lib.GATES[gate], float(lower_bound),
-                      B, T, HV, K, int(chunk_size), _ptr(out), _stream(dev))
+    _need(out, "out", torch.float32, tuple(g_raw.shape), dev)
+    st = lib.kda_gate(_ptr(g_raw), _ptr(A_log), _ptr(dt_bias), _gate_code(gate, per_head),
+                      float(lower_bound), B, T, HV, K, int(chunk_size), _ptr(out), _stream(dev))
     _lib.check("kda_gate", st)
     return out
 
@@ -79,28 +98,16 @@ def chunk_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_b
     """Chunkwise KDA forward.
 
     q, k [B, T, H, K] and v [B, T, HV, V] (float32 or bfloat16, one dtype);
-    g_raw [B, T, HV, K], beta [B, T, HV], A_log [HV], dt_bias [HV, K] or None,
-    initial_state [B, HV, K, V] or None (float32).  Returns (o, final_state)
-    with o [B, T, HV, V] float32 and final_state [B, HV, K, V] float32 (None
-    when output_final_state is False).
+    g_raw [B, T, HV, K] (or [B, T, HV] for a per-head gate), beta [B, T, HV],
+    A_log [HV], dt_bias [HV, K] (or [HV]) or None, initial_state [B, HV, K, V]
+    or None (float32).  Returns (o, final_state) with o [B, T, HV, V] float32
+    and final_state [B, HV, K, V] float32 (None when output_final_state is
+    False).
     """
     lib = _lib.load()
-    dev = q.device
-    B, T, H, K = q.shape
-    HV, V = v.shape[2], v.shape[3]
-    dt = q.dtype
     qkv = _qkv_dtype(q)
-    _need(q, "q", dt, (B, T, H, K), dev)
-    _need(k, "k", dt, (B, T, H, K), dev)
-    _need(v, "v", dt, (B, T, HV, V), dev)
-    _need(g_raw, "g_raw", torch.float32, (B, T, HV, K), dev)
-    _need(beta, "beta", torch.float32, (B, T, HV), dev)
-    if A_log is not None:
-        _need(A_log, "A_log", torch.float32, (HV,), dev)
-    if dt_bias is not None:
-        _need(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
-    if initial_state is not None:
-        _need(initial_state, "initial_state", torch.float32, (B, HV, K, V), dev)
+    dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
+                                                            initial_state)
     if o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
     _need(o, "o", torch.float32, (B, T, HV, V), dev)
@@ -113,7 +120,8 @@ def chunk_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_b
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta), _ptr(A_log),
-                           _ptr(dt_bias), _lib.GATES[gate], float(lower_bound), _ptr(initial_state),
+                           _ptr(dt_bias), _gate_code(gate, per_head), float(lower_bound),
+                           _ptr(initial_state),
                            _ptr(o), _ptr(final_state), B, T, H, HV, K, V, int(chunk_size),
                            _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check("kda_chunk_fwd", st)
@@ -128,15 +136,11 @@ def _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias, initial_state):
     _need(q, "q", dt, (B, T, H, K), dev)
     _need(k, "k", dt, (B, T, H, K), dev)
     _need(v, "v", dt, (B, T, HV, V), dev)
-    _need(g_raw, "g_raw", torch.float32, (B, T, HV, K), dev)
+    per_head = _check_gate_inputs(g_raw, dt_bias, A_log, (B, T), HV, K, dev)
     _need(beta, "beta", torch.float32, (B, T, HV), dev)
-    if A_log is not None:
-        _need(A_log, "A_log", torch.float32, (HV,), dev)
-    if dt_bias is not None:
-        _need(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
     if initial_state is not None:
         _need(initial_state, "initial_state", torch.float32, (B, HV, K, V), dev)
-    return dev, B, T, H, HV, K, V
+    return dev, B, T, H, HV, K, V, per_head
 
 
 def recurrent_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_bound=-5.0,
@@ -146,8 +150,8 @@ def recurrent_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", low
     may differ.  ``final_state`` may be the ``initial_state`` tensor itself."""
     lib = _lib.load()
     qkv = _qkv_dtype(q)
-    dev, B, T, H, HV, K, V = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
-                                                  initial_state)
+    dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
+                                                            initial_state)
     if o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
     _need(o, "o", torch.float32, (B, T, HV, V), dev)
@@ -156,7 +160,8 @@ def recurrent_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", low
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (B, HV, K, V), dev)
     st = lib.kda_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta),
-                               _ptr(A_log), _ptr(dt_bias), _lib.GATES[gate], float(lower_bound),
+                               _ptr(A_log), _ptr(dt_bias), _gate_code(gate, per_head),
+                               float(lower_bound),
                                _ptr(initial_state), _ptr(o), _ptr(final_state), B, T, H, HV, K, V,
                                _stream(dev))
     _lib.check("kda_recurrent_fwd", st)
@@ -165,9 +170,9 @@ def recurrent_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", low
 
 def recurrent_step(q, k, v, g_raw, beta, A_log, dt_bias, state, *, gate="safe", lower_bound=-5.0,
                    o=None):
-    """One decode token: q, k [B, H, K], v [B, HV, V], g_raw [B, HV, K], beta
-    [B, HV]; state [B, HV, K, V] float32 is updated in place.  Returns o
-    [B, HV, V] float32."""
+    """One decode token: q, k [B, H, K], v [B, HV, V], g_raw [B, HV, K] (or
+    [B, HV] for a per-head gate), beta [B, HV]; state [B, HV, K, V] float32 is
+    updated in place.  Returns o [B, HV, V] float32."""
     lib = _lib.load()
     dev = q.device
     B, H, K = q.shape
@@ -177,18 +182,15 @@ def recurrent_step(q, k, v, g_raw, beta, A_log, dt_bias, state, *, gate="safe", 
     _need(q, "q", dt, (B, H, K), dev)
     _need(k, "k", dt, (B, H, K), dev)
     _need(v, "v", dt, (B, HV, V), dev)
-    _need(g_raw, "g_raw", torch.float32, (B, HV, K), dev)
+    per_head = _check_gate_inputs(g_raw, dt_bias, A_log, (B,), HV, K, dev)
     _need(beta, "beta", torch.float32, (B, HV), dev)
-    if A_log is not None:
-        _need(A_log, "A_log", torch.float32, (HV,), dev)
-    if dt_bias is not None:
-        _need(dt_bias, "dt_bias", torch.float32, (HV, K), dev)
     _need(state, "state", torch.float32, (B, HV, K, V), dev)
     if o is None:
         o = torch.empty((B, HV, V), dtype=torch.float32, device=dev)
     _need(o, "o", torch.float32, (B, HV, V), dev)
     st = lib.kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta),
-                                _ptr(A_log), _ptr(dt_bias), _lib.GATES[gate], float(lower_bound),
+                                _ptr(A_log), _ptr(dt_bias), _gate_code(gate, per_head),
+                                float(lower_bound),
                                 _ptr(state), _ptr(o), B, H, HV, K, V, _stream(dev))
     _lib.check("kda_recurrent_step", st)
     return o

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(PKG, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
 GATES = {"standard": 0, "safe": 1, "none": 2}
+KDA_GATE_PER_HEAD = 16
 
 _c_int, _c_float, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
 

@@ -13,36 +13,50 @@ hipError_t launch_gate(const float* g_raw, const float* A_log, const float* dt_b
                        hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k, const void* v, int bf16,
                          const float* g_raw, const float* beta, const float* A_log,
-                         const float* dt_bias, int kind, float lower_bound, float* state,
-                         float* o, int B, int H, int HV, int K, int V, hipStream_t stream);
+                         const float* dt_bias, int kind, int per_head, float lower_bound,
+                         float* state, float* o, int B, int H, int HV, int K, int V,
+                         hipStream_t stream);
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf16,
                             const float* g_raw, const float* beta, const float* A_log,
-                            const float* dt_bias, int kind, float lower_bound, const float* S0,
-                            float* o, float* S_out, int B, int T, int H, int HV, int K, int V,
-                            hipStream_t stream);
+                            const float* dt_bias, int kind, int per_head, float lower_bound,
+                            const float* S0, float* o, float* S_out, int B, int T, int H, int HV,
+                            int K, int V, hipStream_t stream);
 hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
-                        float lower_bound, const float* S0, float* o, float* S_out, int B, int T,
-                        int H, int HV, int K, hipStream_t stream);
+                        int per_head, float lower_bound, const float* S0, float* o, float* S_out,
+                        int B, int T, int H, int HV, int K, hipStream_t stream);
 }  // namespace kda
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool head_size_ok(int n) { return n == 16 || n == 32 || n == 64 || n == 128; }
 
+// The gate kind without the per-head flag, and the flag.
+int gate_base(kda_gate_kind gate) { return (int)gate & ~(int)KDA_GATE_PER_HEAD; }
+int gate_per_head(kda_gate_kind gate) { return ((int)gate & (int)KDA_GATE_PER_HEAD) ? 1 : 0; }
+
 // Gate arguments shared by every entry point.
 kda_status check_gate(kda_gate_kind gate, float lower_bound, const float* A_log) {
-  if (gate != KDA_GATE_STANDARD && gate != KDA_GATE_SAFE && gate != KDA_GATE_NONE)
+  const int kind = gate_base(gate);
+  if (kind != KDA_GATE_STANDARD && kind != KDA_GATE_SAFE && kind != KDA_GATE_NONE)
     return KDA_ERR_INVALID_ARG;
-  if (gate != KDA_GATE_NONE && !A_log) return KDA_ERR_INVALID_ARG;
-  if (gate == KDA_GATE_SAFE && !(lower_bound < 0.0f && isfinite(lower_bound)))
+  if (kind != KDA_GATE_NONE && !A_log) return KDA_ERR_INVALID_ARG;
+  if (kind == KDA_GATE_SAFE && !(lower_bound < 0.0f && isfinite(lower_bound)))
     return KDA_ERR_INVALID_ARG;
   return KDA_OK;
 }
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// Gate inputs: per-channel rows are read as 16-byte vectors; a per-head gate
+// is read one float at a time.
+bool gate_inputs_aligned(kda_gate_kind gate, const float* g_raw, const float* dt_bias) {
+  if (gate_per_head(gate)) return (!g_raw || aligned4(g_raw)) && (!dt_bias || aligned4(dt_bias));
+  return (!g_raw || aligned16(g_raw)) && (!dt_bias || aligned16(dt_bias));
+}
 
 }  // namespace
 
@@ -69,8 +83,10 @@ kda_status kda_gate(const float* g_raw, const float* A_log, const float* dt_bias
   if (B < 0 || T < 0 || HV < 1 || K < 1 || chunk_size < 0) return KDA_ERR_INVALID_ARG;
   if (B == 0 || T == 0) return KDA_OK;
   if (!g_raw || !g_out) return KDA_ERR_INVALID_ARG;
-  return from_hip(kda::launch_gate(g_raw, A_log, dt_bias, (int)gate, lower_bound, B, T, HV, K,
-                                   chunk_size, g_out, reinterpret_cast<hipStream_t>(stream)));
+  // a per-head gate is the per-channel layout with K = 1
+  return from_hip(kda::launch_gate(g_raw, A_log, dt_bias, gate_base(gate), lower_bound, B, T, HV,
+                                   gate_per_head(gate) ? 1 : K, chunk_size, g_out,
+                                   reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int HV, int K, int V, int chunk_size,
@@ -94,15 +110,17 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
   // empty tensors may come with null data pointers: required only when there are tokens
   if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, g_raw, o, initial_state, final_state, dt_bias};
+  const void* ptrs[] = {q, k, v, o, initial_state, final_state};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+  if (!gate_inputs_aligned(gate, g_raw, dt_bias)) return KDA_ERR_INVALID_ARG;
   size_t need = kda_chunk_fwd_workspace_bytes(B, T, H, HV, K, V, chunk_size, qkv_dtype);
   if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
   if (B == 0) return KDA_OK;
   return from_hip(kda::launch_chunk(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log, dt_bias,
-                                    (int)gate, lower_bound, initial_state, o, final_state, B, T, H,
-                                    HV, K, reinterpret_cast<hipStream_t>(stream)));
+                                    gate_base(gate), gate_per_head(gate), lower_bound,
+                                    initial_state, o, final_state, B, T, H, HV, K,
+                                    reinterpret_cast<hipStream_t>(stream)));
 }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -117,13 +135,14 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, kda_d
   if ((long)B * HV > (1L << 28)) return KDA_ERR_INVALID_ARG;
   if (!head_size_ok(K) || !head_size_ok(V)) return KDA_ERR_UNSUPPORTED;
   if (B > 0 && (!q || !k || !v || !g_raw || !beta || !state || !o)) return KDA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, g_raw, state, o, dt_bias};
+  const void* ptrs[] = {q, k, v, state, o};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+  if (!gate_inputs_aligned(gate, g_raw, dt_bias)) return KDA_ERR_INVALID_ARG;
   if (B == 0) return KDA_OK;
   return from_hip(kda::launch_decode(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log, dt_bias,
-                                     (int)gate, lower_bound, state, o, B, H, HV, K, V,
-                                     reinterpret_cast<hipStream_t>(stream)));
+                                     gate_base(gate), gate_per_head(gate), lower_bound, state, o,
+                                     B, H, HV, K, V, reinterpret_cast<hipStream_t>(stream)));
 }
 
 kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
@@ -138,14 +157,15 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, kda_dt
   if ((long)B * HV > (1L << 28)) return KDA_ERR_INVALID_ARG;
   if (!head_size_ok(K) || !head_size_ok(V)) return KDA_ERR_UNSUPPORTED;
   if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, g_raw, o, initial_state, final_state, dt_bias};
+  const void* ptrs[] = {q, k, v, o, initial_state, final_state};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+  if (!gate_inputs_aligned(gate, g_raw, dt_bias)) return KDA_ERR_INVALID_ARG;
   if (B == 0) return KDA_OK;
   return from_hip(kda::launch_recurrent(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log,
-                                        dt_bias, (int)gate, lower_bound, initial_state, o,
-                                        final_state, B, T, H, HV, K, V,
-                                        reinterpret_cast<hipStream_t>(stream)));
+                                        dt_bias, gate_base(gate), gate_per_head(gate),
+                                        lower_bound, initial_state, o, final_state, B, T, H, HV,
+                                        K, V, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -348,7 +348,10 @@ __device__ __forceinline__ void tprod(f32x4& acc, const TokOp<F32, RA>& A, int a
 
 // ----------------------------------------------------------------- kernel
 
-template <int K, typename T, int GK>
+// GS: per-head gate (g_raw [B, T, HV], dt_bias [HV]), one decay shared by all
+// key channels, so the prep computes one gate and one product scan per token
+// pair instead of four.
+template <int K, typename T, int GK, bool GS>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   constexpr bool F32 = std::is_same<T, float>::value;
   constexpr int V = K;
@@ -375,7 +378,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   const int v0 = vt * BV;
   const float scale = 1.0f / __builtin_sqrtf((float)K);
   const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
-  const float* bias = (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias + (long)hv * K : nullptr;
+  constexpr int GKD = GS ? 1 : K;  // gate elements per (token, value head)
+  const float* bias = (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias + (long)hv * GKD : nullptr;
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
@@ -397,13 +401,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     float bias4[4] = {0.f, 0.f, 0.f, 0.f};
     if (bias && prep_thread) {
   #pragma unroll
-      for (int c = 0; c < 4; ++c) bias4[c] = bias[c0 + c];
+      for (int c = 0; c < 4; ++c) bias4[c] = bias[GS ? 0 : c0 + c];
     }
     const GateConsts gc = gate_consts(rate, p.lower_bound);
     float4 pg[2];
     Raw4 pq[2], pk[2];
     // Per-thread row-0 pointers of this sequence; token t adds t times the row stride.
-    const float* g_base = p.g_raw + (b * T_ * HV + hv) * (long)K + c0;
+    const float* g_base = p.g_raw + (b * T_ * HV + hv) * (long)GKD + (GS ? 0 : c0);
     const T* q_base = qg + (b * T_ * H + h) * (long)K + c0;
     const T* k_base = kg + (b * T_ * H + h) * (long)K + c0;
     const T* v_base = vg + (b * T_ * HV + hv) * (long)V + v0 + vc;
@@ -416,7 +420,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const long t = min(tb + 2 * tp + j, T_ - 1);
-          pg[j] = *reinterpret_cast<const float4*>(g_base + t * (HV * K));
+          if constexpr (GS) {
+            const float x = g_base[t * HV];
+            pg[j] = float4{x, x, x, x};
+          } else {
+            pg[j] = *reinterpret_cast<const float4*>(g_base + t * (HV * K));
+          }
           pq[j] = In<T>::raw4(q_base, t * (H * K));
           pk[j] = In<T>::raw4(k_base, t * (H * K));
         }
@@ -442,6 +451,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           const float4 g_in[2] = {pg[0], pg[1]};
           const Raw4 q_in[2] = {pq[0], pq[1]}, k_in[2] = {pk[0], pk[1]};
           if (it + 1 < NT) fetch(it + 1);  // the next block's inputs travel during this step
+          constexpr int NCH = GS ? 1 : 4;  // distinct decays among the four channels
           float al[2][4], qv[2][4], kv[2][4];
   #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -451,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             In<T>::unpack4(k_in[j], kv[j]);
   #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const float a = gate_alpha<GK>(gr[c], bias4[c], gc);
+              const float a = c < NCH ? gate_alpha<GK>(gr[c], bias4[c], gc) : al[j][0];
               al[j][c] = valid ? a : 1.0f;
               qv[j][c] = valid ? qv[j][c] : 0.0f;
               kv[j][c] = valid ? kv[j][c] : 0.0f;
@@ -462,22 +472,22 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           // x and suffix z of the pair products.
           float x[4], z[4], y;
   #pragma unroll
-          for (int c = 0; c < 4; ++c) x[c] = z[c] = al[0][c] * al[1][c];
+          for (int c = 0; c < NCH; ++c) x[c] = z[c] = al[0][c] * al[1][c];
   #pragma unroll
-          for (int c = 0; c < 4; ++c) { y = row_shr<1>(x[c]); if (tp >= 1) x[c] *= y; }
+          for (int c = 0; c < NCH; ++c) { y = row_shr<1>(x[c]); if (tp >= 1) x[c] *= y; }
   #pragma unroll
-          for (int c = 0; c < 4; ++c) { y = row_shl<1>(z[c]); if (tp < 7) z[c] *= y; }
+          for (int c = 0; c < NCH; ++c) { y = row_shl<1>(z[c]); if (tp < 7) z[c] *= y; }
   #pragma unroll
-          for (int c = 0; c < 4; ++c) { y = row_shr<2>(x[c]); if (tp >= 2) x[c] *= y; }
+          for (int c = 0; c < NCH; ++c) { y = row_shr<2>(x[c]); if (tp >= 2) x[c] *= y; }
   #pragma unroll
-          for (int c = 0; c < 4; ++c) { y = row_shl<2>(z[c]); if (tp < 6) z[c] *= y; }
+          for (int c = 0; c < NCH; ++c) { y = row_shl<2>(z[c]); if (tp < 6) z[c] *= y; }
   #pragma unroll
-          for (int c = 0; c < 4; ++c) { y = row_shr<4>(x[c]); if (tp >= 4) x[c] *= y; }
+          for (int c = 0; c < NCH; ++c) { y = row_shr<4>(x[c]); if (tp >= 4) x[c] *= y; }
   #pragma unroll
-          for (int c = 0; c < 4; ++c) { y = row_shl<4>(z[c]); if (tp < 4) z[c] *= y; }
+          for (int c = 0; c < NCH; ++c) { y = row_shl<4>(z[c]); if (tp < 4) z[c] *= y; }
           float E[2][4], Sf[2][4], ig[4], gam[4];
   #pragma unroll
-          for (int c = 0; c < 4; ++c) {
+          for (int c = 0; c < NCH; ++c) {
             float ex = row_shr<1>(x[c]);  // exclusive prefix
             if (tp == 0) ex = 1.0f;
             float sx = row_shl<1>(z[c]);  // exclusive suffix
@@ -489,6 +499,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             gam[c] = x[c] * sx;  // decay over the whole block
             overflow |= !(gam[c] >= kGammaMin && gam[c] <= kGammaMax);
             ig[c] = __builtin_amdgcn_rcpf(gam[c]);
+          }
+  #pragma unroll
+          for (int c = NCH; c < 4; ++c) {  // per-head gate: the other channels share channel 0's
+            E[0][c] = E[0][0];
+            E[1][c] = E[1][0];
+            Sf[0][c] = Sf[0][0];
+            Sf[1][c] = Sf[1][0];
+            gam[c] = gam[0];
+            ig[c] = ig[0];
           }
           if (tp == 0) *reinterpret_cast<float4*>(&B.gam[c0]) = float4{gam[0], gam[1], gam[2], gam[3]};
           float ke[2][4];
@@ -711,7 +730,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           // key rows of its columns, so both reductions stay in the wavefront
           for (int tt = 0; tt < kTok && t0 + tt < T_; ++tt) {
             const long row = b * T_ + t0 + tt;
-            const float* grow = p.g_raw + (row * HV + hv) * K;
+            const float* grow = p.g_raw + (row * HV + hv) * GKD;
+            const float a_head = GS ? slow_path_alpha<GK>(grow[0], bias ? bias[0] : 0.0f, rate,
+                                                          p.lower_bound) : 0.0f;
             const T* krow = kg + (row * H + h) * K;
             const T* qrow = qg + (row * H + h) * K;
             float part = 0.0f;
@@ -720,7 +741,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int c = 16 * kb + 4 * (lane >> 4) + r;
-                sacc[kb][r] *= slow_path_alpha<GK>(grow[c], bias ? bias[c] : 0.0f, rate, p.lower_bound);
+                sacc[kb][r] *= GS ? a_head : slow_path_alpha<GK>(grow[c], bias ? bias[c] : 0.0f, rate,
+                                                                 p.lower_bound);
                 part += In<T>::at(krow, c) * sacc[kb][r];
               }
               // one key block at a time: keeps this rare path's registers bounded
@@ -818,7 +840,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   }
 }
 
-template <int K, typename T, int GK>
+template <int K, typename T, int GK, bool GS>
 static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   constexpr int BV = K < 32 ? K : 32;
   constexpr int NVT = K / BV;
@@ -829,28 +851,31 @@ static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   if (lds < 84 * 1024) lds = 84 * 1024;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK, GS>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int nheads = p.B * p.HV;
   const long blocks = (long)((nheads + 7) / 8) * 8 * NVT;
-  hipLaunchKernelGGL((chunk_fwd_kernel<K, T, GK>), dim3((unsigned)blocks), dim3(kThreads), lds,
+  hipLaunchKernelGGL((chunk_fwd_kernel<K, T, GK, GS>), dim3((unsigned)blocks), dim3(kThreads), lds,
                      stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
-                        float lower_bound, const float* S0, float* o, float* S_out, int B, int T,
-                        int H, int HV, int K, hipStream_t stream) {
+                        int per_head, float lower_bound, const float* S0, float* o, float* S_out,
+                        int B, int T, int H, int HV, int K, hipStream_t stream) {
   ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, B, T, H, HV, kind, lower_bound};
-#define KDA_CHUNK_GATE(KK, TT)                                                            \
-  switch (kind) {                                                                         \
-    case KDA_GATE_SAFE: return launch_chunk_kt<KK, TT, KDA_GATE_SAFE>(p, stream);         \
-    case KDA_GATE_STANDARD: return launch_chunk_kt<KK, TT, KDA_GATE_STANDARD>(p, stream); \
-    default: return launch_chunk_kt<KK, TT, KDA_GATE_NONE>(p, stream);                    \
+#define KDA_CHUNK_GS(KK, TT, GG)                                     \
+  return per_head ? launch_chunk_kt<KK, TT, GG, true>(p, stream)     \
+                  : launch_chunk_kt<KK, TT, GG, false>(p, stream);
+#define KDA_CHUNK_GATE(KK, TT)                                      \
+  switch (kind) {                                                   \
+    case KDA_GATE_SAFE: KDA_CHUNK_GS(KK, TT, KDA_GATE_SAFE)         \
+    case KDA_GATE_STANDARD: KDA_CHUNK_GS(KK, TT, KDA_GATE_STANDARD) \
+    default: KDA_CHUNK_GS(KK, TT, KDA_GATE_NONE)                    \
   }
 #define KDA_CHUNK_CASE(KK)                     \
   if (K == KK) {                               \
@@ -860,6 +885,7 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
   KDA_CHUNK_CASE(16) KDA_CHUNK_CASE(32) KDA_CHUNK_CASE(64) KDA_CHUNK_CASE(128)
 #undef KDA_CHUNK_CASE
 #undef KDA_CHUNK_GATE
+#undef KDA_CHUNK_GS
   return hipErrorInvalidValue;
 }
 

@@ -34,6 +34,7 @@ struct DecodeParams {
   float* state;
   float* o;
   int B, H, HV, kind;
+  int per_head;  // g_raw [B, HV] and dt_bias [HV]: one gate per (b, hv)
   float lower_bound;
 };
 
@@ -85,8 +86,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
       const long b = bh / p.HV;
       const int h = hv / (p.HV / p.H);
       const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
-      const float bias = (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[(long)hv * K + r] : 0.0f;
-      s_al[ts][r] = exp_f(gate_log_decay_k<GK>(p.g_raw[bh * K + r], bias, rate, p.lower_bound));
+      const long gi = p.per_head ? bh : bh * K + r, bi = p.per_head ? hv : (long)hv * K + r;
+      const float bias = (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[bi] : 0.0f;
+      s_al[ts][r] = exp_f(gate_log_decay_k<GK>(p.g_raw[gi], bias, rate, p.lower_bound));
       s_k[ts][r] = In<T>::at(static_cast<const T*>(p.k), (b * p.H + h) * K + r);
       s_q[ts][r] = In<T>::at(static_cast<const T*>(p.q), (b * p.H + h) * K + r);
     }
@@ -180,6 +182,7 @@ struct RecurrentParams {
   float* S_out;
   float* o;
   int B, T, H, HV, kind;
+  int per_head;  // g_raw [B, T, HV] and dt_bias [HV]: one gate per (token, value head)
   float lower_bound;
 };
 
@@ -207,15 +210,17 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecurrentParams p) {
   const long gb = gbh / HV;
   const int gh = ghv / (HV / H);
   const GateConsts gc = gate_consts(GK != KDA_GATE_NONE ? exp_f(p.A_log[ghv]) : 1.0f, p.lower_bound);
-  const float gbias = (p.dt_bias && GK != KDA_GATE_NONE && gactive) ? p.dt_bias[(long)ghv * K + gr] : 0.0f;
-  const float* g_ptr = p.g_raw + (gb * T_ * HV + ghv) * (long)K + gr;
+  const int gK = p.per_head ? 1 : K;  // gate elements per (token, value head)
+  const float gbias = (p.dt_bias && GK != KDA_GATE_NONE && gactive)
+                          ? p.dt_bias[(long)ghv * gK + (p.per_head ? 0 : gr)] : 0.0f;
+  const float* g_ptr = p.g_raw + (gb * T_ * HV + ghv) * (long)gK + (p.per_head ? 0 : gr);
   const T* k_ptr = static_cast<const T*>(p.k) + (gb * T_ * H + gh) * (long)K + gr;
   const T* q_ptr = static_cast<const T*>(p.q) + (gb * T_ * H + gh) * (long)K + gr;
   float pg = 0.0f;
   typename In<T>::Raw1 pk = In<T>::zero1(), pq = In<T>::zero1();
   auto fetch_g = [&](int t) {
     if (gactive) {
-      pg = g_ptr[(long)t * HV * K];
+      pg = g_ptr[(long)t * HV * gK];
       pk = k_ptr[(long)t * H * K];
       pq = q_ptr[(long)t * H * K];
     }
@@ -353,11 +358,11 @@ static hipError_t launch_recurrent_g(const RecurrentParams& p, int K, int V, hip
 
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, int bf16,
                             const float* g_raw, const float* beta, const float* A_log,
-                            const float* dt_bias, int kind, float lower_bound, const float* S0,
-                            float* o, float* S_out, int B, int T, int H, int HV, int K, int V,
-                            hipStream_t stream) {
+                            const float* dt_bias, int kind, int per_head, float lower_bound,
+                            const float* S0, float* o, float* S_out, int B, int T, int H, int HV,
+                            int K, int V, hipStream_t stream) {
   RecurrentParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, S_out, o, B, T, H, HV, kind,
-                    lower_bound};
+                    per_head, lower_bound};
   return bf16 ? launch_recurrent_g<uint16_t>(p, K, V, stream)
               : launch_recurrent_g<float>(p, K, V, stream);
 }
@@ -394,9 +399,11 @@ static hipError_t launch_decode_g(const DecodeParams& p, int K, int V, hipStream
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, int bf16,
                          const float* g_raw, const float* beta, const float* A_log,
-                         const float* dt_bias, int kind, float lower_bound, float* state,
-                         float* o, int B, int H, int HV, int K, int V, hipStream_t stream) {
-  DecodeParams p{q, k, v, g_raw, beta, A_log, dt_bias, state, o, B, H, HV, kind, lower_bound};
+                         const float* dt_bias, int kind, int per_head, float lower_bound,
+                         float* state, float* o, int B, int H, int HV, int K, int V,
+                         hipStream_t stream) {
+  DecodeParams p{q, k, v, g_raw, beta, A_log, dt_bias, state, o, B, H, HV, kind, per_head,
+                 lower_bound};
   return bf16 ? launch_decode_g<uint16_t>(p, K, V, stream) : launch_decode_g<float>(p, K, V, stream);
 }
 

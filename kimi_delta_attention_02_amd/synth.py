@@ -44,6 +44,7 @@ class Workload:
     s0_std: float         # 0 -> zero initial state
     seed: int
     steps: int = 0        # decode workloads: number of single-token steps
+    per_head_gate: bool = False  # g_raw [B,T,HV] and dt_bias [HV] (Gated DeltaNet's scalar gate)
 
     @property
     def tokens(self) -> int:
@@ -66,6 +67,9 @@ WORKLOADS = {
     # long-context GVA chunked prefill
     "long": Workload("long", 1, 65536, 16, 64, 128, 128, 64, "bf16", "safe", -5.0,
                      0.5, -4.0, 0.0, 0.0, seed=5),
+    # the prefill shape with one gate per (token, value head), as in Gated DeltaNet
+    "prefill_head_gate": Workload("prefill_head_gate", 4, 4096, 16, 16, 128, 128, 64, "bf16",
+                                  "safe", -5.0, 0.5, -4.0, 0.0, 0.0, seed=6, per_head_gate=True),
 }
 
 
@@ -87,7 +91,8 @@ def make_inputs(w: Workload, *, T: int | None = None, B: int | None = None, seed
 
     Returns a dict with q, k [B,T,H,K], v [B,T,HV,V] (float32 or bfloat16),
     g_raw [B,T,HV,K], beta [B,T,HV], A_log [HV], dt_bias [HV,K], S0 [B,HV,K,V]
-    or None (all float32).  For decode workloads T is the number of steps and
+    or None (all float32); with a per-head gate g_raw is [B,T,HV] and dt_bias
+    [HV].  For decode workloads T is the number of steps and
     step t reads q[:, t] etc.  ``T``, ``B`` and ``seed`` override the workload.
     """
     B = w.B if B is None else B
@@ -98,22 +103,23 @@ def make_inputs(w: Workload, *, T: int | None = None, B: int | None = None, seed
     q = _l2(_normal((B, T, w.H, w.K), gen))
     k = _l2(_normal((B, T, w.H, w.K), gen))
     v = _normal((B, T, w.HV, w.V), gen)
-    g_raw = _normal((B, T, w.HV, w.K), gen)
+    gk = () if w.per_head_gate else (w.K,)
+    g_raw = _normal((B, T, w.HV) + gk, gen)
     beta = torch.sigmoid(_normal((B, T, w.HV), gen))
     A_log = (_normal((w.HV,), gen, std=w.a_log_std) if w.a_log_std > 0
              else torch.zeros(w.HV, dtype=torch.float32))
-    dt_bias = (_normal((w.HV, w.K), gen, mean=w.dt_bias_mean, std=w.dt_bias_std)
-               if w.dt_bias_std > 0 else torch.full((w.HV, w.K), w.dt_bias_mean, dtype=torch.float32))
+    dt_bias = (_normal((w.HV,) + gk, gen, mean=w.dt_bias_mean, std=w.dt_bias_std)
+               if w.dt_bias_std > 0 else torch.full((w.HV,) + gk, w.dt_bias_mean, dtype=torch.float32))
     if w.dtype == "bf16":
         q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
     return dict(q=q, k=k, v=v, g_raw=g_raw, beta=beta, A_log=A_log, dt_bias=dt_bias, S0=S0)
 
 
 def random_inputs(B, T, H, HV, K, V, *, seed, dtype="f32", a_log_std=0.5, dt_bias_mean=-4.0,
-                  dt_bias_std=0.5, s0_std=0.0, g_std=1.0):
+                  dt_bias_std=0.5, s0_std=0.0, g_std=1.0, per_head_gate=False):
     """Inputs of arbitrary shape with the same recipe (used by edge-case tests)."""
     w = Workload("custom", B, T, H, HV, K, V, 16, dtype, "safe", -5.0, a_log_std,
-                 dt_bias_mean, dt_bias_std, s0_std, seed)
+                 dt_bias_mean, dt_bias_std, s0_std, seed, per_head_gate=per_head_gate)
     d = make_inputs(w)
     if g_std != 1.0:
         d["g_raw"] = d["g_raw"] * g_std

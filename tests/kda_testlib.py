@@ -64,13 +64,29 @@ def run_decode(d, w_gate, lower_bound, state0):
     return o.transpose(0, 1), state
 
 
+def per_channel_gate(d):
+    """A per-head gate (g_raw without the K axis, dt_bias [HV]) written out as
+    the per-channel gate it is, every key channel carrying the head's value:
+    the form the oracle takes."""
+    K = d["q"].shape[-1]
+    if d["g_raw"].dim() == d["q"].dim():
+        return d
+    e = dict(d)
+    e["g_raw"] = d["g_raw"].unsqueeze(-1).expand(*d["g_raw"].shape, K).contiguous()
+    if d["dt_bias"] is not None:
+        e["dt_bias"] = d["dt_bias"].unsqueeze(-1).expand(d["dt_bias"].shape[0], K).contiguous()
+    return e
+
+
 def oracle_full(d, w_gate, lower_bound, initial_state=True):
+    d = per_channel_gate(d)
     return oracle.default().kda_fwd(d["q"], d["k"], d["v"], d["g_raw"], d["beta"], d["A_log"],
                                     d["dt_bias"], w_gate, lower_bound,
                                     d["S0"] if initial_state else None)
 
 
 def oracle_heads(d, w_gate, lower_bound, heads):
+    d = per_channel_gate(d)
     npf = lambda x: None if x is None else x.float().numpy()
     return oracle.default().kda_fwd_heads(npf(d["q"]), npf(d["k"]), npf(d["v"]), npf(d["g_raw"]),
                                           npf(d["beta"]), npf(d["A_log"]), npf(d["dt_bias"]),

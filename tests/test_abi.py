@@ -152,6 +152,19 @@ def test_recurrent_fwd_validation(lib, kw, status):
 
 
 @needs_no_gpu
+def test_per_head_gate_flag_validation(lib):
+    ph = _lib.KDA_GATE_PER_HEAD
+    assert _chunk(lib, gate=ph | 1, B=0) == _lib.KDA_OK
+    assert _chunk(lib, gate=ph | 1, L=0.0) == _lib.KDA_ERR_INVALID_ARG   # safe still needs L < 0
+    assert _chunk(lib, gate=ph | 3) == _lib.KDA_ERR_INVALID_ARG          # no such kind
+    assert _chunk(lib, gate=32 | 1) == _lib.KDA_ERR_INVALID_ARG          # unknown flag bit
+    assert _chunk(lib, gate=ph | 0, A=None) == _lib.KDA_ERR_INVALID_ARG  # standard needs A_log
+    assert _chunk(lib, gate=ph | 2, A=None, B=0) == _lib.KDA_OK
+    assert _rec(lib, gate=ph | 1, B=0) == _lib.KDA_OK
+    assert _step(lib, gate=ph | 7) == _lib.KDA_ERR_INVALID_ARG
+
+
+@needs_no_gpu
 def test_gate_validation(lib):
     f = lambda **kw: lib.kda_gate(kw.get("g", P), kw.get("A", P), None, kw.get("gate", 1),
                                   kw.get("L", -5.0), kw.get("B", 1), kw.get("T", 4), 2, 8,

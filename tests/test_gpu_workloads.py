@@ -36,6 +36,11 @@ def test_workload_gva():
     _chunked("gva", 6)
 
 
+@pytest.mark.timeout(300)
+def test_workload_prefill_head_gate():
+    _chunked("prefill_head_gate", 8)
+
+
 @pytest.mark.timeout(600)
 def test_workload_long():
     _chunked("long", 4)
