@@ -404,6 +404,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       for (int c = 0; c < 4; ++c) bias4[c] = bias[GS ? 0 : c0 + c];
     }
     const GateConsts gc = gate_consts(rate, p.lower_bound);
+  #pragma unroll
+    for (int c = 0; c < 4; ++c) bias4[c] = gate_bias_pre<GK>(bias4[c], gc);
     float4 pg[2];
     Raw4 pq[2], pk[2];
     // Per-thread row-0 pointers of this sequence; token t adds t times the row stride.
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             In<T>::unpack4(k_in[j], kv[j]);
   #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const float a = c < NCH ? gate_alpha<GK>(gr[c], bias4[c], gc) : al[j][0];
+              const float a = c < NCH ? gate_alpha_pre<GK>(gr[c], bias4[c], gc) : al[j][0];
               al[j][c] = valid ? a : 1.0f;
               qv[j][c] = valid ? qv[j][c] : 0.0f;
               kv[j][c] = valid ? kv[j][c] : 0.0f;
@@ -497,7 +499,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             Sf[1][c] = sx;
             Sf[0][c] = al[1][c] * sx;
             gam[c] = x[c] * sx;  // decay over the whole block
-            overflow |= !(gam[c] >= kGammaMin && gam[c] <= kGammaMax);
+            // the safe and standard gates give g <= 0, so gamma <= 1; NaN fails too
+            overflow |= GK == KDA_GATE_NONE ? !(gam[c] >= kGammaMin && gam[c] <= kGammaMax)
+                                            : !(gam[c] >= kGammaMin);
             ig[c] = __builtin_amdgcn_rcpf(gam[c]);
           }
   #pragma unroll

@@ -153,6 +153,22 @@ __device__ __forceinline__ float gate_alpha(float graw, float bias, GateConsts g
   }
 }
 
+// gate_alpha with the bias pre-folded: pass gate_bias_pre<GK>(bias, gc) as
+// `pre`, so the safe gate's argument cr (g_raw + bias) is one fma.
+template <int GK>
+__device__ __forceinline__ float gate_bias_pre(float bias, GateConsts gc) {
+  return GK == KDA_GATE_SAFE ? gc.cr * bias : bias;
+}
+template <int GK>
+__device__ __forceinline__ float gate_alpha_pre(float graw, float pre, GateConsts gc) {
+  if constexpr (GK == KDA_GATE_SAFE) {
+    return __builtin_amdgcn_exp2f(
+        gc.cl * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(graw, gc.cr, pre))));
+  } else {
+    return gate_alpha<GK>(graw, pre, gc);
+  }
+}
+
 // ------------------------------------------------------------ load helpers
 
 template <typename T>
