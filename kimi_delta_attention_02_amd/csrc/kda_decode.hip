@@ -76,6 +76,28 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
   const long tile0 = (long)blockIdx.x * TPW;
   const long ntiles = nheads * NVT;
 
+  const int ts = w / WT, rq = w % WT;  // tile slot, row quarter
+  const long tile = tile0 + ts;
+  const bool active = tile < ntiles;
+  const long bh = tile / NVT;          // b * HV + hv
+  const int vt = (int)(tile % NVT);
+  const int cq = lane % NQ, rg = lane / NQ;
+  const int col = vt * TV + cq * 4;
+  const int row0 = rq * (K / WT) + rg;
+  float* S = p.state + bh * (long)K * V;
+  f32x4 s[RPL];
+  float vv[4] = {0.f, 0.f, 0.f, 0.f};
+  float bt = 0.0f;
+  // the state tile's loads go out first: the decay/key/query loop below waits
+  // on its own (small) loads, and the two latencies overlap
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (long)(row0 + RG * i) * V + col));
+    In<T>::load4(static_cast<const T*>(p.v), bh * V + col, vv);
+    bt = p.beta[bh];
+  }
+
   // decay factors and key/query rows of each tile's (b, hv), once per workgroup
   for (int e = tid; e < TPW * K; e += 256) {
     const int ts = e / K, r = e % K;
@@ -94,25 +116,6 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
     }
   }
 
-  const int ts = w / WT, rq = w % WT;  // tile slot, row quarter
-  const long tile = tile0 + ts;
-  const bool active = tile < ntiles;
-  const long bh = tile / NVT;          // b * HV + hv
-  const int vt = (int)(tile % NVT);
-  const int cq = lane % NQ, rg = lane / NQ;
-  const int col = vt * TV + cq * 4;
-  const int row0 = rq * (K / WT) + rg;
-  float* S = p.state + bh * (long)K * V;
-  f32x4 s[RPL];
-  float vv[4] = {0.f, 0.f, 0.f, 0.f};
-  float bt = 0.0f;
-  if (active) {
-#pragma unroll
-    for (int i = 0; i < RPL; ++i)
-      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (long)(row0 + RG * i) * V + col));
-    In<T>::load4(static_cast<const T*>(p.v), bh * V + col, vv);
-    bt = p.beta[bh];
-  }
   __syncthreads();
 
   // decay, then prediction p = k . S_dec: in-wave butterfly, then across the WT waves
