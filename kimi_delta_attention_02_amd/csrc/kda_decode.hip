@@ -7,18 +7,19 @@
 // owning a tile of the state for the whole step.
 //
 // The step is bound by HBM: the fp32 state [K, V] of every (b, hv) is read once
-// and written once.  A K x TV column tile (TV = min(V, 64)) is split by rows
-// over WT wavefronts (four for K = 128), so each lane keeps only RPL 16-byte
-// rows in flight: many short streams reach a higher fraction of HBM bandwidth
-// than few long ones on this part.  In a wavefront, lane l holds column quad
-// cq = l % NQ (NQ lanes cover one row segment of the tile) and rows row0 + RG i
-// of row group rg = l / NQ, so every load instruction reads RG full row
-// segments; all loads are issued before any arithmetic.  The two reductions
-// over kappa (prediction k.S_dec and read q.S_new) run as log2(RG) butterfly
-// steps inside each wavefront (row swaps for the 16- and 32-lane distances),
-// then one LDS exchange across the WT wavefronts of the tile.  The decay
-// factors exp(g) and the key and query rows are computed once per workgroup
-// into LDS.
+// and written once.  A K x TV column tile (TV = V, at most 128) is split by
+// rows over WT wavefronts (four for K = 128), so each lane keeps RPL 16-byte
+// rows in flight.  In a wavefront, lane l holds column quad cq = l % NQ (NQ
+// lanes cover one row segment of the tile) and rows row0 + RG i of row group
+// rg = l / NQ, so every load instruction reads RG full row segments; the whole
+// tile is loaded before any arithmetic.  The two reductions over kappa
+// (prediction k.S_dec and read q.S_new) run as log2(RG) butterfly steps inside
+// each wavefront (row swaps for the 16- and 32-lane distances), then one LDS
+// exchange across the WT wavefronts of the tile.  The decay factors exp(g) and
+// the key and query rows are computed once per workgroup into LDS.  Measured on
+// the decode workload, whole-head tiles (TV = 128) beat 64- and 32-wide ones:
+// one workgroup per (b, hv) computes exp(g) once and leaves fewer, longer
+// workgroups, which shortens the end-of-launch tail.
 #include "kda_device.h"
 
 namespace kda {
@@ -53,7 +54,7 @@ __device__ __forceinline__ f32x4 sum_row_groups(f32x4 v) {
 
 template <int K, int V>
 struct DecodeTiling {
-  static constexpr int TV = V < 64 ? V : 64;     // columns of a tile
+  static constexpr int TV = V < 128 ? V : 128;   // columns of a tile
   static constexpr int NQ = TV / 4;              // column quads per row segment
   static constexpr int RG = 64 / NQ;             // row groups per wavefront
   static constexpr int WT = K / RG < 4 ? K / RG : 4;  // wavefronts splitting a tile's rows
