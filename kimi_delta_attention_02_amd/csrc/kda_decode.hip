@@ -52,25 +52,29 @@ __device__ __forceinline__ f32x4 sum_row_groups(f32x4 v) {
   }
 }
 
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+
 template <int K, int V>
 struct DecodeTiling {
   static constexpr int TV = V < 128 ? V : 128;   // columns of a tile
   static constexpr int NQ = TV / 4;              // column quads per row segment
   static constexpr int RG = 64 / NQ;             // row groups per wavefront
-  static constexpr int WT = K / RG < 4 ? K / RG : 4;  // wavefronts splitting a tile's rows
+  static constexpr int NW = kDecodeWaves;             // wavefronts per workgroup
+  static constexpr int WT = K / RG < NW ? K / RG : NW;  // wavefronts splitting a tile's rows
   static constexpr int RPL = K / (WT * RG);      // rows per lane
   static constexpr int NVT = V / TV;             // tiles per (b, hv)
-  static constexpr int TPW = 4 / WT;             // tiles per workgroup of 4 wavefronts
+  static constexpr int TPW = NW / WT;            // tiles per workgroup
   static_assert(RPL >= 1 && K % (WT * RG) == 0, "head size too small for this tiling");
 };
 
 template <int K, int V, typename T, int GK>
-__global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeParams p) {
   using D = DecodeTiling<K, V>;
   constexpr int TV = D::TV, NQ = D::NQ, RG = D::RG, WT = D::WT, RPL = D::RPL, NVT = D::NVT,
                 TPW = D::TPW;
   __shared__ float s_al[TPW][K], s_k[TPW][K], s_q[TPW][K];
-  __shared__ f32x4 s_red[2][4][NQ];  // per wavefront partial sums of the two reductions
+  __shared__ f32x4 s_red[2][kDecodeWaves][NQ];  // per wavefront partials of the two reductions
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const long nheads = (long)p.B * p.HV;
@@ -100,7 +104,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
   }
 
   // decay factors and key/query rows of each tile's (b, hv), once per workgroup
-  for (int e = tid; e < TPW * K; e += 256) {
+  for (int e = tid; e < TPW * K; e += kDecodeThreads) {
     const int ts = e / K, r = e % K;
     const long tile = tile0 + ts;
     if (tile < ntiles) {
@@ -191,13 +195,13 @@ struct RecurrentParams {
 };
 
 template <int K, int V, typename T, int GK>
-__global__ __launch_bounds__(256) void recurrent_fwd_kernel(RecurrentParams p) {
+__global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(RecurrentParams p) {
   using D = DecodeTiling<K, V>;
   constexpr int TV = D::TV, NQ = D::NQ, RG = D::RG, WT = D::WT, RPL = D::RPL, NVT = D::NVT,
                 TPW = D::TPW;
-  static_assert(TPW * K <= 256, "one decay/key/query element per thread");
+  static_assert(TPW * K <= kDecodeThreads, "one decay/key/query element per thread");
   __shared__ float s_al[2][TPW][K], s_k[2][TPW][K], s_q[2][TPW][K];
-  __shared__ f32x4 s_red[2][4][NQ];
+  __shared__ f32x4 s_red[2][kDecodeWaves][NQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T_ = p.T, HV = p.HV, H = p.H;
@@ -335,7 +339,7 @@ static hipError_t launch_recurrent_kv(const RecurrentParams& p, hipStream_t stre
   using D = DecodeTiling<K, V>;
   const long tiles = (long)p.B * p.HV * D::NVT;
   const long blocks = (tiles + D::TPW - 1) / D::TPW;
-  hipLaunchKernelGGL((recurrent_fwd_kernel<K, V, T, GK>), dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL((recurrent_fwd_kernel<K, V, T, GK>), dim3((unsigned)blocks), dim3(kDecodeThreads), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -376,7 +380,7 @@ static hipError_t launch_decode_kv(const DecodeParams& p, hipStream_t stream) {
   using D = DecodeTiling<K, V>;
   const long tiles = (long)p.B * p.HV * D::NVT;
   const long blocks = (tiles + D::TPW - 1) / D::TPW;
-  hipLaunchKernelGGL((decode_step_kernel<K, V, T, GK>), dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL((decode_step_kernel<K, V, T, GK>), dim3((unsigned)blocks), dim3(kDecodeThreads), 0,
                      stream, p);
   return hipGetLastError();
 }
