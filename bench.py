@@ -272,7 +272,8 @@ def main():
                 "calls": calls, "value": wd.B * wd.steps / (rms_ * 1e-3), "unit": "tokens/s",
                 "ms_per_call": rms_ / calls,
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                             "frac": gbs / HBM_PEAK_GBS,
+                             "traffic": measured_traffic("recurrent") if per_call == 16 else None,
                              "bytes_per_launch": nbytes}}
             del chunks, outs
         result["recurrent"] = rec
