@@ -173,10 +173,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(DecodeParam
 // the state tile held in registers across all tokens, read from the initial
 // state once and written to the final state once ("DeltaNet family" page, the
 // fused recurrent kernel: one program per (sequence, head, value tile) looping
-// over time).  Per token: exp(g), k and q rows of the next token are formed in
-// a second LDS buffer while the current token runs, so each token costs two
+// over time).  Per token: the row factors of the next token are formed in a
+// second LDS buffer while the current token runs, so each token costs two
 // barriers (after the prediction partials and after the read partials); the
 // HBM inputs of a token are loaded one token ahead.
+//
+// The tile is kept as S_hat = S / D, with D the running product of exp(g) per
+// key row since the last renormalisation.  The decay then costs no
+// multiplication of the tile: the prediction uses k D, the write k / D and the
+// read q D (three factors per row, formed once per row), so each state element
+// takes three fused multiply-adds per token instead of four operations.  A row
+// whose D leaves [2^-64, 2^64] (or is NaN) makes the workgroup fold D into
+// S_hat before that token (S_hat *= D, D = 1; the factor is 1 for the other
+// rows), and D is folded in once more before the final state is stored.
 
 struct RecurrentParams {
   const void* q;
@@ -200,8 +209,12 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(Recurrent
   constexpr int TV = D::TV, NQ = D::NQ, RG = D::RG, WT = D::WT, RPL = D::RPL, NVT = D::NVT,
                 TPW = D::TPW;
   static_assert(TPW * K <= kDecodeThreads, "one decay/key/query element per thread");
-  __shared__ float s_al[2][TPW][K], s_k[2][TPW][K], s_q[2][TPW][K];
+  // per token buffer: renormalisation factor, k D, k / D, q D of every row
+  __shared__ float s_f[2][TPW][K], s_k1[2][TPW][K], s_k2[2][TPW][K], s_q1[2][TPW][K];
+  __shared__ int s_rn[2][kDecodeWaves];  // per wavefront: some row renormalises
+  __shared__ float s_D[TPW][K];
   __shared__ f32x4 s_red[2][kDecodeWaves][NQ];
+  constexpr float kDLo = 5.421010862427522e-20f, kDHi = 1.8446744073709552e19f;  // 2^-64, 2^64
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T_ = p.T, HV = p.HV, H = p.H;
@@ -233,12 +246,35 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(Recurrent
       pq = q_ptr[(long)t * H * K];
     }
   };
-  auto put_g = [&](int buf) {
+  float gD = 1.0f;  // running decay of this thread's row
+  auto put_g = [&](int buf) {  // called by every thread of the workgroup
+    bool rn = false;
     if (gthread) {
-      s_al[buf][gts][gr] = gactive ? gate_alpha<GK>(pg, gbias, gc) : 1.0f;
-      s_k[buf][gts][gr] = gactive ? In<T>::widen(pk) : 0.0f;
-      s_q[buf][gts][gr] = gactive ? In<T>::widen(pq) : 0.0f;
+      float f = 1.0f, k1 = 0.0f, k2 = 0.0f, q1 = 0.0f;
+      if (gactive) {
+        const float kk = In<T>::widen(pk), qq = In<T>::widen(pq);
+        const float dn = gD * gate_alpha<GK>(pg, gbias, gc);
+        rn = !(dn >= kDLo && dn <= kDHi);
+        if (rn) {  // fold this token's decayed state into S_hat
+          f = dn;
+          gD = 1.0f;
+          k1 = kk;
+          k2 = kk;
+          q1 = qq;
+        } else {
+          gD = dn;
+          k1 = kk * dn;
+          k2 = kk * __builtin_amdgcn_rcpf(dn);
+          q1 = qq * dn;
+        }
+      }
+      s_f[buf][gts][gr] = f;
+      s_k1[buf][gts][gr] = k1;
+      s_k2[buf][gts][gr] = k2;
+      s_q1[buf][gts][gr] = q1;
     }
+    const bool any = __any(rn);
+    if (lane == 0) s_rn[buf][w] = any ? 1 : 0;
   };
 
   // ---- the state tile of this thread (layout of the decode step)
@@ -286,14 +322,18 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(Recurrent
     const float bt = pb;
     if (t + 1 < T_) fetch_v(t + 1);
 
-    // decay, then the prediction k . S_dec: in-wave butterfly, then across the WT waves
+    // the prediction k . S_dec = (k D) . S_hat (after a renormalisation where
+    // some row needs one): in-wave butterfly, then across the WT waves
+    int rn = 0;
+#pragma unroll
+    for (int j = 0; j < kDecodeWaves; ++j) rn |= s_rn[buf][j];
+    if (rn) {
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) s[i] *= s_f[buf][ts][row0 + RG * i];
+    }
     f32x4 pr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      const int r = row0 + RG * i;
-      s[i] *= s_al[buf][ts][r];
-      pr += s_k[buf][ts][r] * s[i];
-    }
+    for (int i = 0; i < RPL; ++i) pr += s_k1[buf][ts][row0 + RG * i] * s[i];
     pr = sum_row_groups<NQ>(pr);
     if (rg == 0) s_red[0][w][cq] = pr;
     __syncthreads();
@@ -309,8 +349,8 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(Recurrent
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const int r = row0 + RG * i;
-      s[i] += s_k[buf][ts][r] * rv;
-      ov += s_q[buf][ts][r] * s[i];
+      s[i] += s_k2[buf][ts][r] * rv;  // S_hat += (k / D) r^T
+      ov += s_q1[buf][ts][r] * s[i];  // q . S_new = (q D) . S_hat
     }
     ov = sum_row_groups<NQ>(ov);
     if (rg == 0) s_red[1][w][cq] = ov;
@@ -326,11 +366,16 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(Recurrent
       *reinterpret_cast<f32x4*>(o_ptr + (long)t * HV * V) = o * scale;
     }
   }
+  // S = diag(D) S_hat
+  if (gthread) s_D[gts][gr] = gD;
+  __syncthreads();
   if (active && p.S_out) {
     float* S = p.S_out + bh * (long)K * V;
 #pragma unroll
-    for (int i = 0; i < RPL; ++i)
-      __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (long)(row0 + RG * i) * V + col));
+    for (int i = 0; i < RPL; ++i) {
+      const int r = row0 + RG * i;
+      __builtin_nontemporal_store(s[i] * s_D[ts][r], reinterpret_cast<f32x4*>(S + (long)r * V + col));
+    }
   }
 }
 
