@@ -25,15 +25,22 @@
 // Schedule.  One workgroup owns one (sequence b, value head hv, 32-wide value
 // tile); the four value tiles of a head share blockIdx % 8 and so an XCD (and
 // its L2, which serves their common q, k, g_raw reads).  Its eight wavefronts
-// form a three-stage pipeline over 16-token blocks, one barrier per step:
-//   waves 0-3  prep of block n+2: gate, cumulative products, scaled operands,
-//              with the block's HBM inputs prefetched into registers a step ahead
-//   wave 4     A for block n+1 (MFMA)
-//   wave 5     R for block n+1 (MFMA), then (I + R)^{-1} by fp32 substitution
-//   waves 6-7  the state chain of block n, one 16-wide value column block each:
-//              K_hat S, Q_hat S, Ebar, U, O and the state update, with that
-//              column block of the fp32 state held in registers for the whole
-//              sequence (no other wave touches it, so the chain needs no barrier)
+// form a four-stage pipeline over 16-token blocks, one barrier per step; each
+// role runs its own loop over the NT + 3 steps:
+//   waves 0-3  prep of block n+3: gate, cumulative products, scaled operands
+//              (hi/lo words) and the block's v tile into a triple-buffered LDS
+//              slot, with the next block's HBM inputs loaded a step ahead
+//   wave 4     A^T of block n+2 (kept in registers), s Q_hat S of block n+1
+//              from the chain's LDS copy of the state, and O = s Q_hat S + A U
+//              of block n with U handed over by the chain, then the o stores
+//   wave 5     R of block n+2 (MFMA), then (I + R)^{-1} = X_d - X_d N X_d
+//              (X_d: the two 8x8 diagonal inverses by substitution, N: the
+//              lower-left 8x8 block of R), on fp32 MFMA
+//   waves 6-7  the state chain of block n+1, one 16-wide value column block
+//              each, with that column block of the fp32 state held in
+//              registers for the whole sequence: diag(gamma) S, K_hat S, Ebar,
+//              U and the state update; U goes to wave 4 and a hi/lo copy of
+//              the new state to a double-buffered LDS slot
 // bf16 inputs use bf16 MFMA with fp32 accumulation.  Every operand of these
 // products is derived (scaled by decay factors, the state, or a solve result),
 // and a single bf16 rounding of them costs far more than the 1e-2 error budget
