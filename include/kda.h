@@ -183,6 +183,39 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, kda_dt
                              const float* initial_state, float* o, float* final_state, int B,
                              int T, int H, int HV, int K, int V, kda_stream_t stream);
 
+/*
+ * kda_chunk_fwd_split -- the chunkwise forward as three stages with the entry
+ * state of every chunk materialised ("DeltaNet family" page, "Chunkwise Triton
+ * pipeline": an intra-chunk stage, one pass across chunks producing the
+ * chunk-entry states h and the resolved values, and an output stage parallel
+ * over chunks).  Only the middle stage is sequential over a sequence, and it
+ * carries just two K x V products per chunk, so this schedule fills the GPU
+ * where B * HV is too small for kda_chunk_fwd (one long sequence, few heads);
+ * it also hands the caller the state at every chunk boundary.
+ *
+ *   arguments as kda_chunk_fwd, plus
+ *   h             [B, HV, NC, K, V] float32 output, NC = ceil(T / chunk_size):
+ *                 h[b, hv, c] is the state entering chunk c (h[.., 0] is the
+ *                 initial state); NULL keeps h inside the workspace
+ *   workspace     device scratch of at least
+ *                 kda_chunk_fwd_split_workspace_bytes(...) bytes, 16-byte aligned,
+ *                 owned by the caller; its contents need not be initialised and
+ *                 are meaningless afterwards
+ * Supported: K == V in {16, 32, 64, 128}; chunk_size 16, 32 or 64; HV % H == 0;
+ * T >= 0.  Arithmetic: fp32 matrix products with fp32 accumulation for both
+ * input dtypes (bf16 inputs are widened exactly).  Three kernels run in order on
+ * `stream`.  Returns KDA_ERR_WORKSPACE if the workspace is missing or too small.
+ */
+size_t kda_chunk_fwd_split_workspace_bytes(int B, int T, int H, int HV, int K, int V,
+                                           int chunk_size);
+
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                               const float* g_raw, const float* beta, const float* A_log,
+                               const float* dt_bias, kda_gate_kind gate, float lower_bound,
+                               const float* initial_state, float* o, float* final_state, float* h,
+                               int B, int T, int H, int HV, int K, int V, int chunk_size,
+                               void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

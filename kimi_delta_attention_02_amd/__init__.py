@@ -10,6 +10,8 @@ DeltaNet (dt_bias [HV]); the binding passes KDA_GATE_PER_HEAD for the latter.
 
 * :func:`gate`           -- gate activation (+ optional chunk-local cumulative sum)
 * :func:`chunk_fwd`      -- chunkwise forward over whole sequences
+* :func:`chunk_fwd_split` -- the chunkwise forward as three stages with the
+                            chunk-entry states materialised (few heads, long sequences)
 * :func:`recurrent_fwd`  -- T tokens per call with the state kept on chip
 * :func:`recurrent_step` -- one decode token, state updated in place
 """
@@ -19,8 +21,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["gate", "chunk_fwd", "recurrent_fwd", "recurrent_step", "chunk_fwd_workspace_bytes",
-           "KDAError"]
+__all__ = ["gate", "chunk_fwd", "chunk_fwd_split", "recurrent_fwd", "recurrent_step",
+           "chunk_fwd_workspace_bytes", "chunk_fwd_split_workspace_bytes", "KDAError"]
 
 KDAError = _lib.KDAError
 
@@ -126,6 +128,47 @@ def chunk_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_b
                            _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check("kda_chunk_fwd", st)
     return o, final_state
+
+
+def chunk_fwd_split_workspace_bytes(B, T, H, HV, K, V, chunk_size=64):
+    return int(_lib.load().kda_chunk_fwd_split_workspace_bytes(B, T, H, HV, K, V, chunk_size))
+
+
+def chunk_fwd_split(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_bound=-5.0,
+                    chunk_size=64, initial_state=None, output_final_state=True,
+                    output_states=False, o=None, final_state=None, h=None, workspace=None):
+    """Chunkwise forward in three stages (intra-chunk, state pass, output),
+    with the entry state of every chunk materialised.  Arguments as
+    :func:`chunk_fwd`.  Returns (o, final_state, h): h [B, HV, NC, K, V]
+    float32 with NC = ceil(T / chunk_size) when output_states is True (or an
+    ``h`` tensor is given), else None."""
+    lib = _lib.load()
+    qkv = _qkv_dtype(q)
+    dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
+                                                            initial_state)
+    if o is None:
+        o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (B, HV, K, V), dev)
+    NC = (T + chunk_size - 1) // chunk_size if chunk_size > 0 else 0
+    if output_states and h is None:
+        h = torch.empty((B, HV, NC, K, V), dtype=torch.float32, device=dev)
+    if h is not None:
+        _need(h, "h", torch.float32, (B, HV, NC, K, V), dev)
+    need = int(lib.kda_chunk_fwd_split_workspace_bytes(B, T, H, HV, K, V, chunk_size))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_fwd_split(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta),
+                                 _ptr(A_log), _ptr(dt_bias), _gate_code(gate, per_head),
+                                 float(lower_bound), _ptr(initial_state), _ptr(o),
+                                 _ptr(final_state), _ptr(h), B, T, H, HV, K, V, int(chunk_size),
+                                 _ptr(workspace), ws_bytes, _stream(dev))
+    _lib.check("kda_chunk_fwd_split", st)
+    return o, final_state, h
 
 
 def _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias, initial_state):

@@ -30,6 +30,10 @@ SIGNATURES = {
                                     _vp, _vp] + [_c_int] * 5 + [_vp]),
     "kda_recurrent_fwd": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_float,
                                    _vp, _vp, _vp] + [_c_int] * 6 + [_vp]),
+    "kda_chunk_fwd_split_workspace_bytes": (ctypes.c_size_t, [_c_int] * 7),
+    "kda_chunk_fwd_split": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_float,
+                                     _vp, _vp, _vp, _vp] + [_c_int] * 7
+                            + [_vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None

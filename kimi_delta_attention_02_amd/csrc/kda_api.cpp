@@ -25,6 +25,12 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
                         int per_head, float lower_bound, const float* S0, float* o, float* S_out,
                         int B, int T, int H, int HV, int K, hipStream_t stream);
+size_t split_workspace_floats(int K, int V, int C);
+hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
+                        const float* beta, const float* A_log, const float* dt_bias, int kind,
+                        int per_head, float lower_bound, const float* S0, float* o, float* S_out,
+                        float* h, void* workspace, int B, int T, int H, int HV, int K, int C,
+                        hipStream_t stream);
 }  // namespace kda
 
 namespace {
@@ -166,6 +172,43 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, kda_dt
                                         dt_bias, gate_base(gate), gate_per_head(gate),
                                         lower_bound, initial_state, o, final_state, B, T, H, HV,
                                         K, V, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t kda_chunk_fwd_split_workspace_bytes(int B, int T, int H, int HV, int K, int V,
+                                           int chunk_size) {
+  (void)H;
+  if (B <= 0 || T <= 0 || HV < 1 || K < 1 || V < 1 || chunk_size < 1) return 0;
+  const size_t nc = ((size_t)T + chunk_size - 1) / chunk_size;
+  return (size_t)B * HV * nc * kda::split_workspace_floats(K, V, chunk_size) * sizeof(float);
+}
+
+kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                               const float* g_raw, const float* beta, const float* A_log,
+                               const float* dt_bias, kda_gate_kind gate, float lower_bound,
+                               const float* initial_state, float* o, float* final_state, float* h,
+                               int B, int T, int H, int HV, int K, int V, int chunk_size,
+                               void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+  kda_status st = check_gate(gate, lower_bound, A_log);
+  if (st != KDA_OK) return st;
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0) return KDA_ERR_INVALID_ARG;
+  if ((long)B * HV > (1L << 28)) return KDA_ERR_INVALID_ARG;
+  if (!head_size_ok(K) || V != K) return KDA_ERR_UNSUPPORTED;
+  if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+  const long nc = ((long)T + chunk_size - 1) / chunk_size;
+  if ((long)B * HV * nc > 0x7fffffffL) return KDA_ERR_INVALID_ARG;  // one workgroup per chunk
+  if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, initial_state, final_state, h, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+  if (!gate_inputs_aligned(gate, g_raw, dt_bias)) return KDA_ERR_INVALID_ARG;
+  const size_t need = kda_chunk_fwd_split_workspace_bytes(B, T, H, HV, K, V, chunk_size);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (B == 0) return KDA_OK;
+  return from_hip(kda::launch_split(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log, dt_bias,
+                                    gate_base(gate), gate_per_head(gate), lower_bound,
+                                    initial_state, o, final_state, h, workspace, B, T, H, HV, K,
+                                    chunk_size, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -70,6 +70,10 @@ WORKLOADS = {
     # the prefill shape with one gate per (token, value head), as in Gated DeltaNet
     "prefill_head_gate": Workload("prefill_head_gate", 4, 4096, 16, 16, 128, 128, 64, "bf16",
                                   "safe", -5.0, 0.5, -4.0, 0.0, 0.0, seed=6, per_head_gate=True),
+    # one GPU's share of the long-context workload split over eight GPUs by GVA
+    # head groups: one 65,536-token sequence, 2 q/k heads, 8 value heads
+    "long_shard": Workload("long_shard", 1, 65536, 2, 8, 128, 128, 64, "bf16", "safe", -5.0,
+                           0.5, -4.0, 0.0, 0.0, seed=7),
 }
 
 

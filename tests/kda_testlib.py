@@ -119,3 +119,41 @@ def compare_heads(o, S, ref, tol, what):
     assert eo <= tol, "%s: o error %.3e > %.0e" % (what, eo, tol)
     assert eS <= tol, "%s: state error %.3e > %.0e" % (what, eS, tol)
     return eo, eS
+
+
+def run_split(d, w_gate, lower_bound, chunk, initial_state=True):
+    """kda_chunk_fwd_split with the chunk-entry states; returns (o, S, h)."""
+    g = to_dev(d)
+    o, S, h = kda.chunk_fwd_split(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"],
+                                  g["dt_bias"], gate=w_gate, lower_bound=lower_bound,
+                                  chunk_size=chunk,
+                                  initial_state=g["S0"] if initial_state else None,
+                                  output_states=True)
+    torch.cuda.synchronize()
+    return o, S, h
+
+
+def oracle_by_chunks(d, w_gate, lower_bound, chunk, initial_state=True, nchunks=None):
+    """The oracle's recurrence run chunk after chunk, each chunk starting from
+    the state the previous one ended with: (o, final state, h) where
+    h[:, :, c] is the state entering chunk c.  With nchunks, only the first
+    nchunks chunks are run (o and the state then cover those tokens only)."""
+    d = per_channel_gate(d)
+    orc = oracle.default()
+    B, T, H, K = d["q"].shape
+    HV, V = d["v"].shape[2], d["v"].shape[3]
+    S = (d["S0"].double().numpy() if (initial_state and d["S0"] is not None)
+         else np.zeros((B, HV, K, V)))
+    nc = (T + chunk - 1) // chunk
+    if nchunks is not None:
+        nc = min(nc, nchunks)
+    hs, os_ = [], []
+    for c in range(nc):
+        sl = slice(c * chunk, min(T, (c + 1) * chunk))
+        hs.append(S)
+        o_c, S = orc.kda_fwd(d["q"][:, sl], d["k"][:, sl], d["v"][:, sl], d["g_raw"][:, sl],
+                             d["beta"][:, sl], d["A_log"], d["dt_bias"], w_gate, lower_bound, S)
+        os_.append(o_c)
+    o = np.concatenate(os_, axis=1) if os_ else np.zeros((B, 0, HV, V))
+    h = np.stack(hs, axis=2) if hs else np.zeros((B, HV, 0, K, V))
+    return o, S, h

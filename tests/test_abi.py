@@ -38,7 +38,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["kda_status_string", "kda_version", "kda_gate",
                                   "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-                                  "kda_recurrent_step", "kda_recurrent_fwd"])
+                                  "kda_recurrent_step", "kda_recurrent_fwd",
+                                  "kda_chunk_fwd_split_workspace_bytes", "kda_chunk_fwd_split"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -149,6 +150,47 @@ def _rec(lib, **kw):
 ])
 def test_recurrent_fwd_validation(lib, kw, status):
     assert _rec(lib, **kw) == status
+
+
+def test_split_workspace_bytes(lib):
+    # W, Kt^T, u and h per (b, hv, chunk), plus gamma: (3 C K + K + K K) floats
+    nc = (4100 + 63) // 64
+    assert lib.kda_chunk_fwd_split_workspace_bytes(2, 4100, 4, 8, 128, 128, 64) == \
+        2 * 8 * nc * (3 * 64 * 128 + 128 + 128 * 128) * 4
+    assert lib.kda_chunk_fwd_split_workspace_bytes(2, 0, 4, 8, 128, 128, 64) == 0
+    assert lib.kda_chunk_fwd_split_workspace_bytes(0, 64, 4, 8, 128, 128, 64) == 0
+
+
+def _split(lib, **kw):
+    a = dict(q=P, k=P, v=P, dt=_lib.KDA_BF16, g=P, beta=P, A=P, bias=P, gate=1, L=-5.0, S0=None,
+             o=P, S=P, h=None, B=1, T=64, H=2, HV=4, K=128, V=128, C=64, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_chunk_fwd_split(a["q"], a["k"], a["v"], a["dt"], a["g"], a["beta"], a["A"],
+                                   a["bias"], a["gate"], a["L"], a["S0"], a["o"], a["S"], a["h"],
+                                   a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"], a["C"],
+                                   a["ws"], a["wsb"], None)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(HV=3), _lib.KDA_ERR_INVALID_ARG),
+    (dict(k=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(o=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(h=P + 4), _lib.KDA_ERR_INVALID_ARG),        # misaligned h
+    (dict(ws=P + 8), _lib.KDA_ERR_INVALID_ARG),       # misaligned workspace
+    (dict(ws=None), _lib.KDA_ERR_WORKSPACE),
+    (dict(wsb=1000), _lib.KDA_ERR_WORKSPACE),
+    (dict(T=-1), _lib.KDA_ERR_INVALID_ARG),
+    (dict(A=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(L=0.5), _lib.KDA_ERR_INVALID_ARG),
+    (dict(K=96, V=96), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(K=64, V=128), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(C=8), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(B=0), _lib.KDA_OK),
+    (dict(gate=_lib.KDA_GATE_PER_HEAD | 2, A=None, B=0), _lib.KDA_OK),
+])
+def test_chunk_fwd_split_validation(lib, kw, status):
+    assert _split(lib, **kw) == status
 
 
 @needs_no_gpu
