@@ -7,8 +7,10 @@ all in one launch of the fused chunk kernel.  The recurrent decode row is
 timed in the same run on the decode workload (B=256, HV=32, 256 single-token
 steps over a 512 MiB fp32 state) and reported in the "decode" object; the
 fused multi-token recurrent forward runs the same 256 tokens as 16-token calls
-and as one 256-token call ("recurrent" object), and the chunked forward runs the
-prefill shape with one gate per (token, value head) ("head_gate" object).
+and as one 256-token call ("recurrent" object), the chunked forward runs the
+prefill shape with one gate per (token, value head) ("head_gate" object), and
+the one-sequence long shard (T=65536, 8 value heads) runs through both the
+fused chunk kernel and the three-stage split schedule ("split" object).
 
 Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
 HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
@@ -93,6 +95,7 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=["prefill", "gva", "long", "tiny"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -199,6 +202,55 @@ def main():
                      "frac": hgbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": hbytes,
                      "kernel": "chunk_fwd_kernel<128, bf16, per-head gate>"}}
     del gh, oh, Sh
+
+    # One GPU's share of the long-context workload (one sequence, 8 value
+    # heads): the fused chunk kernel against the three-stage split schedule.
+    if not args.no_split:
+        ws_ = synth.WORKLOADS["long_shard"]
+        dsh = synth.make_inputs(ws_)
+        gsh = {n: (t.to(dev) if t is not None else None) for n, t in dsh.items()}
+        osh = torch.empty((ws_.B, ws_.T, ws_.HV, ws_.V), dtype=torch.float32, device=dev)
+        Ssh = torch.empty((ws_.B, ws_.HV, ws_.K, ws_.V), dtype=torch.float32, device=dev)
+        wsp = torch.empty(kda.chunk_fwd_split_workspace_bytes(ws_.B, ws_.T, ws_.H, ws_.HV, ws_.K,
+                                                              ws_.V, ws_.chunk),
+                          dtype=torch.uint8, device=dev)
+        args_sh = (gsh["q"], gsh["k"], gsh["v"], gsh["g_raw"], gsh["beta"], gsh["A_log"],
+                   gsh["dt_bias"])
+        kw_sh = dict(gate=ws_.gate, lower_bound=ws_.lower_bound, chunk_size=ws_.chunk,
+                     initial_state=gsh["S0"], o=osh, final_state=Ssh)
+
+        def time_calls(fn, n):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            z.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(z) / n
+
+        n_sh = max(1, min(args.steps, 5))
+        fused_ms = time_calls(lambda: kda.chunk_fwd(*args_sh, **kw_sh), n_sh)
+        split_ms = time_calls(lambda: kda.chunk_fwd_split(*args_sh, workspace=wsp, **kw_sh), n_sh)
+        sbytes = chunk_bytes(ws_)
+        tok = ws_.B * ws_.T
+
+        def line(ms, kernel):
+            gbs = sbytes / (ms * 1e-3) / 1e9
+            return {"ms_per_call": ms, "value": tok / (ms * 1e-3), "unit": "tokens/s",
+                    "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                 "bytes_per_launch": sbytes, "kernel": kernel}}
+
+        result["split"] = {
+            "workload": ws_.name, "B": ws_.B, "T": ws_.T, "H": ws_.H, "HV": ws_.HV, "K": ws_.K,
+            "chunk": ws_.chunk, "gate": ws_.gate,
+            "fused": line(fused_ms, "chunk_fwd_kernel<128, bf16>"),
+            "split": line(split_ms, "split_intra + split_state + split_output <128, 64>"),
+            "speedup": fused_ms / split_ms}
+        del gsh, osh, Ssh, wsp
 
     if not args.no_decode:
         wd = synth.WORKLOADS["decode"]

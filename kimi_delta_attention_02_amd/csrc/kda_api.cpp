@@ -25,7 +25,7 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
                         int per_head, float lower_bound, const float* S0, float* o, float* S_out,
                         int B, int T, int H, int HV, int K, hipStream_t stream);
-size_t split_workspace_floats(int K, int V, int C);
+size_t split_workspace_bytes_per_chunk(int K, int V, int C);
 hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
                         int per_head, float lower_bound, const float* S0, float* o, float* S_out,
@@ -179,7 +179,7 @@ size_t kda_chunk_fwd_split_workspace_bytes(int B, int T, int H, int HV, int K, i
   (void)H;
   if (B <= 0 || T <= 0 || HV < 1 || K < 1 || V < 1 || chunk_size < 1) return 0;
   const size_t nc = ((size_t)T + chunk_size - 1) / chunk_size;
-  return (size_t)B * HV * nc * kda::split_workspace_floats(K, V, chunk_size) * sizeof(float);
+  return (size_t)B * HV * nc * kda::split_workspace_bytes_per_chunk(K, V, chunk_size);
 }
 
 kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,

@@ -32,8 +32,18 @@
 //   split_output_kernel  one workgroup per (b, hv, chunk): gate and sums
 //                        again, A, O = s (q * exp(G)) h_c + A U
 //
-// All products use the fp32 MFMA (16x16x4) with fp32 accumulation; bf16
-// inputs are widened on load.
+// The state pass is a chain of dependent products, so its per-chunk latency
+// sets the pace: each chunk's W, Kt^T and gamma form one contiguous block of
+// the workspace that all wavefronts copy into a double-buffered LDS slot one
+// chunk ahead, and u is loaded into registers one chunk ahead.  With bf16
+// inputs (K, C >= 32) W and Kt^T are stored as hi + lo bf16 pairs, and the
+// chain runs on the bf16 MFMA (16x16x32, hi*hi + hi*lo + lo*hi), with the key
+// (for W) and token (for Kt^T) axes permuted inside each 32-wide slice so that
+// the state and U serve as B operands straight from the accumulator layout.
+// Everything else, and the fp32-input chain, uses the fp32 MFMA (16x16x4);
+// bf16 inputs are widened on load.
+#include <type_traits>
+
 #include "kda_device.h"
 
 namespace kda {
@@ -49,33 +59,46 @@ struct SplitParams {
   const float* S0;
   float* o;
   float* S_out;
-  float* h;    // [B, HV, NC, K, V] entry state of every chunk
-  float* w;    // workspace: W      [B, HV, NC, C, K]
-  float* kt;   //            Kt^T   [B, HV, NC, K, C]
-  float* u;    //            u -> U [B, HV, NC, C, V]
-  float* gam;  //            gamma  [B, HV, NC, K]
-  int B, T, H, HV, NC, kind, per_head;
+  float* h;    // entry state of every chunk: the caller's [B, HV, NC, K, V] (h_plain)
+               // or, in the workspace, 16 x 16 fragments (see frag_index)
+  char* ops;   // workspace: per (b, hv, chunk) the LDS image of W, Kt^T, gamma
+  float* u;    //            u, then U: C x V per (b, hv, chunk), as fragments
+  int B, T, H, HV, NC, kind, per_head, h_plain;
   float lower_bound;
 };
 
 constexpr int kSplitThreads = 256;
+
+// u, U and the workspace copy of h are kept as 16 x 16 MFMA accumulator
+// fragments: fragment (column block cb, row block rb) of a chunk's R x N
+// matrix is 64 lanes x 4 floats, lane l holding rows 16 rb + 4 (l / 16) + r
+// of column 16 cb + l % 16, so every lane moves 16 contiguous bytes.
+__device__ __forceinline__ long frag_index(long mat, int ncb, int nrb, int cb, int rb, int lane) {
+  return (((mat * ncb + cb) * nrb + rb) * 64 + lane) * 4;
+}
+#ifndef KDA_STATE_WAVES
+#define KDA_STATE_WAVES 1
+#endif
+constexpr int kStateWaves = KDA_STATE_WAVES;  // column-block wavefronts per state-pass workgroup
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // Shared memory of a chunk: the log2 cumulative decay inside each 16-token
-// sub-block, and the k (and q) rows in fp32, row stride K + 4 (16-byte rows,
-// spread over the banks).  The exponent of every decay factor is formed from
-// these local sums and whole sub-block totals, never as the difference of two
-// long prefix sums, so its rounding error scales with the factor's own
-// exponent (terms of one sign add without cancellation).
+// sub-block, and the k rows (plus q or v rows) in fp32, row stride K + 4
+// (16-byte rows, spread over the banks).  The exponent of every decay factor
+// is formed from these local sums and whole sub-block totals, never as the
+// difference of two long prefix sums, so its rounding error scales with the
+// factor's own exponent (terms of one sign add without cancellation).
 template <int K, int C>
 struct alignas(16) ChunkRows {
   static constexpr int LD = K + 4;
   alignas(16) float G2[C * LD];  // G2[i] = sum of log2 alpha over the sub-block of i, up to i
   alignas(16) float k[C * LD];
+  alignas(16) float x[C * LD];   // q rows (output pass) or v rows (intra pass)
   alignas(16) float beta[C];
+  alignas(16) float graw[C];     // per-head gate inputs
 };
 
 // log2 decay of whole sub-blocks J0 .. J1 - 1 in channel c
@@ -86,23 +109,51 @@ __device__ __forceinline__ float blocks_log2(const ChunkRows<K, C>& L, int J0, i
   return s;
 }
 
-// Loads chunk c of head (b, hv): G2 (see ChunkRows), k (and q when qrows is
-// given) widened to fp32, beta.  Tokens at or past T read as g = 0,
-// k = q = 0, beta = 0, which leave the state unchanged.  Ends with a barrier.
+// Loads chunk c of head (b, hv) into L: G2 (see ChunkRows), k, and q (xq) or
+// v (otherwise) widened to fp32, beta.  Every global load of the chunk is
+// issued before the first is used.  Tokens at or past T read as g = 0,
+// k = q = v = 0, beta = 0, which leave the state unchanged.  Ends with a
+// barrier.
 template <int K, int C, typename T>
-__device__ void load_chunk(const SplitParams& p, long bh, int c, ChunkRows<K, C>& L, float* qrows) {
-  constexpr int LD = ChunkRows<K, C>::LD, NB = C / 16;
+__device__ void load_chunk(const SplitParams& p, long bh, int c, ChunkRows<K, C>& L, bool xq) {
+  constexpr int LD = ChunkRows<K, C>::LD, NB = C / 16, Q4 = K / 4;
   const int tid = threadIdx.x;
   const int HV = p.HV, T_ = p.T;
   const int hv = (int)(bh % HV);
   const long b = bh / HV;
   const int hq = hv / (HV / p.H);
   const int t0 = c * C;
+  const T* kp = static_cast<const T*>(p.k);
+  const T* xp = static_cast<const T*>(xq ? p.q : p.v);
+  const int xheads = xq ? p.H : HV, xh = xq ? hq : hv;
+
+  // raw gate inputs, k and q / v rows: four elements per load
+  for (int e = tid; e < C * Q4; e += kSplitThreads) {
+    const int i = e / Q4, c4 = (e % Q4) * 4;
+    const int t = t0 + i;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+    float a[4] = {0.f, 0.f, 0.f, 0.f}, x[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < T_) {
+      if (!p.per_head)
+        g = *reinterpret_cast<const float4*>(p.g_raw + ((b * T_ + t) * HV + hv) * (long)K + c4);
+      In<T>::load4(kp, ((b * T_ + t) * p.H + hq) * (long)K + c4, a);
+      In<T>::load4(xp, ((b * T_ + t) * xheads + xh) * (long)K + c4, x);
+    }
+    *reinterpret_cast<float4*>(L.G2 + i * LD + c4) = g;
+    *reinterpret_cast<float4*>(L.k + i * LD + c4) = make_float4(a[0], a[1], a[2], a[3]);
+    *reinterpret_cast<float4*>(L.x + i * LD + c4) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+  for (int i = tid; i < C; i += kSplitThreads) {
+    const bool in = t0 + i < T_;
+    L.beta[i] = in ? p.beta[(b * T_ + t0 + i) * HV + hv] : 0.0f;
+    if (p.per_head) L.graw[i] = in ? p.g_raw[(b * T_ + t0 + i) * HV + hv] : 0.0f;
+  }
+  __syncthreads();
+
+  // gate and the cumulative sum inside each sub-block, in place: one
+  // (channel, sub-block) pair per thread and pass
   const int gK = p.per_head ? 1 : K;
   const float rate = p.kind != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
-
-  // gate and the cumulative sum inside each sub-block: one (channel,
-  // sub-block) pair per thread and pass
   for (int pr = tid; pr < K * NB; pr += kSplitThreads) {
     const int kap = pr % K, J = pr / K;
     const int gc = p.per_head ? 0 : kap;
@@ -112,33 +163,15 @@ __device__ void load_chunk(const SplitParams& p, long bh, int c, ChunkRows<K, C>
 #pragma unroll 4
     for (int j = 0; j < 16; ++j) {
       const int i = J * 16 + j;
-      const int t = t0 + i;
       float g = 0.0f;
-      if (t < T_)
-        g = gate_log_decay(p.g_raw[((b * T_ + t) * HV + hv) * (long)gK + gc], bias, rate, p.kind,
-                           p.lower_bound);
+      if (t0 + i < T_) {
+        const float graw = p.per_head ? L.graw[i] : L.G2[i * LD + kap];
+        g = gate_log_decay(graw, bias, rate, p.kind, p.lower_bound);
+      }
       run += g * kLog2e;
       L.G2[i * LD + kap] = run;
     }
   }
-
-  // k (and q) rows, four elements per load
-  const T* kp = static_cast<const T*>(p.k);
-  const T* qp = static_cast<const T*>(p.q);
-  for (int e = tid; e < C * K / 4; e += kSplitThreads) {
-    const int i = e / (K / 4), c4 = (e % (K / 4)) * 4;
-    const int t = t0 + i;
-    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < T_) {
-      const long off = ((b * T_ + t) * p.H + hq) * (long)K + c4;
-      In<T>::load4(kp, off, x);
-      if (qrows) In<T>::load4(qp, off, y);
-    }
-    *reinterpret_cast<float4*>(L.k + i * LD + c4) = make_float4(x[0], x[1], x[2], x[3]);
-    if (qrows) *reinterpret_cast<float4*>(qrows + i * LD + c4) = make_float4(y[0], y[1], y[2], y[3]);
-  }
-  for (int i = tid; i < C; i += kSplitThreads)
-    L.beta[i] = t0 + i < T_ ? p.beta[(b * T_ + t0 + i) * HV + hv] : 0.0f;
   __syncthreads();
 }
 
@@ -196,10 +229,56 @@ __device__ __forceinline__ void tri_pair(int pr, bool strict, int& i, int& j) {
   j = pr;
 }
 
+// ----------------------------------------------------------------- chain operand layout
+// Position of element e (0..31) of a 32-wide slice in the bf16 operand rows:
+// lanes of group g read positions 8g .. 8g+7, which must be the elements
+// 4g .. 4g+3 and 16+4g .. 16+4g+3 that the accumulator layout gives them
+// (rows 4g + r of two consecutive 16-row blocks).
+__device__ __forceinline__ int slice_pos(int e) { return 8 * ((e & 15) >> 2) + (e & 3) + 4 * (e >> 4); }
+
+// The chain pass reads bf16 operands when the inputs are bf16 and both
+// contractions are at least 32 long.
+template <int K, int C, typename T>
+struct ChainBF {
+  static constexpr bool value = std::is_same<T, uint16_t>::value && K >= 32 && C >= 32;
+};
+
+// ----------------------------------------------------------------- chain operands
+// The chain operands of one chunk in LDS.  fp32: W [C][K+4], Kt^T [K][C+4];
+// bf16: hi and lo words of W [C][K+8] and Kt^T [K][C+8] (rows padded by 16
+// bytes); then gamma [K].
+template <int K, int C, bool BF>
+struct ChainOps;
+template <int K, int C>
+struct alignas(16) ChainOps<K, C, false> {
+  static constexpr int LW = K + 4, LK = C + 4;
+  alignas(16) float w[C * LW];
+  alignas(16) float kt[K * LK];
+  alignas(16) float gam[K];
+};
+template <int K, int C>
+struct alignas(16) ChainOps<K, C, true> {
+  static constexpr int LW = K + 8, LK = C + 8;
+  alignas(16) uint16_t wh[C * LW];
+  alignas(16) uint16_t wl[C * LW];
+  alignas(16) uint16_t kh[K * LK];
+  alignas(16) uint16_t kl[K * LK];
+  alignas(16) float gam[K];
+};
+
+// Bytes of one chunk's image in the workspace: the larger layout, rounded
+// up to whole 1 KiB copies (one wavefront-wide 16-byte load per lane).
+template <int K, int C>
+constexpr int split_image_bytes() {
+  constexpr int a = (int)sizeof(ChainOps<K, C, false>), b = (int)sizeof(ChainOps<K, C, true>);
+  return ((a > b ? a : b) + 1023) / 1024 * 1024;
+}
+
 // ----------------------------------------------------------------- intra
 template <int K, int C, typename T>
 __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams p) {
   constexpr int NB = C / 16, LD = ChunkRows<K, C>::LD, LR = C + 4, LX = 20;
+  constexpr bool BF = ChainBF<K, C, T>::value;
   __shared__ ChunkRows<K, C> L;
   __shared__ alignas(16) float R[C * LR];
   __shared__ alignas(16) float Xd[NB * 16 * LX];
@@ -207,7 +286,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
   const long ch = blockIdx.x;
   const long bh = ch / p.NC;
   const int c = (int)(ch % p.NC);
-  load_chunk<K, C, T>(p, bh, c, L, nullptr);
+  load_chunk<K, C, T>(p, bh, c, L, false);
 
   // R inside the 16-token sub-blocks, direct
   for (int e = tid; e < NB * 120; e += kSplitThreads) {
@@ -252,12 +331,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
 
   // [W | u] = (I + R)^{-1} diag(beta) [k exp(G) | v], by blocks of 16 rows:
   // Y_I = X_II (B_I - sum_{J<I} R_IJ Y_J), one 16-wide column block per pass
-  const T* vp = static_cast<const T*>(p.v);
-  const int hv = (int)(bh % p.HV);
-  const long b = bh / p.HV;
-  const int t0 = c * C;
-  float* Wout = p.w + ch * (long)C * K;
-  float* Uout = p.u + ch * (long)C * K;
+  using Ops = ChainOps<K, C, BF>;
+  Ops& img = *reinterpret_cast<Ops*>(p.ops + ch * (long)split_image_bytes<K, C>());
+
   for (int cb = w; cb < 2 * (K / 16); cb += kSplitThreads / 64) {
     const bool isw = cb < K / 16;
     const int col = (isw ? cb : cb - K / 16) * 16 + (lane & 15);
@@ -268,13 +344,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = I * 16 + 4 * g4 + r;
-        float x;
-        if (isw) {
-          x = L.k[i * LD + col] *
-              __builtin_amdgcn_exp2f(L.G2[i * LD + col] + blocks_log2(L, 0, I, col));
-        } else {
-          x = t0 + i < p.T ? In<T>::at(vp, ((b * p.T + t0 + i) * p.HV + hv) * (long)K + col) : 0.0f;
-        }
+        const float x = isw ? L.k[i * LD + col] *
+                                  __builtin_amdgcn_exp2f(L.G2[i * LD + col] + blocks_log2(L, 0, I, col))
+                            : L.x[i * LD + col];
         t[r] = L.beta[i] * x;
       }
 #pragma unroll
@@ -293,91 +365,224 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
       z = mfma4(a.w, t[3], z);
       y[I] = z;
     }
-    float* out = isw ? Wout : Uout;
 #pragma unroll
     for (int I = 0; I < NB; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[(I * 16 + 4 * g4 + r) * K + col] = y[I][r];
+      for (int r = 0; r < 4; ++r) {
+        const int i = I * 16 + 4 * g4 + r;
+        if (!isw) {
+          if (r == 0)
+            *reinterpret_cast<f32x4*>(p.u + frag_index(ch, K / 16, NB, cb - K / 16, I, lane)) = y[I];
+        } else if constexpr (BF) {  // hi and lo words, keys permuted per slice
+          uint16_t hi, lo;
+          split_bf16(y[I][r], hi, lo);
+          const int pos = i * Ops::LW + (col & ~31) + slice_pos(col & 31);
+          img.wh[pos] = hi;
+          img.wl[pos] = lo;
+        } else {
+          img.w[i * Ops::LW + col] = y[I][r];
+        }
+      }
   }
 
-  // Kt^T [K][C] and gamma
-  float* kt = p.kt + ch * (long)K * C;
+  // Kt^T and gamma
   for (int e = tid; e < K * C; e += kSplitThreads) {
     const int kap = e / C, i = e % C;
     const int I = i >> 4;
     const float rest = (L.G2[(I * 16 + 15) * LD + kap] - L.G2[i * LD + kap]) + blocks_log2(L, I + 1, NB, kap);
-    kt[e] = L.k[i * LD + kap] * __builtin_amdgcn_exp2f(rest);
+    const float val = L.k[i * LD + kap] * __builtin_amdgcn_exp2f(rest);
+    if constexpr (BF) {  // hi and lo words, tokens permuted per slice
+      uint16_t hi, lo;
+      split_bf16(val, hi, lo);
+      const int pos = kap * Ops::LK + (i & ~31) + slice_pos(i & 31);
+      img.kh[pos] = hi;
+      img.kl[pos] = lo;
+    } else {
+      img.kt[kap * Ops::LK + i] = val;
+    }
   }
   for (int kap = tid; kap < K; kap += kSplitThreads)
-    p.gam[ch * K + kap] = __builtin_amdgcn_exp2f(blocks_log2(L, 0, NB, kap));
+    img.gam[kap] = __builtin_amdgcn_exp2f(blocks_log2(L, 0, NB, kap));
 }
 
-// ----------------------------------------------------------------- states
-// One wavefront per 16-wide column block of the state; lane l holds rows
-// 16 kb + 4 (l / 16) + r of column l % 16 (the MFMA accumulator layout), which
-// is also the layout of the B operand the two products below take.
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// hi and lo words of eight values (two accumulator fragments) as bf16x8 operands
+__device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+  uint4 h, l;
+  split2_bf16(a[0], a[1], h.x, l.x);
+  split2_bf16(a[2], a[3], h.y, l.y);
+  split2_bf16(b[0], b[1], h.z, l.z);
+  split2_bf16(b[2], b[3], h.w, l.w);
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// u of chunk index ch, column block cb: the lane's fragments
 template <int K, int C>
-__global__ __launch_bounds__(K * 4) void split_state_kernel(SplitParams p) {
-  constexpr int NB = C / 16, NKB = K / 16;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g4 = lane >> 4;
-  const long bh = blockIdx.x;
-  const int col = w * 16 + (lane & 15);
+__device__ __forceinline__ void fetch_u(const SplitParams& p, long ch, f32x4 (&un)[C / 16], int cb,
+                                        int lane) {
+#pragma unroll
+  for (int I = 0; I < C / 16; ++I)
+    un[I] = *reinterpret_cast<const f32x4*>(p.u + frag_index(ch, K / 16, C / 16, cb, I, lane));
+}
+
+// Copies a chunk's image from the workspace into LDS with direct global-to-LDS
+// loads (16 bytes per lane, 1 KiB per wavefront instruction), no registers
+// involved.
+template <int IMG>
+__device__ __forceinline__ void copy_image(const char* src, char* dst, int lane) {
+#pragma unroll 8
+  for (int j = 0; j < IMG / 1024; ++j)
+    __builtin_amdgcn_global_load_lds(src + j * 1024 + lane * 16,
+                                     (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, 0, 0);
+}
+
+// The direct copies count as vector memory loads of the issuing wavefront,
+// and its LDS waits cover them too; the barrier's own waits do not, so the
+// copying wavefront waits for them (vmcnt(0)) before the barrier that
+// publishes them.
+__device__ __forceinline__ void image_landed() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// NW wavefronts per workgroup each own one 16-wide column block of the state
+// of one (b, hv); lane l holds rows 16 kb + 4 (l / 16) + r of column l % 16
+// (the MFMA accumulator layout), which is also the B operand layout of the
+// fp32 products; the bf16 products take two such fragments per 32-wide
+// slice.  One more wavefront only streams the next chunk's operand image
+// into LDS, so the copy's latency never enters the computing wavefronts'
+// LDS waits.  The column blocks of a head are independent, so a head spreads
+// over K / 16 / NW workgroups (same blockIdx % 8, so one XCD's L2 serves
+// their common operand images).
+template <int K, int C, bool BF, int NW>
+__global__ __launch_bounds__((NW + 1) * 64) void split_state_kernel(SplitParams p) {
+  constexpr int NB = C / 16, NKB = K / 16, IMG = split_image_bytes<K, C>();
+  using Ops = ChainOps<K, C, BF>;
+  __shared__ alignas(1024) char img[2][IMG];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4;
+  const long nh = (long)p.B * p.HV;
+  const long bh = blockIdx.x % nh;
+  const int cb = (int)(blockIdx.x / nh) * NW + w;
+  const int NC = p.NC;
+  const int col = cb * 16 + (lane & 15);
+  const char* src = p.ops + bh * NC * (long)IMG;
+
+  if (w == NW) {  // the copying wavefront: one barrier per chunk, like the others
+    if (NC > 0) copy_image<IMG>(src, img[0], lane);
+    image_landed();
+    __syncthreads();
+    for (int c = 0; c < NC; ++c) {
+      if (c + 1 < NC) copy_image<IMG>(src + (c + 1) * (long)IMG, img[(c + 1) & 1], lane);
+      image_landed();
+      __syncthreads();
+    }
+    return;
+  }
+
+  f32x4 un[NB];  // u of the next chunk, this lane's elements
   f32x4 s[NKB];
   const float* S0 = p.S0 ? p.S0 + bh * (long)K * K : nullptr;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[kb][r] = S0 ? S0[(kb * 16 + 4 * g4 + r) * K + col] : 0.0f;
+  if (NC > 0) fetch_u<K, C>(p, bh * NC, un, cb, lane);
+  __syncthreads();
 
-  for (int c = 0; c < p.NC; ++c) {
-    const long ch = bh * p.NC + c;
-    float* hc = p.h + ch * (long)K * K;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hc[(kb * 16 + 4 * g4 + r) * K + col] = s[kb][r];
-
-    // X = W h_c, then U = u - X (over u)
-    const float* W = p.w + ch * (long)C * K;
-    float* U = p.u + ch * (long)C * K;
+  for (int c = 0; c < NC; ++c) {
+    const long ch = bh * NC + c;
+    const Ops& op = *reinterpret_cast<const Ops*>(img[c & 1]);
     f32x4 x[NB];
 #pragma unroll
+    for (int I = 0; I < NB; ++I) x[I] = un[I];
+    if (c + 1 < NC) fetch_u<K, C>(p, ch + 1, un, cb, lane);
+    if (p.h_plain) {
+      float* hc = p.h + ch * (long)K * K;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hc[(kb * 16 + 4 * g4 + r) * K + col] = s[kb][r];
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        *reinterpret_cast<f32x4*>(p.h + frag_index(ch, NKB, NKB, cb, kb, lane)) = s[kb];
+    }
+
+    // U = u - W h_c
+    f32x4 xw[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) xw[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF) {
+#pragma unroll
+      for (int q = 0; q < K / 32; ++q) {
+        bf16x8 bh_, bl_;
+        split8(s[2 * q], s[2 * q + 1], bh_, bl_);
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+          const int row = (I * 16 + (lane & 15)) * Ops::LW + 32 * q + 8 * g4;
+          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(op.wh + row);
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(op.wl + row);
+          xw[I] = mfma32(ah, bh_, xw[I]);
+          xw[I] = mfma32(ah, bl_, xw[I]);
+          xw[I] = mfma32(al, bh_, xw[I]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const float4 a = *reinterpret_cast<const float4*>(op.w + (I * 16 + (lane & 15)) * Ops::LW + kb * 16 + 4 * g4);
+          xw[I] = mfma4(a.x, s[kb][0], xw[I]);
+          xw[I] = mfma4(a.y, s[kb][1], xw[I]);
+          xw[I] = mfma4(a.z, s[kb][2], xw[I]);
+          xw[I] = mfma4(a.w, s[kb][3], xw[I]);
+        }
+    }
+#pragma unroll
     for (int I = 0; I < NB; ++I) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float4 a = *reinterpret_cast<const float4*>(W + (I * 16 + (lane & 15)) * K + kb * 16 + 4 * g4);
-        acc = mfma4(a.x, s[kb][0], acc);
-        acc = mfma4(a.y, s[kb][1], acc);
-        acc = mfma4(a.z, s[kb][2], acc);
-        acc = mfma4(a.w, s[kb][3], acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int idx = (I * 16 + 4 * g4 + r) * K + col;
-        const float uu = U[idx] - acc[r];
-        U[idx] = uu;
-        x[I][r] = uu;
-      }
+      x[I] -= xw[I];
+      *reinterpret_cast<f32x4*>(p.u + frag_index(ch, NKB, NB, cb, I, lane)) = x[I];
     }
 
     // h_{c+1} = diag(gamma) h_c + Kt^T U
-    const float* Kt = p.kt + ch * (long)K * C;
-    const float* gm = p.gam + ch * K;
+    if constexpr (BF) {
+      bf16x8 uh[NB / 2], ul[NB / 2];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const float4 gg = *reinterpret_cast<const float4*>(gm + kb * 16 + 4 * g4);
-      f32x4 acc = {gg.x * s[kb][0], gg.y * s[kb][1], gg.z * s[kb][2], gg.w * s[kb][3]};
+      for (int q = 0; q < NB / 2; ++q) split8(x[2 * q], x[2 * q + 1], uh[q], ul[q]);
 #pragma unroll
-      for (int I = 0; I < NB; ++I) {
-        const float4 a = *reinterpret_cast<const float4*>(Kt + (kb * 16 + (lane & 15)) * C + I * 16 + 4 * g4);
-        acc = mfma4(a.x, x[I][0], acc);
-        acc = mfma4(a.y, x[I][1], acc);
-        acc = mfma4(a.z, x[I][2], acc);
-        acc = mfma4(a.w, x[I][3], acc);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float4 gg = *reinterpret_cast<const float4*>(op.gam + kb * 16 + 4 * g4);
+        f32x4 acc = {gg.x * s[kb][0], gg.y * s[kb][1], gg.z * s[kb][2], gg.w * s[kb][3]};
+#pragma unroll
+        for (int q = 0; q < NB / 2; ++q) {
+          const int row = (kb * 16 + (lane & 15)) * Ops::LK + 32 * q + 8 * g4;
+          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(op.kh + row);
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(op.kl + row);
+          acc = mfma32(ah, uh[q], acc);
+          acc = mfma32(ah, ul[q], acc);
+          acc = mfma32(al, uh[q], acc);
+        }
+        s[kb] = acc;
       }
-      s[kb] = acc;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float4 gg = *reinterpret_cast<const float4*>(op.gam + kb * 16 + 4 * g4);
+        f32x4 acc = {gg.x * s[kb][0], gg.y * s[kb][1], gg.z * s[kb][2], gg.w * s[kb][3]};
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+          const float4 a = *reinterpret_cast<const float4*>(op.kt + (kb * 16 + (lane & 15)) * Ops::LK + I * 16 + 4 * g4);
+          acc = mfma4(a.x, x[I][0], acc);
+          acc = mfma4(a.y, x[I][1], acc);
+          acc = mfma4(a.z, x[I][2], acc);
+          acc = mfma4(a.w, x[I][3], acc);
+        }
+        s[kb] = acc;
+      }
     }
+    __syncthreads();  // the next image is in place; this one may be overwritten
   }
   if (p.S_out) {
     float* So = p.S_out + bh * (long)K * K;
@@ -393,13 +598,13 @@ template <int K, int C, typename T>
 __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams p) {
   constexpr int NB = C / 16, LD = ChunkRows<K, C>::LD, LR = C + 4;
   __shared__ ChunkRows<K, C> L;
-  __shared__ alignas(16) float Q[C * LD];
   __shared__ alignas(16) float A[C * LR];
+  float* Q = L.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4;
   const long ch = blockIdx.x;
   const long bh = ch / p.NC;
   const int c = (int)(ch % p.NC);
-  load_chunk<K, C, T>(p, bh, c, L, Q);
+  load_chunk<K, C, T>(p, bh, c, L, true);
   const float scale = 1.0f / __builtin_sqrtf((float)K);
 
   // A inside the sub-blocks (j <= i), direct
@@ -436,30 +641,37 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
   const int hv = (int)(bh % p.HV);
   const long b = bh / p.HV;
   const int t0 = c * C;
-  const float* hc = p.h + ch * (long)K * K;
-  const float* U = p.u + ch * (long)C * K;
-  constexpr int KQ = K / 4;  // key channels per lane group: channel = g4 * KQ + s
-  for (int cb = w; cb < K / 16; cb += kSplitThreads / 64) {
+  constexpr int NKB = K / 16;
+  for (int cb = w; cb < NKB; cb += kSplitThreads / 64) {
     const int col = cb * 16 + (lane & 15);
-    float hf[KQ];
+    // h_c as B operand fragments: lane holds keys 16 kb + 4 (l / 16) + r
+    f32x4 hf[NKB];
+    if (p.h_plain) {
+      const float* hc = p.h + ch * (long)K * K;
 #pragma unroll
-    for (int s = 0; s < KQ; ++s) hf[s] = hc[(g4 * KQ + s) * K + col];
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hf[kb][r] = hc[(kb * 16 + 4 * g4 + r) * K + col];
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        hf[kb] = *reinterpret_cast<const f32x4*>(p.h + frag_index(ch, NKB, NKB, cb, kb, lane));
+    }
     f32x4 uf[NB];
 #pragma unroll
     for (int J = 0; J < NB; ++J)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) uf[J][r] = U[(J * 16 + 4 * g4 + r) * K + col];
+      uf[J] = *reinterpret_cast<const f32x4*>(p.u + frag_index(ch, NKB, NB, cb, J, lane));
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const float* qrow = Q + (I * 16 + (lane & 15)) * LD + g4 * KQ;
+      const float* qrow = Q + (I * 16 + (lane & 15)) * LD + 4 * g4;
 #pragma unroll
-      for (int s = 0; s < KQ; s += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(qrow + s);
-        acc = mfma4(a.x, hf[s], acc);
-        acc = mfma4(a.y, hf[s + 1], acc);
-        acc = mfma4(a.z, hf[s + 2], acc);
-        acc = mfma4(a.w, hf[s + 3], acc);
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float4 a = *reinterpret_cast<const float4*>(qrow + kb * 16);
+        acc = mfma4(a.x, hf[kb][0], acc);
+        acc = mfma4(a.y, hf[kb][1], acc);
+        acc = mfma4(a.z, hf[kb][2], acc);
+        acc = mfma4(a.w, hf[kb][3], acc);
       }
 #pragma unroll
       for (int J = 0; J <= I; ++J) {
@@ -489,7 +701,9 @@ static hipError_t launch_split_kc(const SplitParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((split_state_kernel<K, C>), dim3((unsigned)heads), dim3(K * 4), 0, stream, p);
+  constexpr int NW = kStateWaves < K / 16 ? kStateWaves : K / 16;
+  hipLaunchKernelGGL((split_state_kernel<K, C, ChainBF<K, C, T>::value, NW>),
+                     dim3((unsigned)(heads * (K / 16 / NW))), dim3((NW + 1) * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || chunks == 0) return e;
   hipLaunchKernelGGL((split_output_kernel<K, C, T>), dim3((unsigned)chunks), dim3(kSplitThreads), 0,
@@ -508,9 +722,20 @@ static hipError_t launch_split_t(const SplitParams& p, int K, int C, hipStream_t
   return hipErrorInvalidValue;
 }
 
-// Workspace floats per (b, hv, chunk): W, Kt^T, u / U, gamma and the entry state.
-size_t split_workspace_floats(int K, int V, int C) {
-  return (size_t)C * K + (size_t)K * C + (size_t)C * V + (size_t)K + (size_t)K * V;
+// Workspace bytes per (b, hv, chunk): the chain operand image, u / U and the
+// entry state.
+static size_t image_bytes(int K, int C) {
+#define KDA_IMG_CASE(KK, CC) \
+  if (K == KK && C == CC) return (size_t)split_image_bytes<KK, CC>();
+#define KDA_IMG_ROW(KK) KDA_IMG_CASE(KK, 16) KDA_IMG_CASE(KK, 32) KDA_IMG_CASE(KK, 64)
+  KDA_IMG_ROW(16) KDA_IMG_ROW(32) KDA_IMG_ROW(64) KDA_IMG_ROW(128)
+#undef KDA_IMG_ROW
+#undef KDA_IMG_CASE
+  return 0;
+}
+
+size_t split_workspace_bytes_per_chunk(int K, int V, int C) {
+  return image_bytes(K, C) + ((size_t)C * V + (size_t)K * V) * sizeof(float);
 }
 
 hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
@@ -532,11 +757,10 @@ hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, c
   p.S0 = S0;
   p.o = o;
   p.S_out = S_out;
-  p.w = ws;
-  p.kt = p.w + n * C * K;
-  p.u = p.kt + n * K * C;
-  p.gam = p.u + n * C * K;
-  p.h = h ? h : p.gam + n * K;
+  p.ops = static_cast<char*>(workspace);
+  p.u = ws ? reinterpret_cast<float*>(p.ops + n * image_bytes(K, C)) : nullptr;
+  p.h = h ? h : (ws ? p.u + n * (size_t)C * K : nullptr);
+  p.h_plain = h ? 1 : 0;
   p.B = B;
   p.T = T;
   p.H = H;

@@ -1,7 +1,9 @@
 """GPU parity of the three-stage chunkwise schedule (kda_chunk_fwd_split):
 outputs, final states and the materialised chunk-entry states against the
-CPU oracle run chunk after chunk.  The schedule computes in fp32 for both
-input dtypes, so every case is held to the fp32 bar."""
+CPU oracle run chunk after chunk.  fp32 inputs run fp32 products throughout
+and are held to the fp32 bar; bf16 inputs run the state pass on bf16 MFMA
+(hi + lo operand pairs) when K and the chunk are at least 32, and are held to
+the bf16 bar."""
 import numpy as np
 import pytest
 import torch
@@ -25,12 +27,17 @@ SPLIT_CASES = [
 ]
 
 
+def _tol(d):
+    return L.TOL_F32 if d["q"].dtype == torch.float32 else L.TOL_BF16
+
+
 def _check(d, gate, lb, chunk, what, initial_state=True):
     o, S, h = L.run_split(d, gate, lb, chunk, initial_state)
     ro, rS, rh = L.oracle_by_chunks(d, gate, lb, chunk, initial_state)
     eo, eS, eh = L.rel_err(o, ro), L.rel_err(S, rS), L.rel_err(h, rh)
-    print("%s: o %.2e S %.2e h %.2e" % (what, eo, eS, eh))
-    assert eo <= L.TOL_F32 and eS <= L.TOL_F32 and eh <= L.TOL_F32, (eo, eS, eh)
+    tol = _tol(d)
+    print("%s: o %.2e S %.2e h %.2e (tol %.0e)" % (what, eo, eS, eh, tol))
+    assert eo <= tol and eS <= tol and eh <= tol, (eo, eS, eh)
     return o, S, h
 
 
@@ -47,7 +54,7 @@ def test_split_matches_oracle(case):
 def test_split_tiny_workload():
     w = synth.WORKLOADS["tiny"]
     d = synth.make_inputs(w)
-    o, S, _ = _check(d, w.gate, w.lower_bound, w.chunk, "tiny split")
+    o, S, _ = _check(d, w.gate, w.lower_bound, w.chunk, "tiny split")  # fp32 inputs
     ro, rS = L.oracle_full(d, w.gate, w.lower_bound)
     assert L.rel_err(o, ro) <= L.TOL_F32 and L.rel_err(S, rS) <= L.TOL_F32
 
@@ -107,7 +114,7 @@ def test_split_final_state_may_alias_initial_state():
                                   final_state=state)
     torch.cuda.synchronize()
     assert S.data_ptr() == state.data_ptr()
-    assert L.rel_err(o, ro) <= L.TOL_F32 and L.rel_err(state, rS) <= L.TOL_F32
+    assert L.rel_err(o, ro) <= L.TOL_BF16 and L.rel_err(state, rS) <= L.TOL_BF16
 
 
 def test_split_agrees_with_fused_chunk():
@@ -131,9 +138,9 @@ def test_workload_long_shard():
     o, S, h = L.run_split(d, w.gate, w.lower_bound, w.chunk)
     heads = L.sample_heads(w.B, w.HV, 3, seed=w.seed)
     ref = L.oracle_heads(d, w.gate, w.lower_bound, heads)
-    L.compare_heads(o, S, ref, L.TOL_F32, "long_shard")
+    L.compare_heads(o, S, ref, L.TOL_BF16, "long_shard")
     part = {n: (t[:, :8 * w.chunk] if t is not None and t.dim() >= 3 else t) for n, t in d.items()}
     _, _, rh = L.oracle_by_chunks(part, w.gate, w.lower_bound, w.chunk)
     eh = L.rel_err(h[:, :, :8], rh)
     print("long_shard h[0:8]: %.2e" % eh)
-    assert eh <= L.TOL_F32
+    assert eh <= L.TOL_BF16
