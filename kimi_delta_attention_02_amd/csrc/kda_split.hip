@@ -67,7 +67,7 @@ struct SplitParams {
   float lower_bound;
 };
 
-constexpr int kSplitThreads = 256;
+constexpr int kSplitThreads = 512;
 
 // u, U and the workspace copy of h are kept as 16 x 16 MFMA accumulator
 // fragments: fragment (column block cb, row block rb) of a chunk's R x N
@@ -76,10 +76,10 @@ constexpr int kSplitThreads = 256;
 __device__ __forceinline__ long frag_index(long mat, int ncb, int nrb, int cb, int rb, int lane) {
   return (((mat * ncb + cb) * nrb + rb) * 64 + lane) * 4;
 }
-#ifndef KDA_STATE_WAVES
-#define KDA_STATE_WAVES 1
+#ifndef KDA_STATE_SPLIT
+#define KDA_STATE_SPLIT 1
 #endif
-constexpr int kStateWaves = KDA_STATE_WAVES;  // column-block wavefronts per state-pass workgroup
+constexpr int kStateSplit = KDA_STATE_SPLIT;  // wavefronts sharing one state column block's keys
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -99,6 +99,7 @@ struct alignas(16) ChunkRows {
   alignas(16) float x[C * LD];   // q rows (output pass) or v rows (intra pass)
   alignas(16) float beta[C];
   alignas(16) float graw[C];     // per-head gate inputs
+  int steep[C / 16];             // sub-block whose decay leaves [2^-100, 2^100] in some channel
 };
 
 // log2 decay of whole sub-blocks J0 .. J1 - 1 in channel c
@@ -109,68 +110,120 @@ __device__ __forceinline__ float blocks_log2(const ChunkRows<K, C>& L, int J0, i
   return s;
 }
 
-// Loads chunk c of head (b, hv) into L: G2 (see ChunkRows), k, and q (xq) or
-// v (otherwise) widened to fp32, beta.  Every global load of the chunk is
-// issued before the first is used.  Tokens at or past T read as g = 0,
-// k = q = v = 0, beta = 0, which leave the state unchanged.  Ends with a
-// barrier.
+// The global inputs of one chunk as this thread loads them: raw gate inputs,
+// k and q / v rows (four elements per load), beta, the per-head gate input,
+// and the gate constants of its (channel, sub-block) pairs.  Issued a whole
+// chunk ahead by the persistent intra and output kernels.
 template <int K, int C, typename T>
-__device__ void load_chunk(const SplitParams& p, long bh, int c, ChunkRows<K, C>& L, bool xq) {
-  constexpr int LD = ChunkRows<K, C>::LD, NB = C / 16, Q4 = K / 4;
+struct ChunkRegs {
+  static constexpr int Q4 = K / 4;
+  static constexpr int NL = (C * Q4 + kSplitThreads - 1) / kSplitThreads;
+  static constexpr int NPR = (K * (C / 16) + kSplitThreads - 1) / kSplitThreads;
+  float4 g[NL];
+  typename In<T>::Raw4 a[NL], x[NL];
+  float beta, graw, alog;
+  float bias[NPR];
+};
+
+template <int K, int C, typename T>
+__device__ __forceinline__ void chunk_issue(const SplitParams& p, long ch, bool xq,
+                                            ChunkRegs<K, C, T>& R) {
+  using CR = ChunkRegs<K, C, T>;
+  constexpr int Q4 = CR::Q4;
   const int tid = threadIdx.x;
   const int HV = p.HV, T_ = p.T;
+  const long bh = ch / p.NC;
+  const int t0 = (int)(ch % p.NC) * C;
   const int hv = (int)(bh % HV);
   const long b = bh / HV;
   const int hq = hv / (HV / p.H);
-  const int t0 = c * C;
   const T* kp = static_cast<const T*>(p.k);
   const T* xp = static_cast<const T*>(xq ? p.q : p.v);
   const int xheads = xq ? p.H : HV, xh = xq ? hq : hv;
-
-  // raw gate inputs, k and q / v rows: four elements per load
-  for (int e = tid; e < C * Q4; e += kSplitThreads) {
+  R.alog = p.kind != KDA_GATE_NONE ? p.A_log[hv] : 0.0f;
+  const int gK = p.per_head ? 1 : K;
+#pragma unroll
+  for (int j = 0; j < CR::NPR; ++j) {
+    const int pr = tid + j * kSplitThreads, kap = pr % K;
+    R.bias[j] = (p.dt_bias && p.kind != KDA_GATE_NONE && pr < K * (C / 16))
+                    ? p.dt_bias[(long)hv * gK + (p.per_head ? 0 : kap)] : 0.0f;
+  }
+#pragma unroll
+  for (int it = 0; it < CR::NL; ++it) {
+    const int e = tid + it * kSplitThreads;
     const int i = e / Q4, c4 = (e % Q4) * 4;
     const int t = t0 + i;
-    float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-    float a[4] = {0.f, 0.f, 0.f, 0.f}, x[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < T_) {
+    R.g[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e < C * Q4 && t < T_) {
       if (!p.per_head)
-        g = *reinterpret_cast<const float4*>(p.g_raw + ((b * T_ + t) * HV + hv) * (long)K + c4);
-      In<T>::load4(kp, ((b * T_ + t) * p.H + hq) * (long)K + c4, a);
-      In<T>::load4(xp, ((b * T_ + t) * xheads + xh) * (long)K + c4, x);
+        R.g[it] = *reinterpret_cast<const float4*>(p.g_raw + ((b * T_ + t) * HV + hv) * (long)K + c4);
+      R.a[it] = In<T>::raw4(kp, ((b * T_ + t) * p.H + hq) * (long)K + c4);
+      R.x[it] = In<T>::raw4(xp, ((b * T_ + t) * xheads + xh) * (long)K + c4);
     }
-    *reinterpret_cast<float4*>(L.G2 + i * LD + c4) = g;
-    *reinterpret_cast<float4*>(L.k + i * LD + c4) = make_float4(a[0], a[1], a[2], a[3]);
-    *reinterpret_cast<float4*>(L.x + i * LD + c4) = make_float4(x[0], x[1], x[2], x[3]);
   }
-  for (int i = tid; i < C; i += kSplitThreads) {
-    const bool in = t0 + i < T_;
-    L.beta[i] = in ? p.beta[(b * T_ + t0 + i) * HV + hv] : 0.0f;
-    if (p.per_head) L.graw[i] = in ? p.g_raw[(b * T_ + t0 + i) * HV + hv] : 0.0f;
+  R.beta = R.graw = 0.0f;
+  if (tid < C && t0 + tid < T_) {
+    R.beta = p.beta[(b * T_ + t0 + tid) * HV + hv];
+    if (p.per_head) R.graw = p.g_raw[(b * T_ + t0 + tid) * HV + hv];
+  }
+}
+
+// Chunk ch into L from the registers: G2 (see ChunkRows), k, and q or v
+// widened to fp32, beta.  Tokens at or past T read as g = 0, k = q = v = 0,
+// beta = 0, which leave the state unchanged.  Ends with a barrier.
+template <int K, int C, typename T>
+__device__ void chunk_store(const SplitParams& p, long ch, const ChunkRegs<K, C, T>& R,
+                            ChunkRows<K, C>& L) {
+  using CR = ChunkRegs<K, C, T>;
+  constexpr int LD = ChunkRows<K, C>::LD, NB = C / 16, Q4 = CR::Q4;
+  const int tid = threadIdx.x;
+  const int T_ = p.T;
+  const int t0 = (int)(ch % p.NC) * C;
+#pragma unroll
+  for (int it = 0; it < CR::NL; ++it) {
+    const int e = tid + it * kSplitThreads;
+    const int i = e / Q4, c4 = (e % Q4) * 4;
+    if (e < C * Q4) {
+      float a[4] = {0.f, 0.f, 0.f, 0.f}, x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (t0 + i < T_) {
+        In<T>::unpack4(R.a[it], a);
+        In<T>::unpack4(R.x[it], x);
+      }
+      *reinterpret_cast<float4*>(L.G2 + i * LD + c4) = R.g[it];
+      *reinterpret_cast<float4*>(L.k + i * LD + c4) = make_float4(a[0], a[1], a[2], a[3]);
+      *reinterpret_cast<float4*>(L.x + i * LD + c4) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+  }
+  if (tid < NB) L.steep[tid] = 0;
+  if (tid < C) {
+    L.beta[tid] = R.beta;
+    L.graw[tid] = R.graw;
   }
   __syncthreads();
 
   // gate and the cumulative sum inside each sub-block, in place: one
   // (channel, sub-block) pair per thread and pass
-  const int gK = p.per_head ? 1 : K;
-  const float rate = p.kind != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
-  for (int pr = tid; pr < K * NB; pr += kSplitThreads) {
+  const float rate = p.kind != KDA_GATE_NONE ? exp_f(R.alog) : 1.0f;
+#pragma unroll
+  for (int jp = 0; jp < CR::NPR; ++jp) {
+    const int pr = tid + jp * kSplitThreads;
+    if (pr >= K * NB) break;
     const int kap = pr % K, J = pr / K;
-    const int gc = p.per_head ? 0 : kap;
-    const float bias =
-        (p.dt_bias && p.kind != KDA_GATE_NONE) ? p.dt_bias[(long)hv * gK + gc] : 0.0f;
     float run = 0.0f;
+    bool steep = false;
 #pragma unroll 4
     for (int j = 0; j < 16; ++j) {
       const int i = J * 16 + j;
       float g = 0.0f;
       if (t0 + i < T_) {
         const float graw = p.per_head ? L.graw[i] : L.G2[i * LD + kap];
-        g = gate_log_decay(graw, bias, rate, p.kind, p.lower_bound);
+        g = gate_log_decay(graw, R.bias[jp], rate, p.kind, p.lower_bound);
       }
       run += g * kLog2e;
+      steep |= !(run >= -100.0f && run <= 100.0f);
       L.G2[i * LD + kap] = run;
     }
+    if (steep) L.steep[J] = 1;  // every writer stores 1
   }
   __syncthreads();
 }
@@ -195,27 +248,6 @@ __device__ __forceinline__ float decayed_dot(const ChunkRows<K, C>& L, const flo
   return acc;
 }
 
-// The 16 x 16 block (I, J), I > J, of  sum_k a_ik k_jk 2^(G_ik - G_jk) (G the
-// log2 cumulative decay over the chunk), split at the last token of sub-block
-// J; result in the accumulator layout.
-template <int K, int C>
-__device__ __forceinline__ f32x4 decayed_block(const ChunkRows<K, C>& L, const float* arows, int I,
-                                               int J, int lane) {
-  constexpr int LD = ChunkRows<K, C>::LD;
-  const int ai = I * 16 + (lane & 15), bj = J * 16 + (lane & 15), je = J * 16 + 15;
-  const int kk = lane >> 4;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < K; s += 4) {
-    const int c = s + kk;
-    const float mid = blocks_log2(L, J + 1, I, c);  // whole sub-blocks between J and I
-    const float a = arows[ai * LD + c] * __builtin_amdgcn_exp2f(L.G2[ai * LD + c] + mid);
-    const float bb = L.k[bj * LD + c] * __builtin_amdgcn_exp2f(L.G2[je * LD + c] - L.G2[bj * LD + c]);
-    acc = mfma4(a, bb, acc);
-  }
-  return acc;
-}
-
 // pair index -> (i, j), j < i < 16 (strict) or j <= i < 16
 __device__ __forceinline__ void tri_pair(int pr, bool strict, int& i, int& j) {
   int r = strict ? 1 : 0;
@@ -227,6 +259,77 @@ __device__ __forceinline__ void tri_pair(int pr, bool strict, int& i, int& j) {
   }
   i = r;
   j = pr;
+}
+
+// The 16 x 16 block (I, J), I >= J, of  sum_k a_ik k_jk 2^(G_ik - G_jk) (G
+// the log2 cumulative decay over the chunk), on MFMA; result in the
+// accumulator layout.  I > J: the factor splits at the last token of J,
+// 2^(G_i - G_Jend) 2^(G_Jend - G_j), both at most 1 for a non-positive decay.
+// I == J: it splits at the start of the sub-block, 2^(Lc_i) 2^(-Lc_j), whose
+// second factor is bounded by 2^100 unless the sub-block is steep (then the
+// caller takes the direct form).  Entries above the diagonal are not
+// meaningful.  Key channel of instruction r of step kb in lane group g:
+// 16 kb + 4 g + r, so each lane reads four consecutive channels at once.
+template <int K, int C>
+__device__ __forceinline__ f32x4 decayed_block(const ChunkRows<K, C>& L, const float* arows, int I,
+                                               int J, int lane) {
+  constexpr int LD = ChunkRows<K, C>::LD;
+  const int ai = I * 16 + (lane & 15), bj = J * 16 + (lane & 15), je = J * 16 + 15;
+  const int c0 = 4 * (lane >> 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int kb = 0; kb < K / 16; ++kb) {
+    const int c = kb * 16 + c0;
+    const float4 a4 = *reinterpret_cast<const float4*>(arows + ai * LD + c);
+    const float4 b4 = *reinterpret_cast<const float4*>(L.k + bj * LD + c);
+    const float4 gi = *reinterpret_cast<const float4*>(L.G2 + ai * LD + c);
+    const float4 gj = *reinterpret_cast<const float4*>(L.G2 + bj * LD + c);
+    float4 ea = gi, eb = make_float4(-gj.x, -gj.y, -gj.z, -gj.w);
+    if (I > J) {
+      const float4 ge = *reinterpret_cast<const float4*>(L.G2 + je * LD + c);
+      eb = make_float4(ge.x - gj.x, ge.y - gj.y, ge.z - gj.z, ge.w - gj.w);
+      for (int M = J + 1; M < I; ++M) {  // whole sub-blocks between J and I
+        const float4 gm = *reinterpret_cast<const float4*>(L.G2 + (M * 16 + 15) * LD + c);
+        ea = make_float4(ea.x + gm.x, ea.y + gm.y, ea.z + gm.z, ea.w + gm.w);
+      }
+    }
+    acc = mfma4(a4.x * __builtin_amdgcn_exp2f(ea.x), b4.x * __builtin_amdgcn_exp2f(eb.x), acc);
+    acc = mfma4(a4.y * __builtin_amdgcn_exp2f(ea.y), b4.y * __builtin_amdgcn_exp2f(eb.y), acc);
+    acc = mfma4(a4.z * __builtin_amdgcn_exp2f(ea.z), b4.z * __builtin_amdgcn_exp2f(eb.z), acc);
+    acc = mfma4(a4.w * __builtin_amdgcn_exp2f(ea.w), b4.w * __builtin_amdgcn_exp2f(eb.w), acc);
+  }
+  return acc;
+}
+
+// Every block (I, J), J <= I, of the chunk's decayed product: MFMA blocks,
+// with the diagonal blocks of steep sub-blocks summed directly.  out(i, j, v)
+// receives each value with j <= i (strict: j < i); the rest of the diagonal
+// blocks gets 0.
+template <int K, int C, bool STRICT, class Out>
+__device__ __forceinline__ void decayed_lower(const ChunkRows<K, C>& L, const float* arows, int tid,
+                                              Out out) {
+  constexpr int NB = C / 16, NP = NB * (NB + 1) / 2, NW = kSplitThreads / 64;
+  const int lane = tid & 63, w = tid >> 6, g4 = lane >> 4;
+  for (int pi = w; pi < NP; pi += NW) {
+    int I, J;
+    tri_pair(pi, false, I, J);
+    if (I == J && L.steep[J]) continue;
+    const f32x4 acc = decayed_block<K, C>(L, arows, I, J, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = I * 16 + 4 * g4 + r, j = J * 16 + (lane & 15);
+      const bool keep = I > J || (STRICT ? j < i : j <= i);
+      out(i, j, keep ? acc[r] : 0.0f);
+    }
+  }
+  for (int J = 0; J < NB; ++J) {
+    if (!L.steep[J]) continue;
+    for (int e = tid; e < 256; e += kSplitThreads) {
+      const int i = J * 16 + (e >> 4), j = J * 16 + (e & 15);
+      const bool keep = STRICT ? j < i : j <= i;
+      out(i, j, keep ? decayed_dot<K, C>(L, arows, i, j) : 0.0f);
+    }
+  }
 }
 
 // ----------------------------------------------------------------- chain operand layout
@@ -282,33 +385,17 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
   __shared__ ChunkRows<K, C> L;
   __shared__ alignas(16) float R[C * LR];
   __shared__ alignas(16) float Xd[NB * 16 * LX];
+  __shared__ alignas(16) float Ws[C * LD];  // W in fp32, rows of keys, before the image layout
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4;
-  const long ch = blockIdx.x;
-  const long bh = ch / p.NC;
-  const int c = (int)(ch % p.NC);
-  load_chunk<K, C, T>(p, bh, c, L, false);
+  const long nch = (long)p.B * p.HV * p.NC;
+  ChunkRegs<K, C, T> cr;
+  if ((long)blockIdx.x < nch) chunk_issue<K, C, T>(p, blockIdx.x, false, cr);
+  for (long ch = blockIdx.x; ch < nch; ch += gridDim.x) {
+  chunk_store<K, C, T>(p, ch, cr, L);
+  if (ch + gridDim.x < nch) chunk_issue<K, C, T>(p, ch + gridDim.x, false, cr);  // lands during this chunk
 
-  // R inside the 16-token sub-blocks, direct
-  for (int e = tid; e < NB * 120; e += kSplitThreads) {
-    const int J = e / 120;
-    int i, j;
-    tri_pair(e % 120, true, i, j);
-    i += J * 16;
-    j += J * 16;
-    R[i * LR + j] = L.beta[i] * decayed_dot<K, C>(L, L.k, i, j);
-  }
-  // R between sub-blocks I > J, on MFMA
-  constexpr int NP = NB * (NB - 1) / 2;
-  for (int pi = w; pi < NP; pi += kSplitThreads / 64) {
-    int I, J;
-    tri_pair(pi, true, I, J);
-    const f32x4 acc = decayed_block<K, C>(L, L.k, I, J, lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = I * 16 + 4 * g4 + r;
-      R[i * LR + J * 16 + (lane & 15)] = L.beta[i] * acc[r];
-    }
-  }
+  // R = diag(beta) times the strictly lower decayed k k^T
+  decayed_lower<K, C, true>(L, L.k, tid, [&](int i, int j, float v) { R[i * LR + j] = L.beta[i] * v; });
   __syncthreads();
 
   // (I + R_JJ)^{-1} of each diagonal 16 x 16 block: lane j of group J
@@ -330,79 +417,126 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
   __syncthreads();
 
   // [W | u] = (I + R)^{-1} diag(beta) [k exp(G) | v], by blocks of 16 rows:
-  // Y_I = X_II (B_I - sum_{J<I} R_IJ Y_J), one 16-wide column block per pass
-  using Ops = ChainOps<K, C, BF>;
-  Ops& img = *reinterpret_cast<Ops*>(p.ops + ch * (long)split_image_bytes<K, C>());
-
-  for (int cb = w; cb < 2 * (K / 16); cb += kSplitThreads / 64) {
-    const bool isw = cb < K / 16;
-    const int col = (isw ? cb : cb - K / 16) * 16 + (lane & 15);
-    f32x4 y[NB];
+  // Y_I = X_II (B_I - sum_{J<I} R_IJ Y_J); each wavefront takes two 16-wide
+  // column blocks at a time (two independent product chains)
+  constexpr int NCB = 2 * (K / 16);
+  for (int cb0 = 2 * w; cb0 < NCB; cb0 += 2 * (kSplitThreads / 64)) {
+    f32x4 y[2][NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
-      f32x4 t;
+      f32x4 t[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = I * 16 + 4 * g4 + r;
-        const float x = isw ? L.k[i * LD + col] *
-                                  __builtin_amdgcn_exp2f(L.G2[i * LD + col] + blocks_log2(L, 0, I, col))
-                            : L.x[i * LD + col];
-        t[r] = L.beta[i] * x;
+      for (int h = 0; h < 2; ++h) {
+        const int cb = cb0 + h;
+        const bool isw = cb < K / 16;
+        const int col = (isw ? cb : cb - K / 16) * 16 + (lane & 15);
+        float pre = 0.0f;
+        if (isw) pre = blocks_log2(L, 0, I, col);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = I * 16 + 4 * g4 + r;
+          const float x = isw ? L.k[i * LD + col] * __builtin_amdgcn_exp2f(L.G2[i * LD + col] + pre)
+                              : L.x[i * LD + col];
+          t[h][r] = L.beta[i] * x;
+        }
       }
 #pragma unroll
       for (int J = 0; J < I; ++J) {
         const float4 a = *reinterpret_cast<const float4*>(R + (I * 16 + (lane & 15)) * LR + J * 16 + 4 * g4);
-        t = mfma4(-a.x, y[J][0], t);
-        t = mfma4(-a.y, y[J][1], t);
-        t = mfma4(-a.z, y[J][2], t);
-        t = mfma4(-a.w, y[J][3], t);
-      }
-      const float4 a = *reinterpret_cast<const float4*>(Xd + (I * 16 + (lane & 15)) * LX + 4 * g4);
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      z = mfma4(a.x, t[0], z);
-      z = mfma4(a.y, t[1], z);
-      z = mfma4(a.z, t[2], z);
-      z = mfma4(a.w, t[3], z);
-      y[I] = z;
-    }
 #pragma unroll
-    for (int I = 0; I < NB; ++I)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = I * 16 + 4 * g4 + r;
-        if (!isw) {
-          if (r == 0)
-            *reinterpret_cast<f32x4*>(p.u + frag_index(ch, K / 16, NB, cb - K / 16, I, lane)) = y[I];
-        } else if constexpr (BF) {  // hi and lo words, keys permuted per slice
-          uint16_t hi, lo;
-          split_bf16(y[I][r], hi, lo);
-          const int pos = i * Ops::LW + (col & ~31) + slice_pos(col & 31);
-          img.wh[pos] = hi;
-          img.wl[pos] = lo;
-        } else {
-          img.w[i * Ops::LW + col] = y[I][r];
+        for (int h = 0; h < 2; ++h) {
+          t[h] = mfma4(-a.x, y[h][J][0], t[h]);
+          t[h] = mfma4(-a.y, y[h][J][1], t[h]);
+          t[h] = mfma4(-a.z, y[h][J][2], t[h]);
+          t[h] = mfma4(-a.w, y[h][J][3], t[h]);
         }
       }
+      const float4 a = *reinterpret_cast<const float4*>(Xd + (I * 16 + (lane & 15)) * LX + 4 * g4);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        z = mfma4(a.x, t[h][0], z);
+        z = mfma4(a.y, t[h][1], z);
+        z = mfma4(a.z, t[h][2], z);
+        z = mfma4(a.w, t[h][3], z);
+        y[h][I] = z;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cb = cb0 + h;
+      if (cb >= K / 16) {  // u: fragments straight to the workspace
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+          *reinterpret_cast<f32x4*>(p.u + frag_index(ch, K / 16, NB, cb - K / 16, I, lane)) = y[h][I];
+      } else {  // W: through LDS, to be written out in the image layout
+#pragma unroll
+        for (int I = 0; I < NB; ++I)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ws[(I * 16 + 4 * g4 + r) * LD + cb * 16 + (lane & 15)] = y[h][I][r];
+      }
+    }
   }
+  __syncthreads();
 
-  // Kt^T and gamma
-  for (int e = tid; e < K * C; e += kSplitThreads) {
-    const int kap = e / C, i = e % C;
-    const int I = i >> 4;
-    const float rest = (L.G2[(I * 16 + 15) * LD + kap] - L.G2[i * LD + kap]) + blocks_log2(L, I + 1, NB, kap);
-    const float val = L.k[i * LD + kap] * __builtin_amdgcn_exp2f(rest);
-    if constexpr (BF) {  // hi and lo words, tokens permuted per slice
-      uint16_t hi, lo;
-      split_bf16(val, hi, lo);
-      const int pos = kap * Ops::LK + (i & ~31) + slice_pos(i & 31);
-      img.kh[pos] = hi;
-      img.kl[pos] = lo;
-    } else {
-      img.kt[kap * Ops::LK + i] = val;
+  // the chunk's operand image: W, Kt^T and gamma, 16 bytes per store
+  using Ops = ChainOps<K, C, BF>;
+  Ops& img = *reinterpret_cast<Ops*>(p.ops + ch * (long)split_image_bytes<K, C>());
+  if constexpr (BF) {
+    // W rows: positions 8 g .. 8 g + 7 of key slice q are keys 32 q + 4 g + (0..3)
+    // and 32 q + 16 + 4 g + (0..3)
+    for (int e = tid; e < C * (K / 8); e += kSplitThreads) {
+      const int i = e / (K / 8), q = (e % (K / 8)) >> 2, g = e & 3;
+      const float4 lo4 = *reinterpret_cast<const float4*>(Ws + i * LD + 32 * q + 4 * g);
+      const float4 hi4 = *reinterpret_cast<const float4*>(Ws + i * LD + 32 * q + 16 + 4 * g);
+      uint4 h, l;
+      split2_bf16(lo4.x, lo4.y, h.x, l.x);
+      split2_bf16(lo4.z, lo4.w, h.y, l.y);
+      split2_bf16(hi4.x, hi4.y, h.z, l.z);
+      split2_bf16(hi4.z, hi4.w, h.w, l.w);
+      *reinterpret_cast<uint4*>(img.wh + i * Ops::LW + 32 * q + 8 * g) = h;
+      *reinterpret_cast<uint4*>(img.wl + i * Ops::LW + 32 * q + 8 * g) = l;
+    }
+    // Kt^T rows (key channels): token slices permuted the same way
+    for (int e = tid; e < K * (C / 8); e += kSplitThreads) {
+      const int kap = e / (C / 8), q = (e % (C / 8)) >> 2, g = e & 3;
+      float v[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int i = 32 * q + 4 * g + (m & 3) + 16 * (m >> 2);
+        const int I = i >> 4;
+        const float rest = (L.G2[(I * 16 + 15) * LD + kap] - L.G2[i * LD + kap]) + blocks_log2(L, I + 1, NB, kap);
+        v[m] = L.k[i * LD + kap] * __builtin_amdgcn_exp2f(rest);
+      }
+      uint4 h, l;
+      split2_bf16(v[0], v[1], h.x, l.x);
+      split2_bf16(v[2], v[3], h.y, l.y);
+      split2_bf16(v[4], v[5], h.z, l.z);
+      split2_bf16(v[6], v[7], h.w, l.w);
+      *reinterpret_cast<uint4*>(img.kh + kap * Ops::LK + 32 * q + 8 * g) = h;
+      *reinterpret_cast<uint4*>(img.kl + kap * Ops::LK + 32 * q + 8 * g) = l;
+    }
+  } else {
+    for (int e = tid; e < C * (K / 4); e += kSplitThreads) {
+      const int i = e / (K / 4), c4 = (e % (K / 4)) * 4;
+      *reinterpret_cast<float4*>(img.w + i * Ops::LW + c4) = *reinterpret_cast<const float4*>(Ws + i * LD + c4);
+    }
+    for (int e = tid; e < K * (C / 4); e += kSplitThreads) {
+      const int kap = e / (C / 4), i0 = (e % (C / 4)) * 4;
+      float v[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = i0 + m, I = i >> 4;
+        const float rest = (L.G2[(I * 16 + 15) * LD + kap] - L.G2[i * LD + kap]) + blocks_log2(L, I + 1, NB, kap);
+        v[m] = L.k[i * LD + kap] * __builtin_amdgcn_exp2f(rest);
+      }
+      *reinterpret_cast<float4*>(img.kt + kap * Ops::LK + i0) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
   for (int kap = tid; kap < K; kap += kSplitThreads)
     img.gam[kap] = __builtin_amdgcn_exp2f(blocks_log2(L, 0, NB, kap));
+  __syncthreads();  // LDS is refilled by the next chunk
+  }
 }
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -446,34 +580,41 @@ __device__ __forceinline__ void copy_image(const char* src, char* dst, int lane)
 // publishes them.
 __device__ __forceinline__ void image_landed() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// NW wavefronts per workgroup each own one 16-wide column block of the state
-// of one (b, hv); lane l holds rows 16 kb + 4 (l / 16) + r of column l % 16
-// (the MFMA accumulator layout), which is also the B operand layout of the
-// fp32 products; the bf16 products take two such fragments per 32-wide
-// slice.  One more wavefront only streams the next chunk's operand image
-// into LDS, so the copy's latency never enters the computing wavefronts'
-// LDS waits.  The column blocks of a head are independent, so a head spreads
-// over K / 16 / NW workgroups (same blockIdx % 8, so one XCD's L2 serves
-// their common operand images).
-template <int K, int C, bool BF, int NW>
-__global__ __launch_bounds__((NW + 1) * 64) void split_state_kernel(SplitParams p) {
-  constexpr int NB = C / 16, NKB = K / 16, IMG = split_image_bytes<K, C>();
+// One workgroup per (b, hv, 16-wide column block of the state); its KS
+// computing wavefronts split the key rows: wavefront kp holds rows
+// kp K / KS .. (kp + 1) K / KS - 1, lane l rows 16 kb + 4 (l / 16) + r of
+// column l % 16 (the MFMA accumulator layout, which is also the B operand
+// layout of the fp32 products; the bf16 products take two such fragments
+// per 32-wide slice).  Per chunk each computes its part of W h over its keys,
+// the parts meet in LDS (every wavefront then holds all of U), and each
+// updates its own rows.  One more wavefront only streams the next chunk's
+// operand image into LDS, so the copy's latency never enters the computing
+// wavefronts' LDS waits.  The column blocks of a head are independent
+// workgroups with equal blockIdx % 8, so one XCD's L2 serves their common
+// operand images.
+template <int K, int C, bool BF, int KS>
+__global__ __launch_bounds__((KS + 1) * 64) void split_state_kernel(SplitParams p) {
+  constexpr int NB = C / 16, NKB = K / 16, RB = NKB / KS, IMG = split_image_bytes<K, C>();
+  static_assert(NKB % KS == 0 && (!BF || RB % 2 == 0), "key split must fit the operand slices");
   using Ops = ChainOps<K, C, BF>;
   __shared__ alignas(1024) char img[2][IMG];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4;
+  __shared__ f32x4 xs[KS][NB][64];  // each wavefront's part of W h
+  const int tid = threadIdx.x, lane = tid & 63, kp = tid >> 6, g4 = lane >> 4;
   const long nh = (long)p.B * p.HV;
   const long bh = blockIdx.x % nh;
-  const int cb = (int)(blockIdx.x / nh) * NW + w;
+  const int cb = (int)(blockIdx.x / nh);
   const int NC = p.NC;
   const int col = cb * 16 + (lane & 15);
+  const int kb0 = kp * RB;  // first key row block of this wavefront
   const char* src = p.ops + bh * NC * (long)IMG;
 
-  if (w == NW) {  // the copying wavefront: one barrier per chunk, like the others
+  if (kp == KS) {  // the copying wavefront: the same barriers as the others
     if (NC > 0) copy_image<IMG>(src, img[0], lane);
     image_landed();
     __syncthreads();
     for (int c = 0; c < NC; ++c) {
       if (c + 1 < NC) copy_image<IMG>(src + (c + 1) * (long)IMG, img[(c + 1) & 1], lane);
+      if (KS > 1) __syncthreads();
       image_landed();
       __syncthreads();
     }
@@ -481,12 +622,12 @@ __global__ __launch_bounds__((NW + 1) * 64) void split_state_kernel(SplitParams 
   }
 
   f32x4 un[NB];  // u of the next chunk, this lane's elements
-  f32x4 s[NKB];
+  f32x4 s[RB];
   const float* S0 = p.S0 ? p.S0 + bh * (long)K * K : nullptr;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[kb][r] = S0 ? S0[(kb * 16 + 4 * g4 + r) * K + col] : 0.0f;
+    for (int r = 0; r < 4; ++r) s[rb][r] = S0 ? S0[((kb0 + rb) * 16 + 4 * g4 + r) * K + col] : 0.0f;
   if (NC > 0) fetch_u<K, C>(p, bh * NC, un, cb, lane);
   __syncthreads();
 
@@ -500,77 +641,104 @@ __global__ __launch_bounds__((NW + 1) * 64) void split_state_kernel(SplitParams 
     if (p.h_plain) {
       float* hc = p.h + ch * (long)K * K;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hc[(kb * 16 + 4 * g4 + r) * K + col] = s[kb][r];
+        for (int r = 0; r < 4; ++r) hc[((kb0 + rb) * 16 + 4 * g4 + r) * K + col] = s[rb][r];
     } else {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        *reinterpret_cast<f32x4*>(p.h + frag_index(ch, NKB, NKB, cb, kb, lane)) = s[kb];
+      for (int rb = 0; rb < RB; ++rb)
+        *reinterpret_cast<f32x4*>(p.h + frag_index(ch, NKB, NKB, cb, kb0 + rb, lane)) = s[rb];
     }
 
-    // U = u - W h_c
+    // this wavefront's keys of W h_c
     f32x4 xw[NB];
 #pragma unroll
     for (int I = 0; I < NB; ++I) xw[I] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (BF) {
+      // the NB accumulators are independent: issue them in turn, so that no
+      // product waits on the one before it
 #pragma unroll
-      for (int q = 0; q < K / 32; ++q) {
-        bf16x8 bh_, bl_;
-        split8(s[2 * q], s[2 * q + 1], bh_, bl_);
+      for (int qq = 0; qq < RB / 2; ++qq) {
+        const int q = kb0 / 2 + qq;
+        bf16x8 bh_, bl_, ah[NB], al[NB];
+        split8(s[2 * qq], s[2 * qq + 1], bh_, bl_);
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
           const int row = (I * 16 + (lane & 15)) * Ops::LW + 32 * q + 8 * g4;
-          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(op.wh + row);
-          const bf16x8 al = *reinterpret_cast<const bf16x8*>(op.wl + row);
-          xw[I] = mfma32(ah, bh_, xw[I]);
-          xw[I] = mfma32(ah, bl_, xw[I]);
-          xw[I] = mfma32(al, bh_, xw[I]);
+          ah[I] = *reinterpret_cast<const bf16x8*>(op.wh + row);
+          al[I] = *reinterpret_cast<const bf16x8*>(op.wl + row);
         }
+#pragma unroll
+        for (int I = 0; I < NB; ++I) xw[I] = mfma32(ah[I], bh_, xw[I]);
+#pragma unroll
+        for (int I = 0; I < NB; ++I) xw[I] = mfma32(ah[I], bl_, xw[I]);
+#pragma unroll
+        for (int I = 0; I < NB; ++I) xw[I] = mfma32(al[I], bh_, xw[I]);
       }
     } else {
 #pragma unroll
       for (int I = 0; I < NB; ++I)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const float4 a = *reinterpret_cast<const float4*>(op.w + (I * 16 + (lane & 15)) * Ops::LW + kb * 16 + 4 * g4);
-          xw[I] = mfma4(a.x, s[kb][0], xw[I]);
-          xw[I] = mfma4(a.y, s[kb][1], xw[I]);
-          xw[I] = mfma4(a.z, s[kb][2], xw[I]);
-          xw[I] = mfma4(a.w, s[kb][3], xw[I]);
+        for (int rb = 0; rb < RB; ++rb) {
+          const float4 a = *reinterpret_cast<const float4*>(op.w + (I * 16 + (lane & 15)) * Ops::LW + (kb0 + rb) * 16 + 4 * g4);
+          xw[I] = mfma4(a.x, s[rb][0], xw[I]);
+          xw[I] = mfma4(a.y, s[rb][1], xw[I]);
+          xw[I] = mfma4(a.z, s[rb][2], xw[I]);
+          xw[I] = mfma4(a.w, s[rb][3], xw[I]);
         }
+    }
+    // U = u - W h_c: the parts of all wavefronts, summed in a fixed order
+    if constexpr (KS > 1) {
+#pragma unroll
+      for (int I = 0; I < NB; ++I) xs[kp][I][lane] = xw[I];
+      __syncthreads();
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        f32x4 t = xs[0][I][lane];
+#pragma unroll
+        for (int j = 1; j < KS; ++j) t += xs[j][I][lane];
+        xw[I] = t;
+      }
     }
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
       x[I] -= xw[I];
-      *reinterpret_cast<f32x4*>(p.u + frag_index(ch, NKB, NB, cb, I, lane)) = x[I];
+      if (kp == 0) *reinterpret_cast<f32x4*>(p.u + frag_index(ch, NKB, NB, cb, I, lane)) = x[I];
     }
 
-    // h_{c+1} = diag(gamma) h_c + Kt^T U
+    // this wavefront's rows of h_{c+1} = diag(gamma) h_c + Kt^T U
     if constexpr (BF) {
       bf16x8 uh[NB / 2], ul[NB / 2];
 #pragma unroll
       for (int q = 0; q < NB / 2; ++q) split8(x[2 * q], x[2 * q + 1], uh[q], ul[q]);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float4 gg = *reinterpret_cast<const float4*>(op.gam + kb * 16 + 4 * g4);
-        f32x4 acc = {gg.x * s[kb][0], gg.y * s[kb][1], gg.z * s[kb][2], gg.w * s[kb][3]};
+      for (int rb = 0; rb < RB; ++rb) {
+        const float4 gg = *reinterpret_cast<const float4*>(op.gam + (kb0 + rb) * 16 + 4 * g4);
+        s[rb] = f32x4{gg.x * s[rb][0], gg.y * s[rb][1], gg.z * s[rb][2], gg.w * s[rb][3]};
+      }
+      // RB independent accumulators, issued in turn
 #pragma unroll
-        for (int q = 0; q < NB / 2; ++q) {
-          const int row = (kb * 16 + (lane & 15)) * Ops::LK + 32 * q + 8 * g4;
-          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(op.kh + row);
-          const bf16x8 al = *reinterpret_cast<const bf16x8*>(op.kl + row);
-          acc = mfma32(ah, uh[q], acc);
-          acc = mfma32(ah, ul[q], acc);
-          acc = mfma32(al, uh[q], acc);
+      for (int q = 0; q < NB / 2; ++q) {
+        bf16x8 ah[RB], al[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int row = ((kb0 + rb) * 16 + (lane & 15)) * Ops::LK + 32 * q + 8 * g4;
+          ah[rb] = *reinterpret_cast<const bf16x8*>(op.kh + row);
+          al[rb] = *reinterpret_cast<const bf16x8*>(op.kl + row);
         }
-        s[kb] = acc;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(ah[rb], uh[q], s[rb]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(ah[rb], ul[q], s[rb]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(al[rb], uh[q], s[rb]);
       }
     } else {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int rb = 0; rb < RB; ++rb) {
+        const int kb = kb0 + rb;
         const float4 gg = *reinterpret_cast<const float4*>(op.gam + kb * 16 + 4 * g4);
-        f32x4 acc = {gg.x * s[kb][0], gg.y * s[kb][1], gg.z * s[kb][2], gg.w * s[kb][3]};
+        f32x4 acc = {gg.x * s[rb][0], gg.y * s[rb][1], gg.z * s[rb][2], gg.w * s[rb][3]};
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
           const float4 a = *reinterpret_cast<const float4*>(op.kt + (kb * 16 + (lane & 15)) * Ops::LK + I * 16 + 4 * g4);
@@ -579,17 +747,17 @@ __global__ __launch_bounds__((NW + 1) * 64) void split_state_kernel(SplitParams 
           acc = mfma4(a.z, x[I][2], acc);
           acc = mfma4(a.w, x[I][3], acc);
         }
-        s[kb] = acc;
+        s[rb] = acc;
       }
     }
-    __syncthreads();  // the next image is in place; this one may be overwritten
+    __syncthreads();  // the next image is in place; this one (and xs) may be overwritten
   }
   if (p.S_out) {
     float* So = p.S_out + bh * (long)K * K;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) So[(kb * 16 + 4 * g4 + r) * K + col] = s[kb][r];
+      for (int r = 0; r < 4; ++r) So[((kb0 + rb) * 16 + 4 * g4 + r) * K + col] = s[rb][r];
   }
 }
 
@@ -601,35 +769,18 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
   __shared__ alignas(16) float A[C * LR];
   float* Q = L.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4;
-  const long ch = blockIdx.x;
+  const float scale = 1.0f / __builtin_sqrtf((float)K);
+  const long nch = (long)p.B * p.HV * p.NC;
+  ChunkRegs<K, C, T> cr;
+  if ((long)blockIdx.x < nch) chunk_issue<K, C, T>(p, blockIdx.x, true, cr);
+  for (long ch = blockIdx.x; ch < nch; ch += gridDim.x) {
   const long bh = ch / p.NC;
   const int c = (int)(ch % p.NC);
-  load_chunk<K, C, T>(p, bh, c, L, true);
-  const float scale = 1.0f / __builtin_sqrtf((float)K);
+  chunk_store<K, C, T>(p, ch, cr, L);
+  if (ch + gridDim.x < nch) chunk_issue<K, C, T>(p, ch + gridDim.x, true, cr);  // lands during this chunk
 
-  // A inside the sub-blocks (j <= i), direct
-  for (int e = tid; e < NB * 136; e += kSplitThreads) {
-    const int J = e / 136;
-    int i, j;
-    tri_pair(e % 136, false, i, j);
-    i += J * 16;
-    j += J * 16;
-    A[i * LR + j] = scale * decayed_dot<K, C>(L, Q, i, j);
-  }
-  for (int e = tid; e < NB * 120; e += kSplitThreads) {  // zeros above the diagonal
-    const int J = e / 120;
-    int i, j;
-    tri_pair(e % 120, true, i, j);
-    A[(J * 16 + j) * LR + J * 16 + i] = 0.0f;
-  }
-  constexpr int NP = NB * (NB - 1) / 2;
-  for (int pi = w; pi < NP; pi += kSplitThreads / 64) {
-    int I, J;
-    tri_pair(pi, true, I, J);
-    const f32x4 acc = decayed_block<K, C>(L, Q, I, J, lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) A[(I * 16 + 4 * g4 + r) * LR + J * 16 + (lane & 15)] = scale * acc[r];
-  }
+  // A = s times the lower (diagonal included) decayed q k^T
+  decayed_lower<K, C, false>(L, Q, tid, [&](int i, int j, float v) { A[i * LR + j] = scale * v; });
   __syncthreads();
   // Q <- s q exp(G)
   for (int e = tid; e < C * K; e += kSplitThreads) {
@@ -661,7 +812,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
 #pragma unroll
     for (int J = 0; J < NB; ++J)
       uf[J] = *reinterpret_cast<const f32x4*>(p.u + frag_index(ch, NKB, NB, cb, J, lane));
-#pragma unroll
+#pragma unroll 1
     for (int I = 0; I < NB; ++I) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       const float* qrow = Q + (I * 16 + (lane & 15)) * LD + 4 * g4;
@@ -674,7 +825,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
         acc = mfma4(a.w, hf[kb][3], acc);
       }
 #pragma unroll
-      for (int J = 0; J <= I; ++J) {
+      for (int J = 0; J < NB; ++J) {
+        if (J > I) break;
         const float4 a = *reinterpret_cast<const float4*>(A + (I * 16 + (lane & 15)) * LR + J * 16 + 4 * g4);
         acc = mfma4(a.x, uf[J][0], acc);
         acc = mfma4(a.y, uf[J][1], acc);
@@ -688,6 +840,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
       }
     }
   }
+  __syncthreads();  // LDS is refilled by the next chunk
+  }
 }
 
 // ----------------------------------------------------------------- launch
@@ -695,19 +849,27 @@ template <int K, int C, typename T>
 static hipError_t launch_split_kc(const SplitParams& p, hipStream_t stream) {
   const long heads = (long)p.B * p.HV;
   const long chunks = heads * p.NC;
+  // the intra and output kernels are persistent: one workgroup per compute
+  // unit (their LDS allows no more), each walking chunks with a stride of
+  // the grid and loading the next chunk's inputs while it computes this one
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const unsigned grid = (unsigned)(chunks < cus ? chunks : cus);
   if (chunks > 0) {
-    hipLaunchKernelGGL((split_intra_kernel<K, C, T>), dim3((unsigned)chunks), dim3(kSplitThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((split_intra_kernel<K, C, T>), dim3(grid), dim3(kSplitThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr int NW = kStateWaves < K / 16 ? kStateWaves : K / 16;
-  hipLaunchKernelGGL((split_state_kernel<K, C, ChainBF<K, C, T>::value, NW>),
-                     dim3((unsigned)(heads * (K / 16 / NW))), dim3((NW + 1) * 64), 0, stream, p);
+  constexpr bool BF = ChainBF<K, C, T>::value;
+  constexpr int KSM = BF ? K / 32 : K / 16;  // key splits that keep whole operand slices
+  constexpr int KS = kStateSplit < KSM ? kStateSplit : KSM;
+  hipLaunchKernelGGL((split_state_kernel<K, C, BF, KS>), dim3((unsigned)(heads * (K / 16))),
+                     dim3((KS + 1) * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || chunks == 0) return e;
-  hipLaunchKernelGGL((split_output_kernel<K, C, T>), dim3((unsigned)chunks), dim3(kSplitThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((split_output_kernel<K, C, T>), dim3(grid), dim3(kSplitThreads), 0, stream, p);
   return hipGetLastError();
 }
 
