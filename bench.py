@@ -237,18 +237,19 @@ def main():
         sbytes = chunk_bytes(ws_)
         tok = ws_.B * ws_.T
 
-        def line(ms, kernel):
+        def line(ms, kernel, traffic):
             gbs = sbytes / (ms * 1e-3) / 1e9
             return {"ms_per_call": ms, "value": tok / (ms * 1e-3), "unit": "tokens/s",
                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                                 "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                 "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
                                  "bytes_per_launch": sbytes, "kernel": kernel}}
 
         result["split"] = {
             "workload": ws_.name, "B": ws_.B, "T": ws_.T, "H": ws_.H, "HV": ws_.HV, "K": ws_.K,
             "chunk": ws_.chunk, "gate": ws_.gate,
-            "fused": line(fused_ms, "chunk_fwd_kernel<128, bf16>"),
-            "split": line(split_ms, "split_intra + split_state + split_output <128, 64>"),
+            "fused": line(fused_ms, "chunk_fwd_kernel<128, bf16>", None),
+            "split": line(split_ms, "split_intra + split_state + split_output <128, 64>",
+                          measured_traffic("split")),
             "speedup": fused_ms / split_ms}
         del gsh, osh, Ssh, wsp
 
