@@ -76,10 +76,7 @@ constexpr int kSplitThreads = 512;
 __device__ __forceinline__ long frag_index(long mat, int ncb, int nrb, int cb, int rb, int lane) {
   return (((mat * ncb + cb) * nrb + rb) * 64 + lane) * 4;
 }
-#ifndef KDA_STATE_SPLIT
-#define KDA_STATE_SPLIT 1
-#endif
-constexpr int kStateSplit = KDA_STATE_SPLIT;  // wavefronts sharing one state column block's keys
+
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -563,15 +560,19 @@ __device__ __forceinline__ void fetch_u(const SplitParams& p, long ch, f32x4 (&u
     un[I] = *reinterpret_cast<const f32x4*>(p.u + frag_index(ch, K / 16, C / 16, cb, I, lane));
 }
 
-// Copies a chunk's image from the workspace into LDS with direct global-to-LDS
-// loads (16 bytes per lane, 1 KiB per wavefront instruction), no registers
-// involved.
-template <int IMG>
-__device__ __forceinline__ void copy_image(const char* src, char* dst, int lane) {
-#pragma unroll 8
-  for (int j = 0; j < IMG / 1024; ++j)
-    __builtin_amdgcn_global_load_lds(src + j * 1024 + lane * 16,
-                                     (__attribute__((address_space(3))) void*)(dst + j * 1024), 16, 0, 0);
+// Copies n bytes (a multiple of 16) from the workspace into LDS with direct
+// global-to-LDS loads: 16 bytes per lane, 1 KiB per wavefront instruction, no
+// registers involved; copier wavefront cw of NCP takes every NCP-th KiB.
+template <int NCP, int N>
+__device__ __forceinline__ void copy_to_lds(const char* src, char* dst, int cw, int lane) {
+  constexpr int ROUNDS = (N + NCP * 1024 - 1) / (NCP * 1024);
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int j = (r * NCP + cw) * 1024;
+    if (j + lane * 16 < N)
+      __builtin_amdgcn_global_load_lds(src + j + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + j), 16, 0, 0);
+  }
 }
 
 // The direct copies count as vector memory loads of the issuing wavefront,
@@ -580,184 +581,235 @@ __device__ __forceinline__ void copy_image(const char* src, char* dst, int lane)
 // publishes them.
 __device__ __forceinline__ void image_landed() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// One workgroup per (b, hv, 16-wide column block of the state); its KS
-// computing wavefronts split the key rows: wavefront kp holds rows
-// kp K / KS .. (kp + 1) K / KS - 1, lane l rows 16 kb + 4 (l / 16) + r of
-// column l % 16 (the MFMA accumulator layout, which is also the B operand
-// layout of the fp32 products; the bf16 products take two such fragments
-// per 32-wide slice).  Per chunk each computes its part of W h over its keys,
-// the parts meet in LDS (every wavefront then holds all of U), and each
-// updates its own rows.  One more wavefront only streams the next chunk's
-// operand image into LDS, so the copy's latency never enters the computing
-// wavefronts' LDS waits.  The column blocks of a head are independent
-// workgroups with equal blockIdx % 8, so one XCD's L2 serves their common
-// operand images.
-template <int K, int C, bool BF, int KS>
-__global__ __launch_bounds__((KS + 1) * 64) void split_state_kernel(SplitParams p) {
-  constexpr int NB = C / 16, NKB = K / 16, RB = NKB / KS, IMG = split_image_bytes<K, C>();
-  static_assert(NKB % KS == 0 && (!BF || RB % 2 == 0), "key split must fit the operand slices");
+// Byte ranges of a chunk's image: W (or its hi/lo pair) first, then Kt^T and
+// gamma.
+template <int K, int C, bool BF>
+struct ImageHalves {
   using Ops = ChainOps<K, C, BF>;
-  __shared__ alignas(1024) char img[2][IMG];
-  __shared__ f32x4 xs[KS][NB][64];  // each wavefront's part of W h
-  const int tid = threadIdx.x, lane = tid & 63, kp = tid >> 6, g4 = lane >> 4;
+  static constexpr int WB = (int)(sizeof(Ops::w) + 0);                         // W bytes
+  static constexpr int KB = (int)sizeof(Ops) - WB;                             // Kt^T + gamma bytes
+  static constexpr int GOFF = (int)(sizeof(Ops::kt) + 0);                      // gamma within them
+};
+template <int K, int C>
+struct ImageHalves<K, C, true> {
+  using Ops = ChainOps<K, C, true>;
+  static constexpr int WB = (int)(sizeof(Ops::wh) + sizeof(Ops::wl));
+  static constexpr int KB = (int)sizeof(Ops) - WB;
+  static constexpr int GOFF = (int)(sizeof(Ops::kh) + sizeof(Ops::kl));
+};
+
+// One workgroup per (b, hv, 16-wide column block of the state): one
+// wavefront holds that block of the fp32 state in registers for the whole
+// sequence, lane l rows 16 kb + 4 (l / 16) + r of column l % 16 (the MFMA
+// accumulator layout, which is also the B operand layout of the fp32
+// products; the bf16 products take two such fragments per 32-wide slice).
+// Further wavefronts only stream operands into LDS, so the copy's latency
+// never enters the computing wavefront's LDS waits; several of them keep
+// enough copies in flight (one wavefront can have 63 outstanding).
+//
+// The chain is software-pipelined across chunks: iteration c forms h_{c+1} =
+// diag(gamma_c) h_c + Kt_c^T U_c one 32-row slice at a time and, as each slice
+// is final, adds its part of W_{c+1} h_{c+1}, so the products of the two
+// halves of the recurrence keep the matrix core busy together; U_{c+1} =
+// u_{c+1} - W_{c+1} h_{c+1} closes the iteration.  W and Kt^T are therefore
+// double-buffered separately: iteration c reads Kt_c and W_{c+1} while the
+// copier brings Kt_{c+1} and W_{c+2}.  The column blocks of a head are
+// independent workgroups with equal blockIdx % 8, so one XCD's L2 serves
+// their common operand images.
+#ifndef KDA_STATE_COPIERS
+#define KDA_STATE_COPIERS 4
+#endif
+constexpr int kCopiers = KDA_STATE_COPIERS;  // copying wavefronts per state-pass workgroup
+
+template <int K, int C, bool BF>
+__global__ __launch_bounds__(64 * (1 + kCopiers)) void split_state_kernel(SplitParams p) {
+  constexpr int NB = C / 16, NKB = K / 16, IMG = split_image_bytes<K, C>();
+  using Ops = ChainOps<K, C, BF>;
+  using IH = ImageHalves<K, C, BF>;
+  constexpr int WB = IH::WB, KB = IH::KB;
+  constexpr int WBR = (WB + 15) / 16 * 16, KBR = (KB + 15) / 16 * 16;
+  __shared__ alignas(16) char wbuf[2][WBR];
+  __shared__ alignas(16) char kbuf[2][KBR];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g4 = lane >> 4;
   const long nh = (long)p.B * p.HV;
   const long bh = blockIdx.x % nh;
   const int cb = (int)(blockIdx.x / nh);
   const int NC = p.NC;
   const int col = cb * 16 + (lane & 15);
-  const int kb0 = kp * RB;  // first key row block of this wavefront
-  const char* src = p.ops + bh * NC * (long)IMG;
+  const char* src = p.ops + bh * NC * (long)IMG;  // image of chunk c at src + c IMG
 
-  if (kp == KS) {  // the copying wavefront: the same barriers as the others
-    if (NC > 0) copy_image<IMG>(src, img[0], lane);
+  if (w >= 1) {  // the copying wavefronts: the same barriers as the computing one
+    const int cw = w - 1;
+    if (NC > 0) {
+      copy_to_lds<kCopiers, WB>(src, wbuf[0], cw, lane);
+      copy_to_lds<kCopiers, KB>(src + WB, kbuf[0], cw, lane);
+      if (NC > 1) copy_to_lds<kCopiers, WB>(src + IMG, wbuf[1], cw, lane);
+    }
     image_landed();
     __syncthreads();
+    __syncthreads();  // W_0 consumed
     for (int c = 0; c < NC; ++c) {
-      if (c + 1 < NC) copy_image<IMG>(src + (c + 1) * (long)IMG, img[(c + 1) & 1], lane);
-      if (KS > 1) __syncthreads();
+      if (c + 1 < NC) copy_to_lds<kCopiers, KB>(src + (c + 1) * (long)IMG + WB, kbuf[(c + 1) & 1], cw, lane);
+      if (c + 2 < NC) copy_to_lds<kCopiers, WB>(src + (c + 2) * (long)IMG, wbuf[c & 1], cw, lane);
       image_landed();
       __syncthreads();
     }
     return;
   }
 
-  f32x4 un[NB];  // u of the next chunk, this lane's elements
-  f32x4 s[RB];
+  // operand views of the buffers
+  auto Wv = [&](int slot) { return reinterpret_cast<const char*>(wbuf[slot]); };
+  auto Kv = [&](int slot) { return reinterpret_cast<const char*>(kbuf[slot]); };
+
+  f32x4 s[NKB];
   const float* S0 = p.S0 ? p.S0 + bh * (long)K * K : nullptr;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[rb][r] = S0 ? S0[((kb0 + rb) * 16 + 4 * g4 + r) * K + col] : 0.0f;
-  if (NC > 0) fetch_u<K, C>(p, bh * NC, un, cb, lane);
+    for (int r = 0; r < 4; ++r) s[kb][r] = S0 ? S0[(kb * 16 + 4 * g4 + r) * K + col] : 0.0f;
+  f32x4 x[NB], un[NB];
+  if (NC > 0) fetch_u<K, C>(p, bh * NC, x, cb, lane);
+  if (NC > 1) fetch_u<K, C>(p, bh * NC + 1, un, cb, lane);
   __syncthreads();
+
+  // X_c: add the part of W h over key slice q (bf16) or key block kb (fp32)
+  auto x_part = [&](const char* wsrc, int q) {
+    if constexpr (BF) {
+      const uint16_t* wh = reinterpret_cast<const uint16_t*>(wsrc);
+      const uint16_t* wl = wh + C * Ops::LW;
+      bf16x8 bh_, bl_, ah[NB], al[NB];
+      split8(s[2 * q], s[2 * q + 1], bh_, bl_);
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        const int row = (I * 16 + (lane & 15)) * Ops::LW + 32 * q + 8 * g4;
+        ah[I] = *reinterpret_cast<const bf16x8*>(wh + row);
+        al[I] = *reinterpret_cast<const bf16x8*>(wl + row);
+      }
+#pragma unroll
+      for (int I = 0; I < NB; ++I) x[I] = mfma32(ah[I], bh_, x[I]);
+#pragma unroll
+      for (int I = 0; I < NB; ++I) x[I] = mfma32(ah[I], bl_, x[I]);
+#pragma unroll
+      for (int I = 0; I < NB; ++I) x[I] = mfma32(al[I], bh_, x[I]);
+    } else {
+      const float* wf = reinterpret_cast<const float*>(wsrc);
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        const float4 a = *reinterpret_cast<const float4*>(wf + (I * 16 + (lane & 15)) * Ops::LW + q * 16 + 4 * g4);
+        x[I] = mfma4(a.x, s[q][0], x[I]);
+        x[I] = mfma4(a.y, s[q][1], x[I]);
+        x[I] = mfma4(a.z, s[q][2], x[I]);
+        x[I] = mfma4(a.w, s[q][3], x[I]);
+      }
+    }
+  };
+  constexpr int NQ = BF ? K / 32 : NKB;  // key slices (bf16) or blocks (fp32) of x_part
+  constexpr int RPQ = BF ? 2 : 1;        // state row blocks per slice
+
+  // X_0 = W_0 h_0, then U_0 = u_0 - X_0
+  if (NC > 0) {
+    f32x4 xw[NB];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      xw[I] = x[I];
+      x[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) x_part(Wv(0), q);
+#pragma unroll
+    for (int I = 0; I < NB; ++I) x[I] = xw[I] - x[I];
+  }
+  __syncthreads();  // W_0 consumed
 
   for (int c = 0; c < NC; ++c) {
     const long ch = bh * NC + c;
-    const Ops& op = *reinterpret_cast<const Ops*>(img[c & 1]);
-    f32x4 x[NB];
+    const bool more = c + 1 < NC;
+    // this iteration's U and h_c go out; u_{c+2} comes in
+    f32x4 ucur[NB];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) x[I] = un[I];
-    if (c + 1 < NC) fetch_u<K, C>(p, ch + 1, un, cb, lane);
+    for (int I = 0; I < NB; ++I) {
+      ucur[I] = x[I];
+      *reinterpret_cast<f32x4*>(p.u + frag_index(ch, NKB, NB, cb, I, lane)) = x[I];
+      x[I] = un[I];  // u_{c+1}: X_{c+1} accumulates into its negative below
+    }
+    if (c + 2 < NC) fetch_u<K, C>(p, ch + 2, un, cb, lane);
     if (p.h_plain) {
       float* hc = p.h + ch * (long)K * K;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hc[((kb0 + rb) * 16 + 4 * g4 + r) * K + col] = s[rb][r];
+        for (int r = 0; r < 4; ++r) hc[(kb * 16 + 4 * g4 + r) * K + col] = s[kb][r];
     } else {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        *reinterpret_cast<f32x4*>(p.h + frag_index(ch, NKB, NKB, cb, kb0 + rb, lane)) = s[rb];
+      for (int kb = 0; kb < NKB; ++kb)
+        *reinterpret_cast<f32x4*>(p.h + frag_index(ch, NKB, NKB, cb, kb, lane)) = s[kb];
     }
+    // X_{c+1} is accumulated negated onto u_{c+1}, so U_{c+1} = x at the end
+#pragma unroll
+    for (int I = 0; I < NB; ++I) x[I] = -x[I];
 
-    // this wavefront's keys of W h_c
-    f32x4 xw[NB];
-#pragma unroll
-    for (int I = 0; I < NB; ++I) xw[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char* kt = Kv(c & 1);
+    const float* gm = reinterpret_cast<const float*>(kt + IH::GOFF);
+    bf16x8 uh[NB / 2 > 0 ? NB / 2 : 1], ul[NB / 2 > 0 ? NB / 2 : 1];
     if constexpr (BF) {
-      // the NB accumulators are independent: issue them in turn, so that no
-      // product waits on the one before it
 #pragma unroll
-      for (int qq = 0; qq < RB / 2; ++qq) {
-        const int q = kb0 / 2 + qq;
-        bf16x8 bh_, bl_, ah[NB], al[NB];
-        split8(s[2 * qq], s[2 * qq + 1], bh_, bl_);
+      for (int q = 0; q < NB / 2; ++q) split8(ucur[2 * q], ucur[2 * q + 1], uh[q], ul[q]);
+    }
+    // rows of h_{c+1} in slices; each finished slice feeds X_{c+1}
+    auto s_part = [&](int q) {
+#pragma unroll
+      for (int rr = 0; rr < RPQ; ++rr) {
+        const int kb = q * RPQ + rr;
+        const float4 gg = *reinterpret_cast<const float4*>(gm + kb * 16 + 4 * g4);
+        s[kb] = f32x4{gg.x * s[kb][0], gg.y * s[kb][1], gg.z * s[kb][2], gg.w * s[kb][3]};
+      }
+      if constexpr (BF) {
+        const uint16_t* kh = reinterpret_cast<const uint16_t*>(kt);
+        const uint16_t* kl = kh + K * Ops::LK;
+#pragma unroll
+        for (int t = 0; t < NB / 2; ++t) {
+          bf16x8 ah[RPQ], al[RPQ];
+#pragma unroll
+          for (int rr = 0; rr < RPQ; ++rr) {
+            const int row = ((q * RPQ + rr) * 16 + (lane & 15)) * Ops::LK + 32 * t + 8 * g4;
+            ah[rr] = *reinterpret_cast<const bf16x8*>(kh + row);
+            al[rr] = *reinterpret_cast<const bf16x8*>(kl + row);
+          }
+#pragma unroll
+          for (int rr = 0; rr < RPQ; ++rr) s[q * RPQ + rr] = mfma32(ah[rr], uh[t], s[q * RPQ + rr]);
+#pragma unroll
+          for (int rr = 0; rr < RPQ; ++rr) s[q * RPQ + rr] = mfma32(ah[rr], ul[t], s[q * RPQ + rr]);
+#pragma unroll
+          for (int rr = 0; rr < RPQ; ++rr) s[q * RPQ + rr] = mfma32(al[rr], uh[t], s[q * RPQ + rr]);
+        }
+      } else {
+        const float* kf = reinterpret_cast<const float*>(kt);
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
-          const int row = (I * 16 + (lane & 15)) * Ops::LW + 32 * q + 8 * g4;
-          ah[I] = *reinterpret_cast<const bf16x8*>(op.wh + row);
-          al[I] = *reinterpret_cast<const bf16x8*>(op.wl + row);
+          const float4 a = *reinterpret_cast<const float4*>(kf + (q * 16 + (lane & 15)) * Ops::LK + I * 16 + 4 * g4);
+          s[q] = mfma4(a.x, ucur[I][0], s[q]);
+          s[q] = mfma4(a.y, ucur[I][1], s[q]);
+          s[q] = mfma4(a.z, ucur[I][2], s[q]);
+          s[q] = mfma4(a.w, ucur[I][3], s[q]);
         }
-#pragma unroll
-        for (int I = 0; I < NB; ++I) xw[I] = mfma32(ah[I], bh_, xw[I]);
-#pragma unroll
-        for (int I = 0; I < NB; ++I) xw[I] = mfma32(ah[I], bl_, xw[I]);
-#pragma unroll
-        for (int I = 0; I < NB; ++I) xw[I] = mfma32(al[I], bh_, xw[I]);
       }
-    } else {
+    };
+    s_part(0);
 #pragma unroll
-      for (int I = 0; I < NB; ++I)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float4 a = *reinterpret_cast<const float4*>(op.w + (I * 16 + (lane & 15)) * Ops::LW + (kb0 + rb) * 16 + 4 * g4);
-          xw[I] = mfma4(a.x, s[rb][0], xw[I]);
-          xw[I] = mfma4(a.y, s[rb][1], xw[I]);
-          xw[I] = mfma4(a.z, s[rb][2], xw[I]);
-          xw[I] = mfma4(a.w, s[rb][3], xw[I]);
-        }
-    }
-    // U = u - W h_c: the parts of all wavefronts, summed in a fixed order
-    if constexpr (KS > 1) {
-#pragma unroll
-      for (int I = 0; I < NB; ++I) xs[kp][I][lane] = xw[I];
-      __syncthreads();
-#pragma unroll
-      for (int I = 0; I < NB; ++I) {
-        f32x4 t = xs[0][I][lane];
-#pragma unroll
-        for (int j = 1; j < KS; ++j) t += xs[j][I][lane];
-        xw[I] = t;
-      }
+    for (int q = 0; q < NQ; ++q) {
+      if (q + 1 < NQ) s_part(q + 1);
+      if (more) x_part(Wv((c + 1) & 1), q);
     }
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      x[I] -= xw[I];
-      if (kp == 0) *reinterpret_cast<f32x4*>(p.u + frag_index(ch, NKB, NB, cb, I, lane)) = x[I];
-    }
-
-    // this wavefront's rows of h_{c+1} = diag(gamma) h_c + Kt^T U
-    if constexpr (BF) {
-      bf16x8 uh[NB / 2], ul[NB / 2];
-#pragma unroll
-      for (int q = 0; q < NB / 2; ++q) split8(x[2 * q], x[2 * q + 1], uh[q], ul[q]);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float4 gg = *reinterpret_cast<const float4*>(op.gam + (kb0 + rb) * 16 + 4 * g4);
-        s[rb] = f32x4{gg.x * s[rb][0], gg.y * s[rb][1], gg.z * s[rb][2], gg.w * s[rb][3]};
-      }
-      // RB independent accumulators, issued in turn
-#pragma unroll
-      for (int q = 0; q < NB / 2; ++q) {
-        bf16x8 ah[RB], al[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int row = ((kb0 + rb) * 16 + (lane & 15)) * Ops::LK + 32 * q + 8 * g4;
-          ah[rb] = *reinterpret_cast<const bf16x8*>(op.kh + row);
-          al[rb] = *reinterpret_cast<const bf16x8*>(op.kl + row);
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(ah[rb], uh[q], s[rb]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(ah[rb], ul[q], s[rb]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32(al[rb], uh[q], s[rb]);
-      }
-    } else {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int kb = kb0 + rb;
-        const float4 gg = *reinterpret_cast<const float4*>(op.gam + kb * 16 + 4 * g4);
-        f32x4 acc = {gg.x * s[rb][0], gg.y * s[rb][1], gg.z * s[rb][2], gg.w * s[rb][3]};
-#pragma unroll
-        for (int I = 0; I < NB; ++I) {
-          const float4 a = *reinterpret_cast<const float4*>(op.kt + (kb * 16 + (lane & 15)) * Ops::LK + I * 16 + 4 * g4);
-          acc = mfma4(a.x, x[I][0], acc);
-          acc = mfma4(a.y, x[I][1], acc);
-          acc = mfma4(a.z, x[I][2], acc);
-          acc = mfma4(a.w, x[I][3], acc);
-        }
-        s[rb] = acc;
-      }
-    }
-    __syncthreads();  // the next image is in place; this one (and xs) may be overwritten
+    for (int I = 0; I < NB; ++I) x[I] = -x[I];  // U_{c+1} = u_{c+1} - X_{c+1}
+    __syncthreads();  // next operands in place; these may be overwritten
   }
   if (p.S_out) {
     float* So = p.S_out + bh * (long)K * K;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) So[((kb0 + rb) * 16 + 4 * g4 + r) * K + col] = s[rb][r];
+      for (int r = 0; r < 4; ++r) So[(kb * 16 + 4 * g4 + r) * K + col] = s[kb][r];
   }
 }
 
@@ -862,11 +914,8 @@ static hipError_t launch_split_kc(const SplitParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr bool BF = ChainBF<K, C, T>::value;
-  constexpr int KSM = BF ? K / 32 : K / 16;  // key splits that keep whole operand slices
-  constexpr int KS = kStateSplit < KSM ? kStateSplit : KSM;
-  hipLaunchKernelGGL((split_state_kernel<K, C, BF, KS>), dim3((unsigned)(heads * (K / 16))),
-                     dim3((KS + 1) * 64), 0, stream, p);
+  hipLaunchKernelGGL((split_state_kernel<K, C, ChainBF<K, C, T>::value>),
+                     dim3((unsigned)(heads * (K / 16))), dim3(64 * (1 + kCopiers)), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || chunks == 0) return e;
   hipLaunchKernelGGL((split_output_kernel<K, C, T>), dim3(grid), dim3(kSplitThreads), 0, stream, p);
