@@ -143,3 +143,23 @@ def test_recurrent_fwd_decode_workload_multi_token():
     heads = L.sample_heads(w.B, w.HV, 16, seed=w.seed)
     ref = L.oracle_heads(d, w.gate, w.lower_bound, heads)
     L.compare_heads(o, st, ref, L.TOL_F32, "decode workload, 16-token calls")
+
+
+@pytest.mark.timeout(600)
+def test_large_state_takes_the_streaming_loads():
+    """A state above the cached-state size (800 MiB here) is read with
+    non-temporal loads by both the one-token step and the multi-token
+    forward: the same results as the oracle on sampled heads."""
+    w = synth.WORKLOADS["decode"]
+    B, T = 400, 3
+    d = synth.make_inputs(w, B=B, T=T, seed=77)
+    assert B * w.HV * w.K * w.V * 4 > 768 << 20
+    print("large state: B=%d HV=%d (%d MiB)" % (B, w.HV, B * w.HV * w.K * w.V * 4 >> 20), flush=True)
+    heads = L.sample_heads(B, w.HV, 6, seed=3)
+    ref = L.oracle_heads(d, w.gate, w.lower_bound, heads)
+    o, S = L.run_decode(d, w.gate, w.lower_bound, d["S0"])
+    L.compare_heads(o, S, ref, L.TOL_F32, "large state, one-token steps")
+    del o, S
+    torch.cuda.empty_cache()
+    o, S = _run(d, w.gate, w.lower_bound)
+    L.compare_heads(o, S, ref, L.TOL_F32, "large state, one multi-token call")
