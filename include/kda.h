@@ -202,9 +202,11 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, kda_dt
  *                 owned by the caller; its contents need not be initialised and
  *                 are meaningless afterwards
  * Supported: K == V in {16, 32, 64, 128}; chunk_size 16, 32 or 64; HV % H == 0;
- * T >= 0.  Arithmetic: fp32 matrix products with fp32 accumulation for both
- * input dtypes (bf16 inputs are widened exactly).  Three kernels run in order on
- * `stream`.  Returns KDA_ERR_WORKSPACE if the workspace is missing or too small.
+ * T >= 0.  Arithmetic: fp32 matrix products with fp32 accumulation, except
+ * that with bf16 inputs (and K, chunk_size >= 32) the state pass runs bf16 MFMA
+ * products on split (hi + lo) operands; the state is fp32 throughout.  Three
+ * kernels run in order on `stream`.  Returns KDA_ERR_WORKSPACE if the
+ * workspace is missing or too small.
  */
 size_t kda_chunk_fwd_split_workspace_bytes(int B, int T, int H, int HV, int K, int V,
                                            int chunk_size);
