@@ -24,6 +24,8 @@ SPLIT_CASES = [
     (1, 257, 1, 1, 128, "bf16", "standard", 0.0, 32),
     (3, 48, 1, 3, 16, "bf16", "safe", 0.1, 64),       # a single partial chunk
     (1, 320, 4, 8, 64, "f32", "safe", 0.0, 64),
+    (2, 100, 2, 2, 32, "bf16", "safe", 0.05, 32),     # bf16 state pass with one key slice
+    (1, 130, 1, 2, 128, "f32", "standard", 0.02, 64),  # fp32 state pass at the largest shape
 ]
 
 
@@ -144,3 +146,18 @@ def test_workload_long_shard():
     eh = L.rel_err(h[:, :, :8], rh)
     print("long_shard h[0:8]: %.2e" % eh)
     assert eh <= L.TOL_BF16
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_split_h_in_workspace_matches_h_given(dt):
+    """The entry states kept in the workspace (as fragments) and handed to the
+    caller (row-major) give the same outputs and final state, bit for bit."""
+    d = synth.random_inputs(2, 200, 2, 4, 64, 64, seed=18, dtype=dt, s0_std=0.02)
+    g = L.to_dev(d)
+    args = (g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"])
+    o1, S1, h1 = kda.chunk_fwd_split(*args, chunk_size=64, initial_state=g["S0"],
+                                     output_states=True)
+    o2, S2, h2 = kda.chunk_fwd_split(*args, chunk_size=64, initial_state=g["S0"])
+    torch.cuda.synchronize()
+    assert h2 is None and h1.shape == (2, 4, 4, 64, 64)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
