@@ -15,9 +15,11 @@ fused chunk kernel and the three-stage split schedule ("split" object).
 Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
 HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
 bytes per launch / mean launch time (HIP events on the launch stream) against
-the 8 TB/s HBM peak; `mfma_frac` adds algorithmic FLOPs against the 2.5166
-PFLOP/s dense bf16 MFMA peak.  `cpu_baseline` times the fp64 CPU oracle on all
-host cores over a sample of the same workload.
+the 8 TB/s HBM peak; `mfma` adds algorithmic FLOPs against the 2.5166
+PFLOP/s dense bf16 MFMA peak and, from the committed counter passes, the
+fraction of cycles the matrix pipes were busy and the MFMA flops executed.
+`cpu_baseline` times the fp64 CPU oracle on all host cores over a sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -69,9 +71,9 @@ def recurrent_bytes(w, tokens):
     return 2 * w.B * w.HV * w.K * w.V * 4 + tokens * per_token
 
 
-def measured_traffic(key):
-    """HBM bytes per launch from the counter passes summarised in
-    profiles/traffic.json, or None when the kernel sources changed since."""
+def profile_record(key):
+    """The counter-pass record of a kernel in profiles/traffic.json, or None
+    when the kernel sources changed since it was taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -80,11 +82,23 @@ def measured_traffic(key):
         h = hashlib.sha256()
         for f in rec["sources"]:
             h.update(open(os.path.join(ROOT, f), "rb").read())
-        if h.hexdigest()[:16] != rec["source_sha256_16"]:
-            return None
-        return rec["traffic_bytes_per_launch"]
+        return rec if h.hexdigest()[:16] == rec["source_sha256_16"] else None
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE passes."""
+    rec = profile_record(key)
+    return rec["traffic_bytes_per_launch"] if rec else None
+
+
+def measured_mfma(key):
+    """MFMA counters of the same kernel: the fraction of SIMD cycles its
+    matrix pipe was busy (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x
+    SIMDs) and the MFMA flops it executed (SQ_INSTS_VALU_MFMA_MOPS_* x 512)."""
+    rec = profile_record(key)
+    return rec.get("mfma") if rec else None
 
 
 def main():
@@ -164,7 +178,8 @@ def main():
         "mfma": {"algorithmic_flops": flops,
                  "achieved_tflops": flops / (launch_ms * 1e-3) / 1e12,
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                 "frac": flops / (launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+                 "frac": flops / (launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                 "rocprof": measured_mfma("chunk") if args.workload == "prefill" else None},
         "wall_s_timed": t_wall,
     }
     del o, S, g
@@ -248,8 +263,8 @@ def main():
             "workload": ws_.name, "B": ws_.B, "T": ws_.T, "H": ws_.H, "HV": ws_.HV, "K": ws_.K,
             "chunk": ws_.chunk, "gate": ws_.gate,
             "fused": line(fused_ms, "chunk_fwd_kernel<128, bf16>", None),
-            "split": line(split_ms, "split_intra + split_state + split_output <128, 64>",
-                          measured_traffic("split")),
+            "split": dict(line(split_ms, "split_intra + split_state + split_output <128, 64>",
+                               measured_traffic("split")), mfma_rocprof=measured_mfma("split")),
             "speedup": fused_ms / split_ms}
         del gsh, osh, Ssh, wsp
 

@@ -80,13 +80,29 @@ constexpr float kGammaMax = 1.2676506002282294e30f;  // 2^100 (only a positive l
 
 // ------------------------------------------------------------------ LDS
 // ROWS x K operand with the key axis contiguous (bf16: hi and lo words).
+// bf16 rows with K a multiple of 32 are unpadded and swizzled: the 16-byte
+// chunk j of row r (key channels 8j .. 8j+7) sits at chunk position
+// j ^ (r mod K/8).  An MFMA operand read (lane l: row l % 16, one chunk) then
+// spreads every group of lanes that the LDS serves together over distinct
+// banks, and the prep's row writes keep their cost; padded rows of 272 bytes
+// cost half as much again per read.  Rows must start at multiples of 16.
 template <bool F32, int ROWS, int K>
 struct alignas(16) RowOp;
 template <int ROWS, int K>
 struct alignas(16) RowOp<false, ROWS, K> {
-  static constexpr int LD = K + 8;
+  static constexpr bool kSwz = K % 32 == 0;
+  static constexpr int LD = kSwz ? K : K + 8;
   uint16_t hi[ROWS * LD], lo[ROWS * LD];
 };
+
+// position in its row of key channel c (c % 4 == 0: four channels stay together)
+template <int K>
+__device__ __forceinline__ int row_pos(int r, int c) {
+  if constexpr (K % 32 == 0)
+    return (((c >> 3) ^ (r & (K / 8 - 1))) << 3) | (c & 7);
+  else
+    return c;
+}
 template <int ROWS, int K>
 struct alignas(16) RowOp<true, ROWS, K> {
   static constexpr int LD = K + 1;
@@ -161,15 +177,15 @@ __device__ __forceinline__ void mma_kappa_bf16(f32x4& acc, const uint16_t* Ah, c
                                                int lane) {
   const int row = lane & 15;
   if constexpr (K % 32 == 0) {
-    const int kq = (lane >> 4) * 8;
 #pragma unroll
     for (int s = 0; s < K; s += 32) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ah + row * ld + s + kq);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bh + row * ld + s + kq);
+      const int o = row * ld + row_pos<K>(row, s + (lane >> 4) * 8);  // swizzled rows
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ah + o);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bh + o);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
       if constexpr (HL == 3) {
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(Al + row * ld + s + kq);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Bl + row * ld + s + kq);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(Al + o);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Bl + o);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
       }
@@ -240,8 +256,9 @@ __device__ __forceinline__ void put4(RowOp<F32, ROWS, K>& op, int row, int c0, c
     uint2 h, l;
     split2_bf16(x[0], x[1], h.x, l.x);
     split2_bf16(x[2], x[3], h.y, l.y);
-    *reinterpret_cast<uint2*>(op.hi + row * LD + c0) = h;
-    *reinterpret_cast<uint2*>(op.lo + row * LD + c0) = l;
+    const int o = row * LD + row_pos<K>(row, c0);
+    *reinterpret_cast<uint2*>(op.hi + o) = h;
+    *reinterpret_cast<uint2*>(op.lo + o) = l;
   }
 }
 
@@ -313,34 +330,13 @@ __device__ __forceinline__ void tprod_reg(f32x4& acc, const uint16_t* Acat, bf16
   acc = mfma16(al, bh, acc);
 }
 
-// acc1 += A1 x B^T and acc2 += A2 x B^T over the key axis, B's fragments read once
-template <bool F32, int K, int RB>
-__device__ __forceinline__ void kprod2(f32x4& acc1, f32x4& acc2, const RowOp<F32, kTok, K>& A1,
-                                       const RowOp<F32, kTok, K>& A2, const RowOp<F32, RB, K>& B,
+// fp32 inputs: acc1 += A1 x B^T and acc2 += A2 x B^T over the key axis
+template <int K, int RB>
+__device__ __forceinline__ void kprod2(f32x4& acc1, f32x4& acc2, const RowOp<true, kTok, K>& A1,
+                                       const RowOp<true, kTok, K>& A2, const RowOp<true, RB, K>& B,
                                        int lane) {
-  constexpr int LD = RowOp<F32, kTok, K>::LD;
-  if constexpr (F32 || K % 32 != 0) {
-    kprod(acc1, A1, 0, B, 0, lane);
-    kprod(acc2, A2, 0, B, 0, lane);
-  } else {
-    const int row = lane & 15, kq = (lane >> 4) * 8;
-#pragma unroll
-    for (int s = 0; s < K; s += 32) {
-      const int o = row * LD + s + kq;
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(B.hi + o);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(B.lo + o);
-      const bf16x8 a1h = *reinterpret_cast<const bf16x8*>(A1.hi + o);
-      const bf16x8 a1l = *reinterpret_cast<const bf16x8*>(A1.lo + o);
-      const bf16x8 a2h = *reinterpret_cast<const bf16x8*>(A2.hi + o);
-      const bf16x8 a2l = *reinterpret_cast<const bf16x8*>(A2.lo + o);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, bh, acc1, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h, bh, acc2, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, bl, acc1, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2h, bl, acc2, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1l, bh, acc1, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2l, bh, acc2, 0, 0, 0);
-    }
-  }
+  kprod(acc1, A1, 0, B, 0, lane);
+  kprod(acc2, A2, 0, B, 0, lane);
 }
 
 // acc += A[arow0 .. +16) (16 tokens) x B (16 tokens x 16, given by its columns)
