@@ -9,8 +9,10 @@ steps over a 512 MiB fp32 state) and reported in the "decode" object; the
 fused multi-token recurrent forward runs the same 256 tokens as 16-token calls
 and as one 256-token call ("recurrent" object), the chunked forward runs the
 prefill shape with one gate per (token, value head) ("head_gate" object), and
-the one-sequence long shard (T=65536, 8 value heads) runs through both the
-fused chunk kernel and the three-stage split schedule ("split" object).
+the full-size GVA and long-context prefill workloads run through the same
+kernel ("configs" object), and the one-sequence long shard (T=65536, 8 value
+heads) runs through both the fused chunk kernel and the three-stage split
+schedule ("split" object).
 
 Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
 HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
@@ -110,6 +112,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-split", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the full-size GVA and long-context prefill lines")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -217,6 +221,48 @@ def main():
                      "frac": hgbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": hbytes,
                      "kernel": "chunk_fwd_kernel<128, bf16, per-head gate>"}}
     del gh, oh, Sh
+
+    # The other two chunked-prefill workloads at full size, through the same
+    # kernel: GVA (B=2, T=16384, 8 q/k heads for 32 value heads, standard
+    # gate, random initial state) and long context (B=1, T=65536, 16 q/k heads
+    # for 64 value heads).
+    if not args.no_configs:
+        result["configs"] = {}
+        for name in ("gva", "long"):
+            wc = synth.WORKLOADS[name]
+            gc = {n: (t.to(dev) if t is not None else None)
+                  for n, t in synth.make_inputs(wc).items()}
+            oc = torch.empty((wc.B, wc.T, wc.HV, wc.V), dtype=torch.float32, device=dev)
+            Sc = torch.empty((wc.B, wc.HV, wc.K, wc.V), dtype=torch.float32, device=dev)
+
+            def cstep():
+                kda.chunk_fwd(gc["q"], gc["k"], gc["v"], gc["g_raw"], gc["beta"], gc["A_log"],
+                              gc["dt_bias"], gate=wc.gate, lower_bound=wc.lower_bound,
+                              chunk_size=wc.chunk, initial_state=gc["S0"], o=oc, final_state=Sc)
+
+            cstep()
+            torch.cuda.synchronize()
+            n_c = max(1, min(args.steps, 5))
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            for _ in range(n_c):
+                cstep()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cms = c0.elapsed_time(c1) / n_c
+            cbytes, cflops = chunk_bytes(wc), chunk_flops(wc, wc.chunk)
+            cgbs = cbytes / (cms * 1e-3) / 1e9
+            result["configs"][name] = {
+                "B": wc.B, "T": wc.T, "H": wc.H, "HV": wc.HV, "K": wc.K, "V": wc.V,
+                "chunk": wc.chunk, "gate": wc.gate, "initial_state": wc.s0_std > 0,
+                "value": wc.B * wc.T / (cms * 1e-3), "unit": "tokens/s", "ms_per_call": cms,
+                "calls": n_c,
+                "roofline": {"bound": "hbm", "achieved": cgbs, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": cgbs / HBM_PEAK_GBS, "traffic": None,
+                             "bytes_per_launch": cbytes, "kernel": "chunk_fwd_kernel<128, bf16>"},
+                "mfma": {"algorithmic_flops": cflops,
+                         "frac": cflops / (cms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}}
+            del gc, oc, Sc
 
     # One GPU's share of the long-context workload (one sequence, 8 value
     # heads): the fused chunk kernel against the three-stage split schedule.
