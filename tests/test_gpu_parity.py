@@ -175,6 +175,23 @@ def test_chunk_split_continuation_and_decode_handoff():
     assert L.rel_err(o, ro) <= L.TOL_BF16 and L.rel_err(S3, rS) <= L.TOL_BF16
 
 
+@pytest.mark.parametrize("K,dtype", [(128, "bf16"), (64, "f32")])
+def test_chunk_state_in_place(K, dtype):
+    """final_state may be the initial_state tensor itself: each workgroup reads
+    its columns of the state before any of them is written back."""
+    d = synth.random_inputs(2, 150, 2, 4, K, K, seed=14 + K, dtype=dtype, s0_std=0.3)
+    g = L.to_dev(d)
+    st = g["S0"].clone()
+    o, S = kda.chunk_fwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"],
+                         gate="standard", lower_bound=-5.0, chunk_size=64, initial_state=st,
+                         final_state=st)
+    torch.cuda.synchronize()
+    ro, rS = L.oracle_full(d, "standard", -5.0)
+    tol = L.TOL_F32 if dtype == "f32" else L.TOL_BF16
+    assert S.data_ptr() == st.data_ptr()
+    assert L.rel_err(o, ro) <= tol and L.rel_err(st, rS) <= tol
+
+
 def test_chunk_deterministic():
     d = synth.random_inputs(1, 300, 2, 4, 128, 128, seed=13, dtype="bf16", s0_std=0.05)
     a = L.run_chunk(d, "safe", -5.0, 64)
