@@ -49,6 +49,7 @@
 // a product takes 3 MFMAs (hi*hi + hi*lo + lo*hi) over the key axis, or 2 over
 // the 16-token axis, where one k = 32 instruction covers the hi and lo halves.
 // fp32 inputs use fp32 MFMA throughout.
+#include <atomic>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -856,12 +857,19 @@ static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   // workgroup per CU, so the B*HV*NVT workgroups spread over all CUs.
   size_t lds = sizeof(SM);
   if (lds < 84 * 1024) lds = 84 * 1024;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK, GS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // the dynamic LDS limit is raised once per device (several threads may
+  // race to do it; each call sets the same value)
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> configured[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool known = dev >= 0 && dev < kMaxDevices;
+  if (!known || !configured[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK, GS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    configured = true;
+    if (known) configured[dev].store(true, std::memory_order_release);
   }
   const int nheads = p.B * p.HV;
   const long blocks = (long)((nheads + 7) / 8) * 8 * NVT;
