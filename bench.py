@@ -186,6 +186,35 @@ def main():
                  "rocprof": measured_mfma("chunk") if args.workload == "prefill" else None},
         "wall_s_timed": t_wall,
     }
+    # The standalone gate entry point on the prefill workload's g_raw: the
+    # activation and the chunk-local cumulative log-decay (chunk 64), one
+    # read and one write of every element.
+    gout = torch.empty_like(g["g_raw"])
+
+    def gstep():
+        kda.gate(g["g_raw"], g["A_log"], g["dt_bias"], gate=w.gate, lower_bound=w.lower_bound,
+                 chunk_size=w.chunk, out=gout)
+
+    for _ in range(args.warmup):
+        gstep()
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(args.steps):
+        gstep()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    gms = a0.elapsed_time(a1) / args.steps
+    gbytes = 2 * g["g_raw"].numel() * 4
+    ggbs = gbytes / (gms * 1e-3) / 1e9
+    result["gate"] = {
+        "workload": w.name, "elements": g["g_raw"].numel(), "chunk": w.chunk, "gate": w.gate,
+        "ms_per_call": gms,
+        "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ggbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": gbytes,
+                     "kernel": "gate_cumsum_kernel"}}
+    del gout
+
     del o, S, g
 
     # The same chunked forward with one gate per (token, value head) (the
