@@ -345,8 +345,10 @@ struct ChainBF {
 
 // ----------------------------------------------------------------- chain operands
 // The chain operands of one chunk in LDS.  fp32: W [C][K+4], Kt^T [K][C+4];
-// bf16: hi and lo words of W [C][K+8] and Kt^T [K][C+8] (rows padded by 16
-// bytes); then gamma [K].
+// bf16: hi and lo words of W [C][K] and Kt^T [K][C], unpadded, with the
+// 16-byte chunk j of row r at chunk position j ^ (r mod chunks per row)
+// (see img_pos), so that the operand reads of 16 rows spread over the banks;
+// then gamma [K].
 template <int K, int C, bool BF>
 struct ChainOps;
 template <int K, int C>
@@ -358,13 +360,20 @@ struct alignas(16) ChainOps<K, C, false> {
 };
 template <int K, int C>
 struct alignas(16) ChainOps<K, C, true> {
-  static constexpr int LW = K + 8, LK = C + 8;
+  static constexpr int LW = K, LK = C;
   alignas(16) uint16_t wh[C * LW];
   alignas(16) uint16_t wl[C * LW];
   alignas(16) uint16_t kh[K * LK];
   alignas(16) uint16_t kl[K * LK];
   alignas(16) float gam[K];
 };
+
+// Element offset of 16-byte chunk j of row r in a bf16 image array of rows of
+// N elements (N / 8 chunks, a power of two).
+template <int N>
+__device__ __forceinline__ int img_pos(int r, int j) {
+  return r * N + 8 * (j ^ (r & (N / 8 - 1)));
+}
 
 // Bytes of one chunk's image in the workspace: the larger layout, rounded
 // up to whole 1 KiB copies (one wavefront-wide 16-byte load per lane).
@@ -491,8 +500,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
       split2_bf16(lo4.z, lo4.w, h.y, l.y);
       split2_bf16(hi4.x, hi4.y, h.z, l.z);
       split2_bf16(hi4.z, hi4.w, h.w, l.w);
-      *reinterpret_cast<uint4*>(img.wh + i * Ops::LW + 32 * q + 8 * g) = h;
-      *reinterpret_cast<uint4*>(img.wl + i * Ops::LW + 32 * q + 8 * g) = l;
+      *reinterpret_cast<uint4*>(img.wh + img_pos<Ops::LW>(i, 4 * q + g)) = h;
+      *reinterpret_cast<uint4*>(img.wl + img_pos<Ops::LW>(i, 4 * q + g)) = l;
     }
     // Kt^T rows (key channels): token slices permuted the same way
     for (int e = tid; e < K * (C / 8); e += kSplitThreads) {
@@ -510,8 +519,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
       split2_bf16(v[2], v[3], h.y, l.y);
       split2_bf16(v[4], v[5], h.z, l.z);
       split2_bf16(v[6], v[7], h.w, l.w);
-      *reinterpret_cast<uint4*>(img.kh + kap * Ops::LK + 32 * q + 8 * g) = h;
-      *reinterpret_cast<uint4*>(img.kl + kap * Ops::LK + 32 * q + 8 * g) = l;
+      *reinterpret_cast<uint4*>(img.kh + img_pos<Ops::LK>(kap, 4 * q + g)) = h;
+      *reinterpret_cast<uint4*>(img.kl + img_pos<Ops::LK>(kap, 4 * q + g)) = l;
     }
   } else {
     for (int e = tid; e < C * (K / 4); e += kSplitThreads) {
@@ -681,9 +690,9 @@ __global__ __launch_bounds__(64 * (1 + kCopiers)) void split_state_kernel(SplitP
       split8(s[2 * q], s[2 * q + 1], bh_, bl_);
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
-        const int row = (I * 16 + (lane & 15)) * Ops::LW + 32 * q + 8 * g4;
-        ah[I] = *reinterpret_cast<const bf16x8*>(wh + row);
-        al[I] = *reinterpret_cast<const bf16x8*>(wl + row);
+        const int pos = img_pos<Ops::LW>(I * 16 + (lane & 15), 4 * q + g4);
+        ah[I] = *reinterpret_cast<const bf16x8*>(wh + pos);
+        al[I] = *reinterpret_cast<const bf16x8*>(wl + pos);
       }
 #pragma unroll
       for (int I = 0; I < NB; ++I) x[I] = mfma32(ah[I], bh_, x[I]);
@@ -771,9 +780,9 @@ __global__ __launch_bounds__(64 * (1 + kCopiers)) void split_state_kernel(SplitP
           bf16x8 ah[RPQ], al[RPQ];
 #pragma unroll
           for (int rr = 0; rr < RPQ; ++rr) {
-            const int row = ((q * RPQ + rr) * 16 + (lane & 15)) * Ops::LK + 32 * t + 8 * g4;
-            ah[rr] = *reinterpret_cast<const bf16x8*>(kh + row);
-            al[rr] = *reinterpret_cast<const bf16x8*>(kl + row);
+            const int pos = img_pos<Ops::LK>((q * RPQ + rr) * 16 + (lane & 15), 4 * t + g4);
+            ah[rr] = *reinterpret_cast<const bf16x8*>(kh + pos);
+            al[rr] = *reinterpret_cast<const bf16x8*>(kl + pos);
           }
 #pragma unroll
           for (int rr = 0; rr < RPQ; ++rr) s[q * RPQ + rr] = mfma32(ah[rr], uh[t], s[q * RPQ + rr]);
