@@ -37,7 +37,10 @@
  *  - All tensor pointers are DEVICE pointers to contiguous row-major memory
  *    with the shapes given below, aligned to 16 bytes (4 bytes suffice for
  *    g_raw and dt_bias with KDA_GATE_PER_HEAD).  The caller owns every
- *    buffer; the library allocates nothing and keeps no global state.
+ *    buffer; the library allocates nothing.  Its only global state is a
+ *    per-device flag recording that the chunk kernel's LDS limit was raised
+ *    (set once, thread-safely); every entry point may be called from several
+ *    host threads and streams.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
  *    default stream).  Nothing synchronises the host.  Input buffers must stay
  *    valid, and outputs unread, until the stream reaches the enqueued work.
