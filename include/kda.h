@@ -122,9 +122,10 @@ kda_status kda_gate(const float* g_raw, const float* A_log, const float* dt_bias
  *                 beyond rounding)
  *   workspace     device scratch of kda_chunk_fwd_workspace_bytes(...) bytes, or
  *                 NULL when that size is 0
- * Supported head sizes: K == V in {16, 32, 64, 128}; HV % H == 0.  T may be any
- * length >= 0 (a ragged last chunk is handled in-kernel); T == 0 copies the
- * initial state (or zeros) to final_state.
+ * Supported head sizes: K == V in {16, 32, 64, 128}; HV % H == 0; HV * K <=
+ * 2^24 (KDA_ERR_UNSUPPORTED beyond; the kernel addresses 16 tokens of one
+ * tensor with 32-bit offsets).  T may be any length >= 0 (a ragged last chunk is
+ * handled in-kernel); T == 0 copies the initial state (or zeros) to final_state.
  * Arithmetic: fp32 inputs run fp32 matrix products; bf16 inputs run bf16 MFMA
  * products with fp32 accumulation and split (hi + lo) operands where precision
  * needs them; the state is fp32 throughout.

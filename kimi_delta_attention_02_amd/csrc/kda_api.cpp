@@ -114,6 +114,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, kda_dtype 
   if ((long)B * HV > (1L << 28)) return KDA_ERR_INVALID_ARG;
   if (!head_size_ok(K) || V != K) return KDA_ERR_UNSUPPORTED;
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+  // 16 tokens of g_raw (the widest per-token row) must span less than 2^31 bytes
+  if ((long)HV * K > (1L << 24)) return KDA_ERR_UNSUPPORTED;
   // empty tensors may come with null data pointers: required only when there are tokens
   if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, initial_state, final_state};

@@ -350,6 +350,24 @@ __device__ __forceinline__ void tprod(f32x4& acc, const TokOp<F32, RA>& A, int a
     mma_tok_bf16(acc, A.c + arow0 * kCat, B.c, lane);
 }
 
+// raw buffer loads of four q / k elements and of a thread's v values
+template <typename T>
+__device__ __forceinline__ typename In<T>::Raw4 buffer_load_raw4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (std::is_same<T, float>::value)
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+template <typename VR>
+__device__ __forceinline__ VR buffer_load_v(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(VR) == 2)
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  else if constexpr (sizeof(VR) == 4)
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  else
+    return __builtin_bit_cast(VR, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // ----------------------------------------------------------------- kernel
 
 // GS: per-head gate (g_raw [B, T, HV], dt_bias [HV]), one decay shared by all
@@ -400,7 +418,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     typedef typename std::conditional<VPT * sizeof(T) == 2, uint16_t,
             typename std::conditional<VPT * sizeof(T) == 4, uint32_t, uint2>::type>::type VRaw;
     const int vtt = tid / (BV / VPT), vc = (tid % (BV / VPT)) * VPT;
-    VRaw pvv;
     const int tp = tid & 7, c0 = (tid >> 3) * 4;
     float bias4[4] = {0.f, 0.f, 0.f, 0.f};
     if (bias && prep_thread) {
@@ -410,43 +427,78 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     const GateConsts gc = gate_consts(rate, p.lower_bound);
   #pragma unroll
     for (int c = 0; c < 4; ++c) bias4[c] = gate_bias_pre<GK>(bias4[c], gc);
-    float4 pg[2];
-    Raw4 pq[2], pk[2];
-    // Per-thread row-0 pointers of this sequence; token t adds t times the row stride.
-    const float* g_base = p.g_raw + (b * T_ * HV + hv) * (long)GKD + (GS ? 0 : c0);
-    const T* q_base = qg + (b * T_ * H + h) * (long)K + c0;
-    const T* k_base = kg + (b * T_ * H + h) * (long)K + c0;
-    const T* v_base = vg + (b * T_ * HV + hv) * (long)V + v0 + vc;
-    const float* beta_base = p.beta + b * T_ * HV + hv;
-    // Loads past the end of the sequence read the last token instead (always a
-    // valid address) and are replaced by padding values where they are used.
-    auto fetch = [&](int blk) {
-      const int tb = blk * kTok;
-      if (prep_thread) {
+    // One block's inputs as loaded.  Two sets alternate between the steps of
+    // the loop below (unrolled by two), so the loads of block n + 1 land in
+    // the set not being read for block n and nothing is copied between them.
+    struct PrepIn {
+      float4 g[2];
+      Raw4 q[2], k[2];
+      VRaw v;
+      float beta;
+    };
+    // Token rows of this sequence and head; a block's rows sit at fixed
+    // per-thread byte offsets from a block base that is uniform over the
+    // workgroup, so a full block's loads need no per-step address arithmetic.
+    const long gs = (long)HV * GKD, qs = (long)H * K, vs = (long)HV * V;
+    const float* g_seq = p.g_raw + (b * T_ * HV + hv) * (long)GKD;
+    const T* q_seq = qg + (b * T_ * H + h) * (long)K;
+    const T* k_seq = kg + (b * T_ * H + h) * (long)K;
+    const T* v_seq = vg + (b * T_ * HV + hv) * (long)V + v0;
+    const float* beta_seq = p.beta + b * T_ * HV + hv;
+    // threads without a row (K < 128) take an offset beyond every range, so
+    // their loads return zero without touching memory
+    constexpr uint32_t kNoRow = 0x80000000u;
+    uint32_t og[2], oq[2];
   #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const long t = min(tb + 2 * tp + j, T_ - 1);
-          if constexpr (GS) {
-            const float x = g_base[t * HV];
-            pg[j] = float4{x, x, x, x};
-          } else {
-            pg[j] = *reinterpret_cast<const float4*>(g_base + t * (HV * K));
-          }
-          pq[j] = In<T>::raw4(q_base, t * (H * K));
-          pk[j] = In<T>::raw4(k_base, t * (H * K));
-        }
-      }
-    };
-    float pbeta = 0.0f;
-    auto fetch_v = [&](int blk) {
-      pvv = *reinterpret_cast<const VRaw*>(v_base + (long)min(blk * kTok + vtt, T_ - 1) * (HV * V));
-      if (tid < kTok) pbeta = beta_base[(long)min(blk * kTok + tid, T_ - 1) * HV];
-    };
-    if (NT > 0) {
-      fetch(0);
-      fetch_v(0);
+    for (int j = 0; j < 2; ++j) {
+      og[j] = prep_thread ? (uint32_t)(((2 * tp + j) * gs + (GS ? 0 : c0)) * sizeof(float)) : kNoRow;
+      oq[j] = prep_thread ? (uint32_t)(((2 * tp + j) * qs + c0) * sizeof(T)) : kNoRow;
     }
-    for (int it = 0; it < NT + 3; ++it) {
+    const uint32_t ov = (uint32_t)((vtt * vs + vc) * sizeof(T));
+    // threads 16 and up repeat the beta of tokens 0..15
+    const uint32_t ob = (uint32_t)((tid & (kTok - 1)) * HV * sizeof(float));
+    // A block's rows are read as raw buffer loads: a descriptor on the block
+    // base (scalar registers, formed per step) plus each thread's fixed 32-bit
+    // byte offset, so no address is formed in vector registers.  The
+    // descriptor's range ends at the sequence's last token, so rows past the
+    // end of a ragged last block read as zero (and are replaced by padding
+    // values where they are used).  Every load is unconditional: results
+    // merged from two paths would be copied, and each copy waits for every
+    // load in flight, the next block's included.
+    auto rsrc = [](const void* base, uint32_t bytes) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                               0x00020000);
+    };
+    auto fetch = [&](int blk, PrepIn& in) {
+      // a block past the end gets an empty range: its loads touch no memory
+      // (the clamp is read back as a scalar: the descriptor must be uniform)
+      const int rows_i = __builtin_amdgcn_readfirstlane(max(0, min(kTok, T_ - blk * kTok)));
+      const int tb = rows_i > 0 ? blk * kTok : 0;
+      const uint32_t rows = (uint32_t)rows_i;
+      const auto rg = rsrc(g_seq + tb * gs, rows * (uint32_t)(gs * sizeof(float)));
+      const auto rq = rsrc(q_seq + tb * qs, rows * (uint32_t)(qs * sizeof(T)));
+      const auto rk = rsrc(k_seq + tb * qs, rows * (uint32_t)(qs * sizeof(T)));
+      const auto rv = rsrc(v_seq + tb * vs, rows * (uint32_t)(vs * sizeof(T)));
+      const auto rb = rsrc(beta_seq + (long)tb * HV, rows * (uint32_t)(HV * sizeof(float)));
+  #pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (GS) {
+          const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, og[j], 0, 0));
+          in.g[j] = float4{x, x, x, x};
+        } else {
+          in.g[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, og[j], 0, 0));
+        }
+        in.q[j] = buffer_load_raw4<T>(rq, oq[j]);
+        in.k[j] = buffer_load_raw4<T>(rk, oq[j]);
+      }
+      in.v = buffer_load_v<VRaw>(rv, ov);
+      in.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, ob, 0, 0));
+    };
+    PrepIn in0, in1;
+    fetch(0, in0);
+    // one pipeline step: prep of block it from `cur`, loads of block it + 1 into `nxt`
+    auto step = [&](int it, const PrepIn& cur, PrepIn& nxt) {
+      fetch(it + 1, nxt);  // the next block's inputs travel during this step
       if (it < NT) {
         Ops& B = sm.blk[it % 3];
         bool overflow = false;
@@ -454,9 +506,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
         auto prep_block = [&](auto full) {
           constexpr bool kFull = decltype(full)::value;
           const int t0 = it * kTok;
-          const float4 g_in[2] = {pg[0], pg[1]};
-          const Raw4 q_in[2] = {pq[0], pq[1]}, k_in[2] = {pk[0], pk[1]};
-          if (it + 1 < NT) fetch(it + 1);  // the next block's inputs travel during this step
+          const float4* g_in = cur.g;
+          const Raw4 *q_in = cur.q, *k_in = cur.k;
           constexpr int NCH = GS ? 1 : 4;  // distinct decays among the four channels
           float al[2][4], qv[2][4], kv[2][4];
   #pragma unroll
@@ -538,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           for (int c = 0; c < 4; ++c) put_tok2(B.keT, c0 + c, 2 * tp, ke[0][c], ke[1][c]);
         };
         {  // v tile, transposed for the chain waves (padding rows: 0)
-          const VRaw x = it * kTok + vtt < T_ ? pvv : VRaw{};
+          const VRaw x = it * kTok + vtt < T_ ? cur.v : VRaw{};
           if constexpr (F32 && VPT == 1) {
             B.vT[vc][vtt] = __uint_as_float(x);
           } else if constexpr (F32) {
@@ -550,8 +601,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             B.vT[vc][vtt] = (uint16_t)(x & 0xffffu);
             B.vT[vc + 1][vtt] = (uint16_t)(x >> 16);
           }
-          if (tid < kTok) B.beta[tid] = it * kTok + tid < T_ ? pbeta : 0.0f;
-          if (it + 1 < NT) fetch_v(it + 1);
+          if (tid < kTok) B.beta[tid] = it * kTok + tid < T_ ? cur.beta : 0.0f;
         }
         if (prep_thread) {
           if ((it + 1) * kTok <= T_) prep_block(std::true_type{});
@@ -561,7 +611,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
         if (lane == 0) B.flag[w] = ov ? 1 : 0;
       }
       __syncthreads();
+    };
+    int it = 0;
+    for (; it + 1 < NT + 3; it += 2) {
+      step(it, in0, in1);
+      step(it + 1, in1, in0);
     }
+    if (it < NT + 3) step(it, in0, in1);
   } else if (w == kAqkWave || w == kInvWave) {
     // bf16 inputs: the A wave also forms the outputs, one step behind the
     // chain: O = s Q_hat S + A U for the block whose U the chain produced last
