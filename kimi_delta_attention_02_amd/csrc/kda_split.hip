@@ -96,6 +96,11 @@ struct alignas(16) ChunkRows {
   alignas(16) float x[C * LD];   // q rows (output pass) or v rows (intra pass)
   alignas(16) float beta[C];
   alignas(16) float graw[C];     // per-head gate inputs
+  // whole sub-block sums of G2 per channel, each added in increasing
+  // sub-block order: pre[J][c] over sub-blocks 0 .. J-1 (J = 0 .. C/16),
+  // suf[J][c] over sub-blocks J+1 .. C/16-1
+  alignas(16) float pre[(C / 16 + 1) * K];
+  alignas(16) float suf[(C / 16) * K];
   int steep[C / 16];             // sub-block whose decay leaves [2^-100, 2^100] in some channel
 };
 
@@ -165,8 +170,8 @@ __device__ __forceinline__ void chunk_issue(const SplitParams& p, long ch, bool 
   }
 }
 
-// Chunk ch into L from the registers: G2 (see ChunkRows), k, and q or v
-// widened to fp32, beta.  Tokens at or past T read as g = 0, k = q = v = 0,
+// Chunk ch into L from the registers: G2 (see ChunkRows) and its sub-block
+// sum tables, k, and q or v widened to fp32, beta.  Tokens at or past T read as g = 0, k = q = v = 0,
 // beta = 0, which leave the state unchanged.  Ends with a barrier.
 template <int K, int C, typename T>
 __device__ void chunk_store(const SplitParams& p, long ch, const ChunkRegs<K, C, T>& R,
@@ -221,6 +226,14 @@ __device__ void chunk_store(const SplitParams& p, long ch, const ChunkRegs<K, C,
       L.G2[i * LD + kap] = run;
     }
     if (steep) L.steep[J] = 1;  // every writer stores 1
+  }
+  __syncthreads();
+  for (int kap = tid; kap < K; kap += kSplitThreads) {
+    L.pre[kap] = 0.0f;
+    for (int J = 0; J < NB; ++J) {
+      L.pre[(J + 1) * K + kap] = blocks_log2(L, 0, J + 1, kap);
+      L.suf[J * K + kap] = blocks_log2(L, J + 1, NB, kap);
+    }
   }
   __syncthreads();
 }
@@ -437,7 +450,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
         const bool isw = cb < K / 16;
         const int col = (isw ? cb : cb - K / 16) * 16 + (lane & 15);
         float pre = 0.0f;
-        if (isw) pre = blocks_log2(L, 0, I, col);
+        if (isw) pre = L.pre[I * K + col];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = I * 16 + 4 * g4 + r;
@@ -511,7 +524,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
       for (int m = 0; m < 8; ++m) {
         const int i = 32 * q + 4 * g + (m & 3) + 16 * (m >> 2);
         const int I = i >> 4;
-        const float rest = (L.G2[(I * 16 + 15) * LD + kap] - L.G2[i * LD + kap]) + blocks_log2(L, I + 1, NB, kap);
+        const float rest = (L.G2[(I * 16 + 15) * LD + kap] - L.G2[i * LD + kap]) + L.suf[I * K + kap];
         v[m] = L.k[i * LD + kap] * __builtin_amdgcn_exp2f(rest);
       }
       uint4 h, l;
@@ -533,14 +546,14 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int i = i0 + m, I = i >> 4;
-        const float rest = (L.G2[(I * 16 + 15) * LD + kap] - L.G2[i * LD + kap]) + blocks_log2(L, I + 1, NB, kap);
+        const float rest = (L.G2[(I * 16 + 15) * LD + kap] - L.G2[i * LD + kap]) + L.suf[I * K + kap];
         v[m] = L.k[i * LD + kap] * __builtin_amdgcn_exp2f(rest);
       }
       *reinterpret_cast<float4*>(img.kt + kap * Ops::LK + i0) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
   for (int kap = tid; kap < K; kap += kSplitThreads)
-    img.gam[kap] = __builtin_amdgcn_exp2f(blocks_log2(L, 0, NB, kap));
+    img.gam[kap] = __builtin_amdgcn_exp2f(L.pre[NB * K + kap]);
   __syncthreads();  // LDS is refilled by the next chunk
   }
 }
@@ -846,7 +859,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
   // Q <- s q exp(G)
   for (int e = tid; e < C * K; e += kSplitThreads) {
     const int i = e / K, kap = e % K;
-    Q[i * LD + kap] *= scale * __builtin_amdgcn_exp2f(L.G2[i * LD + kap] + blocks_log2(L, 0, i >> 4, kap));
+    Q[i * LD + kap] *= scale * __builtin_amdgcn_exp2f(L.G2[i * LD + kap] + L.pre[(i >> 4) * K + kap]);
   }
   __syncthreads();
 
