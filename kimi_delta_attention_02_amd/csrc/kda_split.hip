@@ -573,6 +573,24 @@ __device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo)
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 16x16x16 bf16 MFMA: its B operand layout (lane l holds k = 4 (l/16) .. +3 of
+// column l % 16) is the accumulator layout of a 16 x 16 fragment
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// hi and lo words of four values as bf16x4 operands
+__device__ __forceinline__ void split4(float a0, float a1, float a2, float a3, bf16x4& hi,
+                                       bf16x4& lo) {
+  uint2 h, l;
+  split2_bf16(a0, a1, h.x, l.x);
+  split2_bf16(a2, a3, h.y, l.y);
+  hi = __builtin_bit_cast(bf16x4, h);
+  lo = __builtin_bit_cast(bf16x4, l);
+}
+
 // u of chunk index ch, column block cb: the lane's fragments
 template <int K, int C>
 __device__ __forceinline__ void fetch_u(const SplitParams& p, long ch, f32x4 (&un)[C / 16], int cb,
@@ -839,6 +857,8 @@ __global__ __launch_bounds__(64 * (1 + kCopiers)) void split_state_kernel(SplitP
 template <int K, int C, typename T>
 __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams p) {
   constexpr int NB = C / 16, LD = ChunkRows<K, C>::LD, LR = C + 4;
+  // bf16 inputs run the products on hi/lo bf16 MFMA (key slices of 32)
+  constexpr bool OBF = std::is_same<T, uint16_t>::value && K >= 32;
   __shared__ ChunkRows<K, C> L;
   __shared__ alignas(16) float A[C * LR];
   float* Q = L.x;
@@ -856,19 +876,46 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
   // A = s times the lower (diagonal included) decayed q k^T
   decayed_lower<K, C, false>(L, Q, tid, [&](int i, int j, float v) { A[i * LR + j] = scale * v; });
   __syncthreads();
-  // Q <- s q exp(G)
-  for (int e = tid; e < C * K; e += kSplitThreads) {
-    const int i = e / K, kap = e % K;
-    Q[i * LD + kap] *= scale * __builtin_amdgcn_exp2f(L.G2[i * LD + kap] + L.pre[(i >> 4) * K + kap]);
+  // Q = s q exp(G).  bf16 inputs: as hi and lo bf16 rows in the space of the k
+  // rows (free once A is formed), the keys of each 32-wide slice at the
+  // positions slice_pos gives them and the 16-byte chunks placed by img_pos,
+  // so that the fragments of h_c serve as B operands as they are loaded.
+  uint16_t* qh = reinterpret_cast<uint16_t*>(L.k);
+  uint16_t* ql = qh + C * K;
+  if constexpr (OBF) {
+    for (int e = tid; e < C * (K / 8); e += kSplitThreads) {
+      const int i = e / (K / 8), q = (e % (K / 8)) >> 2, g = e & 3;
+      float v[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int kap = 32 * q + 4 * g + (m & 3) + 16 * (m >> 2);
+        v[m] = Q[i * LD + kap] * scale *
+               __builtin_amdgcn_exp2f(L.G2[i * LD + kap] + L.pre[(i >> 4) * K + kap]);
+      }
+      uint4 h, l;
+      split2_bf16(v[0], v[1], h.x, l.x);
+      split2_bf16(v[2], v[3], h.y, l.y);
+      split2_bf16(v[4], v[5], h.z, l.z);
+      split2_bf16(v[6], v[7], h.w, l.w);
+      *reinterpret_cast<uint4*>(qh + img_pos<K>(i, 4 * q + g)) = h;
+      *reinterpret_cast<uint4*>(ql + img_pos<K>(i, 4 * q + g)) = l;
+    }
+  } else {
+    for (int e = tid; e < C * K; e += kSplitThreads) {
+      const int i = e / K, kap = e % K;
+      Q[i * LD + kap] *= scale * __builtin_amdgcn_exp2f(L.G2[i * LD + kap] + L.pre[(i >> 4) * K + kap]);
+    }
   }
   __syncthreads();
 
   const int hv = (int)(bh % p.HV);
   const long b = bh / p.HV;
   const int t0 = c * C;
+  // one column block per wavefront (K / 16 <= 8 wavefronts)
   constexpr int NKB = K / 16;
-  for (int cb = w; cb < NKB; cb += kSplitThreads / 64) {
-    const int col = cb * 16 + (lane & 15);
+  static_assert(NKB <= kSplitThreads / 64, "one column block per wavefront");
+  if (w < NKB) {
+    const int col = w * 16 + (lane & 15);
     // h_c as B operand fragments: lane holds keys 16 kb + 4 (l / 16) + r
     f32x4 hf[NKB];
     if (p.h_plain) {
@@ -880,37 +927,78 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
     } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        hf[kb] = *reinterpret_cast<const f32x4*>(p.h + frag_index(ch, NKB, NKB, cb, kb, lane));
+        hf[kb] = *reinterpret_cast<const f32x4*>(p.h + frag_index(ch, NKB, NKB, w, kb, lane));
     }
     f32x4 uf[NB];
 #pragma unroll
     for (int J = 0; J < NB; ++J)
-      uf[J] = *reinterpret_cast<const f32x4*>(p.u + frag_index(ch, NKB, NB, cb, J, lane));
+      uf[J] = *reinterpret_cast<const f32x4*>(p.u + frag_index(ch, NKB, NB, w, J, lane));
+    if constexpr (OBF) {
+      // hi/lo products: (A_hi + A_lo)(B_hi + B_lo) without the lo*lo term.
+      // Slice s of h_c: positions 8 (l/16) .. +7 of lane l are keys
+      // 32 s + 4 (l/16) + 0..3 and 32 s + 16 + 4 (l/16) + 0..3, i.e. the
+      // fragments 2s and 2s+1 as loaded.
+      bf16x8 hh[NKB / 2], hl[NKB / 2];
+#pragma unroll
+      for (int q = 0; q < NKB / 2; ++q) split8(hf[2 * q], hf[2 * q + 1], hh[q], hl[q]);
+      bf16x4 uh[NB], ul[NB];
+#pragma unroll
+      for (int J = 0; J < NB; ++J) split4(uf[J][0], uf[J][1], uf[J][2], uf[J][3], uh[J], ul[J]);
 #pragma unroll 1
-    for (int I = 0; I < NB; ++I) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const float* qrow = Q + (I * 16 + (lane & 15)) * LD + 4 * g4;
+      for (int I = 0; I < NB; ++I) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int row = I * 16 + (lane & 15);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float4 a = *reinterpret_cast<const float4*>(qrow + kb * 16);
-        acc = mfma4(a.x, hf[kb][0], acc);
-        acc = mfma4(a.y, hf[kb][1], acc);
-        acc = mfma4(a.z, hf[kb][2], acc);
-        acc = mfma4(a.w, hf[kb][3], acc);
+        for (int q = 0; q < NKB / 2; ++q) {
+          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(qh + img_pos<K>(row, 4 * q + g4));
+          const bf16x8 al = *reinterpret_cast<const bf16x8*>(ql + img_pos<K>(row, 4 * q + g4));
+          acc = mfma32(ah, hh[q], acc);
+          acc = mfma32(ah, hl[q], acc);
+          acc = mfma32(al, hh[q], acc);
+        }
+#pragma unroll
+        for (int J = 0; J < NB; ++J) {
+          if (J > I) break;
+          const float4 a = *reinterpret_cast<const float4*>(A + row * LR + J * 16 + 4 * g4);
+          bf16x4 ah, al;
+          split4(a.x, a.y, a.z, a.w, ah, al);
+          acc = mfma16(ah, uh[J], acc);
+          acc = mfma16(ah, ul[J], acc);
+          acc = mfma16(al, uh[J], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + I * 16 + 4 * g4 + r;
+          if (t < p.T) p.o[((b * p.T + t) * p.HV + hv) * (long)K + col] = acc[r];
+        }
       }
+    } else {
+#pragma unroll 1
+      for (int I = 0; I < NB; ++I) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float* qrow = Q + (I * 16 + (lane & 15)) * LD + 4 * g4;
 #pragma unroll
-      for (int J = 0; J < NB; ++J) {
-        if (J > I) break;
-        const float4 a = *reinterpret_cast<const float4*>(A + (I * 16 + (lane & 15)) * LR + J * 16 + 4 * g4);
-        acc = mfma4(a.x, uf[J][0], acc);
-        acc = mfma4(a.y, uf[J][1], acc);
-        acc = mfma4(a.z, uf[J][2], acc);
-        acc = mfma4(a.w, uf[J][3], acc);
-      }
+        for (int kb = 0; kb < NKB; ++kb) {
+          const float4 a = *reinterpret_cast<const float4*>(qrow + kb * 16);
+          acc = mfma4(a.x, hf[kb][0], acc);
+          acc = mfma4(a.y, hf[kb][1], acc);
+          acc = mfma4(a.z, hf[kb][2], acc);
+          acc = mfma4(a.w, hf[kb][3], acc);
+        }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + I * 16 + 4 * g4 + r;
-        if (t < p.T) p.o[((b * p.T + t) * p.HV + hv) * (long)K + col] = acc[r];
+        for (int J = 0; J < NB; ++J) {
+          if (J > I) break;
+          const float4 a = *reinterpret_cast<const float4*>(A + (I * 16 + (lane & 15)) * LR + J * 16 + 4 * g4);
+          acc = mfma4(a.x, uf[J][0], acc);
+          acc = mfma4(a.y, uf[J][1], acc);
+          acc = mfma4(a.z, uf[J][2], acc);
+          acc = mfma4(a.w, uf[J][3], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + I * 16 + 4 * g4 + r;
+          if (t < p.T) p.o[((b * p.T + t) * p.HV + hv) * (long)K + col] = acc[r];
+        }
       }
     }
   }
