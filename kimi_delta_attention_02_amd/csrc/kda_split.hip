@@ -311,11 +311,68 @@ __device__ __forceinline__ f32x4 decayed_block(const ChunkRows<K, C>& L, const f
   return acc;
 }
 
+// The same block on hi/lo bf16 MFMA (16x16x32, three products per slice of
+// 32 keys, the lo*lo term dropped): lane group g takes keys 32 s + 8 g .. +7 of
+// both rows.  The decay factors are split exactly as above; bf16 keeps fp32's
+// exponent range, so the 2^100 bound of the diagonal split still holds.
+template <int K, int C>
+__device__ __forceinline__ f32x4 decayed_block_bf16(const ChunkRows<K, C>& L, const float* arows,
+                                                    int I, int J, int lane) {
+  constexpr int LD = ChunkRows<K, C>::LD;
+  const int ai = I * 16 + (lane & 15), bj = J * 16 + (lane & 15), je = J * 16 + 15;
+  const int c0 = 8 * (lane >> 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int s = 0; s < K / 32; ++s) {
+    float av[8], bv[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 32 * s + c0 + 4 * h;
+      const float4 a4 = *reinterpret_cast<const float4*>(arows + ai * LD + c);
+      const float4 b4 = *reinterpret_cast<const float4*>(L.k + bj * LD + c);
+      const float4 gi = *reinterpret_cast<const float4*>(L.G2 + ai * LD + c);
+      const float4 gj = *reinterpret_cast<const float4*>(L.G2 + bj * LD + c);
+      float4 ea = gi, eb = make_float4(-gj.x, -gj.y, -gj.z, -gj.w);
+      if (I > J) {
+        const float4 ge = *reinterpret_cast<const float4*>(L.G2 + je * LD + c);
+        eb = make_float4(ge.x - gj.x, ge.y - gj.y, ge.z - gj.z, ge.w - gj.w);
+        for (int M = J + 1; M < I; ++M) {  // whole sub-blocks between J and I
+          const float4 gm = *reinterpret_cast<const float4*>(L.G2 + (M * 16 + 15) * LD + c);
+          ea = make_float4(ea.x + gm.x, ea.y + gm.y, ea.z + gm.z, ea.w + gm.w);
+        }
+      }
+      av[4 * h + 0] = a4.x * __builtin_amdgcn_exp2f(ea.x);
+      av[4 * h + 1] = a4.y * __builtin_amdgcn_exp2f(ea.y);
+      av[4 * h + 2] = a4.z * __builtin_amdgcn_exp2f(ea.z);
+      av[4 * h + 3] = a4.w * __builtin_amdgcn_exp2f(ea.w);
+      bv[4 * h + 0] = b4.x * __builtin_amdgcn_exp2f(eb.x);
+      bv[4 * h + 1] = b4.y * __builtin_amdgcn_exp2f(eb.y);
+      bv[4 * h + 2] = b4.z * __builtin_amdgcn_exp2f(eb.z);
+      bv[4 * h + 3] = b4.w * __builtin_amdgcn_exp2f(eb.w);
+    }
+    uint4 ah, al, bh, bl;
+    split2_bf16(av[0], av[1], ah.x, al.x);
+    split2_bf16(av[2], av[3], ah.y, al.y);
+    split2_bf16(av[4], av[5], ah.z, al.z);
+    split2_bf16(av[6], av[7], ah.w, al.w);
+    split2_bf16(bv[0], bv[1], bh.x, bl.x);
+    split2_bf16(bv[2], bv[3], bh.y, bl.y);
+    split2_bf16(bv[4], bv[5], bh.z, bl.z);
+    split2_bf16(bv[6], bv[7], bh.w, bl.w);
+    const bf16x8 a_h = __builtin_bit_cast(bf16x8, ah), a_l = __builtin_bit_cast(bf16x8, al);
+    const bf16x8 b_h = __builtin_bit_cast(bf16x8, bh), b_l = __builtin_bit_cast(bf16x8, bl);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_h, b_h, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_h, b_l, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_l, b_h, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // Every block (I, J), J <= I, of the chunk's decayed product: MFMA blocks,
 // with the diagonal blocks of steep sub-blocks summed directly.  out(i, j, v)
 // receives each value with j <= i (strict: j < i); the rest of the diagonal
 // blocks gets 0.
-template <int K, int C, bool STRICT, class Out>
+template <int K, int C, bool STRICT, bool BF, class Out>
 __device__ __forceinline__ void decayed_lower(const ChunkRows<K, C>& L, const float* arows, int tid,
                                               Out out) {
   constexpr int NB = C / 16, NP = NB * (NB + 1) / 2, NW = kSplitThreads / 64;
@@ -324,7 +381,9 @@ __device__ __forceinline__ void decayed_lower(const ChunkRows<K, C>& L, const fl
     int I, J;
     tri_pair(pi, false, I, J);
     if (I == J && L.steep[J]) continue;
-    const f32x4 acc = decayed_block<K, C>(L, arows, I, J, lane);
+    f32x4 acc;
+    if constexpr (BF) acc = decayed_block_bf16<K, C>(L, arows, I, J, lane);
+    else acc = decayed_block<K, C>(L, arows, I, J, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = I * 16 + 4 * g4 + r, j = J * 16 + (lane & 15);
@@ -414,7 +473,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_intra_kernel(SplitParams 
   if (ch + gridDim.x < nch) chunk_issue<K, C, T>(p, ch + gridDim.x, false, cr);  // lands during this chunk
 
   // R = diag(beta) times the strictly lower decayed k k^T
-  decayed_lower<K, C, true>(L, L.k, tid, [&](int i, int j, float v) { R[i * LR + j] = L.beta[i] * v; });
+  decayed_lower<K, C, true, std::is_same<T, uint16_t>::value && K >= 32>(
+      L, L.k, tid, [&](int i, int j, float v) { R[i * LR + j] = L.beta[i] * v; });
   __syncthreads();
 
   // (I + R_JJ)^{-1} of each diagonal 16 x 16 block: lane j of group J
@@ -571,24 +631,6 @@ __device__ __forceinline__ void split8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo)
   split2_bf16(b[2], b[3], h.w, l.w);
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, l);
-}
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// 16x16x16 bf16 MFMA: its B operand layout (lane l holds k = 4 (l/16) .. +3 of
-// column l % 16) is the accumulator layout of a 16 x 16 fragment
-__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-// hi and lo words of four values as bf16x4 operands
-__device__ __forceinline__ void split4(float a0, float a1, float a2, float a3, bf16x4& hi,
-                                       bf16x4& lo) {
-  uint2 h, l;
-  split2_bf16(a0, a1, h.x, l.x);
-  split2_bf16(a2, a3, h.y, l.y);
-  hi = __builtin_bit_cast(bf16x4, h);
-  lo = __builtin_bit_cast(bf16x4, l);
 }
 
 // u of chunk index ch, column block cb: the lane's fragments
@@ -857,8 +899,6 @@ __global__ __launch_bounds__(64 * (1 + kCopiers)) void split_state_kernel(SplitP
 template <int K, int C, typename T>
 __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams p) {
   constexpr int NB = C / 16, LD = ChunkRows<K, C>::LD, LR = C + 4;
-  // bf16 inputs run the products on hi/lo bf16 MFMA (key slices of 32)
-  constexpr bool OBF = std::is_same<T, uint16_t>::value && K >= 32;
   __shared__ ChunkRows<K, C> L;
   __shared__ alignas(16) float A[C * LR];
   float* Q = L.x;
@@ -874,48 +914,22 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
   if (ch + gridDim.x < nch) chunk_issue<K, C, T>(p, ch + gridDim.x, true, cr);  // lands during this chunk
 
   // A = s times the lower (diagonal included) decayed q k^T
-  decayed_lower<K, C, false>(L, Q, tid, [&](int i, int j, float v) { A[i * LR + j] = scale * v; });
+  decayed_lower<K, C, false, std::is_same<T, uint16_t>::value && K >= 32>(
+      L, Q, tid, [&](int i, int j, float v) { A[i * LR + j] = scale * v; });
   __syncthreads();
-  // Q = s q exp(G).  bf16 inputs: as hi and lo bf16 rows in the space of the k
-  // rows (free once A is formed), the keys of each 32-wide slice at the
-  // positions slice_pos gives them and the 16-byte chunks placed by img_pos,
-  // so that the fragments of h_c serve as B operands as they are loaded.
-  uint16_t* qh = reinterpret_cast<uint16_t*>(L.k);
-  uint16_t* ql = qh + C * K;
-  if constexpr (OBF) {
-    for (int e = tid; e < C * (K / 8); e += kSplitThreads) {
-      const int i = e / (K / 8), q = (e % (K / 8)) >> 2, g = e & 3;
-      float v[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int kap = 32 * q + 4 * g + (m & 3) + 16 * (m >> 2);
-        v[m] = Q[i * LD + kap] * scale *
-               __builtin_amdgcn_exp2f(L.G2[i * LD + kap] + L.pre[(i >> 4) * K + kap]);
-      }
-      uint4 h, l;
-      split2_bf16(v[0], v[1], h.x, l.x);
-      split2_bf16(v[2], v[3], h.y, l.y);
-      split2_bf16(v[4], v[5], h.z, l.z);
-      split2_bf16(v[6], v[7], h.w, l.w);
-      *reinterpret_cast<uint4*>(qh + img_pos<K>(i, 4 * q + g)) = h;
-      *reinterpret_cast<uint4*>(ql + img_pos<K>(i, 4 * q + g)) = l;
-    }
-  } else {
-    for (int e = tid; e < C * K; e += kSplitThreads) {
-      const int i = e / K, kap = e % K;
-      Q[i * LD + kap] *= scale * __builtin_amdgcn_exp2f(L.G2[i * LD + kap] + L.pre[(i >> 4) * K + kap]);
-    }
+  // Q <- s q exp(G)
+  for (int e = tid; e < C * K; e += kSplitThreads) {
+    const int i = e / K, kap = e % K;
+    Q[i * LD + kap] *= scale * __builtin_amdgcn_exp2f(L.G2[i * LD + kap] + L.pre[(i >> 4) * K + kap]);
   }
   __syncthreads();
 
   const int hv = (int)(bh % p.HV);
   const long b = bh / p.HV;
   const int t0 = c * C;
-  // one column block per wavefront (K / 16 <= 8 wavefronts)
   constexpr int NKB = K / 16;
-  static_assert(NKB <= kSplitThreads / 64, "one column block per wavefront");
-  if (w < NKB) {
-    const int col = w * 16 + (lane & 15);
+  for (int cb = w; cb < NKB; cb += kSplitThreads / 64) {
+    const int col = cb * 16 + (lane & 15);
     // h_c as B operand fragments: lane holds keys 16 kb + 4 (l / 16) + r
     f32x4 hf[NKB];
     if (p.h_plain) {
@@ -927,78 +941,37 @@ __global__ __launch_bounds__(kSplitThreads) void split_output_kernel(SplitParams
     } else {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        hf[kb] = *reinterpret_cast<const f32x4*>(p.h + frag_index(ch, NKB, NKB, w, kb, lane));
+        hf[kb] = *reinterpret_cast<const f32x4*>(p.h + frag_index(ch, NKB, NKB, cb, kb, lane));
     }
     f32x4 uf[NB];
 #pragma unroll
     for (int J = 0; J < NB; ++J)
-      uf[J] = *reinterpret_cast<const f32x4*>(p.u + frag_index(ch, NKB, NB, w, J, lane));
-    if constexpr (OBF) {
-      // hi/lo products: (A_hi + A_lo)(B_hi + B_lo) without the lo*lo term.
-      // Slice s of h_c: positions 8 (l/16) .. +7 of lane l are keys
-      // 32 s + 4 (l/16) + 0..3 and 32 s + 16 + 4 (l/16) + 0..3, i.e. the
-      // fragments 2s and 2s+1 as loaded.
-      bf16x8 hh[NKB / 2], hl[NKB / 2];
-#pragma unroll
-      for (int q = 0; q < NKB / 2; ++q) split8(hf[2 * q], hf[2 * q + 1], hh[q], hl[q]);
-      bf16x4 uh[NB], ul[NB];
-#pragma unroll
-      for (int J = 0; J < NB; ++J) split4(uf[J][0], uf[J][1], uf[J][2], uf[J][3], uh[J], ul[J]);
+      uf[J] = *reinterpret_cast<const f32x4*>(p.u + frag_index(ch, NKB, NB, cb, J, lane));
 #pragma unroll 1
-      for (int I = 0; I < NB; ++I) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int row = I * 16 + (lane & 15);
+    for (int I = 0; I < NB; ++I) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const float* qrow = Q + (I * 16 + (lane & 15)) * LD + 4 * g4;
 #pragma unroll
-        for (int q = 0; q < NKB / 2; ++q) {
-          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(qh + img_pos<K>(row, 4 * q + g4));
-          const bf16x8 al = *reinterpret_cast<const bf16x8*>(ql + img_pos<K>(row, 4 * q + g4));
-          acc = mfma32(ah, hh[q], acc);
-          acc = mfma32(ah, hl[q], acc);
-          acc = mfma32(al, hh[q], acc);
-        }
-#pragma unroll
-        for (int J = 0; J < NB; ++J) {
-          if (J > I) break;
-          const float4 a = *reinterpret_cast<const float4*>(A + row * LR + J * 16 + 4 * g4);
-          bf16x4 ah, al;
-          split4(a.x, a.y, a.z, a.w, ah, al);
-          acc = mfma16(ah, uh[J], acc);
-          acc = mfma16(ah, ul[J], acc);
-          acc = mfma16(al, uh[J], acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + I * 16 + 4 * g4 + r;
-          if (t < p.T) p.o[((b * p.T + t) * p.HV + hv) * (long)K + col] = acc[r];
-        }
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float4 a = *reinterpret_cast<const float4*>(qrow + kb * 16);
+        acc = mfma4(a.x, hf[kb][0], acc);
+        acc = mfma4(a.y, hf[kb][1], acc);
+        acc = mfma4(a.z, hf[kb][2], acc);
+        acc = mfma4(a.w, hf[kb][3], acc);
       }
-    } else {
-#pragma unroll 1
-      for (int I = 0; I < NB; ++I) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const float* qrow = Q + (I * 16 + (lane & 15)) * LD + 4 * g4;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const float4 a = *reinterpret_cast<const float4*>(qrow + kb * 16);
-          acc = mfma4(a.x, hf[kb][0], acc);
-          acc = mfma4(a.y, hf[kb][1], acc);
-          acc = mfma4(a.z, hf[kb][2], acc);
-          acc = mfma4(a.w, hf[kb][3], acc);
-        }
+      for (int J = 0; J < NB; ++J) {
+        if (J > I) break;
+        const float4 a = *reinterpret_cast<const float4*>(A + (I * 16 + (lane & 15)) * LR + J * 16 + 4 * g4);
+        acc = mfma4(a.x, uf[J][0], acc);
+        acc = mfma4(a.y, uf[J][1], acc);
+        acc = mfma4(a.z, uf[J][2], acc);
+        acc = mfma4(a.w, uf[J][3], acc);
+      }
 #pragma unroll
-        for (int J = 0; J < NB; ++J) {
-          if (J > I) break;
-          const float4 a = *reinterpret_cast<const float4*>(A + (I * 16 + (lane & 15)) * LR + J * 16 + 4 * g4);
-          acc = mfma4(a.x, uf[J][0], acc);
-          acc = mfma4(a.y, uf[J][1], acc);
-          acc = mfma4(a.z, uf[J][2], acc);
-          acc = mfma4(a.w, uf[J][3], acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + I * 16 + 4 * g4 + r;
-          if (t < p.T) p.o[((b * p.T + t) * p.HV + hv) * (long)K + col] = acc[r];
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + I * 16 + 4 * g4 + r;
+        if (t < p.T) p.o[((b * p.T + t) * p.HV + hv) * (long)K + col] = acc[r];
       }
     }
   }
