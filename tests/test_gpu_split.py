@@ -2,8 +2,8 @@
 outputs, final states and the materialised chunk-entry states against the
 CPU oracle run chunk after chunk.  fp32 inputs run fp32 products throughout
 and are held to the fp32 bar; bf16 inputs run the state pass on bf16 MFMA
-(hi + lo operand pairs) when K and the chunk are at least 32, and are held to
-the bf16 bar."""
+(hi + lo operand pairs) when K and the chunk are at least 32, and R and A when
+K is, and are held to the bf16 bar and to a guard a tenth of it."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +33,13 @@ def _tol(d):
     return L.TOL_F32 if d["q"].dtype == torch.float32 else L.TOL_BF16
 
 
+# The hi/lo operand pairs keep the bf16 path near 1e-4 of RMS; a tenth of the
+# bar flags a change that loses precision well before the bar itself would
+# (a hi/lo form of the output products, whose two terms can nearly cancel,
+# reached 8.6e-3 on these cases).
+GUARD_BF16 = 1e-3
+
+
 def _check(d, gate, lb, chunk, what, initial_state=True):
     o, S, h = L.run_split(d, gate, lb, chunk, initial_state)
     ro, rS, rh = L.oracle_by_chunks(d, gate, lb, chunk, initial_state)
@@ -40,6 +47,8 @@ def _check(d, gate, lb, chunk, what, initial_state=True):
     tol = _tol(d)
     print("%s: o %.2e S %.2e h %.2e (tol %.0e)" % (what, eo, eS, eh, tol))
     assert eo <= tol and eS <= tol and eh <= tol, (eo, eS, eh)
+    if tol == L.TOL_BF16:
+        assert eo <= GUARD_BF16 and eS <= GUARD_BF16 and eh <= GUARD_BF16, (eo, eS, eh)
     return o, S, h
 
 
