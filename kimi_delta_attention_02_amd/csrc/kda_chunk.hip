@@ -368,6 +368,33 @@ __device__ __forceinline__ VR buffer_load_v(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_bit_cast(VR, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+// One level of the products over the token pairs of a 16-lane row (lanes
+// 2 tp + parity hold token pair tp of two channel groups): each prefix value
+// x[c] takes the product with the value 2 S lanes below, each suffix value
+// z[c] with the value 2 S lanes above.  A lane whose partner falls outside its
+// row is not written by the DPP instruction and keeps its value, so no lane
+// select is needed.  The s_nop gives the two wait states a DPP read of a VGPR
+// needs after a VALU write of it.
+#define KDA_PAIR_SCAN(SH, NCH_)                                                                  \
+  if constexpr (NCH_ == 4) {                                                                     \
+    asm("s_nop 1\n\t"                                                                            \
+        "v_mul_f32_dpp %0, %0, %0 row_shr:" #SH " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %1, %1, %1 row_shr:" #SH " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %2, %2, %2 row_shr:" #SH " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %3, %3, %3 row_shr:" #SH " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %4, %4, %4 row_shl:" #SH " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %5, %5, %5 row_shl:" #SH " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %6, %6, %6 row_shl:" #SH " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %7, %7, %7 row_shl:" #SH " row_mask:0xf bank_mask:0xf"                    \
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(z[0]), "+v"(z[1]), "+v"(z[2]),    \
+          "+v"(z[3]));                                                                           \
+  } else {                                                                                       \
+    asm("s_nop 1\n\t"                                                                            \
+        "v_mul_f32_dpp %0, %0, %0 row_shr:" #SH " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_mul_f32_dpp %1, %1, %1 row_shl:" #SH " row_mask:0xf bank_mask:0xf"                    \
+        : "+v"(x[0]), "+v"(z[0]));                                                               \
+  }
+
 // ----------------------------------------------------------------- kernel
 
 // GS: per-head gate (g_raw [B, T, HV], dt_bias [HV]), one decay shared by all
@@ -409,7 +436,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   // Each role runs its own loop over the pipeline steps; every loop executes
   // the same NT + 3 barriers, and registers are allocated per role.
   if (w < kPrepWaves) {
-    // ---- prep threads: token pair tp (tokens 2tp, 2tp+1), key channels c0 .. c0+3
+    // ---- prep threads: token pair tp (tokens 2tp, 2tp+1), key channels c0 .. c0+3;
+    // a 16-lane row holds the eight token pairs of two channel groups, interleaved
     const bool prep_thread = tid < 2 * K;
     // v of the workgroup's value tile, spread over all prep threads:
     // thread -> token vtt, columns vc .. vc + VPT - 1
@@ -418,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     typedef typename std::conditional<VPT * sizeof(T) == 2, uint16_t,
             typename std::conditional<VPT * sizeof(T) == 4, uint32_t, uint2>::type>::type VRaw;
     const int vtt = tid / (BV / VPT), vc = (tid % (BV / VPT)) * VPT;
-    const int tp = tid & 7, c0 = (tid >> 3) * 4;
+    const int tp = (tid >> 1) & 7, c0 = ((tid >> 4) * 2 + (tid & 1)) * 4;
     float bias4[4] = {0.f, 0.f, 0.f, 0.f};
     if (bias && prep_thread) {
   #pragma unroll
@@ -524,30 +552,21 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               kv[j][c] = valid ? kv[j][c] : 0.0f;
             }
           }
-          // Products over the token pairs of an 8-lane segment by DPP row shifts,
-          // each shift applied to the four channels together: inclusive prefix
+          // Products over the token pairs of a 16-lane row by DPP row shifts,
+          // each level applied to the four channels together: inclusive prefix
           // x and suffix z of the pair products.
-          float x[4], z[4], y;
+          float x[4], z[4];
   #pragma unroll
           for (int c = 0; c < NCH; ++c) x[c] = z[c] = al[0][c] * al[1][c];
-  #pragma unroll
-          for (int c = 0; c < NCH; ++c) { y = row_shr<1>(x[c]); if (tp >= 1) x[c] *= y; }
-  #pragma unroll
-          for (int c = 0; c < NCH; ++c) { y = row_shl<1>(z[c]); if (tp < 7) z[c] *= y; }
-  #pragma unroll
-          for (int c = 0; c < NCH; ++c) { y = row_shr<2>(x[c]); if (tp >= 2) x[c] *= y; }
-  #pragma unroll
-          for (int c = 0; c < NCH; ++c) { y = row_shl<2>(z[c]); if (tp < 6) z[c] *= y; }
-  #pragma unroll
-          for (int c = 0; c < NCH; ++c) { y = row_shr<4>(x[c]); if (tp >= 4) x[c] *= y; }
-  #pragma unroll
-          for (int c = 0; c < NCH; ++c) { y = row_shl<4>(z[c]); if (tp < 4) z[c] *= y; }
+          KDA_PAIR_SCAN(2, NCH)
+          KDA_PAIR_SCAN(4, NCH)
+          KDA_PAIR_SCAN(8, NCH)
           float E[2][4], Sf[2][4], ig[4], gam[4];
   #pragma unroll
           for (int c = 0; c < NCH; ++c) {
-            float ex = row_shr<1>(x[c]);  // exclusive prefix
+            float ex = row_shr<2>(x[c]);  // exclusive prefix
             if (tp == 0) ex = 1.0f;
-            float sx = row_shl<1>(z[c]);  // exclusive suffix
+            float sx = row_shl<2>(z[c]);  // exclusive suffix
             if (tp == 7) sx = 1.0f;
             E[0][c] = ex * al[0][c];
             E[1][c] = x[c];
@@ -619,6 +638,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     }
     if (it < NT + 3) step(it, in0, in1);
   } else if (w == kAqkWave || w == kInvWave) {
+    // The A wave (A, then the outputs) shares its SIMD with a prep wave that
+    // has slack; it takes the issue arbitration, the prep wave absorbs the wait.
+    if (w == kAqkWave) __builtin_amdgcn_s_setprio(1);
     // bf16 inputs: the A wave also forms the outputs, one step behind the
     // chain: O = s Q_hat S + A U for the block whose U the chain produced last
     // step.  A is computed as A^T = (k / E)(q E)^T, whose accumulator layout is
