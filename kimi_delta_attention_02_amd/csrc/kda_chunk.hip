@@ -528,7 +528,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     auto step = [&](int it, const PrepIn& cur, PrepIn& nxt) {
       fetch(it + 1, nxt);  // the next block's inputs travel during this step
       if (it < NT) {
-        Ops& B = sm.blk[it % 3];
+        // the slot as one scalar, so that each LDS address is one add to it
+        Ops& B = sm.blk[__builtin_amdgcn_readfirstlane(it % 3)];
         bool overflow = false;
         // Full blocks (all but possibly the last) skip the padding selects.
         auto prep_block = [&](auto full) {
@@ -564,10 +565,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           float E[2][4], Sf[2][4], ig[4], gam[4];
   #pragma unroll
           for (int c = 0; c < NCH; ++c) {
-            float ex = row_shr<2>(x[c]);  // exclusive prefix
-            if (tp == 0) ex = 1.0f;
-            float sx = row_shl<2>(z[c]);  // exclusive suffix
-            if (tp == 7) sx = 1.0f;
+            // exclusive prefix and suffix: the lanes of the row's first and last
+            // token pair have no partner and read 1
+            const float ex = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, x[c]), 0x112, 0xF, 0xF, false));
+            const float sx = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, z[c]), 0x102, 0xF, 0xF, false));
             E[0][c] = ex * al[0][c];
             E[1][c] = x[c];
             Sf[1][c] = sx;
