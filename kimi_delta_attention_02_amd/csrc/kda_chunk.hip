@@ -97,6 +97,18 @@ struct alignas(16) RowOp<false, ROWS, K> {
 };
 
 // position in its row of key channel c (c % 4 == 0: four channels stay together)
+// Position of the four keys c .. c+3 (c a multiple of 4) in a bf16 operand
+// row: inside each 32-key slice, key e goes to 8 ((e mod 16) / 4) + 4 (e / 16)
+// + e mod 4, so that an MFMA lane's eight positions 8 g .. 8 g + 7 hold keys
+// 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, the rows a 16 x 16 accumulator
+// fragment pair gives that lane.  Products over the keys do not depend on the
+// order, since both operands of each use it.
+template <int K>
+__device__ __forceinline__ int key_pos(int c) {
+  if constexpr (K % 32 == 0) return (c & ~31) | (((c & 15) >> 2) << 3) | (((c >> 4) & 1) << 2);
+  else return c;
+}
+
 template <int K>
 __device__ __forceinline__ int row_pos(int r, int c) {
   if constexpr (K % 32 == 0)
@@ -257,7 +269,7 @@ __device__ __forceinline__ void put4(RowOp<F32, ROWS, K>& op, int row, int c0, c
     uint2 h, l;
     split2_bf16(x[0], x[1], h.x, l.x);
     split2_bf16(x[2], x[3], h.y, l.y);
-    const int o = row * LD + row_pos<K>(row, c0);
+    const int o = row * LD + row_pos<K>(row, key_pos<K>(c0));
     *reinterpret_cast<uint2*>(op.hi + o) = h;
     *reinterpret_cast<uint2*>(op.lo + o) = l;
   }
@@ -789,11 +801,35 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     const bool chain = cb >= 0 && cb < NCB;
     const int vcol = v0 + 16 * cb + (lane & 15);
     f32x4 sacc[NKB];
+    // bf16, K a multiple of 32: the hi/lo words of the state by 32-key slice,
+    // kept for the next step's K_hat S.  With the key order that key_pos gives
+    // the rows, positions 8 (l/16) .. +7 of slice s hold keys 32 s + 4 (l/16)
+    // + 0..3 and 32 s + 16 + 4 (l/16) + 0..3: fragments 2s and 2s+1 as they are.
+    constexpr bool kRegB = !F32 && K % 32 == 0;
+    constexpr int NSL = kRegB ? K / 32 : 1;
+    bf16x8 sh[NSL], sl[NSL];
     auto write_state_operand = [&](RowOp<F32, 16, K>& st) {
+      if constexpr (kRegB) {
+        const int row = lane & 15;
   #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float x[4] = {sacc[kb][0], sacc[kb][1], sacc[kb][2], sacc[kb][3]};
-        put4(st, lane & 15, 16 * kb + 4 * (lane >> 4), x);
+        for (int q = 0; q < NSL; ++q) {
+          uint4 h, l;
+          split2_bf16(sacc[2 * q][0], sacc[2 * q][1], h.x, l.x);
+          split2_bf16(sacc[2 * q][2], sacc[2 * q][3], h.y, l.y);
+          split2_bf16(sacc[2 * q + 1][0], sacc[2 * q + 1][1], h.z, l.z);
+          split2_bf16(sacc[2 * q + 1][2], sacc[2 * q + 1][3], h.w, l.w);
+          sh[q] = __builtin_bit_cast(bf16x8, h);
+          sl[q] = __builtin_bit_cast(bf16x8, l);
+          const int o = row * RowOp<F32, 16, K>::LD + row_pos<K>(row, 32 * q + 8 * (lane >> 4));
+          *reinterpret_cast<uint4*>(st.hi + o) = h;
+          *reinterpret_cast<uint4*>(st.lo + o) = l;
+        }
+      } else {
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const float x[4] = {sacc[kb][0], sacc[kb][1], sacc[kb][2], sacc[kb][3]};
+          put4(st, lane & 15, 16 * kb + 4 * (lane >> 4), x);
+        }
       }
     };
     if (chain) {
@@ -865,7 +901,18 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           f32x4 pk = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
           if constexpr (F32)
             kprod2(pk, qs, B.kh, B.qh, C.st[tc & 1], lane);  // K_hat S and Q_hat S
-          else
+          else if constexpr (kRegB) {  // K_hat S, the state from registers
+            const int row = lane & 15;
+  #pragma unroll
+            for (int q = 0; q < NSL; ++q) {
+              const int o = row * RowOp<F32, kTok, K>::LD + row_pos<K>(row, 32 * q + 8 * (lane >> 4));
+              const bf16x8 ah = *reinterpret_cast<const bf16x8*>(B.kh.hi + o);
+              const bf16x8 al = *reinterpret_cast<const bf16x8*>(B.kh.lo + o);
+              pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh[q], pk, 0, 0, 0);
+              pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl[q], pk, 0, 0, 0);
+              pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, sh[q], pk, 0, 0, 0);
+            }
+          } else
             kprod(pk, B.kh, 0, C.st[tc & 1], 0, lane);        // K_hat S
           const float4 bt4 = *reinterpret_cast<const float4*>(&B.beta[4 * g]);
           float vv[4];  // v of tokens 4g .. 4g+3 in this lane's column (padding: 0)
