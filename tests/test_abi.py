@@ -101,6 +101,7 @@ def _step(lib, **kw):
     (dict(K=96, V=96), _lib.KDA_ERR_UNSUPPORTED),
     (dict(K=128, V=64), _lib.KDA_ERR_UNSUPPORTED),
     (dict(C=48), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(H=1, HV=(1 << 17) + 1), _lib.KDA_ERR_UNSUPPORTED),  # HV * K > 2^24 (32-bit row offsets)
     (dict(B=0), _lib.KDA_OK),                         # empty batch: nothing to do
 ])
 def test_chunk_fwd_validation(lib, kw, status):
