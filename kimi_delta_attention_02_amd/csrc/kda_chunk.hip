@@ -845,6 +845,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       wave_lds_sync();
     }
     for (int it = 0; it < NT + 3; ++it) {
+      __builtin_amdgcn_s_setprio(2);  // the critical part: K_hat S to U
       const int tc = it - 2;
       if (tc >= 0 && tc < NT && chain) {
         const Ops& B = sm.blk[tc % 3];
@@ -953,6 +954,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               const uint2 h2 = __builtin_bit_cast(uint2, uh), l2 = __builtin_bit_cast(uint2, ul);
               sm.uo.u[cb][tc & 1][lane] = uint4{h2.x, h2.y, l2.x, l2.y};
             }
+            // The update and split feed only the next step, after the barrier,
+            // and the chain has slack: the prep wave on this SIMD issues first.
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)  // S = gamma S + (k Suf)^T U
               tprod_reg(sacc[kb], B.keT.c + 16 * kb * kCat, uh, ul, lane);
