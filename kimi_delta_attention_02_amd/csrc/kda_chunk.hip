@@ -41,6 +41,9 @@
 //              registers for the whole sequence: diag(gamma) S, K_hat S, Ebar,
 //              U and the state update; U goes to wave 4 and a hi/lo copy of
 //              the new state to a double-buffered LDS slot
+// Issue priority: the chain waves win their SIMD's arbitration from K_hat S
+// to U and yield it for the state update and its split, which only the next
+// step needs; wave 4 wins it over the prep wave on its SIMD.
 // bf16 inputs use bf16 MFMA with fp32 accumulation.  Every operand of these
 // products is derived (scaled by decay factors, the state, or a solve result),
 // and a single bf16 rounding of them costs far more than the 1e-2 error budget
@@ -382,8 +385,8 @@ __device__ __forceinline__ VR buffer_load_v(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 // One level of the products over the token pairs of a 16-lane row (lanes
 // 2 tp + parity hold token pair tp of two channel groups): each prefix value
-// x[c] takes the product with the value 2 S lanes below, each suffix value
-// z[c] with the value 2 S lanes above.  A lane whose partner falls outside its
+// x[c] takes the product with the value SH lanes below, each suffix value
+// z[c] with the value SH lanes above (SH = 2, 4, 8: one, two, four pairs).  A lane whose partner falls outside its
 // row is not written by the DPP instruction and keeps its value, so no lane
 // select is needed.  The s_nop gives the two wait states a DPP read of a VGPR
 // needs after a VALU write of it.
