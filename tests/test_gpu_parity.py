@@ -92,6 +92,12 @@ CHUNK_CASES = [
 ]
 
 
+# A tenth of the bf16 bar: the hi/lo pairs hold the measured errors near 1e-4
+# (a single bf16 rounding of any derived operand would cost 2-6e-2), so a
+# change that drops a lo word shows here long before the bar itself is hit.
+BF16_GUARD = 1e-3
+
+
 @pytest.mark.parametrize("B,T,H,HV,K,dtype,gate,s0,chunk", CHUNK_CASES)
 def test_chunk_matches_oracle(B, T, H, HV, K, dtype, gate, s0, chunk):
     d = synth.random_inputs(B, T, H, HV, K, K, seed=1000 + T + K, dtype=dtype,
@@ -102,6 +108,8 @@ def test_chunk_matches_oracle(B, T, H, HV, K, dtype, gate, s0, chunk):
     eo, eS = L.rel_err(o, ro), L.rel_err(S, rS)
     print("chunk %s: o %.2e S %.2e" % ((B, T, H, HV, K, dtype, gate, s0, chunk), eo, eS))
     assert eo <= tol and eS <= tol
+    if dtype == "bf16":  # the hi/lo operand pairs keep this near 1e-4: guard a tenth of the bar
+        assert eo <= BF16_GUARD and eS <= BF16_GUARD, (eo, eS)
 
 
 def test_chunk_empty_sequence_copies_state():
