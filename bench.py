@@ -1,27 +1,31 @@
 """Benchmark of the KDA forward on one MI355X.
 
-A step is one chunked-prefill forward of the prefill workload (B=4, T=4096,
-H=HV=16, K=V=128, chunk 64, bf16 q/k/v, fp32 gate inputs and state, safe
-gate): gate, cumulative decay, intra-chunk solve and inter-chunk propagation,
-all in one launch of the fused chunk kernel.  The recurrent decode row is
-timed in the same run on the decode workload (B=256, HV=32, 256 single-token
-steps over a 512 MiB fp32 state) and reported in the "decode" object; the
-fused multi-token recurrent forward runs the same 256 tokens as 16-token calls
-and as one 256-token call ("recurrent" object), the chunked forward runs the
-prefill shape with one gate per (token, value head) ("head_gate" object), and
-the full-size GVA and long-context prefill workloads run through the same
-kernel ("configs" object), and the one-sequence long shard (T=65536, 8 value
-heads) runs through both the fused chunk kernel and the three-stage split
-schedule ("split" object).
+A step is one chunked-prefill forward of the long-context workload (B=1,
+T=65536, 16 query/key heads for 64 value heads, K=V=128, chunk 64 requested,
+bf16 q/k/v, fp32 gate inputs and state, safe gate): gate, cumulative decay,
+intra-chunk solve and inter-chunk propagation, all in one launch of the fused
+chunk kernel, which solves each chunk's triangular system in 16-token diagonal
+blocks (the block size is reported next to the requested chunk size).  The
+other chunked-prefill workloads (prefill: B=4, T=4096, H=HV=16; GVA: B=2,
+T=16384, 8 q/k heads for 32 value heads, standard gate, random initial state)
+run at full size through the same kernel ("configs" object).  The recurrent
+decode row is timed in the same run on the decode workload (B=256, HV=32, 256
+single-token steps over a 512 MiB fp32 state) and reported in the "decode"
+object; the fused multi-token recurrent forward runs the same 256 tokens as
+16-token calls and as one 256-token call ("recurrent" object), the chunked
+forward runs the prefill shape with one gate per (token, value head)
+("head_gate" object), and the one-sequence long shard (T=65536, 8 value heads)
+runs through both the fused chunk kernel and the three-stage split schedule
+("split" object).
 
 Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
 HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
 bytes per launch / mean launch time (HIP events on the launch stream) against
-the 8 TB/s HBM peak; `mfma` adds algorithmic FLOPs against the 2.5166
-PFLOP/s dense bf16 MFMA peak and, from the committed counter passes, the
-fraction of cycles the matrix pipes were busy and the MFMA flops executed.
-`cpu_baseline` times the fp64 CPU oracle on all host cores over a sample of
-the same workload.
+the 8 TB/s HBM peak; `mfma` adds algorithmic FLOPs (counted at the 16-token
+block the kernel solves) against the 2.5166 PFLOP/s dense bf16 MFMA peak and,
+from the committed counter passes, the fraction of cycles the matrix pipes
+were busy and the MFMA flops executed.  `cpu_baseline` times the fp64 CPU
+oracle on all host cores over a sample of the same workload.
 """
 from __future__ import annotations
 
@@ -50,9 +54,16 @@ def chunk_bytes(w):
     return qk + v + g + beta + o + state
 
 
-def chunk_flops(w, C=64):
-    """Dense FLOPs of the chunkwise algorithm: 2 (3 C K + 2 C V + 3 K V) per
-    token and value head (A_qk, R, w, u, U, Q S, A U, state update)."""
+# The fused chunk kernel solves every chunk's triangular system in diagonal
+# blocks of this many tokens, whatever chunk size is requested (the result
+# does not depend on it).
+BLOCK = 16
+
+
+def chunk_flops(w, C=BLOCK):
+    """Dense FLOPs of the chunkwise algorithm with blocks of C tokens:
+    2 (3 C K + 2 C V + 3 K V) per token and value head (A_qk, R, w, u, U,
+    Q S, A U, state update)."""
     return 2 * (3 * C * w.K + 2 * C * w.V + 3 * w.K * w.V) * w.B * w.T * w.HV
 
 
@@ -103,17 +114,69 @@ def measured_mfma(key):
     return rec.get("mfma") if rec else None
 
 
+def chunk_line(kda, synth, w, dev, stream, steps, warmup):
+    """Times kda.chunk_fwd on workload w (inputs resident in HBM, HIP events
+    on the launch stream around the timed launches); returns the line's
+    fields and the device inputs."""
+    import torch
+
+    d = synth.make_inputs(w)
+    g = {n: (t.to(dev) if t is not None else None) for n, t in d.items()}
+    o = torch.empty((w.B, w.T, w.HV, w.V), dtype=torch.float32, device=dev)
+    S = torch.empty((w.B, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.chunk_fwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"],
+                      gate=w.gate, lower_bound=w.lower_bound, chunk_size=w.chunk,
+                      initial_state=g["S0"], o=o, final_state=S)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    ms = ev[0].elapsed_time(ev[-1]) / steps
+    launch_ms = sum(per) / len(per)
+    nbytes, flops = chunk_bytes(w), chunk_flops(w)
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    key = "chunk_" + w.name
+    line = {
+        "ms_per_step": ms, "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s",
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(key),
+                     "kernel": "chunk_fwd_kernel<128, bf16, %s gate>" % w.gate,
+                     "bytes_per_launch": nbytes, "launch_ms": launch_ms},
+        "mfma": {"algorithmic_flops": flops, "block": BLOCK,
+                 "algorithmic_flops_chunk_%d" % w.chunk: chunk_flops(w, w.chunk),
+                 "achieved_tflops": flops / (launch_ms * 1e-3) / 1e12,
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": flops / (launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                 "rocprof": measured_mfma(key)},
+        "wall_s_timed": t_wall,
+    }
+    return line, d, g
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "gva", "long", "tiny"])
+    ap.add_argument("--workload", default="long", choices=["long", "prefill", "gva", "tiny"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-split", action="store_true")
+    ap.add_argument("--no-gate", action="store_true", help="skip the standalone gate line")
+    ap.add_argument("--no-head-gate", action="store_true", help="skip the per-head gate line")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the full-size GVA and long-context prefill lines")
+                    help="skip the other full-size chunked-prefill workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -128,170 +191,114 @@ def main():
     from kimi_delta_attention_02_amd import synth
 
     dev = torch.device("cuda:0")
-    w = synth.WORKLOADS[args.workload]
-    d = synth.make_inputs(w)
-    g = {n: (t.to(dev) if t is not None else None) for n, t in d.items()}
-    o = torch.empty((w.B, w.T, w.HV, w.V), dtype=torch.float32, device=dev)
-    S = torch.empty((w.B, w.HV, w.K, w.V), dtype=torch.float32, device=dev)
-
-    def step():
-        kda.chunk_fwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"],
-                      gate=w.gate, lower_bound=w.lower_bound, chunk_size=w.chunk,
-                      initial_state=g["S0"], o=o, final_state=S)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t_wall = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    ms = ev[0].elapsed_time(ev[-1]) / args.steps
-    tokens = w.B * w.T
-    nbytes = chunk_bytes(w)
-    flops = chunk_flops(w, w.chunk)
-    launch_ms = sum(per) / len(per)
-    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    w = synth.WORKLOADS[args.workload]
+    line, d, g = chunk_line(kda, synth, w, dev, stream, args.steps, args.warmup)
     result = {
         "metric": "KDA fwd tokens/s (chunked prefill, decode) + % of MFMA / HBM roofline",
-        "value": tokens / (ms * 1e-3),
+        "value": line["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": line["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v,g_raw N(0,1), beta=sigmoid(N(0,1)))",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "HV": w.HV, "K": w.K,
-                   "V": w.V, "chunk": w.chunk, "gate": w.gate, "global_batch": w.B,
+                   "V": w.V, "chunk": w.chunk, "block": BLOCK, "gate": w.gate,
+                   "initial_state": w.s0_std > 0, "global_batch": w.B,
                    "seq_len": w.T, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("chunk") if args.workload == "prefill" else None,
-                     "kernel": "chunk_fwd_kernel<128, bf16>", "bytes_per_launch": nbytes,
-                     "launch_ms": launch_ms},
-        "mfma": {"algorithmic_flops": flops,
-                 "achieved_tflops": flops / (launch_ms * 1e-3) / 1e12,
-                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                 "frac": flops / (launch_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                 "rocprof": measured_mfma("chunk") if args.workload == "prefill" else None},
-        "wall_s_timed": t_wall,
+        "roofline": line["roofline"],
+        "mfma": line["mfma"],
+        "wall_s_timed": line["wall_s_timed"],
     }
-    # The standalone gate entry point on the prefill workload's g_raw: the
+    # The standalone gate entry point on the headline workload's g_raw: the
     # activation and the chunk-local cumulative log-decay (chunk 64), one
     # read and one write of every element.
-    gout = torch.empty_like(g["g_raw"])
+    if not args.no_gate:
+        gout = torch.empty_like(g["g_raw"])
 
-    def gstep():
-        kda.gate(g["g_raw"], g["A_log"], g["dt_bias"], gate=w.gate, lower_bound=w.lower_bound,
-                 chunk_size=w.chunk, out=gout)
+        def gstep():
+            kda.gate(g["g_raw"], g["A_log"], g["dt_bias"], gate=w.gate, lower_bound=w.lower_bound,
+                     chunk_size=w.chunk, out=gout)
 
-    for _ in range(args.warmup):
-        gstep()
-    torch.cuda.synchronize()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record(stream)
-    for _ in range(args.steps):
-        gstep()
-    a1.record(stream)
-    torch.cuda.synchronize()
-    gms = a0.elapsed_time(a1) / args.steps
-    gbytes = 2 * g["g_raw"].numel() * 4
-    ggbs = gbytes / (gms * 1e-3) / 1e9
-    result["gate"] = {
-        "workload": w.name, "elements": g["g_raw"].numel(), "chunk": w.chunk, "gate": w.gate,
-        "ms_per_call": gms,
-        "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ggbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": gbytes,
-                     "kernel": "gate_cumsum_kernel"}}
-    del gout
+        for _ in range(args.warmup):
+            gstep()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(args.steps):
+            gstep()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        gms = a0.elapsed_time(a1) / args.steps
+        gbytes = 2 * g["g_raw"].numel() * 4
+        ggbs = gbytes / (gms * 1e-3) / 1e9
+        result["gate"] = {
+            "workload": w.name, "elements": g["g_raw"].numel(), "chunk": w.chunk, "gate": w.gate,
+            "ms_per_call": gms,
+            "roofline": {"bound": "hbm", "achieved": ggbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ggbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": gbytes,
+                         "kernel": "gate_cumsum_kernel"}}
+        del gout
+    del g
 
-    del o, S, g
-
-    # The same chunked forward with one gate per (token, value head) (the
-    # Gated DeltaNet form) on the prefill shape.
-    wh = synth.WORKLOADS["prefill_head_gate"]
-    dh = synth.make_inputs(wh)
-    gh = {n: (t.to(dev) if t is not None else None) for n, t in dh.items()}
-    oh = torch.empty((wh.B, wh.T, wh.HV, wh.V), dtype=torch.float32, device=dev)
-    Sh = torch.empty((wh.B, wh.HV, wh.K, wh.V), dtype=torch.float32, device=dev)
-
-    def hstep():
-        kda.chunk_fwd(gh["q"], gh["k"], gh["v"], gh["g_raw"], gh["beta"], gh["A_log"],
-                      gh["dt_bias"], gate=wh.gate, lower_bound=wh.lower_bound,
-                      chunk_size=wh.chunk, initial_state=gh["S0"], o=oh, final_state=Sh)
-
-    for _ in range(args.warmup):
-        hstep()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        hstep()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    hms = e0.elapsed_time(e1) / args.steps
-    hbytes = chunk_bytes(wh)
-    hgbs = hbytes / (hms * 1e-3) / 1e9
-    result["head_gate"] = {
-        "workload": wh.name, "B": wh.B, "T": wh.T, "H": wh.H, "HV": wh.HV, "K": wh.K,
-        "gate": wh.gate + ", one per (token, value head)", "value": wh.B * wh.T / (hms * 1e-3),
-        "unit": "tokens/s", "ms_per_step": hms,
-        "roofline": {"bound": "hbm", "achieved": hgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": hgbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": hbytes,
-                     "kernel": "chunk_fwd_kernel<128, bf16, per-head gate>"}}
-    del gh, oh, Sh
-
-    # The other two chunked-prefill workloads at full size, through the same
-    # kernel: GVA (B=2, T=16384, 8 q/k heads for 32 value heads, standard
-    # gate, random initial state) and long context (B=1, T=65536, 16 q/k heads
-    # for 64 value heads).
+    # The other chunked-prefill workloads at full size, through the same
+    # kernel: prefill (B=4, T=4096, H=HV=16), GVA (B=2, T=16384, 8 q/k heads
+    # for 32 value heads, standard gate, random initial state) and long
+    # context (B=1, T=65536, 16 q/k heads for 64 value heads), less the
+    # headline workload.
     if not args.no_configs:
         result["configs"] = {}
-        for name in ("gva", "long"):
+        for name in ("prefill", "gva", "long"):
+            if name == w.name:
+                continue
             wc = synth.WORKLOADS[name]
-            gc = {n: (t.to(dev) if t is not None else None)
-                  for n, t in synth.make_inputs(wc).items()}
-            oc = torch.empty((wc.B, wc.T, wc.HV, wc.V), dtype=torch.float32, device=dev)
-            Sc = torch.empty((wc.B, wc.HV, wc.K, wc.V), dtype=torch.float32, device=dev)
+            n_c = max(1, min(args.steps, 10))
+            cl, _, gc = chunk_line(kda, synth, wc, dev, stream, n_c, 1)
+            del gc
+            result["configs"][name] = dict(
+                {"B": wc.B, "T": wc.T, "H": wc.H, "HV": wc.HV, "K": wc.K, "V": wc.V,
+                 "chunk": wc.chunk, "block": BLOCK, "gate": wc.gate,
+                 "initial_state": wc.s0_std > 0, "calls": n_c}, **cl)
 
-            def cstep():
-                kda.chunk_fwd(gc["q"], gc["k"], gc["v"], gc["g_raw"], gc["beta"], gc["A_log"],
-                              gc["dt_bias"], gate=wc.gate, lower_bound=wc.lower_bound,
-                              chunk_size=wc.chunk, initial_state=gc["S0"], o=oc, final_state=Sc)
+    if not args.no_head_gate:
+        # The same chunked forward with one gate per (token, value head) (the
+        # Gated DeltaNet form) on the prefill shape.
+        wh = synth.WORKLOADS["prefill_head_gate"]
+        dh = synth.make_inputs(wh)
+        gh = {n: (t.to(dev) if t is not None else None) for n, t in dh.items()}
+        oh = torch.empty((wh.B, wh.T, wh.HV, wh.V), dtype=torch.float32, device=dev)
+        Sh = torch.empty((wh.B, wh.HV, wh.K, wh.V), dtype=torch.float32, device=dev)
 
-            cstep()
-            torch.cuda.synchronize()
-            n_c = max(1, min(args.steps, 5))
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            for _ in range(n_c):
-                cstep()
-            c1.record(stream)
-            torch.cuda.synchronize()
-            cms = c0.elapsed_time(c1) / n_c
-            cbytes, cflops = chunk_bytes(wc), chunk_flops(wc, wc.chunk)
-            cgbs = cbytes / (cms * 1e-3) / 1e9
-            result["configs"][name] = {
-                "B": wc.B, "T": wc.T, "H": wc.H, "HV": wc.HV, "K": wc.K, "V": wc.V,
-                "chunk": wc.chunk, "gate": wc.gate, "initial_state": wc.s0_std > 0,
-                "value": wc.B * wc.T / (cms * 1e-3), "unit": "tokens/s", "ms_per_call": cms,
-                "calls": n_c,
-                "roofline": {"bound": "hbm", "achieved": cgbs, "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": cgbs / HBM_PEAK_GBS, "traffic": None,
-                             "bytes_per_launch": cbytes, "kernel": "chunk_fwd_kernel<128, bf16>"},
-                "mfma": {"algorithmic_flops": cflops,
-                         "frac": cflops / (cms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}}
-            del gc, oc, Sc
+        def hstep():
+            kda.chunk_fwd(gh["q"], gh["k"], gh["v"], gh["g_raw"], gh["beta"], gh["A_log"],
+                          gh["dt_bias"], gate=wh.gate, lower_bound=wh.lower_bound,
+                          chunk_size=wh.chunk, initial_state=gh["S0"], o=oh, final_state=Sh)
+
+        for _ in range(args.warmup):
+            hstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            hstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        hms = e0.elapsed_time(e1) / args.steps
+        hbytes = chunk_bytes(wh)
+        hgbs = hbytes / (hms * 1e-3) / 1e9
+        result["head_gate"] = {
+            "workload": wh.name, "B": wh.B, "T": wh.T, "H": wh.H, "HV": wh.HV, "K": wh.K,
+            "gate": wh.gate + ", one per (token, value head)", "value": wh.B * wh.T / (hms * 1e-3),
+            "unit": "tokens/s", "ms_per_step": hms,
+            "roofline": {"bound": "hbm", "achieved": hgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": hgbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": hbytes,
+                         "kernel": "chunk_fwd_kernel<128, bf16, per-head gate>"}}
+        del gh, oh, Sh
 
     # One GPU's share of the long-context workload (one sequence, 8 value
     # heads): the fused chunk kernel against the three-stage split schedule.
@@ -373,13 +380,15 @@ def main():
             "workload": wd.name, "B": wd.B, "HV": wd.HV, "K": wd.K, "V": wd.V, "steps": wd.steps,
             "value": wd.B * wd.steps / (dms * 1e-3), "unit": "tokens/s",
             "ms_per_token_step": per_step_ms,
-            "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": dgbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
+            "roofline": {"bound": "hbm+llc", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("decode"),
                          "kernel": "decode_step_kernel<128, 128, bf16>",
                          "bytes_per_launch": decode_bytes(wd),
-                         "note": "the 512 MiB state is read with ordinary loads, so the "
-                                 "last-level cache serves part of each step's reads and "
-                                 "achieved exceeds what HBM alone streams; see large_state"},
+                         "note": "cache-assisted: the 512 MiB state is read with ordinary "
+                                 "loads, so the 256 MB last-level cache serves part of each "
+                                 "step's reads and achieved exceeds what HBM alone streams; "
+                                 "hbm_roofline is the same step on a 1 GiB state"},
         }
 
         # The same steps with twice the sequences (a 1 GiB state, read with
@@ -406,6 +415,12 @@ def main():
         torch.cuda.synchronize()
         lms = e0.elapsed_time(e1) / nl
         lgbs = decode_bytes(wl) / (lms * 1e-3) / 1e9
+        result["decode"]["hbm_roofline"] = {
+            "bound": "hbm", "achieved": lgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": lgbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": decode_bytes(wl),
+            "kernel": "decode_step_kernel<128, 128, bf16, non-temporal loads>",
+            "note": "the decode step with twice the sequences (1 GiB state, beyond the "
+                    "last-level cache): HBM alone"}
         result["decode"]["large_state"] = {
             "B": wl.B, "state_mib": wl.B * wl.HV * wl.K * wl.V * 4 >> 20, "steps": nl,
             "ms_per_token_step": lms, "value": wl.B / (lms * 1e-3), "unit": "tokens/s",
