@@ -37,10 +37,8 @@
  *  - All tensor pointers are DEVICE pointers to contiguous row-major memory
  *    with the shapes given below, aligned to 16 bytes (4 bytes suffice for
  *    g_raw and dt_bias with KDA_GATE_PER_HEAD).  The caller owns every
- *    buffer; the library allocates nothing.  Its only global state is a
- *    per-device flag recording that the chunk kernel's LDS limit was raised
- *    (set once, thread-safely); every entry point may be called from several
- *    host threads and streams.
+ *    buffer; the library allocates nothing and keeps no global state; every
+ *    entry point may be called from several host threads and streams.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means the
  *    default stream).  Nothing synchronises the host.  Input buffers must stay
  *    valid, and outputs unread, until the stream reaches the enqueued work.
@@ -118,8 +116,12 @@ kda_status kda_gate(const float* g_raw, const float* A_log, const float* dt_bias
  *   initial_state [B, HV, K, V]  float32, or NULL for zeros
  *   o             [B, T, HV, V]  float32 output
  *   final_state   [B, HV, K, V]  float32 output, or NULL; may alias initial_state
- *   chunk_size    16, 32 or 64 (tokens per chunk; the result does not depend on it
- *                 beyond rounding)
+ *   chunk_size    16, 32 or 64, validated and otherwise unused: the kernel always
+ *                 solves the chunk's lower-triangular system in its 16-token diagonal
+ *                 blocks, carrying the coupling between blocks through the on-chip
+ *                 state (block forward substitution, the "Chunkwise Triton pipeline"
+ *                 section's 16-token diagonal blocks), so any accepted chunk size
+ *                 gives the same result, bit for bit
  *   workspace     device scratch of kda_chunk_fwd_workspace_bytes(...) bytes, or
  *                 NULL when that size is 0
  * Supported head sizes: K == V in {16, 32, 64, 128}; HV % H == 0; HV * K <=

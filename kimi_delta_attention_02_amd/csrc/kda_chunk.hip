@@ -13,11 +13,13 @@
 //                      A_ij   = s sum_c (q_ic E_ic) (k_jc / E_jc)         (j <= i)
 //   block-end state    S'     = diag(gamma) S + (k * Suf)^T U
 //
-// with s = 1/sqrt(K).  Every factor is bounded: E and Suf lie in [gamma, 1]
-// and k / E in [|k|, |k| / gamma], finite as long as gamma >= 2^-100 in every
-// channel (69 nats of decay inside 16 tokens; the safe gate with lower bound
-// -5 stays under 80 nats, and real data far less).  A block that breaks the
-// bound is run token by token instead (the recurrence itself, no
+// with s = 1/sqrt(K).  Every factor is bounded: for the safe and standard
+// gates (log-decay g <= 0) E and Suf lie in [gamma, 1] and k / E in [|k|,
+// |k| / gamma], finite as long as gamma >= 2^-100 in every channel (69 nats
+// of decay inside 16 tokens; the safe gate with lower bound -5 stays under 80
+// nats, and real data far less).  With a caller-supplied log-decay of either
+// sign (gate none) gamma, E and Suf are each held to [2^-100, 2^100].  A block
+// that breaks a bound is run token by token instead (the recurrence itself, no
 // factorisation), so every input is handled exactly.  Across blocks the state
 // carries the coupling between earlier and later tokens, which makes the
 // 16-token blocks the diagonal blocks of the chunk's triangular system.
@@ -52,7 +54,6 @@
 // a product takes 3 MFMAs (hi*hi + hi*lo + lo*hi) over the key axis, or 2 over
 // the 16-token axis, where one k = 32 instruction covers the hi and lo halves.
 // fp32 inputs use fp32 MFMA throughout.
-#include <atomic>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -71,6 +72,7 @@ struct ChunkParams {
   float* o;
   float* S_out;
   int B, T, H, HV, kind;
+  int G;  // value heads per XCD group (a divisor of HV / H)
   float lower_bound;
 };
 
@@ -81,6 +83,9 @@ constexpr int kThreads = 512;  // eight wavefronts
 constexpr int kPrepWaves = 4, kAqkWave = 4, kInvWave = 5, kChainWave0 = 6;
 constexpr float kGammaMin = 7.888609052210118e-31f;  // 2^-100
 constexpr float kGammaMax = 1.2676506002282294e30f;  // 2^100 (only a positive log-decay can get here)
+
+// A decay factor the factorised block form can use as it is (NaN fails).
+__device__ __forceinline__ bool in_bounds(float x) { return x >= kGammaMin && x <= kGammaMax; }
 
 // ------------------------------------------------------------------ LDS
 // ROWS x K operand with the key axis contiguous (bf16: hi and lo words).
@@ -431,10 +436,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   const int T_ = p.T, HV = p.HV, H = p.H;
   const int NT = (T_ + kTok - 1) / kTok;
 
-  // workgroup -> (head, value tile): the NVT tiles of a head share blockIdx % 8
+  // workgroup -> (head, value tile).  blockIdx % 8 picks the XCD (workgroups
+  // are dispatched to the eight XCDs in turn); the NVT tiles of a head, and
+  // the p.G value heads of one query/key group, share it and so its L2.
   const int nheads = p.B * HV;
   const int x8 = blockIdx.x & 7, y8 = blockIdx.x >> 3;
-  const int hd = (y8 / NVT) * 8 + x8, vt = y8 % NVT;
+  const int m8 = y8 / NVT, vt = y8 % NVT;
+  const int hd = ((m8 / p.G) * 8 + x8) * p.G + m8 % p.G;
   if (hd >= nheads) return;
   const long b = hd / HV;
   const int hv = hd % HV;
@@ -591,9 +599,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             Sf[1][c] = sx;
             Sf[0][c] = al[1][c] * sx;
             gam[c] = x[c] * sx;  // decay over the whole block
-            // the safe and standard gates give g <= 0, so gamma <= 1; NaN fails too
-            overflow |= GK == KDA_GATE_NONE ? !(gam[c] >= kGammaMin && gam[c] <= kGammaMax)
-                                            : !(gam[c] >= kGammaMin);
+            // the safe and standard gates give g <= 0, so E, Suf in [gamma, 1]: gamma
+            // bounds them all; NaN fails too
+            overflow |= !(gam[c] >= kGammaMin);
+            if constexpr (GK == KDA_GATE_NONE)  // any sign: every factor on its own
+              overflow |= !(gam[c] <= kGammaMax) | !in_bounds(E[0][c]) | !in_bounds(E[1][c]) |
+                          !in_bounds(Sf[0][c]) | !in_bounds(Sf[1][c]);
             ig[c] = __builtin_amdgcn_rcpf(gam[c]);
           }
   #pragma unroll
@@ -992,22 +1003,13 @@ static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   // workgroup per CU, so the B*HV*NVT workgroups spread over all CUs.
   size_t lds = sizeof(SM);
   if (lds < 84 * 1024) lds = 84 * 1024;
-  // the dynamic LDS limit is raised once per device (several threads may
-  // race to do it; each call sets the same value)
-  constexpr int kMaxDevices = 64;
-  static std::atomic<bool> configured[kMaxDevices];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  // the dynamic LDS limit above 64 KiB is raised on every launch (a host-side
+  // attribute of the function: cheap, and it leaves the library stateless)
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK, GS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const bool known = dev >= 0 && dev < kMaxDevices;
-  if (!known || !configured[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK, GS>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    if (known) configured[dev].store(true, std::memory_order_release);
-  }
   const int nheads = p.B * p.HV;
-  const long blocks = (long)((nheads + 7) / 8) * 8 * NVT;
+  const long blocks = (long)((nheads / p.G + 7) / 8) * 8 * p.G * NVT;
   hipLaunchKernelGGL((chunk_fwd_kernel<K, T, GK, GS>), dim3((unsigned)blocks), dim3(kThreads), lds,
                      stream, p);
   return hipGetLastError();
@@ -1017,7 +1019,12 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
                         int per_head, float lower_bound, const float* S0, float* o, float* S_out,
                         int B, int T, int H, int HV, int K, hipStream_t stream) {
-  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, B, T, H, HV, kind, lower_bound};
+  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, B, T, H, HV, kind, 1,
+                lower_bound};
+  // The value heads of one query/key head share an XCD (and their q, k reads
+  // its L2) when that keeps the eight XCDs evenly loaded.
+  const int Gq = HV / H;
+  p.G = (B * HV / Gq) % 8 == 0 ? Gq : 1;
 #define KDA_CHUNK_GS(KK, TT, GG)                                     \
   return per_head ? launch_chunk_kt<KK, TT, GG, true>(p, stream)     \
                   : launch_chunk_kt<KK, TT, GG, false>(p, stream);

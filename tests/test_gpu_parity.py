@@ -226,3 +226,27 @@ def test_decode_matches_oracle(B, T, H, HV, K, V, dtype):
     eo, eS = L.rel_err(o, ro), L.rel_err(S, rS)
     print("decode %s: o %.2e S %.2e" % ((B, T, H, HV, K, V, dtype), eo, eS))
     assert eo <= L.TOL_F32 and eS <= L.TOL_F32
+
+
+@pytest.mark.parametrize("K,dtype", [(16, "f32"), (128, "bf16")])
+def test_mixed_sign_decay_inside_a_block(K, dtype):
+    """Gate none with a log-decay of +15 then -15 per token inside a block,
+    entered with a zero state and beta = 0 up to the end of the growth: the
+    block's total decay is 1, but the partial products reach e^120, beyond
+    what the factorised form can hold, so the block must run token by token.
+    The recurrence stays finite."""
+    d = synth.random_inputs(1, 64, 2, 4, K, K, seed=31, dtype=dtype, s0_std=0.0)
+    g = torch.zeros_like(d["g_raw"])
+    g[:, 16:24] = 15.0
+    g[:, 24:32] = -15.0
+    d["g_raw"] = g
+    beta = d["beta"].clone()
+    beta[:, :24] = 0.0
+    d["beta"] = beta
+    print("mixed-sign decay: K=%d %s" % (K, dtype), flush=True)
+    o, S = L.run_chunk(d, "none", -5.0, 64)
+    ro, rS = L.oracle_full(d, "none", -5.0)
+    tol = L.TOL_F32 if dtype == "f32" else L.TOL_BF16
+    eo, eS = L.rel_err(o, ro), L.rel_err(S, rS)
+    print("  max|err|/rms o %.2e S %.2e" % (eo, eS))
+    assert eo <= tol and eS <= tol
