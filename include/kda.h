@@ -62,7 +62,9 @@ typedef enum {
   KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, HV % H != 0, ... */
   KDA_ERR_UNSUPPORTED = 2, /* valid but not built: head size, chunk size */
   KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-  KDA_ERR_HIP = 4          /* a kernel launch failed */
+  KDA_ERR_HIP = 4,         /* a kernel launch failed */
+  KDA_ERR_SCRATCH = 5      /* kda_chunk_fwd_split_noalloc: the workspace this call needs
+                              exceeds the library's fixed scratch */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -223,6 +225,36 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
                                const float* initial_state, float* o, float* final_state, float* h,
                                int B, int T, int H, int HV, int K, int V, int chunk_size,
                                void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_chunk_fwd_split_noalloc -- kda_chunk_fwd_split for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation and arguments, minus
+ * the workspace, which instead lives in a scratch array inside the library.
+ *
+ *   limit   the workspace kda_chunk_fwd_split_workspace_bytes(...) gives for
+ *           the call must not exceed 64 MiB (67,108,864 bytes), else
+ *           KDA_ERR_SCRATCH and nothing is enqueued.  For K = V = 128 and
+ *           chunk 64 a (sequence, value head, chunk) triple takes 164 KiB, so
+ *           e.g. 8 value heads x 3,136 tokens (49 chunks) fit, 3,200 do not.
+ *   memory  the call allocates nothing and calls no allocating routine.  Each
+ *           GPU the library runs on holds its own 64 MiB copy of the scratch
+ *           from the first use until the process ends; its address is looked
+ *           up once per device, on the first call made with that device
+ *           current.  Nothing in it needs to start at zero.
+ *   races   every call on one GPU shares that GPU's scratch: calls that may
+ *           overlap in time on one device (different streams, or host threads
+ *           enqueueing concurrently) must be ordered by the caller.  Calls on
+ *           one stream are ordered by it.
+ * Everything else as kda_chunk_fwd_split.
+ */
+kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v,
+                                       kda_dtype qkv_dtype, const float* g_raw, const float* beta,
+                                       const float* A_log, const float* dt_bias,
+                                       kda_gate_kind gate, float lower_bound,
+                                       const float* initial_state, float* o, float* final_state,
+                                       float* h, int B, int T, int H, int HV, int K, int V,
+                                       int chunk_size, kda_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["gate", "chunk_fwd", "chunk_fwd_split", "recurrent_fwd", "recurrent_step",
+__all__ = ["gate", "chunk_fwd", "chunk_fwd_split", "chunk_fwd_split_noalloc", "recurrent_fwd",
+           "recurrent_step",
            "chunk_fwd_workspace_bytes", "chunk_fwd_split_workspace_bytes", "KDAError"]
 
 KDAError = _lib.KDAError
@@ -168,6 +169,35 @@ def chunk_fwd_split(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", l
                                  _ptr(final_state), _ptr(h), B, T, H, HV, K, V, int(chunk_size),
                                  _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check("kda_chunk_fwd_split", st)
+    return o, final_state, h
+
+
+def chunk_fwd_split_noalloc(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe",
+                            lower_bound=-5.0, chunk_size=64, initial_state=None, o=None,
+                            final_state=None, h=None):
+    """:func:`chunk_fwd_split` without a workspace: the library's fixed 64 MiB
+    scratch holds it (kda_chunk_fwd_split_noalloc), so the call allocates no
+    device memory when o, final_state (and h, if wanted) are given.  Calls on
+    one device share that scratch and must not overlap.  Returns (o,
+    final_state, h)."""
+    lib = _lib.load()
+    qkv = _qkv_dtype(q)
+    dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
+                                                            initial_state)
+    if o is None:
+        o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (B, HV, K, V), dev)
+    if h is not None:
+        NC = (T + chunk_size - 1) // chunk_size if chunk_size > 0 else 0
+        _need(h, "h", torch.float32, (B, HV, NC, K, V), dev)
+    st = lib.kda_chunk_fwd_split_noalloc(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta),
+                                         _ptr(A_log), _ptr(dt_bias), _gate_code(gate, per_head),
+                                         float(lower_bound), _ptr(initial_state), _ptr(o),
+                                         _ptr(final_state), _ptr(h), B, T, H, HV, K, V,
+                                         int(chunk_size), _stream(dev))
+    _lib.check("kda_chunk_fwd_split_noalloc", st)
     return o, final_state, h
 
 

@@ -10,7 +10,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkda.so")
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+(KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP,
+ KDA_ERR_SCRATCH) = range(6)
 KDA_F32, KDA_BF16 = 0, 1
 GATES = {"standard": 0, "safe": 1, "none": 2}
 KDA_GATE_PER_HEAD = 16
@@ -34,6 +35,9 @@ SIGNATURES = {
     "kda_chunk_fwd_split": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_float,
                                      _vp, _vp, _vp, _vp] + [_c_int] * 7
                             + [_vp, ctypes.c_size_t, _vp]),
+    "kda_chunk_fwd_split_noalloc": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int,
+                                             _c_float, _vp, _vp, _vp, _vp] + [_c_int] * 7
+                                    + [_vp]),
 }
 
 _lib = None

@@ -42,6 +42,7 @@
 // the state and U serve as B operands straight from the accumulator layout.
 // Everything else, and the fp32-input chain, uses the fp32 MFMA (16x16x4);
 // bf16 inputs are widened on load.
+#include <mutex>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -1030,6 +1031,37 @@ static size_t image_bytes(int K, int C) {
 
 size_t split_workspace_bytes_per_chunk(int K, int V, int C) {
   return image_bytes(K, C) + ((size_t)C * V + (size_t)K * V) * sizeof(float);
+}
+
+// Scratch of the allocation-free entry point (kda_chunk_fwd_split_noalloc): the
+// split schedule's workspace in a fixed device array.  Each device holds its
+// own copy for the life of the process; host code must never pass the array's
+// name to a kernel (on the host it only stands for the symbol), only the
+// device address hipGetSymbolAddress gives for the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// This device's address of `scratch`, looked up once per device (the first
+// call on it) and kept; the lookup allocates nothing.
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, const float* g_raw,

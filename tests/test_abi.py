@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(["kda_status_string", "kda_version", "kda_gate",
                                   "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
                                   "kda_recurrent_step", "kda_recurrent_fwd",
-                                  "kda_chunk_fwd_split_workspace_bytes", "kda_chunk_fwd_split"])
+                                  "kda_chunk_fwd_split_workspace_bytes", "kda_chunk_fwd_split",
+                                  "kda_chunk_fwd_split_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -49,7 +50,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
+    for s in range(6):
         assert lib.kda_status_string(s).decode().startswith("KDA_")
     assert lib.kda_status_string(99) == b"unknown kda_status"
     assert lib.kda_version() >= 10000
@@ -232,3 +233,38 @@ def test_binding_refuses_without_library(tmp_path):
             _lib.load(str(tmp_path / "missing.so"))
     finally:
         _lib._lib = saved
+
+
+def _split_noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, dt=_lib.KDA_BF16, g=P, beta=P, A=P, bias=P, gate=1, L=-5.0, S0=None,
+             o=P, S=P, h=None, B=1, T=64, H=2, HV=4, K=128, V=128, C=64)
+    a.update(kw)
+    return lib.kda_chunk_fwd_split_noalloc(a["q"], a["k"], a["v"], a["dt"], a["g"], a["beta"],
+                                           a["A"], a["bias"], a["gate"], a["L"], a["S0"], a["o"],
+                                           a["S"], a["h"], a["B"], a["T"], a["H"], a["HV"], a["K"],
+                                           a["V"], a["C"], None)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    # 8 value heads x 3,200 tokens at chunk 64 need 8 * 50 * 164 KiB > 64 MiB
+    (dict(HV=8, T=3200), _lib.KDA_ERR_SCRATCH),
+    (dict(B=2, HV=64, T=4096), _lib.KDA_ERR_SCRATCH),
+    (dict(HV=3), _lib.KDA_ERR_INVALID_ARG),
+    (dict(k=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(h=P + 4), _lib.KDA_ERR_INVALID_ARG),
+    (dict(K=96, V=96), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(C=8), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(B=0), _lib.KDA_OK),
+])
+def test_chunk_fwd_split_noalloc_validation(lib, kw, status):
+    """Rejected on the host before anything touches a device, including a
+    problem whose workspace exceeds the fixed scratch."""
+    assert _split_noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_limit(lib):
+    """8 value heads x 3,136 tokens (49 chunks of 164 KiB each) fit in 64 MiB,
+    3,200 tokens (50 chunks) do not."""
+    assert lib.kda_chunk_fwd_split_workspace_bytes(1, 3136, 2, 8, 128, 128, 64) <= 64 << 20
+    assert lib.kda_chunk_fwd_split_workspace_bytes(1, 3200, 2, 8, 128, 128, 64) > 64 << 20
