@@ -121,6 +121,43 @@ def compare_heads(o, S, ref, tol, what):
     return eo, eS
 
 
+def compare_all_heads(d, w_gate, lower_bound, o, S, tol, what, group=16):
+    """Every (b, hv) pair against the oracle, element by element: the oracle
+    runs `group` pairs at a time (one per thread) so that host memory stays
+    bounded; the error is max |gpu - oracle| over all pairs divided by the RMS
+    of the oracle over all pairs, separately for o and the final state."""
+    d = per_channel_gate(d)
+    npf = lambda x: None if x is None else x.float().numpy()
+    args = [npf(d[n]) for n in ("q", "k", "v", "g_raw", "beta", "A_log", "dt_bias")]
+    s0 = npf(d["S0"])
+    B, HV = d["v"].shape[0], d["v"].shape[2]
+    o_cpu, S_cpu = o.detach().cpu(), S.detach().cpu()
+    pairs = [(b, hv) for b in range(B) for hv in range(HV)]
+    stats = {"o": [0.0, 0.0, 0], "S": [0.0, 0.0, 0]}  # max |err|, sum of squares, count
+
+    def acc(key, got, ref):
+        got = got.double().numpy()
+        if np.isnan(got).any():
+            raise AssertionError("%s: NaN in %s" % (what, key))
+        st = stats[key]
+        st[0] = max(st[0], float(np.abs(got - ref).max()) if ref.size else 0.0)
+        st[1] += float((ref * ref).sum())
+        st[2] += ref.size
+
+    orc = oracle.default()
+    for i in range(0, len(pairs), group):
+        ref = orc.kda_fwd_heads(*args, w_gate, lower_bound, s0, pairs[i:i + group])
+        for (b, hv), (o_ref, s_ref) in ref.items():
+            acc("o", o_cpu[b, :, hv], o_ref)
+            acc("S", S_cpu[b, hv], s_ref)
+    err = {k: (v[0] / math.sqrt(v[1] / v[2]) if v[1] > 0 else v[0]) for k, v in stats.items()}
+    print("%s: max|err|/rms  o %.3e  S %.3e  (tol %.0e, all %d pairs)" % (what, err["o"], err["S"],
+                                                                         tol, len(pairs)))
+    assert err["o"] <= tol, "%s: o error %.3e > %.0e" % (what, err["o"], tol)
+    assert err["S"] <= tol, "%s: state error %.3e > %.0e" % (what, err["S"], tol)
+    return err["o"], err["S"]
+
+
 def run_split(d, w_gate, lower_bound, chunk, initial_state=True):
     """kda_chunk_fwd_split with the chunk-entry states; returns (o, S, h)."""
     g = to_dev(d)
