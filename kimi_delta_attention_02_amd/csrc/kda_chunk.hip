@@ -913,6 +913,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             const float4 gm = *reinterpret_cast<const float4*>(&B.gam[16 * kb + 4 * g]);
             sacc[kb] *= f32x4{gm.x, gm.y, gm.z, gm.w};
           }
+          // bf16: the (k Suf)^T operands of the state update, read now so that
+          // their LDS latency passes under K_hat S and U
+          bf16x4 kth[F32 ? 1 : NKB], ktl[F32 ? 1 : NKB];
+          if constexpr (!F32) {
+            const uint16_t* a = B.keT.c + (lane & 15) * kCat + 4 * (lane >> 4);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+              kth[kb] = *reinterpret_cast<const bf16x4*>(a + 16 * kb * kCat);
+              ktl[kb] = *reinterpret_cast<const bf16x4*>(a + 16 * kb * kCat + 16);
+            }
+          }
           f32x4 pk = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
           if constexpr (F32)
             kprod2(pk, qs, B.kh, B.qh, C.st[tc & 1], lane);  // K_hat S and Q_hat S
@@ -972,8 +983,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             // and the chain has slack: the prep wave on this SIMD issues first.
             __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)  // S = gamma S + (k Suf)^T U
-              tprod_reg(sacc[kb], B.keT.c + 16 * kb * kCat, uh, ul, lane);
+            for (int kb = 0; kb < NKB; ++kb) {  // S = gamma S + (k Suf)^T U
+              sacc[kb] = mfma16(kth[kb], uh, sacc[kb]);
+              sacc[kb] = mfma16(kth[kb], ul, sacc[kb]);
+              sacc[kb] = mfma16(ktl[kb], uh, sacc[kb]);
+            }
           }
         }
         write_state_operand(C.st[(tc + 1) & 1]);
