@@ -13,6 +13,10 @@ time.  Definitions followed, all from the "K3 notes" pages:
 * recurrence: section "KDA 递归核心", four-step update with the 1/sqrt(K) read
   scale of step 4;
 * GVA: the input table of the same section (q, k repeat_interleave'd to HV).
+
+``kda_oracle_bwd.c`` differentiates the same recurrence and gate in reverse
+mode (the gradients the backward pass must produce); it is pinned by finite
+differences of the forward oracle, not by anything of its own.
 """
 from __future__ import annotations
 
@@ -32,11 +36,15 @@ GATE_KINDS = {"standard": 0, "safe": 1, "none": 2}
 _dp = ctypes.POINTER(ctypes.c_double)
 
 
-def build(source: str = SOURCE, out: str = LIBRARY) -> str:
-    """Compile the oracle with gcc into a shared library; returns its path."""
+BWD_SOURCE = os.path.join(_HERE, "kda_oracle_bwd.c")
+
+
+def build(source: str = SOURCE, out: str = LIBRARY, extra=(BWD_SOURCE,)) -> str:
+    """Compile the oracle with gcc into a shared library (the forward source,
+    plus the gradient source unless `extra` is empty); returns its path."""
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-D_POSIX_C_SOURCE=200809L",
-           "-o", tmp, source, "-lm", "-lpthread"]
+           "-o", tmp, source] + list(extra) + ["-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -70,6 +78,10 @@ class Oracle:
         lib.oracle_kda_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int,
                                        ctypes.c_double, _dp] + [ctypes.c_long] * 6 + [_dp, _dp,
                                                                                        ctypes.c_int]
+        if hasattr(lib, "oracle_kda_bwd"):
+            lib.oracle_kda_bwd.restype = ctypes.c_int
+            lib.oracle_kda_bwd.argtypes = ([_dp] * 7 + [ctypes.c_int, ctypes.c_double] + [_dp] * 3
+                                           + [ctypes.c_long] * 6 + [_dp] * 8 + [ctypes.c_int])
         self.lib = lib
 
     def gate(self, g_raw, A_log, dt_bias=None, gate="safe", lower_bound=-5.0):
@@ -109,6 +121,41 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_kda_fwd rejected its arguments")
         return o, s_out
+
+    def kda_bwd(self, q, k, v, g_raw, beta, A_log, dt_bias=None, gate="safe", lower_bound=-5.0,
+                initial_state=None, dout=None, dfinal_state=None, threads=None):
+        """Gradients of sum(o * dout) + sum(S_T * dfinal_state) with respect to
+        the inputs (reverse mode through the naive recurrence and the gate, in
+        float64).  Returns a dict with dq, dk [B,T,H,K], dv [B,T,HV,V], dbeta
+        [B,T,HV], dg_raw [B,T,HV,K], dA_log [HV], ddt_bias [HV,K] (None without
+        dt_bias) and dS0 [B,HV,K,V]."""
+        qa, qp = _arr(q)
+        B, T, H, K = qa.shape
+        va, vp = _arr(v)
+        HV, V = va.shape[2], va.shape[3]
+        _, kp = _arr(k, (B, T, H, K))
+        _, gp = _arr(g_raw, (B, T, HV, K))
+        _, bp = _arr(beta, (B, T, HV))
+        _, ap = _arr(A_log, (HV,))
+        _, dp = _arr(dt_bias, (HV, K))
+        _, sp = _arr(initial_state, (B, HV, K, V))
+        _, op = _arr(dout, (B, T, HV, V))
+        _, fp = _arr(dfinal_state, (B, HV, K, V))
+        out = {"dq": np.empty((B, T, H, K)), "dk": np.empty((B, T, H, K)),
+               "dv": np.empty((B, T, HV, V)), "dbeta": np.empty((B, T, HV)),
+               "dg_raw": np.empty((B, T, HV, K)), "dA_log": np.empty((HV,)),
+               "ddt_bias": np.empty((HV, K)) if dt_bias is not None else None,
+               "dS0": np.empty((B, HV, K, V))}
+        ptr = lambda a: None if a is None else a.ctypes.data_as(_dp)
+        n = threads or os.cpu_count() or 1
+        rc = self.lib.oracle_kda_bwd(qp, kp, vp, gp, bp, ap, dp, GATE_KINDS[gate],
+                                     float(lower_bound), sp, op, fp, B, T, H, HV, K, V,
+                                     ptr(out["dq"]), ptr(out["dk"]), ptr(out["dv"]),
+                                     ptr(out["dbeta"]), ptr(out["dg_raw"]), ptr(out["dA_log"]),
+                                     ptr(out["ddt_bias"]), ptr(out["dS0"]), int(n))
+        if rc != 0:
+            raise ValueError("oracle_kda_bwd rejected its arguments")
+        return out
 
     def kda_fwd_heads(self, q, k, v, g_raw, beta, A_log, dt_bias, gate, lower_bound,
                       initial_state, heads, threads=None):
@@ -159,4 +206,14 @@ def build_variant(source_text: str, directory: str | None = None) -> Oracle:
     src = os.path.join(d, "variant.c")
     with open(src, "w") as f:
         f.write(source_text)
-    return Oracle(build(src, os.path.join(d, "libvariant.so")))
+    return Oracle(build(src, os.path.join(d, "libvariant.so"), extra=()))
+
+
+def build_bwd_variant(source_text: str, directory: str | None = None) -> Oracle:
+    """Compile the oracle with a modified copy of the gradient source (the
+    gradient pins plant a mistake there and check that they catch it)."""
+    d = directory or tempfile.mkdtemp(prefix="oracle_bwd_variant_")
+    src = os.path.join(d, "variant_bwd.c")
+    with open(src, "w") as f:
+        f.write(source_text)
+    return Oracle(build(SOURCE, os.path.join(d, "libvariant.so"), extra=(src,)))
