@@ -170,7 +170,7 @@ static void bwd_pair(const bwd_job_t* J, long b, long hv, double* S, double* alp
       for (long j = 0; j < V; ++j) dS[c * V + j] = al * dSd[c * V + j];
       /* gate */
       J->dg_raw[(bt * HV + hv) * K + c] = dg * dgx[t * K + c];
-      dbias[c] += dg * dgx[t * K + c];
+      if (J->kind != BWD_GATE_NONE) dbias[c] += dg * dgx[t * K + c]; /* none: no bias */
       dalog += dg * dga[t * K + c];
     }
   }

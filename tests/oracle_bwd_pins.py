@@ -55,8 +55,6 @@ def pin_bwd_finite_differences(orc):
         gname = {"q": "dq", "k": "dk", "v": "dv", "g_raw": "dg_raw", "beta": "dbeta",
                  "A_log": "dA_log", "dt_bias": "ddt_bias", "S0": "dS0"}
         for name in NAMES:
-            if gate == "none" and name in ("A_log", "dt_bias"):
-                continue  # the gate is the identity: nothing depends on them
             x = d[name]
             flat = x.reshape(-1)
             got = g[gname[name]].reshape(-1)
