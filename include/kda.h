@@ -256,6 +256,64 @@ kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void*
                                        float* h, int B, int T, int H, int HV, int K, int V,
                                        int chunk_size, kda_stream_t stream);
 
+/*
+ * kda_bwd -- gradients of the KDA forward (kda_chunk_fwd and its siblings
+ * compute the same function) for a loss L(o, S_T), given dL/do and dL/dS_T.
+ * The "K3 notes" ledger lists a backward derivation ("反向传播推导") whose
+ * text the pages do not keep; these are the reverse-mode gradients of the
+ * four-step update of section "KDA 递归核心" and of the gate of section
+ * "Gate 激活", for one (sequence, value head) with dS the running dL/dS_t,
+ * token by token from the last (s = 1/sqrt(K), alpha = exp(g)):
+ *     dS += s q_t do_t^T,  dq_t = s S_t do_t,  a = dS^T k_t,  dr = beta_t a,
+ *     dv_t = dr,  dbeta_t = a . r_t,  dk_t = beta_t dS r_t - Sd_t dr,
+ *     dSd = dS - k_t dr^T,  dg_t = rowsum(dSd (.) Sd_t),  dS <- diag(alpha_t) dSd
+ * then the gate's chain rule: dg_raw = dg dg/dx with x = g_raw + dt_bias, and
+ * the sums of dg dg/dx (dt_bias) and dg dg/dA_log (A_log) over sequences and
+ * tokens.  Under the none gate dt_bias and A_log do not enter the forward and
+ * their gradients are zero.  Under GVA, dq and dk sum over the value heads
+ * that read the same query/key head.
+ *
+ *   q, k, v, qkv_dtype, g_raw, beta, A_log, dt_bias, gate, lower_bound,
+ *   initial_state        the forward's inputs, as kda_chunk_fwd (per-channel
+ *                        gate only)
+ *   dout                 [B, T, HV, V]  float32, dL/do
+ *   dfinal_state         [B, HV, K, V]  float32, dL/dS_T, or NULL for zero
+ *   dq, dk               [B, T, H, K]   float32 outputs
+ *   dv                   [B, T, HV, V]  float32 output
+ *   dbeta                [B, T, HV]     float32 output
+ *   dg_raw               [B, T, HV, K]  float32 output
+ *   dA_log               [HV]           float32 output, or NULL to skip
+ *   ddt_bias             [HV, K]        float32 output, or NULL to skip (with
+ *                                       dt_bias NULL it is the gradient at a
+ *                                       zero bias)
+ *   dinitial_state       [B, HV, K, V]  float32 output (dL/dS_0), or NULL
+ *   workspace            device scratch of at least kda_bwd_workspace_bytes(...)
+ *                        bytes, 16-byte aligned, owned by the caller; it holds
+ *                        the state entering every 16-token segment, written by
+ *                        the split schedule's forward, and that schedule's own
+ *                        scratch; its contents are meaningless afterwards
+ * Every output is overwritten (none needs initialising).  dq, dk, dg_raw,
+ * dbeta, dA_log and ddt_bias are sums accumulated with fp32 atomics, so their
+ * last bits can differ from run to run; dv and dinitial_state are written
+ * once.  All pointers are device pointers; outputs must not alias inputs or
+ * each other.
+ * Supported: K == V in {32, 64, 128}; HV % H == 0; T >= 0; a per-channel gate
+ * (KDA_GATE_PER_HEAD is KDA_ERR_UNSUPPORTED).  Arithmetic is fp32 throughout
+ * (bf16 inputs widened exactly; the forward pass that writes the segment
+ * states is that of kda_chunk_fwd_split with chunk 16).  Several kernels run
+ * in order on `stream`.  Returns KDA_ERR_WORKSPACE if the workspace is missing
+ * or too small.
+ */
+size_t kda_bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V);
+
+kda_status kda_bwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                   const float* g_raw, const float* beta, const float* A_log, const float* dt_bias,
+                   kda_gate_kind gate, float lower_bound, const float* initial_state,
+                   const float* dout, const float* dfinal_state, float* dq, float* dk, float* dv,
+                   float* dbeta, float* dg_raw, float* dA_log, float* ddt_bias,
+                   float* dinitial_state, int B, int T, int H, int HV, int K, int V,
+                   void* workspace, size_t workspace_bytes, kda_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

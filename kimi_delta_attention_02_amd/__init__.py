@@ -22,8 +22,9 @@ import torch
 from . import _lib
 
 __all__ = ["gate", "chunk_fwd", "chunk_fwd_split", "chunk_fwd_split_noalloc", "recurrent_fwd",
-           "recurrent_step",
-           "chunk_fwd_workspace_bytes", "chunk_fwd_split_workspace_bytes", "KDAError"]
+           "recurrent_step", "bwd",
+           "chunk_fwd_workspace_bytes", "chunk_fwd_split_workspace_bytes", "bwd_workspace_bytes",
+           "KDAError"]
 
 KDAError = _lib.KDAError
 
@@ -199,6 +200,52 @@ def chunk_fwd_split_noalloc(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="
                                          int(chunk_size), _stream(dev))
     _lib.check("kda_chunk_fwd_split_noalloc", st)
     return o, final_state, h
+
+
+def bwd_workspace_bytes(B, T, H, HV, K, V):
+    """Device workspace bytes kda_bwd needs for these sizes."""
+    return int(_lib.load().kda_bwd_workspace_bytes(B, T, H, HV, K, V))
+
+
+def bwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_bound=-5.0,
+        initial_state=None, dout, dfinal_state=None, want_dA_log=True, want_ddt_bias=None,
+        want_dinitial_state=None, workspace=None):
+    """Gradients of the forward (kda_bwd) for dL/do = dout [B, T, HV, V] and
+    dL/dS_T = dfinal_state (or zero).  Returns a dict of float32 tensors: dq,
+    dk [B, T, H, K], dv [B, T, HV, V], dbeta [B, T, HV], dg_raw [B, T, HV, K],
+    dA_log [HV] (None unless want_dA_log), ddt_bias [HV, K] (by default when
+    dt_bias is given), dS0 [B, HV, K, V] (by default when initial_state is
+    given)."""
+    lib = _lib.load()
+    qkv = _qkv_dtype(q)
+    dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
+                                                            initial_state)
+    _need(dout, "dout", torch.float32, (B, T, HV, V), dev)
+    if dfinal_state is not None:
+        _need(dfinal_state, "dfinal_state", torch.float32, (B, HV, K, V), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
+           "dv": torch.empty((B, T, HV, V), **f32), "dbeta": torch.empty((B, T, HV), **f32),
+           "dg_raw": torch.empty((B, T, HV, K), **f32)}
+    out["dA_log"] = torch.empty((HV,), **f32) if want_dA_log else None
+    if want_ddt_bias is None:
+        want_ddt_bias = dt_bias is not None
+    out["ddt_bias"] = torch.empty((HV, K), **f32) if want_ddt_bias else None
+    if want_dinitial_state is None:
+        want_dinitial_state = initial_state is not None
+    out["dS0"] = torch.empty((B, HV, K, V), **f32) if want_dinitial_state else None
+    need = int(lib.kda_bwd_workspace_bytes(B, T, H, HV, K, V))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), qkv, _ptr(g_raw), _ptr(beta), _ptr(A_log),
+                     _ptr(dt_bias), _gate_code(gate, per_head), float(lower_bound),
+                     _ptr(initial_state), _ptr(dout), _ptr(dfinal_state), _ptr(out["dq"]),
+                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dg_raw"]),
+                     _ptr(out["dA_log"]), _ptr(out["ddt_bias"]), _ptr(out["dS0"]),
+                     B, T, H, HV, K, V, _ptr(workspace), ws_bytes, _stream(dev))
+    _lib.check("kda_bwd", st)
+    return out
 
 
 def _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias, initial_state):

@@ -38,6 +38,10 @@ SIGNATURES = {
     "kda_chunk_fwd_split_noalloc": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int,
                                              _c_float, _vp, _vp, _vp, _vp] + [_c_int] * 7
                                     + [_vp]),
+    "kda_bwd_workspace_bytes": (ctypes.c_size_t, [_c_int] * 6),
+    "kda_bwd": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_float, _vp,
+                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 6
+                + [_vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None

@@ -31,6 +31,13 @@ hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, c
                         int per_head, float lower_bound, const float* S0, float* o, float* S_out,
                         float* h, void* workspace, int B, int T, int H, int HV, int K, int C,
                         hipStream_t stream);
+size_t bwd_workspace_bytes(int B, int T, int HV, int K, int V);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
+                      const float* beta, const float* A_log, const float* dt_bias, int kind,
+                      float lower_bound, const float* S0, const float* dout, const float* dST,
+                      float* dq, float* dk, float* dv, float* dbeta, float* dg_raw, float* dA_log,
+                      float* ddt_bias, float* dS0, void* workspace, int B, int T, int H, int HV,
+                      int K, hipStream_t stream);
 size_t noalloc_scratch_bytes();
 hipError_t noalloc_scratch(void** out);
 }  // namespace kda
@@ -271,6 +278,51 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
                                     gate_base(gate), gate_per_head(gate), lower_bound,
                                     initial_state, o, final_state, h, workspace, B, T, H, HV, K,
                                     chunk_size, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t kda_bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V) {
+  (void)H;
+  if (B <= 0 || T <= 0 || HV <= 0 || K != V || (K != 32 && K != 64 && K != 128)) return 0;
+  return kda::bwd_workspace_bytes(B, T, HV, K, V);
+}
+
+kda_status kda_bwd(const void* q, const void* k, const void* v, kda_dtype qkv_dtype,
+                   const float* g_raw, const float* beta, const float* A_log, const float* dt_bias,
+                   kda_gate_kind gate, float lower_bound, const float* initial_state,
+                   const float* dout, const float* dfinal_state, float* dq, float* dk, float* dv,
+                   float* dbeta, float* dg_raw, float* dA_log, float* ddt_bias,
+                   float* dinitial_state, int B, int T, int H, int HV, int K, int V,
+                   void* workspace, size_t workspace_bytes, kda_stream_t stream) {
+  kda_status st = check_gate(gate, lower_bound, A_log);
+  if (st != KDA_OK) return st;
+  if (gate_per_head(gate)) return KDA_ERR_UNSUPPORTED;
+  if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0) return KDA_ERR_INVALID_ARG;
+  if ((long)B * HV > (1L << 26) || HV > 65535) return KDA_ERR_INVALID_ARG;
+  if ((K != 32 && K != 64 && K != 128) || V != K) return KDA_ERR_UNSUPPORTED;
+  const long nc = ((long)T + 15) / 16;
+  if ((long)B * HV * nc > 0x7fffffffL || (long)B * T > 0x7fffffffL) return KDA_ERR_INVALID_ARG;
+  if (B > 0 && T > 0 &&
+      (!q || !k || !v || !g_raw || !beta || !dout || !dq || !dk || !dv || !dbeta || !dg_raw))
+    return KDA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, dv, initial_state, dinitial_state, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+  const void* ptrs4[] = {dout, dfinal_state, dq, dk, dbeta, dg_raw, dA_log, ddt_bias};
+  for (const void* ptr : ptrs4)
+    if (ptr && !aligned4(ptr)) return KDA_ERR_INVALID_ARG;
+  if (!gate_inputs_aligned(gate, g_raw, dt_bias)) return KDA_ERR_INVALID_ARG;
+  const size_t need = kda_bwd_workspace_bytes(B, T, H, HV, K, V);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (B == 0 && !dA_log && !ddt_bias) return KDA_OK;  // else those two sums are zero-filled
+  return from_hip(kda::launch_bwd(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log, dt_bias,
+                                  gate_base(gate), lower_bound, initial_state, dout, dfinal_state,
+                                  dq, dk, dv, dbeta, dg_raw, dA_log, ddt_bias, dinitial_state,
+                                  workspace, B, T, H, HV, K, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -91,6 +91,29 @@ int main() {
     return kda_chunk_fwd_split_noalloc(P, P, P, KDA_BF16, F, F, F, F, KDA_GATE_SAFE, -5.f, nullptr,
                                        F, F, nullptr, 4, 65536, 16, 64, 128, 128, 64, nullptr); });
 
+  // kda_bwd
+  const size_t bneed = kda_bwd_workspace_bytes(2, 37, 2, 4, 64, 64);
+  CHECK(bneed > 0, "bwd workspace size");
+  CHECK(kda_bwd_workspace_bytes(2, 37, 2, 4, 16, 16) == 0, "bwd workspace of an unsupported size");
+  auto bwd = [&](kda_gate_kind gate, int K, int V, const void* q, float* dq, void* ws, size_t wsb,
+                 int H, int HV, int T) {
+    return kda_bwd(q, P, P, KDA_F32, F, F, F, F, gate, -5.f, F, F, nullptr, dq, F, F, F, F, F, F,
+                   F, 2, T, H, HV, K, V, ws, wsb, nullptr);
+  };
+  expect("bwd ok", KDA_OK, true, [&] { return bwd(KDA_GATE_SAFE, 64, 64, P, F, P, bneed, 2, 4, 37); });
+  CHECK(g_last.B == 2 && g_last.T == 37 && g_last.H == 2 && g_last.HV == 4 && g_last.K == 64 &&
+        g_last.workspace == P, "bwd sizes not forwarded");
+  expect("bwd small ws", KDA_ERR_WORKSPACE, false, [&] {
+    return bwd(KDA_GATE_SAFE, 64, 64, P, F, P, bneed - 1, 2, 4, 37); });
+  expect("bwd per-head", KDA_ERR_UNSUPPORTED, false, [&] {
+    return bwd((kda_gate_kind)(KDA_GATE_SAFE | KDA_GATE_PER_HEAD), 64, 64, P, F, P, bneed, 2, 4, 37); });
+  expect("bwd K=16", KDA_ERR_UNSUPPORTED, false, [&] { return bwd(KDA_GATE_SAFE, 16, 16, P, F, P, bneed, 2, 4, 37); });
+  expect("bwd K!=V", KDA_ERR_UNSUPPORTED, false, [&] { return bwd(KDA_GATE_SAFE, 64, 32, P, F, P, bneed, 2, 4, 37); });
+  expect("bwd null dq", KDA_ERR_INVALID_ARG, false, [&] { return bwd(KDA_GATE_SAFE, 64, 64, P, nullptr, P, bneed, 2, 4, 37); });
+  expect("bwd align", KDA_ERR_INVALID_ARG, false, [&] { return bwd(KDA_GATE_SAFE, 64, 64, P2, F, P, bneed, 2, 4, 37); });
+  expect("bwd HV%H", KDA_ERR_INVALID_ARG, false, [&] { return bwd(KDA_GATE_SAFE, 64, 64, P, F, P, bneed, 3, 4, 37); });
+  expect("bwd T=0", KDA_OK, true, [&] { return bwd(KDA_GATE_SAFE, 64, 64, P, F, nullptr, 0, 2, 4, 0); });
+
   if (fails) { fprintf(stderr, "%d check(s) failed\n", fails); return 1; }
   printf("api driver: all checks passed (%d launches)\n", g_last.count);
   return 0;

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
                                   "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
                                   "kda_recurrent_step", "kda_recurrent_fwd",
                                   "kda_chunk_fwd_split_workspace_bytes", "kda_chunk_fwd_split",
-                                  "kda_chunk_fwd_split_noalloc"])
+                                  "kda_chunk_fwd_split_noalloc", "kda_bwd_workspace_bytes",
+                                  "kda_bwd"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -268,3 +269,48 @@ def test_noalloc_scratch_limit(lib):
     3,200 tokens (50 chunks) do not."""
     assert lib.kda_chunk_fwd_split_workspace_bytes(1, 3136, 2, 8, 128, 128, 64) <= 64 << 20
     assert lib.kda_chunk_fwd_split_workspace_bytes(1, 3200, 2, 8, 128, 128, 64) > 64 << 20
+
+
+def _bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, dt=_lib.KDA_F32, g=P, beta=P, A=P, bias=P, gate=1, L=-5.0, S0=None,
+             do=P, dST=None, dq=P, dk=P, dv=P, dbeta=P, dg=P, dA=P, dbias=P, dS0=None,
+             B=2, T=37, H=2, HV=4, K=64, V=64, ws=P, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.kda_bwd_workspace_bytes(a["B"], a["T"], a["H"], a["HV"], a["K"], a["V"])
+    return lib.kda_bwd(a["q"], a["k"], a["v"], a["dt"], a["g"], a["beta"], a["A"], a["bias"],
+                       a["gate"], a["L"], a["S0"], a["do"], a["dST"], a["dq"], a["dk"], a["dv"],
+                       a["dbeta"], a["dg"], a["dA"], a["dbias"], a["dS0"], a["B"], a["T"], a["H"],
+                       a["HV"], a["K"], a["V"], a["ws"], a["wsb"], None)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(gate=_lib.KDA_GATE_PER_HEAD | 1), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(K=16, V=16), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(K=64, V=32), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(dq=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(do=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(dv=P + 4), _lib.KDA_ERR_INVALID_ARG),
+    (dict(dq=P + 2), _lib.KDA_ERR_INVALID_ARG),
+    (dict(HV=3), _lib.KDA_ERR_INVALID_ARG),
+    (dict(A=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(L=0.0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(ws=None), _lib.KDA_ERR_WORKSPACE),
+    (dict(wsb=1024), _lib.KDA_ERR_WORKSPACE),
+    (dict(B=0, ws=None, wsb=0, dA=None, dbias=None), _lib.KDA_OK),
+])
+def test_bwd_validation(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_bytes(lib):
+    """Segment states (one K x V fp32 state per 16 tokens) plus the forward's
+    outputs and the split schedule's own scratch at chunk 16."""
+    n = lib.kda_bwd_workspace_bytes(1, 4096, 16, 16, 128, 128)
+    states = 16 * 256 * 128 * 128 * 4
+    assert n >= states + 4096 * 16 * 128 * 4 + 16 * 256 * lib.kda_chunk_fwd_split_workspace_bytes(
+        1, 16, 1, 1, 128, 128, 16)
+    assert lib.kda_bwd_workspace_bytes(1, 4096, 16, 16, 16, 16) == 0
+    assert lib.kda_bwd_workspace_bytes(0, 4096, 16, 16, 128, 128) == 0
+
