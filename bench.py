@@ -16,7 +16,10 @@ object; the fused multi-token recurrent forward runs the same 256 tokens as
 forward runs the prefill shape with one gate per (token, value head)
 ("head_gate" object), and the one-sequence long shard (T=65536, 8 value heads)
 runs through both the fused chunk kernel and the three-stage split schedule
-("split" object).
+("split" object).  The backward pass (kda_bwd) runs on the prefill shape
+("backward" object): its roofline covers the segment phase, the call's time
+minus that of the chunk-16 split forward it starts with, against the fp32
+vector peak.
 
 Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
 HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
@@ -40,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 
 
 def chunk_bytes(w):
@@ -65,6 +69,27 @@ def chunk_flops(w, C=BLOCK):
     2 (3 C K + 2 C V + 3 K V) per token and value head (A_qk, R, w, u, U,
     Q S, A U, state update)."""
     return 2 * (3 * C * w.K + 2 * C * w.V + 3 * w.K * w.V) * w.B * w.T * w.HV
+
+
+def bwd_flops(w):
+    """Arithmetic of the backward's segment phase per token and value head,
+    an FMA counted as two: the state rebuilt from its segment checkpoint
+    (Sd = alpha S, Sd^T k, S = Sd + beta k r^T: 5 K V) and the reverse step
+    (dS += s q do^T, S_t do, dS^T k, beta dS r - Sd dr, dS - k dr^T,
+    rowsum(dSd Sd), alpha dSd: 15 K V)."""
+    return 20 * w.K * w.V * w.B * w.T * w.HV
+
+
+def bwd_bytes(w):
+    """Algorithmic HBM bytes of one backward pass: the forward's inputs and
+    dL/do read once, every gradient written once (dq, dk per query/key head)."""
+    e = 2 if w.dtype == "bf16" else 4
+    tok = w.B * w.T
+    reads = (2 * tok * w.H * w.K * e + tok * w.HV * w.V * e + tok * w.HV * w.K * 4
+             + tok * w.HV * 4 + tok * w.HV * w.V * 4)
+    writes = 2 * tok * w.H * w.K * 4 + tok * w.HV * w.V * 4 + tok * w.HV * 4 + tok * w.HV * w.K * 4
+    state = w.B * w.HV * w.K * w.V * 4 * (2 if w.s0_std > 0 else 0)
+    return reads + writes + state
 
 
 def decode_bytes(w):
@@ -173,6 +198,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-split", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward line")
     ap.add_argument("--no-gate", action="store_true", help="skip the standalone gate line")
     ap.add_argument("--no-head-gate", action="store_true", help="skip the per-head gate line")
     ap.add_argument("--no-configs", action="store_true",
@@ -471,6 +497,59 @@ def main():
             del chunks, outs
         result["recurrent"] = rec
         del gd, st
+
+    # Backward pass on the prefill shape: kda_bwd (the split forward at chunk
+    # 16 writing segment checkpoints, then the segment and gate kernels).
+    if not args.no_bwd:
+        wb = synth.WORKLOADS["prefill"]
+        db = synth.make_inputs(wb)
+        gb = {n: (t.to(dev) if t is not None else None) for n, t in db.items()}
+        gen = torch.Generator(device="cpu").manual_seed(77)
+        dout = torch.randn((wb.B, wb.T, wb.HV, wb.V), generator=gen).to(dev)
+        wsb = torch.empty(kda.bwd_workspace_bytes(wb.B, wb.T, wb.H, wb.HV, wb.K, wb.V),
+                          dtype=torch.uint8, device=dev)
+        nc16 = (wb.T + 15) // 16
+        hb = torch.empty((wb.B, wb.HV, nc16, wb.K, wb.V), dtype=torch.float32, device=dev)
+        ob = torch.empty((wb.B, wb.T, wb.HV, wb.V), dtype=torch.float32, device=dev)
+        wss = torch.empty(kda.chunk_fwd_split_workspace_bytes(wb.B, wb.T, wb.H, wb.HV, wb.K, wb.V,
+                                                              16), dtype=torch.uint8, device=dev)
+        argsb = (gb["q"], gb["k"], gb["v"], gb["g_raw"], gb["beta"], gb["A_log"], gb["dt_bias"])
+
+        def timed(fn, n):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            z.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(z) / n
+
+        n_b = max(1, min(args.steps, 5))
+        bwd_ms = timed(lambda: kda.bwd(*argsb, gate=wb.gate, lower_bound=wb.lower_bound,
+                                       initial_state=gb["S0"], dout=dout, workspace=wsb), n_b)
+        fwd16_ms = timed(lambda: kda.chunk_fwd_split(*argsb, gate=wb.gate,
+                                                     lower_bound=wb.lower_bound, chunk_size=16,
+                                                     initial_state=gb["S0"], o=ob, h=hb,
+                                                     output_final_state=False, workspace=wss), n_b)
+        seg_ms = bwd_ms - fwd16_ms
+        fl = bwd_flops(wb)
+        result["backward"] = {
+            "workload": wb.name, "B": wb.B, "T": wb.T, "H": wb.H, "HV": wb.HV, "K": wb.K,
+            "gate": wb.gate, "dtype": wb.dtype, "calls": n_b, "ms_per_call": bwd_ms,
+            "value": wb.B * wb.T / (bwd_ms * 1e-3), "unit": "tokens/s",
+            "algorithmic_bytes": bwd_bytes(wb),
+            "hbm_frac_whole_call": bwd_bytes(wb) / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "split_forward_chunk16_ms": fwd16_ms,
+            "roofline": {"bound": "alu", "achieved": fl / (seg_ms * 1e-3) / 1e12,
+                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": fl / (seg_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+                         "traffic": None, "flops_per_launch": fl, "launch_ms": seg_ms,
+                         "kernel": "bwd_segment_kernel<128, bf16, safe gate> (with the gate and "
+                                   "zero-fill kernels: the call minus its split forward)"}}
+        del gb, dout, wsb, hb, ob, wss
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4

@@ -20,18 +20,24 @@
 // heads that share a query/key head.
 //
 // Schedule.  The states S_{t-1} the reverse pass needs come from checkpoints:
-// the split schedule (kda_split.hip) writes the state entering every 16-token
-// segment; then one workgroup per (sequence, value head, 16-wide value tile)
-// walks the segments from the last, recomputes a segment's sixteen states from
-// its checkpoint into LDS (128 KiB for K = 128) and runs the reverse recurrence
-// over them with its tile of dS in registers.  Thread 2 kappa + c holds key row
-// kappa, value columns 8 c .. 8 c + 7 of the tile: sums over the columns are
-// in-thread plus one lane exchange, sums over the keys are DPP row rotations,
-// row swaps and one LDS exchange across the wavefronts.  The per-key results
-// (dq, dk, dg) and dbeta, summed over the value tiles (and the value heads of a
-// GVA group), are accumulated with fp32 atomics into zeroed outputs, so their
-// last bits depend on the order the tiles finish in.  A last kernel applies
-// the gate's chain rule and sums dt_bias and A_log over the sequences.
+// the split schedule (kda_split.hip, chunk 16, without its output stage)
+// writes the state entering every 16-token segment and leaves U_t = beta_t r_t
+// of every token in its workspace.  One workgroup per (sequence, value head,
+// 16-wide value tile) then walks the segments from the last.  Thread
+// 4 kappa + c holds key row kappa, value columns 4 c .. 4 c + 3 of the tile.
+// Per segment it stages the retain factors, k and q of the sixteen tokens in
+// LDS, rebuilds the sixteen states from the checkpoint in registers with
+// S_t = diag(alpha_t) S_{t-1} + k_t U_t^T (no reduction), then runs the
+// reverse recurrence with its tile of dS in registers.  Each reverse token
+// needs one sum over the keys, of dS^T k_t and of the prediction Sd_t^T k_t
+// together (the residual r_t is formed again from the latter): DPP row
+// rotations, row swaps and one LDS exchange across the wavefronts; sums over
+// the tile's columns are in-thread plus two lane exchanges.  The per-key
+// results (dq, dk, dg) and dbeta, summed over the value tiles (and the value
+// heads of a GVA group), are accumulated with fp32 atomics into zeroed
+// outputs, so their last bits depend on the order the tiles finish in.  A
+// last kernel applies the gate's chain rule and sums dt_bias and A_log over
+// the sequences.
 // Arithmetic is fp32 throughout (bf16 inputs widened exactly).
 #include <type_traits>
 
@@ -50,6 +56,7 @@ struct BwdParams {
   const float* dout;
   const float* dST;   // dL/dS_T or null
   const float* ckpt;  // [B, HV, NC, K, V]: the state entering each 16-token segment
+  const float* u;     // U = beta r of every token, as the split schedule's state pass left it
   float* dq;
   float* dk;
   float* dv;
@@ -70,196 +77,314 @@ __global__ void bwd_zero_kernel(float* p, long n) {
   if (i < n) p[i] = 0.0f;
 }
 
-// x + the value N lanes further round its 16-lane row (DPP row rotation)
+// x + the value N lanes further round its 16-lane row (DPP row rotation).
+// Every source lane of these permutations exists, so bound_ctrl (which only
+// matters for missing ones) is set: it lets the add take the DPP operand.
 template <int N>
 __device__ __forceinline__ float ror_add(float x) {
   return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                           0, __builtin_bit_cast(int, x), 0x120 + N, 0xF, 0xF, false));
+                                           0, __builtin_bit_cast(int, x), 0x120 + N, 0xF, 0xF, true));
 }
-// x + the value of the neighbouring lane (quad permutation [1, 0, 3, 2])
-__device__ __forceinline__ float pair_add(float x) {
+// the sum of x over each group of eight lanes (quad permutations [1, 0, 3, 2]
+// and [2, 3, 0, 1], then the mirror inside each half-row of 8)
+__device__ __forceinline__ float oct_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1,
+                                                             0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E,
+                                                             0xF, 0xF, true));
   return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                   0xB1, 0xF, 0xF, false));
+                                                                   0x141, 0xF, 0xF, true));
+}
+// the sum of x over each group of four lanes (quad permutations [1, 0, 3, 2]
+// then [2, 3, 0, 1])
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1,
+                                                             0xF, 0xF, true));
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                   0x4E, 0xF, 0xF, true));
 }
 
 template <int K>
 struct BwdSmem {
-  float st[kSeg][K][kBV];  // S_{t-1} of the segment's tokens, this tile's columns
-  float r[kSeg][kBV];      // residuals
+  float al[kSeg][K];  // retain factors of the segment's tokens
+  float k[kSeg][K];
+  float q[kSeg][K];    // s q
+  float u[kSeg][kBV];  // U = beta r from the forward's state pass
   float v[kSeg][kBV];
   float dout[kSeg][kBV];
   float beta[kSeg];
-  float red[2][K / 32][kBV];  // per-wavefront partial sums over the keys (two buffers)
+  float red[2][K / 16][2][kBV];  // per-wavefront key sums of a and Sd^T k (two buffers)
+  float fin[K / 16][8][4];        // each wavefront's totals of the 8 groups of 4 (quantity, column)
+  // the segment's results, written out together once it is done
+  float dq[kSeg][K];
+  float dk[kSeg][K];
+  float dg[kSeg][K];
+  float dv[kSeg][kBV];
+  float db[kSeg];
 };
 
-template <int K, int V, typename T, int GK>
-__global__ __launch_bounds__(2 * K) void bwd_segment_kernel(BwdParams p) {
-  constexpr int NW = 2 * K / 64;  // wavefronts
-  constexpr int NVT = V / kBV;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  BwdSmem<K>& sm = *reinterpret_cast<BwdSmem<K>*>(smem_raw);
+// One segment's inputs in flight: this thread's share of g_raw, k and q
+// (key channel tid % K, tokens tid / K + 4 i), of v, dL/do, U and beta, and
+// its own row of the checkpoint.
+template <typename T, int NVD>
+struct SegLoads {
+  float g[4];
+  typename In<T>::Raw1 k[4], q[4], v[NVD];
+  float dout[NVD], beta;
+  float4 u, ckpt;
+};
+
+template <int K, typename T, int GK>
+__global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void bwd_segment_kernel(
+    BwdParams p) {
+  constexpr int V = K, NT = 4 * K, NW = NT / 64, NVT = V / kBV;
+  constexpr int NVD = (kSeg * kBV + NT - 1) / NT;  // v and dL/do elements each thread stages
+  static_assert(kSeg * K / NT == 4 && NT >= 64, "thread layout");
+  __shared__ BwdSmem<K> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int kap = tid >> 1, ch = tid & 1, c8 = 8 * ch;
+  const int kap = tid >> 2, cg = tid & 3, c4 = 4 * cg;
   const int vt = blockIdx.x % NVT, hd = blockIdx.x / NVT;
-  const int HV = p.HV, H = p.H, T_ = p.T;
+  const int HV = p.HV, H = p.H, T_ = p.T, NC = p.NC;
   const long b = hd / HV;
   const int hv = hd % HV, h = hv / (HV / H), v0 = vt * kBV;
   const float scale = 1.0f / __builtin_sqrtf((float)K);
   const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
   const GateConsts gc = gate_consts(rate, p.lower_bound);
-  const float bias = gate_bias_pre<GK>((p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * K + kap] : 0.0f, gc);
+  const int cown = tid % K, town = tid / K;  // the key channel and first token this thread stages
+  const float bias = gate_bias_pre<GK>(
+      (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * K + cown] : 0.0f, gc);
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
 
-  // sum over the keys of each of this thread's 8 columns: rows of 16 lanes
-  // hold 8 keys x 2 column halves, so rotations by 2, 4, 8 keep the half;
-  // then the four rows of the wavefront; then the wavefronts, through LDS
+  // Issue the loads of segment seg (rows past the end re-read the last
+  // token, n >= 1; what they hold is never used).  Addresses are a base
+  // uniform over the workgroup plus a 32-bit per-thread offset.
+  auto issue = [&](int seg, SegLoads<T, NVD>& L) {
+    const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
+    const long row0 = b * T_ + t0;
+    const float* gb = p.g_raw + (row0 * HV + hv) * K;
+    const T* kb = kg + (row0 * H + h) * K;
+    const T* qb = qg + (row0 * H + h) * K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = min(town + 4 * i, n - 1);
+      L.g[i] = gb[r * HV * K + cown];
+      L.k[i] = kb[r * H * K + cown];
+      L.q[i] = qb[r * H * K + cown];
+    }
+    const T* vb = vg + (row0 * HV + hv) * V + v0;
+    const float* db = p.dout + (row0 * HV + hv) * V + v0;
+#pragma unroll
+    for (int i = 0; i < NVD; ++i) {  // elements past the tile re-read its first ones
+      const int e = (tid + i * NT) % (kSeg * kBV);
+      const int o = min(e / kBV, n - 1) * HV * V + e % kBV;
+      L.v[i] = vb[o];
+      L.dout[i] = db[o];
+    }
+    L.u = *reinterpret_cast<const float4*>(p.u + (((long)hd * NC + seg) * NVT + vt) * 256 +
+                                           4 * (tid & 63));
+    L.beta = p.beta[row0 * HV + hv + min(tid & 15, n - 1) * HV];
+    L.ckpt = *reinterpret_cast<const float4*>(p.ckpt + ((long)hd * NC + seg) * K * V + v0 +
+                                              kap * V + c4);
+  };
+  // Place them in LDS (gate applied, q scaled).
+  auto stage = [&](const SegLoads<T, NVD>& L) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sm.al[town + 4 * i][cown] = gate_alpha_pre<GK>(L.g[i], bias, gc);
+      sm.k[town + 4 * i][cown] = In<T>::widen(L.k[i]);
+      sm.q[town + 4 * i][cown] = scale * In<T>::widen(L.q[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NVD; ++i) {
+      const int e = tid + i * NT;
+      if (e < kSeg * kBV) {
+        sm.v[e / kBV][e % kBV] = In<T>::widen(L.v[i]);
+        sm.dout[e / kBV][e % kBV] = L.dout[i];
+      }
+    }
+    if (tid < 64) {  // U: one 16 x 16 fragment, lane l holding rows 4 (l / 16) + r of column l % 16
+      const int r0 = 4 * (tid >> 4), j = tid & 15;
+      sm.u[r0][j] = L.u.x;
+      sm.u[r0 + 1][j] = L.u.y;
+      sm.u[r0 + 2][j] = L.u.z;
+      sm.u[r0 + 3][j] = L.u.w;
+    }
+    if (tid < kSeg) sm.beta[tid] = L.beta;
+  };
+  // Add the finished segment's results to the outputs.
+  auto flush = [&](int seg) {
+    const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
+    const long row0 = b * T_ + t0;
+    float* dqb = p.dq + (row0 * H + h) * K;
+    float* dkb = p.dk + (row0 * H + h) * K;
+    float* dgb = p.dg + (row0 * HV + hv) * K;
+    float vals[4][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = town + 4 * i;
+      vals[i][0] = sm.dq[tt][cown];
+      vals[i][1] = sm.dk[tt][cown];
+      vals[i][2] = sm.dg[tt][cown];
+    }
+    float4 dv4 = *reinterpret_cast<const float4*>(&sm.dv[(tid >> 2) & 15][4 * (tid & 3)]);
+    const float dbv = sm.db[tid & 15];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = town + 4 * i;
+      if (tt < n) {
+        atomicAdd(dqb + tt * H * K + cown, vals[i][0]);
+        atomicAdd(dkb + tt * H * K + cown, vals[i][1]);
+        atomicAdd(dgb + tt * HV * K + cown, vals[i][2]);
+      }
+    }
+    if (tid < 64 && (tid >> 2) < n)
+      *reinterpret_cast<float4*>(p.dv + (row0 * HV + hv) * V + v0 + (tid >> 2) * HV * V +
+                                 4 * (tid & 3)) = dv4;
+    if (tid < n) atomicAdd(p.dbeta + row0 * HV + hv + tid * HV, dbv);
+  };
+
+  // Sums over the keys of x[0..7] (columns c4 .. c4 + 3 of a, then of
+  // Sd^T k).  A 16-lane row holds 4 keys x 4 column groups, so rotations by 4
+  // and 8 keep the group, and the row swaps add the wavefront's four rows;
+  // lanes 0..3 then hold the wavefront's partial sums of all 32 (quantity,
+  // column) pairs, which go to LDS.  After the barrier lane l of every
+  // wavefront reads wavefront l % 8's partials of pair group l / 8 (four
+  // columns), three lane exchanges inside each group of 8 lanes add the
+  // wavefronts, and the totals come back through a slot of the wavefront's
+  // own (no further barrier).  The partials are double-buffered: one barrier
+  // per call.
+  static_assert(NW == 8 || NW == 4 || NW == 2, "wavefronts per workgroup");
   int rb = 0;
-  auto key_sum = [&](float x[8]) {
+  auto key_sum8 = [&](float x[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      x[i] = ror_add<2>(x[i]);
       x[i] = ror_add<4>(x[i]);
       x[i] = ror_add<8>(x[i]);
       x[i] = xor_sum<16>(x[i]);
       x[i] = xor_sum<32>(x[i]);
     }
-    if (lane < 2) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.red[rb][w][c8 + i] = x[i];
+    if (lane < 4) {
+      *reinterpret_cast<float4*>(&sm.red[rb][w][0][c4]) = float4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<float4*>(&sm.red[rb][w][1][c4]) = float4{x[4], x[5], x[6], x[7]};
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float s = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) s += sm.red[rb][ww][c8 + i];
-      x[i] = s;
-    }
+    const int grp = lane >> 3;  // pair group: quantity grp / 4, columns 4 (grp % 4) ..
+    float4 t = *reinterpret_cast<const float4*>(
+        &sm.red[rb][lane & (NW - 1)][grp >> 2][4 * (grp & 3)]);
+    if (NW < 8 && (lane & 7) >= NW) t = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    t.x = oct_sum(t.x);
+    t.y = oct_sum(t.y);
+    t.z = oct_sum(t.z);
+    t.w = oct_sum(t.w);
+    if ((lane & 7) == 0) *reinterpret_cast<float4*>(&sm.fin[w][grp][0]) = t;
+    // the slot is read back by the same wavefront: LDS accesses of one
+    // wavefront complete in order
+    const float4 a = *reinterpret_cast<const float4*>(&sm.fin[w][cg][0]);
+    const float4 z = *reinterpret_cast<const float4*>(&sm.fin[w][4 + cg][0]);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = z.x; x[5] = z.y; x[6] = z.z; x[7] = z.w;
     rb ^= 1;
   };
 
-  float dS[8];
+  float dS[4];
   {
-    const long o = ((long)hd * K + kap) * V + v0 + c8;
+    const long o = ((long)hd * K + kap) * V + v0 + c4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dS[i] = p.dST ? p.dST[o + i] : 0.0f;
+    for (int i = 0; i < 4; ++i) dS[i] = p.dST ? p.dST[o + i] : 0.0f;
   }
-  for (int seg = p.NC - 1; seg >= 0; --seg) {
-    const int t0 = seg * kSeg;
-    const int n = min(kSeg, T_ - t0);
-    // this key's retain factor, k and q for the segment's tokens
-    float al[kSeg], kk[kSeg], qq[kSeg];
-#pragma unroll
-    for (int tt = 0; tt < kSeg; ++tt) {
-      al[tt] = 1.0f;
-      kk[tt] = 0.0f;
-      qq[tt] = 0.0f;
-      if (tt < n) {
-        const long row = b * T_ + t0 + tt;
-        al[tt] = gate_alpha_pre<GK>(p.g_raw[(row * HV + hv) * K + kap], bias, gc);
-        kk[tt] = In<T>::at(kg, (row * H + h) * K + kap);
-        qq[tt] = In<T>::at(qg, (row * H + h) * K + kap);
-      }
-    }
-    for (int e = tid; e < kSeg * kBV; e += 2 * K) {
-      const int tt = e / kBV, j = e % kBV;
-      const long row = b * T_ + t0 + tt;
-      sm.v[tt][j] = tt < n ? In<T>::at(vg, (row * HV + hv) * V + v0 + j) : 0.0f;
-      sm.dout[tt][j] = tt < n ? p.dout[(row * HV + hv) * V + v0 + j] : 0.0f;
-    }
-    if (tid < kSeg) sm.beta[tid] = tid < n ? p.beta[(b * T_ + t0 + tid) * HV + hv] : 0.0f;
-    float S[8];
-    {
-      const float* c = p.ckpt + (((long)hd * p.NC + seg) * K + kap) * V + v0 + c8;
-      const float4 a = *reinterpret_cast<const float4*>(c);
-      const float4 z = *reinterpret_cast<const float4*>(c + 4);
-      S[0] = a.x; S[1] = a.y; S[2] = a.z; S[3] = a.w;
-      S[4] = z.x; S[5] = z.y; S[6] = z.z; S[7] = z.w;
-    }
+  SegLoads<T, NVD> L;
+  if (NC > 0) issue(NC - 1, L);
+  for (int seg = NC - 1; seg >= 0; --seg) {
+    const int n = min(kSeg, T_ - seg * kSeg);
+    stage(L);
+    const float4 ck = L.ckpt;
     __syncthreads();
-    // forward through the segment: keep S_{t-1} and the residual of every token
+    // S_t = alpha_t S_{t-1} + k_t U_t^T, from the checkpoint
+    auto advance = [&](int tt, float S[4]) {
+      const float a = sm.al[tt][kap], kv = sm.k[tt][kap];
+      const float4 u = *reinterpret_cast<const float4*>(&sm.u[tt][c4]);
+      S[0] = a * S[0] + kv * u.x;
+      S[1] = a * S[1] + kv * u.y;
+      S[2] = a * S[2] + kv * u.z;
+      S[3] = a * S[3] + kv * u.w;
+    };
+    // The reverse step of token tt, given S_{t-1} (no global memory access).
+    auto reverse = [&](int tt, const float sp[4]) {
+      const float a_ = sm.al[tt][kap], kv = sm.k[tt][kap], qv = sm.q[tt][kap];
+      const float bt = sm.beta[tt];
+      const float4 d4 = *reinterpret_cast<const float4*>(&sm.dout[tt][c4]);
+      const float4 v4 = *reinterpret_cast<const float4*>(&sm.v[tt][c4]);
+      const float d[4] = {d4.x, d4.y, d4.z, d4.w}, vv[4] = {v4.x, v4.y, v4.z, v4.w};
+      float Sd[4], x[8];
 #pragma unroll
-    for (int tt = 0; tt < kSeg; ++tt) {
-      if (tt < n) {
-        float* dst = &sm.st[tt][kap][c8];
-        *reinterpret_cast<float4*>(dst) = float4{S[0], S[1], S[2], S[3]};
-        *reinterpret_cast<float4*>(dst + 4) = float4{S[4], S[5], S[6], S[7]};
-        float x[8];
+      for (int i = 0; i < 4; ++i) {
+        Sd[i] = a_ * sp[i];
+        dS[i] += qv * d[i];  // the read o_t = s S_t^T q_t
+        x[i] = kv * dS[i];
+        x[4 + i] = kv * Sd[i];
+      }
+      key_sum8(x);  // a_t = dS^T k_t and the prediction Sd^T k_t, per column
+      float dq = 0.0f, dk = 0.0f, dg = 0.0f, db = 0.0f;
+      const float bk = bt * kv;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          S[i] *= al[tt];
-          x[i] = kk[tt] * S[i];
-        }
-        key_sum(x);  // prediction Sd^T k
-        const float bk = sm.beta[tt] * kk[tt];
+      for (int i = 0; i < 4; ++i) {
+        const float r = vv[i] - x[4 + i];
+        dq += (Sd[i] + bk * r) * d[i];
+        const float dr = bt * x[i];
+        db += x[i] * r;
+        dk += bt * dS[i] * r - Sd[i] * dr;
+        const float dsd = dS[i] - kv * dr;
+        dg += dsd * Sd[i];
+        dS[i] = a_ * dsd;
+        x[i] = dr;
+      }
+      dq = quad_sum(dq) * scale;
+      dk = quad_sum(dk);
+      dg = quad_sum(dg);
+      if (cg == 0) {
+        sm.dq[tt][kap] = dq;
+        sm.dk[tt][kap] = dk;
+        sm.dg[tt][kap] = dg;
+      }
+      if (kap == 0) {
+        *reinterpret_cast<float4*>(&sm.dv[tt][c4]) = float4{x[0], x[1], x[2], x[3]};
+        db = quad_sum(db);
+        if (cg == 0) sm.db[tt] = db;
+      }
+    };
+    // The two halves of the segment, the later first: each rebuilds its
+    // eight states S_{t-1} from the checkpoint into registers, then runs
+    // them in reverse.
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float r = sm.v[tt][c8 + i] - x[i];
-          S[i] += bk * r;
-          x[i] = r;
-        }
-        if (kap == 0) {
+    for (int half = 1; half >= 0; --half) {
+      const int base = half * (kSeg / 2);
+      float S[4] = {ck.x, ck.y, ck.z, ck.w};
+      for (int tt = 0; tt < base && tt < n; ++tt) advance(tt, S);
+      float st[kSeg / 2][4];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) sm.r[tt][c8 + i] = x[i];
+      for (int j = 0; j < kSeg / 2; ++j) {
+        if (base + j < n) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st[j][i] = S[i];
+          advance(base + j, S);
         }
       }
+#pragma unroll
+      for (int j = kSeg / 2 - 1; j >= 0; --j)
+        if (base + j < n) reverse(base + j, st[j]);
     }
-    __syncthreads();
-    // reverse through the segment
-#pragma unroll
-    for (int tt = kSeg - 1; tt >= 0; --tt) {
-      if (tt < n) {
-        const long row = b * T_ + t0 + tt;
-        const float bt = sm.beta[tt];
-        float Sd[8], r[8], a[8], St, dq = 0.0f, dkr = 0.0f, dg = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          Sd[i] = al[tt] * sm.st[tt][kap][c8 + i];
-          r[i] = sm.r[tt][c8 + i];
-          const float d = sm.dout[tt][c8 + i];
-          St = Sd[i] + bt * kk[tt] * r[i];
-          dq += St * d;
-          dS[i] += scale * qq[tt] * d;
-          a[i] = kk[tt] * dS[i];
-        }
-        dq = pair_add(dq) * scale;
-        key_sum(a);  // a_t = dS^T k_t, per column
-        float db = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float dr = bt * a[i];
-          db += a[i] * r[i];
-          dkr += bt * dS[i] * r[i] - Sd[i] * dr;
-          const float dsd = dS[i] - kk[tt] * dr;
-          dg += dsd * Sd[i];
-          dS[i] = al[tt] * dsd;
-          a[i] = dr;
-        }
-        dkr = pair_add(dkr);
-        dg = pair_add(dg);
-        db = pair_add(db);
-        if (ch == 0) {
-          atomicAdd(p.dq + (row * H + h) * K + kap, dq);
-          atomicAdd(p.dk + (row * H + h) * K + kap, dkr);
-          atomicAdd(p.dg + (row * HV + hv) * K + kap, dg);
-        }
-        if (kap == 0) {
-          float* dvp = p.dv + (row * HV + hv) * V + v0 + c8;
-          *reinterpret_cast<float4*>(dvp) = float4{a[0], a[1], a[2], a[3]};
-          *reinterpret_cast<float4*>(dvp + 4) = float4{a[4], a[5], a[6], a[7]};
-          if (ch == 0) atomicAdd(p.dbeta + row * HV + hv, db);
-        }
-      }
-    }
-    __syncthreads();  // the next segment rewrites the LDS
+    __syncthreads();  // the segment's results are in LDS; its inputs are no longer read
+    // the next segment's loads go out before the atomics, so that waiting for
+    // them does not wait for the atomics; unconditional (the last re-reads
+    // segment 0) so that no earlier load stays live through the segment
+    issue(max(seg - 1, 0), L);
+    flush(seg);
   }
-  if (p.dS0) {
-    float* o = p.dS0 + ((long)hd * K + kap) * V + v0 + c8;
-    *reinterpret_cast<float4*>(o) = float4{dS[0], dS[1], dS[2], dS[3]};
-    *reinterpret_cast<float4*>(o + 4) = float4{dS[4], dS[5], dS[6], dS[7]};
-  }
+  if (p.dS0)
+    *reinterpret_cast<float4*>(p.dS0 + ((long)hd * K + kap) * V + v0 + c4) =
+        float4{dS[0], dS[1], dS[2], dS[3]};
 }
 
 // dg -> dg_raw in place (chain rule through the gate), and the sums of the
@@ -310,15 +435,15 @@ hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, c
                         float* h, void* workspace, int B, int T, int H, int HV, int K, int C,
                         hipStream_t stream);
 size_t split_workspace_bytes_per_chunk(int K, int V, int C);
+const float* split_resolved_values(const void* workspace, long chunks, int K, int C);
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace: checkpoints [B, HV, NC, K, V], the forward outputs the split
-// schedule writes on the way, its own workspace.
+// Workspace: the segment checkpoints [B, HV, NC, K, V], then the split
+// schedule's own workspace (which keeps U for the segment kernel).
 size_t bwd_workspace_bytes(int B, int T, int HV, int K, int V) {
   const size_t nc = ((size_t)T + kSeg - 1) / kSeg;
   return align256((size_t)B * HV * nc * K * V * sizeof(float)) +
-         align256((size_t)B * T * HV * V * sizeof(float)) +
          (size_t)B * HV * nc * split_workspace_bytes_per_chunk(K, V, kSeg);
 }
 
@@ -330,16 +455,11 @@ static hipError_t zero(float* p, long n, hipStream_t stream) {
 
 template <int K, typename T, int GK>
 static hipError_t launch_bwd_kt(BwdParams p, hipStream_t stream) {
-  const size_t lds = sizeof(BwdSmem<K>);
   const long nblk = (long)p.B * p.HV * (K / kBV);
   if (nblk > 0) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bwd_segment_kernel<K, K, T, GK>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_segment_kernel<K, K, T, GK>), dim3((unsigned)nblk), dim3(2 * K), lds,
-                       stream, p);
-    e = hipGetLastError();
+    hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK>), dim3((unsigned)nblk), dim3(4 * K), 0, stream,
+                       p);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long rows = (long)p.B * p.T;
@@ -358,8 +478,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
   const int NC = (T + kSeg - 1) / kSeg;
   char* ws = static_cast<char*>(workspace);
   float* ckpt = reinterpret_cast<float*>(ws);
-  float* o = reinterpret_cast<float*>(ws + align256((size_t)B * HV * NC * K * K * sizeof(float)));
-  void* split_ws = reinterpret_cast<char*>(o) + align256((size_t)B * T * HV * K * sizeof(float));
+  void* split_ws = ws + align256((size_t)B * HV * NC * K * K * sizeof(float));
   hipError_t e;
   const long nq = (long)B * T * H * K, ng = (long)B * T * HV * K;
   if ((e = zero(dq, nq, stream)) != hipSuccess || (e = zero(dk, nq, stream)) != hipSuccess ||
@@ -368,12 +487,14 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
       (e = zero(ddt_bias, (long)HV * K, stream)) != hipSuccess)
     return e;
   if (T > 0) {
-    e = launch_split(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, 0, lower_bound, S0, o,
-                     nullptr, ckpt, split_ws, B, T, H, HV, K, kSeg, stream);
+    // the states and U only (no o): the split skips its output stage
+    e = launch_split(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, 0, lower_bound, S0,
+                     nullptr, nullptr, ckpt, split_ws, B, T, H, HV, K, kSeg, stream);
     if (e != hipSuccess) return e;
   }
-  BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, dq, dk, dv, dbeta, dg_raw,
-              dS0, dA_log, ddt_bias, B, T, H, HV, NC, lower_bound};
+  const float* u = split_resolved_values(split_ws, (long)B * HV * NC, K, kSeg);
+  BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, u, dq, dk, dv, dbeta,
+              dg_raw, dS0, dA_log, ddt_bias, B, T, H, HV, NC, lower_bound};
 #define KDA_BWD_GATE(KK, TT)                                                       \
   switch (kind) {                                                                  \
     case KDA_GATE_SAFE: return launch_bwd_kt<KK, TT, KDA_GATE_SAFE>(p, stream);    \

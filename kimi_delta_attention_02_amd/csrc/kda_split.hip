@@ -1001,7 +1001,7 @@ static hipError_t launch_split_kc(const SplitParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((split_state_kernel<K, C, ChainBF<K, C, T>::value>),
                      dim3((unsigned)(heads * (K / 16))), dim3(64 * (1 + kCopiers)), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || chunks == 0) return e;
+  if (e != hipSuccess || chunks == 0 || !p.o) return e;  // no o wanted: the states and U only
   hipLaunchKernelGGL((split_output_kernel<K, C, T>), dim3(grid), dim3(kSplitThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -1027,6 +1027,14 @@ static size_t image_bytes(int K, int C) {
 #undef KDA_IMG_ROW
 #undef KDA_IMG_CASE
   return 0;
+}
+
+// Where the state pass leaves U (the resolved values beta_t r_t of every
+// token) in a workspace laid out for B * HV * NC chunks: per (b, hv, chunk)
+// and 16-wide column block cb, one 16 x 16 fragment (frag_index) for C = 16.
+const float* split_resolved_values(const void* workspace, long chunks, int K, int C) {
+  return reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
+                                        chunks * image_bytes(K, C));
 }
 
 size_t split_workspace_bytes_per_chunk(int K, int V, int C) {

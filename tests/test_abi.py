@@ -305,12 +305,12 @@ def test_bwd_validation(lib, kw, status):
 
 
 def test_bwd_workspace_bytes(lib):
-    """Segment states (one K x V fp32 state per 16 tokens) plus the forward's
-    outputs and the split schedule's own scratch at chunk 16."""
+    """Segment states (one K x V fp32 state per 16 tokens) plus the split
+    schedule's own scratch at chunk 16."""
     n = lib.kda_bwd_workspace_bytes(1, 4096, 16, 16, 128, 128)
     states = 16 * 256 * 128 * 128 * 4
-    assert n >= states + 4096 * 16 * 128 * 4 + 16 * 256 * lib.kda_chunk_fwd_split_workspace_bytes(
-        1, 16, 1, 1, 128, 128, 16)
+    split = 16 * 256 * lib.kda_chunk_fwd_split_workspace_bytes(1, 16, 1, 1, 128, 128, 16)
+    assert states + split <= n <= states + split + 256
     assert lib.kda_bwd_workspace_bytes(1, 4096, 16, 16, 16, 16) == 0
     assert lib.kda_bwd_workspace_bytes(0, 4096, 16, 16, 128, 128) == 0
 
