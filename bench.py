@@ -510,7 +510,6 @@ def main():
                           dtype=torch.uint8, device=dev)
         nc16 = (wb.T + 15) // 16
         hb = torch.empty((wb.B, wb.HV, nc16, wb.K, wb.V), dtype=torch.float32, device=dev)
-        ob = torch.empty((wb.B, wb.T, wb.HV, wb.V), dtype=torch.float32, device=dev)
         wss = torch.empty(kda.chunk_fwd_split_workspace_bytes(wb.B, wb.T, wb.H, wb.HV, wb.K, wb.V,
                                                               16), dtype=torch.uint8, device=dev)
         argsb = (gb["q"], gb["k"], gb["v"], gb["g_raw"], gb["beta"], gb["A_log"], gb["dt_bias"])
@@ -530,9 +529,10 @@ def main():
         n_b = max(1, min(args.steps, 5))
         bwd_ms = timed(lambda: kda.bwd(*argsb, gate=wb.gate, lower_bound=wb.lower_bound,
                                        initial_state=gb["S0"], dout=dout, workspace=wsb), n_b)
+        # the states-only split forward at chunk 16: what kda_bwd runs first
         fwd16_ms = timed(lambda: kda.chunk_fwd_split(*argsb, gate=wb.gate,
                                                      lower_bound=wb.lower_bound, chunk_size=16,
-                                                     initial_state=gb["S0"], o=ob, h=hb,
+                                                     initial_state=gb["S0"], h=hb, output_o=False,
                                                      output_final_state=False, workspace=wss), n_b)
         seg_ms = bwd_ms - fwd16_ms
         fl = bwd_flops(wb)
@@ -546,10 +546,12 @@ def main():
             "roofline": {"bound": "alu", "achieved": fl / (seg_ms * 1e-3) / 1e12,
                          "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": fl / (seg_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
-                         "traffic": None, "flops_per_launch": fl, "launch_ms": seg_ms,
+                         "traffic": measured_traffic("bwd_prefill"), "flops_per_launch": fl,
+                         "launch_ms": seg_ms,
                          "kernel": "bwd_segment_kernel<128, bf16, safe gate> (with the gate and "
-                                   "zero-fill kernels: the call minus its split forward)"}}
-        del gb, dout, wsb, hb, ob, wss
+                                   "zero-fill kernels: the call minus its states-only split "
+                                   "forward at chunk 16)"}}
+        del gb, dout, wsb, hb, wss
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4

@@ -205,6 +205,10 @@ kda_status kda_recurrent_fwd(const void* q, const void* k, const void* v, kda_dt
  *   h             [B, HV, NC, K, V] float32 output, NC = ceil(T / chunk_size):
  *                 h[b, hv, c] is the state entering chunk c (h[.., 0] is the
  *                 initial state); NULL keeps h inside the workspace
+ *   o             as kda_chunk_fwd, or NULL when h is given: then only the
+ *                 states are produced (h and final_state) and the output
+ *                 stage is skipped, as a training forward that keeps the
+ *                 states for the backward would do
  *   workspace     device scratch of at least
  *                 kda_chunk_fwd_split_workspace_bytes(...) bytes, 16-byte aligned,
  *                 owned by the caller; its contents need not be initialised and

@@ -112,9 +112,14 @@ def chunk_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_b
     qkv = _qkv_dtype(q)
     dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
                                                             initial_state)
-    if o is None:
+    if not output_o:
+        if not (output_states or h is not None):
+            raise ValueError("output_o=False needs the states (output_states or h)")
+        o = None
+    elif o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
-    _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    if o is not None:
+        _need(o, "o", torch.float32, (B, T, HV, V), dev)
     if output_final_state and final_state is None:
         final_state = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     if final_state is not None:
@@ -138,19 +143,26 @@ def chunk_fwd_split_workspace_bytes(B, T, H, HV, K, V, chunk_size=64):
 
 def chunk_fwd_split(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_bound=-5.0,
                     chunk_size=64, initial_state=None, output_final_state=True,
-                    output_states=False, o=None, final_state=None, h=None, workspace=None):
+                    output_states=False, o=None, final_state=None, h=None, workspace=None,
+                    output_o=True):
     """Chunkwise forward in three stages (intra-chunk, state pass, output),
     with the entry state of every chunk materialised.  Arguments as
     :func:`chunk_fwd`.  Returns (o, final_state, h): h [B, HV, NC, K, V]
     float32 with NC = ceil(T / chunk_size) when output_states is True (or an
-    ``h`` tensor is given), else None."""
+    ``h`` tensor is given), else None.  With output_o=False (h required) the
+    output stage is skipped and o is None."""
     lib = _lib.load()
     qkv = _qkv_dtype(q)
     dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
                                                             initial_state)
-    if o is None:
+    if not output_o:
+        if not (output_states or h is not None):
+            raise ValueError("output_o=False needs the states (output_states or h)")
+        o = None
+    elif o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
-    _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    if o is not None:
+        _need(o, "o", torch.float32, (B, T, HV, V), dev)
     if output_final_state and final_state is None:
         final_state = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     if final_state is not None:
@@ -272,9 +284,14 @@ def recurrent_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", low
     qkv = _qkv_dtype(q)
     dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
                                                             initial_state)
-    if o is None:
+    if not output_o:
+        if not (output_states or h is not None):
+            raise ValueError("output_o=False needs the states (output_states or h)")
+        o = None
+    elif o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
-    _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    if o is not None:
+        _need(o, "o", torch.float32, (B, T, HV, V), dev)
     if output_final_state and final_state is None:
         final_state = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     if final_state is not None:

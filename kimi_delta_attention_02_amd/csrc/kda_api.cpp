@@ -215,7 +215,9 @@ kda_status check_split(const void* q, const void* k, const void* v, kda_dtype qk
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
   const long nc = ((long)T + chunk_size - 1) / chunk_size;
   if ((long)B * HV * nc > 0x7fffffffL) return KDA_ERR_INVALID_ARG;  // one workgroup per chunk
-  if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  // o may be NULL when h is wanted: the states only, without the output stage
+  if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || (!o && !h)))
+    return KDA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, initial_state, final_state, h};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
@@ -266,7 +268,9 @@ kda_status kda_chunk_fwd_split(const void* q, const void* k, const void* v, kda_
   if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) return KDA_ERR_UNSUPPORTED;
   const long nc = ((long)T + chunk_size - 1) / chunk_size;
   if ((long)B * HV * nc > 0x7fffffffL) return KDA_ERR_INVALID_ARG;  // one workgroup per chunk
-  if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  // o may be NULL when h is wanted: the states only, without the output stage
+  if (B > 0 && T > 0 && (!q || !k || !v || !g_raw || !beta || (!o && !h)))
+    return KDA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, initial_state, final_state, h, workspace};
   for (const void* ptr : ptrs)
     if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;

@@ -83,6 +83,12 @@ int main() {
   expect("split small ws", KDA_ERR_WORKSPACE, false, [&] {
     return kda_chunk_fwd_split(P, P, P, KDA_BF16, F, F, F, F, KDA_GATE_SAFE, -5.f, nullptr, F, F,
                                nullptr, 1, 100, 2, 4, 128, 128, 64, P, need - 1, nullptr); });
+  expect("split states only", KDA_OK, true, [&] {
+    return kda_chunk_fwd_split(P, P, P, KDA_BF16, F, F, F, F, KDA_GATE_SAFE, -5.f, nullptr,
+                               nullptr, nullptr, F, 1, 100, 2, 4, 128, 128, 64, P, need, nullptr); });
+  expect("split no o, no h", KDA_ERR_INVALID_ARG, false, [&] {
+    return kda_chunk_fwd_split(P, P, P, KDA_BF16, F, F, F, F, KDA_GATE_SAFE, -5.f, nullptr,
+                               nullptr, F, nullptr, 1, 100, 2, 4, 128, 128, 64, P, need, nullptr); });
   expect("noalloc ok", KDA_OK, true, [&] {
     return kda_chunk_fwd_split_noalloc(P, P, P, KDA_BF16, F, F, F, F, KDA_GATE_SAFE, -5.f, nullptr,
                                        F, F, nullptr, 1, 100, 2, 4, 128, 128, 64, nullptr); });

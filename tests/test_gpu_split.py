@@ -170,3 +170,21 @@ def test_split_h_in_workspace_matches_h_given(dt):
     torch.cuda.synchronize()
     assert h2 is None and h1.shape == (2, 4, 4, 64, 64)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_split_states_only(chunk):
+    """o = NULL with h given: the output stage is skipped; h and the final
+    state equal those of the full call bit for bit."""
+    d = synth.random_inputs(2, 150, 2, 4, 128, 128, seed=19, dtype="bf16", s0_std=0.02)
+    g = L.to_dev(d)
+    args = (g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"])
+    o1, S1, h1 = kda.chunk_fwd_split(*args, chunk_size=chunk, initial_state=g["S0"],
+                                     output_states=True)
+    o2, S2, h2 = kda.chunk_fwd_split(*args, chunk_size=chunk, initial_state=g["S0"],
+                                     output_states=True, output_o=False)
+    torch.cuda.synchronize()
+    assert o2 is None and o1 is not None
+    assert torch.equal(h1, h2) and torch.equal(S1, S2)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd_split(*args, chunk_size=chunk, output_o=False)
