@@ -1,5 +1,5 @@
 /* Host driver for the sanitizer builds of the oracle (test infrastructure).
- * Runs oracle_gate and oracle_kda_fwd on small random problems, with and
+ * Runs oracle_gate, oracle_kda_fwd and oracle_kda_bwd on small random problems, with and
  * without dt_bias and an initial state, every gate kind, several thread
  * counts, empty and rejected shapes, and checks what the four-step update of
  * the "K3 notes" (section "KDA 递归核心") fixes exactly: the result does not
@@ -17,6 +17,13 @@ int oracle_kda_fwd(const double* q, const double* k, const double* v, const doub
                    double lower_bound, const double* S0, long B, long T, long H, long HV,
                    long K, long V, double* o, double* S_out, int nthreads);
 
+int oracle_kda_bwd(const double* q, const double* k, const double* v, const double* g_raw,
+                   const double* beta, const double* A_log, const double* dt_bias, int kind,
+                   double lower_bound, const double* S0, const double* dout, const double* dST,
+                   long B, long T, long H, long HV, long K, long V, double* dq, double* dk,
+                   double* dv, double* dbeta, double* dg_raw, double* dA_log, double* ddt_bias,
+                   double* dS0, int nthreads);
+
 static double urand(void) { return (double)rand() / RAND_MAX * 2.0 - 1.0; }
 
 static double* fill(long n, double scale) {
@@ -27,6 +34,37 @@ static double* fill(long n, double scale) {
 
 static int fails = 0;
 #define CHECK(c, ...) do { if (!(c)) { fprintf(stderr, __VA_ARGS__); fputc('\n', stderr); ++fails; } } while (0)
+
+/* The gradient oracle on the same kind of problem, with one and with three
+ * threads: the results must be equal element for element. */
+static void run_bwd_case(long B, long T, long H, long HV, long K, long V, int kind, int bias,
+                         int s0, int dst) {
+  double *q = fill(B * T * H * K, 0.3), *k = fill(B * T * H * K, 0.3), *v = fill(B * T * HV * V, 1.0);
+  double *g = fill(B * T * HV * K, 1.0), *beta = fill(B * T * HV, 0.5), *A = fill(HV, 0.5);
+  double *dt = bias ? fill(HV * K, 1.0) : NULL, *S0 = s0 ? fill(B * HV * K * V, 0.1) : NULL;
+  double *dout = fill(B * T * HV * V, 1.0), *dST = dst ? fill(B * HV * K * V, 1.0) : NULL;
+  if (kind == 2)
+    for (long i = 0; i < B * T * HV * K; ++i) g[i] = -0.2 * fabs(g[i]);
+  const long n[8] = {B * T * H * K, B * T * H * K, B * T * HV * V, B * T * HV, B * T * HV * K, HV,
+                     HV * K, B * HV * K * V};
+  double* out[2][8];
+  for (int r = 0; r < 2; ++r) {
+    for (int j = 0; j < 8; ++j) out[r][j] = fill(n[j], 0);
+    CHECK(oracle_kda_bwd(q, k, v, g, beta, A, dt, kind, -5.0, S0, dout, dST, B, T, H, HV, K, V,
+                         out[r][0], out[r][1], out[r][2], out[r][3], out[r][4], out[r][5],
+                         bias ? out[r][6] : NULL, out[r][7], r ? 3 : 1) == 0,
+          "kda_bwd rejected a valid case");
+  }
+  for (int j = 0; j < 8; ++j)
+    for (long i = 0; i < n[j]; ++i)
+      if ((j != 6 || bias) && out[0][j][i] != out[1][j][i]) {
+        CHECK(0, "bwd output %d differs with the thread count", j);
+        break;
+      }
+  for (int r = 0; r < 2; ++r)
+    for (int j = 0; j < 8; ++j) free(out[r][j]);
+  free(q); free(k); free(v); free(g); free(beta); free(A); free(dt); free(S0); free(dout); free(dST);
+}
 
 static void run_case(long B, long T, long H, long HV, long K, long V, int kind, int bias, int s0) {
   double *q = fill(B * T * H * K, 0.3), *k = fill(B * T * H * K, 0.3), *v = fill(B * T * HV * V, 1.0);
@@ -83,7 +121,12 @@ int main(void) {
   run_case(3, 0, 1, 1, 4, 4, 0, 0, 1);   /* T = 0: the state passes through */
   run_case(0, 5, 1, 2, 4, 4, 1, 0, 0);   /* B = 0: nothing to do */
   reconstruction();
+  for (int kind = 0; kind < 3; ++kind) run_bwd_case(2, 21, 1, 2, 6, 5, kind, kind != 2, 1, 1);
+  run_bwd_case(1, 9, 2, 2, 4, 4, 1, 0, 0, 0);
+  run_bwd_case(2, 0, 1, 1, 4, 4, 0, 1, 1, 1);  /* T = 0: dS0 = dST */
   double x = 0.0, y = 0.0;
+  CHECK(oracle_kda_bwd(&x, &x, &x, &x, &x, &x, NULL, 1, -5.0, NULL, &x, NULL, 1, 1, 2, 3, 1, 1,
+                       &y, &y, &y, &y, &y, &y, NULL, NULL, 1) == -1, "bwd: HV %% H != 0 accepted");
   CHECK(oracle_kda_fwd(&x, &x, &x, &x, &x, &x, NULL, 1, -5.0, NULL, 1, 1, 2, 3, 1, 1, &y, NULL, 1) == -1,
         "HV %% H != 0 accepted");
   CHECK(oracle_kda_fwd(NULL, &x, &x, &x, &x, &x, NULL, 1, -5.0, NULL, 1, 1, 1, 1, 1, 1, &y, NULL, 1) == -1,

@@ -1,5 +1,6 @@
 """Host code under AddressSanitizer + UndefinedBehaviorSanitizer (and the
-threaded oracle under ThreadSanitizer): the fp64 oracle with its thread pool,
+threaded oracle under ThreadSanitizer): the fp64 oracles (forward and
+gradients) with their thread pools,
 and the C ABI's argument validation in kda_api.cpp with the kernel launchers
 replaced by stubs (tests/sanitize/launch_stubs.cpp).  Each build runs a small
 driver that checks its own results; any sanitizer report fails the run.
@@ -40,6 +41,7 @@ def tmp():
 def test_oracle_asan_ubsan(tmp):
     _build_and_run(["gcc", "-std=c99", "-D_POSIX_C_SOURCE=200809L"] + ASAN_UBSAN +
                    [os.path.join(SAN, "oracle_driver.c"), os.path.join(ROOT, "oracle", "kda_oracle.c"),
+                    os.path.join(ROOT, "oracle", "kda_oracle_bwd.c"),
                     "-lm", "-lpthread"], os.path.join(tmp, "oracle_asan"),
                    {"ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0"})
 
@@ -48,7 +50,8 @@ def test_oracle_asan_ubsan(tmp):
 def test_oracle_tsan(tmp):
     _build_and_run(["gcc", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-O1", "-g",
                     "-fsanitize=thread", os.path.join(SAN, "oracle_driver.c"),
-                    os.path.join(ROOT, "oracle", "kda_oracle.c"), "-lm", "-lpthread"],
+                    os.path.join(ROOT, "oracle", "kda_oracle.c"),
+                    os.path.join(ROOT, "oracle", "kda_oracle_bwd.c"), "-lm", "-lpthread"],
                    os.path.join(tmp, "oracle_tsan"), {"TSAN_OPTIONS": "halt_on_error=1"})
 
 
