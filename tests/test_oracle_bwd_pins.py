@@ -34,6 +34,9 @@ MUTANTS = {
                                             "acc += Sp[c * V + j] * dot[j];")],
     "dSd sign": [("dSd[c * V + j] = dS[c * V + j] - kt[c] * dr[j];",
                   "dSd[c * V + j] = dS[c * V + j] + kt[c] * dr[j];")],
+    "dt_bias gradient under the none gate": [
+        ("if (J->kind != BWD_GATE_NONE) dbias[c] += dg * dgx[t * K + c];",
+         "dbias[c] += dg * dgx[t * K + c];")],
 }
 
 
