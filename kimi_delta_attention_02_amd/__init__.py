@@ -112,14 +112,9 @@ def chunk_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_b
     qkv = _qkv_dtype(q)
     dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
                                                             initial_state)
-    if not output_o:
-        if not (output_states or h is not None):
-            raise ValueError("output_o=False needs the states (output_states or h)")
-        o = None
-    elif o is None:
+    if o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
-    if o is not None:
-        _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    _need(o, "o", torch.float32, (B, T, HV, V), dev)
     if output_final_state and final_state is None:
         final_state = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     if final_state is not None:
@@ -284,14 +279,9 @@ def recurrent_fwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", low
     qkv = _qkv_dtype(q)
     dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
                                                             initial_state)
-    if not output_o:
-        if not (output_states or h is not None):
-            raise ValueError("output_o=False needs the states (output_states or h)")
-        o = None
-    elif o is None:
+    if o is None:
         o = torch.empty((B, T, HV, V), dtype=torch.float32, device=dev)
-    if o is not None:
-        _need(o, "o", torch.float32, (B, T, HV, V), dev)
+    _need(o, "o", torch.float32, (B, T, HV, V), dev)
     if output_final_state and final_state is None:
         final_state = torch.empty((B, HV, K, V), dtype=torch.float32, device=dev)
     if final_state is not None:
