@@ -104,28 +104,48 @@ __device__ __forceinline__ float quad_sum(float x) {
                                                                    0x4E, 0xF, 0xF, true));
 }
 
+// DPP broadcast of lane I of each group of four lanes (quad permutation
+// [I, I, I, I]).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               I * 0x55, 0xF, 0xF, true));
+}
+
 template <int K>
-struct BwdSmem {
-  float al[kSeg][K];  // retain factors of the segment's tokens
-  float k[kSeg][K];
-  float q[kSeg][K];    // s q
-  float u[kSeg][kBV];  // U = beta r from the forward's state pass
+struct alignas(16) BwdSmem {
+  static constexpr int KP = K + 4;  // row stride: the 16 rows of an MFMA operand read spread over the banks
+  // the segment's inputs per (token, key channel)
+  float al[kSeg][KP];  // retain factors (1 for tokens past the end)
+  float k[kSeg][KP];   // k (0 past the end)
+  float q[kSeg][KP];   // s q (0 past the end)
+  float E[kSeg][KP];   // prod_{m <= t} alpha_m from the segment start; after the solve, dg
+  float s0[K][kBV];    // the tile of the checkpoint S_0
+  float u[kSeg][kBV];  // U = beta r from the forward's state pass (0 past the end)
   float v[kSeg][kBV];
   float dout[kSeg][kBV];
   float beta[kSeg];
-  float red[2][K / 16][2][kBV];  // per-wavefront key sums of a and Sd^T k (two buffers)
-  float fin[K / 16][8][4];        // each wavefront's totals of the 8 groups of 4 (quantity, column)
+  // the segment's matrix products and what the solve makes of them
+  float dsin[K][kBV];    // the tile of dL/dS entering the segment's reverse pass
+  float ps[kSeg][kBV];   // (k E) S_0
+  float kd[kSeg][kBV];   // (k Suf) dS_in
+  float g1[kSeg][kSeg];  // (k / E)(k E)^T
+  float g2[kSeg][kSeg];  // (k / E)(s q E)^T
+  float a[kSeg][kBV];    // a_t = G_t^T k_t
+  float r[kSeg][kBV];    // r_t = v_t - Sd_t^T k_t
+  // the per-token key sums of the fallback
+  float red[2][K / 16][2][kBV];
+  float fin[K / 16][8][4];
   // the segment's results, written out together once it is done
   float dq[kSeg][K];
   float dk[kSeg][K];
-  float dg[kSeg][K];
   float dv[kSeg][kBV];
   float db[kSeg];
 };
 
-// One segment's inputs in flight: this thread's share of g_raw, k and q
-// (key channel tid % K, tokens tid / K + 4 i), of v, dL/do, U and beta, and
-// its own row of the checkpoint.
+// One segment's inputs in flight: this thread's share of g_raw, k and q (key
+// channel kappa, tokens 4 c .. 4 c + 3), of v, dL/do, U and beta, and its own
+// row of the checkpoint.
 template <typename T, int NVD>
 struct SegLoads {
   float g[4];
@@ -150,16 +170,16 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   const float scale = 1.0f / __builtin_sqrtf((float)K);
   const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
   const GateConsts gc = gate_consts(rate, p.lower_bound);
-  const int cown = tid % K, town = tid / K;  // the key channel and first token this thread stages
   const float bias = gate_bias_pre<GK>(
-      (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * K + cown] : 0.0f, gc);
+      (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * K + kap] : 0.0f, gc);
+  const int town = tid / K, cown = tid % K;  // the layout of the results' write-out
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
 
   // Issue the loads of segment seg (rows past the end re-read the last
-  // token, n >= 1; what they hold is never used).  Addresses are a base
-  // uniform over the workgroup plus a 32-bit per-thread offset.
+  // token, n >= 1).  Addresses are a base uniform over the workgroup plus a
+  // 32-bit per-thread offset.
   auto issue = [&](int seg, SegLoads<T, NVD>& L) {
     const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
     const long row0 = b * T_ + t0;
@@ -168,10 +188,10 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     const T* qb = qg + (row0 * H + h) * K;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = min(town + 4 * i, n - 1);
-      L.g[i] = gb[r * HV * K + cown];
-      L.k[i] = kb[r * H * K + cown];
-      L.q[i] = qb[r * H * K + cown];
+      const int r = min(c4 + i, n - 1);
+      L.g[i] = gb[r * HV * K + kap];
+      L.k[i] = kb[r * H * K + kap];
+      L.q[i] = qb[r * H * K + kap];
     }
     const T* vb = vg + (row0 * HV + hv) * V + v0;
     const float* db = p.dout + (row0 * HV + hv) * V + v0;
@@ -188,30 +208,55 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     L.ckpt = *reinterpret_cast<const float4*>(p.ckpt + ((long)hd * NC + seg) * K * V + v0 +
                                               kap * V + c4);
   };
-  // Place them in LDS (gate applied, q scaled).
-  auto stage = [&](const SegLoads<T, NVD>& L) {
+  // Place them in LDS, tokens past the end as an identity (alpha = 1, k, q,
+  // v, dL/do, U and beta zero), with the cumulative retain factors E.
+  // Returns whether an E of this thread leaves [2^-100, 2^100] (or is NaN).
+  auto stage = [&](const SegLoads<T, NVD>& L, int n) {
+    float al4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sm.al[town + 4 * i][cown] = gate_alpha_pre<GK>(L.g[i], bias, gc);
-      sm.k[town + 4 * i][cown] = In<T>::widen(L.k[i]);
-      sm.q[town + 4 * i][cown] = scale * In<T>::widen(L.q[i]);
+      const int tt = c4 + i;
+      const bool in = tt < n;
+      al4[i] = in ? gate_alpha_pre<GK>(L.g[i], bias, gc) : 1.0f;
+      sm.al[tt][kap] = al4[i];
+      sm.k[tt][kap] = in ? In<T>::widen(L.k[i]) : 0.0f;
+      sm.q[tt][kap] = in ? scale * In<T>::widen(L.q[i]) : 0.0f;
+    }
+    // E: products over this thread's four tokens, then over the earlier
+    // groups of four (the other lanes of the quad)
+    float e4[4];
+    e4[0] = al4[0];
+    e4[1] = e4[0] * al4[1];
+    e4[2] = e4[1] * al4[2];
+    e4[3] = e4[2] * al4[3];
+    const float g0 = quad_bcast<0>(e4[3]), g1 = quad_bcast<1>(e4[3]), g2 = quad_bcast<2>(e4[3]);
+    const float ex = cg == 0 ? 1.0f : cg == 1 ? g0 : cg == 2 ? g0 * g1 : (g0 * g1) * g2;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float E = ex * e4[i];
+      sm.E[c4 + i][kap] = E;
+      bad |= !(E >= 0x1p-100f && E <= 0x1p100f);
     }
 #pragma unroll
     for (int i = 0; i < NVD; ++i) {
       const int e = tid + i * NT;
       if (e < kSeg * kBV) {
-        sm.v[e / kBV][e % kBV] = In<T>::widen(L.v[i]);
-        sm.dout[e / kBV][e % kBV] = L.dout[i];
+        const bool in = e / kBV < n;
+        sm.v[e / kBV][e % kBV] = in ? In<T>::widen(L.v[i]) : 0.0f;
+        sm.dout[e / kBV][e % kBV] = in ? L.dout[i] : 0.0f;
       }
     }
     if (tid < 64) {  // U: one 16 x 16 fragment, lane l holding rows 4 (l / 16) + r of column l % 16
       const int r0 = 4 * (tid >> 4), j = tid & 15;
-      sm.u[r0][j] = L.u.x;
-      sm.u[r0 + 1][j] = L.u.y;
-      sm.u[r0 + 2][j] = L.u.z;
-      sm.u[r0 + 3][j] = L.u.w;
+      sm.u[r0][j] = r0 < n ? L.u.x : 0.0f;
+      sm.u[r0 + 1][j] = r0 + 1 < n ? L.u.y : 0.0f;
+      sm.u[r0 + 2][j] = r0 + 2 < n ? L.u.z : 0.0f;
+      sm.u[r0 + 3][j] = r0 + 3 < n ? L.u.w : 0.0f;
     }
-    if (tid < kSeg) sm.beta[tid] = L.beta;
+    if (tid < kSeg) sm.beta[tid] = tid < n ? L.beta : 0.0f;
+    *reinterpret_cast<float4*>(&sm.s0[kap][c4]) = L.ckpt;
+    return bad;
   };
   // Add the finished segment's results to the outputs.
   auto flush = [&](int seg) {
@@ -226,10 +271,11 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       const int tt = town + 4 * i;
       vals[i][0] = sm.dq[tt][cown];
       vals[i][1] = sm.dk[tt][cown];
-      vals[i][2] = sm.dg[tt][cown];
+      vals[i][2] = sm.E[tt][cown];  // dg
     }
     float4 dv4 = *reinterpret_cast<const float4*>(&sm.dv[(tid >> 2) & 15][4 * (tid & 3)]);
     const float dbv = sm.db[tid & 15];
+    __syncthreads();  // the next segment's staging overwrites E
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tt = town + 4 * i;
@@ -245,12 +291,90 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     if (tid < n) atomicAdd(p.dbeta + row0 * HV + hv + tid * HV, dbv);
   };
 
-  // Sums over the keys of x[0..7] (columns c4 .. c4 + 3 of a, then of
-  // Sd^T k).  A 16-lane row holds 4 keys x 4 column groups, so rotations by 4
-  // and 8 keep the group, and the row swaps add the wavefront's four rows;
-  // lanes 0..3 then hold the wavefront's partial sums of all 32 (quantity,
-  // column) pairs, which go to LDS.  After the barrier lane l of every
-  // wavefront reads wavefront l % 8's partials of pair group l / 8 (four
+  // The segment's per-token key sums as matrix products (16 x 16 outputs,
+  // fp32 MFMA 16x16x4, the key axis in steps of 4): lane l supplies the
+  // operands of row l % 16 (a token, or a value column of B) and key step
+  // position l / 16, and holds output rows 4 (l / 16) .. + 3 of column l % 16.
+  // Wavefront 0 % NW forms (k E) S_0, wavefront 1 % NW both (k / E)(k E)^T and
+  // (k / E)(s q E)^T, wavefront 2 % NW (k Suf) dS_in with Suf = gamma / E.
+  auto products = [&]() {
+    const int row = lane & 15, kq = lane >> 4;
+    if (w == 0 % NW) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+      for (int kb = 0; kb < K; kb += 4) {
+        const int key = kb + kq;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.k[row][key] * sm.E[row][key],
+                                                   sm.s0[key][row], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.ps[4 * kq + r][row] = acc[r];
+    }
+    if (w == 1 % NW) {
+      f32x4 a1 = {0.0f, 0.0f, 0.0f, 0.0f}, a2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+      for (int kb = 0; kb < K; kb += 4) {
+        const int key = kb + kq;
+        const float e = sm.E[row][key], kv = sm.k[row][key];
+        const float kh = kv * __builtin_amdgcn_rcpf(e);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, kv * e, a1, 0, 0, 0);
+        a2 = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, sm.q[row][key] * e, a2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sm.g1[4 * kq + r][row] = a1[r];
+        sm.g2[4 * kq + r][row] = a2[r];
+      }
+    }
+    if (w == 2 % NW) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+      for (int kb = 0; kb < K; kb += 4) {
+        const int key = kb + kq;
+        const float ks = sm.k[row][key] * sm.E[kSeg - 1][key] * __builtin_amdgcn_rcpf(sm.E[row][key]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ks, sm.dsin[key][row], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.kd[4 * kq + r][row] = acc[r];
+    }
+  };
+  // From the products, per (token t, column j) of the tile (L_tj = g1[j][t]
+  // for j < t, M_tj = g2[t][j] for j >= t):
+  //   p_t = ps_t + sum_{j<t} L_tj U_j,   r_t = v_t - p_t
+  //   y_t = kd_t + sum_{j>=t} M_tj dL/do_j
+  // then a by back substitution, a_t = y_t - sum_{j>t} L_jt beta_j a_j.
+  auto solve = [&]() {
+    for (int e = tid; e < kSeg * kBV; e += NT) {
+      const int t = e / kBV, j = e % kBV;
+      float pt = sm.ps[t][j], yt = sm.kd[t][j];
+      for (int m = 0; m < t; ++m) pt += sm.g1[m][t] * sm.u[m][j];
+      for (int m = t; m < kSeg; ++m) yt += sm.g2[t][m] * sm.dout[m][j];
+      sm.r[t][j] = sm.v[t][j] - pt;
+      sm.a[t][j] = yt;
+    }
+    __syncthreads();
+    if (tid < kBV) {
+      float y[kSeg];
+#pragma unroll
+      for (int t = 0; t < kSeg; ++t) y[t] = sm.a[t][tid];
+#pragma unroll
+      for (int m = kSeg - 1; m >= 0; --m) {
+        const float am = y[m];
+        sm.a[m][tid] = am;
+        const float bam = sm.beta[m] * am;
+#pragma unroll
+        for (int t = 0; t < m; ++t) y[t] -= sm.g1[t][m] * bam;
+      }
+    }
+  };
+
+  // Fallback for segments whose cumulative decay leaves [2^-100, 2^100]: the
+  // per-token sums over the keys of x[0..7] (columns c4 .. c4 + 3 of a, then
+  // of Sd^T k).  A 16-lane row holds 4 keys x 4 column groups, so rotations
+  // by 4 and 8 keep the group, and the row swaps add the wavefront's four
+  // rows; lanes 0..3 then hold the wavefront's partial sums of all 32
+  // (quantity, column) pairs, which go to LDS.  After the barrier lane l of
+  // every wavefront reads wavefront l % 8's partials of pair group l / 8 (four
   // columns), three lane exchanges inside each group of 8 lanes add the
   // wavefronts, and the totals come back through a slot of the wavefront's
   // own (no further barrier).  The partials are double-buffered: one barrier
@@ -298,9 +422,16 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   if (NC > 0) issue(NC - 1, L);
   for (int seg = NC - 1; seg >= 0; --seg) {
     const int n = min(kSeg, T_ - seg * kSeg);
-    stage(L);
+    const bool bad = stage(L, n);
+    *reinterpret_cast<float4*>(&sm.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
     const float4 ck = L.ckpt;
-    __syncthreads();
+    const bool fallback = __syncthreads_or(bad);
+    if (!fallback) {
+      products();
+      __syncthreads();
+      solve();
+      __syncthreads();
+    }
     // S_t = alpha_t S_{t-1} + k_t U_t^T, from the checkpoint
     auto advance = [&](int tt, float S[4]) {
       const float a = sm.al[tt][kap], kv = sm.k[tt][kap];
@@ -310,27 +441,42 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       S[2] = a * S[2] + kv * u.z;
       S[3] = a * S[3] + kv * u.w;
     };
-    // The reverse step of token tt, given S_{t-1} (no global memory access).
-    auto reverse = [&](int tt, const float sp[4]) {
+    // The reverse step of token tt, given S_{t-1} (no global memory access):
+    // a_t and r_t from the solve, or (fallback) from one sum over the keys.
+    auto reverse = [&](auto from_solve, int tt, const float sp[4]) {
       const float a_ = sm.al[tt][kap], kv = sm.k[tt][kap], qv = sm.q[tt][kap];
       const float bt = sm.beta[tt];
       const float4 d4 = *reinterpret_cast<const float4*>(&sm.dout[tt][c4]);
-      const float4 v4 = *reinterpret_cast<const float4*>(&sm.v[tt][c4]);
-      const float d[4] = {d4.x, d4.y, d4.z, d4.w}, vv[4] = {v4.x, v4.y, v4.z, v4.w};
+      const float d[4] = {d4.x, d4.y, d4.z, d4.w};
       float Sd[4], x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         Sd[i] = a_ * sp[i];
         dS[i] += qv * d[i];  // the read o_t = s S_t^T q_t
-        x[i] = kv * dS[i];
-        x[4 + i] = kv * Sd[i];
       }
-      key_sum8(x);  // a_t = dS^T k_t and the prediction Sd^T k_t, per column
+      if constexpr (decltype(from_solve)::value) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&sm.a[tt][c4]);
+        const float4 r4 = *reinterpret_cast<const float4*>(&sm.r[tt][c4]);
+        x[0] = a4.x; x[1] = a4.y; x[2] = a4.z; x[3] = a4.w;
+        x[4] = r4.x; x[5] = r4.y; x[6] = r4.z; x[7] = r4.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = kv * dS[i];
+          x[4 + i] = kv * Sd[i];
+        }
+        key_sum8(x);  // a_t = dS^T k_t and the prediction Sd^T k_t, per column
+        const float4 v4 = *reinterpret_cast<const float4*>(&sm.v[tt][c4]);
+        x[4] = v4.x - x[4];
+        x[5] = v4.y - x[5];
+        x[6] = v4.z - x[6];
+        x[7] = v4.w - x[7];
+      }
       float dq = 0.0f, dk = 0.0f, dg = 0.0f, db = 0.0f;
       const float bk = bt * kv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float r = vv[i] - x[4 + i];
+        const float r = x[4 + i];
         dq += (Sd[i] + bk * r) * d[i];
         const float dr = bt * x[i];
         db += x[i] * r;
@@ -346,7 +492,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       if (cg == 0) {
         sm.dq[tt][kap] = dq;
         sm.dk[tt][kap] = dk;
-        sm.dg[tt][kap] = dg;
+        sm.E[tt][kap] = dg;  // E is not read after the solve
       }
       if (kap == 0) {
         *reinterpret_cast<float4*>(&sm.dv[tt][c4]) = float4{x[0], x[1], x[2], x[3]};
@@ -357,24 +503,30 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     // The two halves of the segment, the later first: each rebuilds its
     // eight states S_{t-1} from the checkpoint into registers, then runs
     // them in reverse.
+    auto halves = [&](auto from_solve) {
 #pragma unroll
-    for (int half = 1; half >= 0; --half) {
-      const int base = half * (kSeg / 2);
-      float S[4] = {ck.x, ck.y, ck.z, ck.w};
-      for (int tt = 0; tt < base && tt < n; ++tt) advance(tt, S);
-      float st[kSeg / 2][4];
+      for (int half = 1; half >= 0; --half) {
+        const int base = half * (kSeg / 2);
+        float S[4] = {ck.x, ck.y, ck.z, ck.w};
+        for (int tt = 0; tt < base && tt < n; ++tt) advance(tt, S);
+        float st[kSeg / 2][4];
 #pragma unroll
-      for (int j = 0; j < kSeg / 2; ++j) {
-        if (base + j < n) {
+        for (int j = 0; j < kSeg / 2; ++j) {
+          if (base + j < n) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) st[j][i] = S[i];
-          advance(base + j, S);
+            for (int i = 0; i < 4; ++i) st[j][i] = S[i];
+            advance(base + j, S);
+          }
         }
-      }
 #pragma unroll
-      for (int j = kSeg / 2 - 1; j >= 0; --j)
-        if (base + j < n) reverse(base + j, st[j]);
-    }
+        for (int j = kSeg / 2 - 1; j >= 0; --j)
+          if (base + j < n) reverse(from_solve, base + j, st[j]);
+      }
+    };
+    if (fallback)
+      halves(std::false_type{});
+    else
+      halves(std::true_type{});
     __syncthreads();  // the segment's results are in LDS; its inputs are no longer read
     // the next segment's loads go out before the atomics, so that waiting for
     // them does not wait for the atomics; unconditional (the last re-reads

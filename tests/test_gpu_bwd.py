@@ -145,3 +145,29 @@ def test_bwd_unsupported_and_invalid():
     with pytest.raises(kda.KDAError, match="UNSUPPORTED"):
         kda.bwd(e["q"], e["k"], e["v"], e["g_raw"], e["beta"], e["A_log"], e["dt_bias"],
                 dout=torch.zeros((1, 8, 1, 32), device=L.DEV))
+
+
+def test_bwd_strong_decay_takes_the_per_token_path():
+    """Safe gate with L = -20 and a wide g_raw: many 16-token segments decay
+    below 2^-100 in some channel and run the per-token key sums; the others
+    run the matrix form.  Both must match the oracle."""
+    d, dout, dST = _case(1, 120, 2, 4, 64, gate="safe", seed=41)
+    d["g_raw"] = d["g_raw"] * 4.0 + 4.0
+    g = L.to_dev(d)
+    got = kda.bwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"],
+                  gate="safe", lower_bound=-20.0, initial_state=g["S0"], dout=dout.to(L.DEV),
+                  dfinal_state=dST.to(L.DEV))
+    torch.cuda.synchronize()
+    ref = oracle.default().kda_bwd(d["q"], d["k"], d["v"], d["g_raw"], d["beta"], d["A_log"],
+                                   d["dt_bias"], "safe", -20.0, d["S0"], dout, dST)
+    _compare(got, ref, "strong decay")
+
+
+def test_bwd_growth_gate_none():
+    """Gate none with positive log-decays inside segments (the cumulative
+    factor grows above 1, within the matrix form's range)."""
+    d, dout, dST = _case(1, 64, 1, 2, 32, gate="none", seed=43)
+    gen = torch.Generator().manual_seed(44)
+    d["g_raw"] = 0.15 * torch.randn(d["g_raw"].shape, generator=gen)
+    got, ref = _run(d, dout, dST, "none")
+    _compare(got, ref, "growth")
