@@ -115,32 +115,35 @@ __device__ __forceinline__ float quad_bcast(float x) {
 template <int K>
 struct alignas(16) BwdSmem {
   static constexpr int KP = K + 4;  // row stride: the 16 rows of an MFMA operand read spread over the banks
+  // Everything the token loop reads or writes comes first, within the 64 KiB
+  // that a DS instruction's immediate offset reaches, so that one address
+  // register per array serves all tokens.
+  float beta[kSeg];
+  float db[kSeg];
+  float u[kSeg][kBV];  // U = beta r from the forward's state pass (0 past the end)
+  float v[kSeg][kBV];
+  float dout[kSeg][kBV];
+  float a[kSeg][kBV];   // a_t = G_t^T k_t
+  float r[kSeg][kBV];   // r_t = v_t - Sd_t^T k_t
+  float dv[kSeg][kBV];
   // the segment's inputs per (token, key channel)
   float al[kSeg][KP];  // retain factors (1 for tokens past the end)
   float k[kSeg][KP];   // k (0 past the end)
   float q[kSeg][KP];   // s q (0 past the end)
   float E[kSeg][KP];   // prod_{m <= t} alpha_m from the segment start; after the solve, dg
-  float s0[K][kBV];    // the tile of the checkpoint S_0
-  float u[kSeg][kBV];  // U = beta r from the forward's state pass (0 past the end)
-  float v[kSeg][kBV];
-  float dout[kSeg][kBV];
-  float beta[kSeg];
-  // the segment's matrix products and what the solve makes of them
-  float dsin[K][kBV];    // the tile of dL/dS entering the segment's reverse pass
+  // the segment's results, written out together once it is done
+  float dq[kSeg][K];
+  float dk[kSeg][K];
+  // the segment's matrix products and their operands
   float ps[kSeg][kBV];   // (k E) S_0
   float kd[kSeg][kBV];   // (k Suf) dS_in
   float g1[kSeg][kSeg];  // (k / E)(k E)^T
   float g2[kSeg][kSeg];  // (k / E)(s q E)^T
-  float a[kSeg][kBV];    // a_t = G_t^T k_t
-  float r[kSeg][kBV];    // r_t = v_t - Sd_t^T k_t
+  float dsin[K][kBV];    // the tile of dL/dS entering the segment's reverse pass
+  float s0[K][kBV];      // the tile of the checkpoint S_0
   // the per-token key sums of the fallback
   float red[2][K / 16][2][kBV];
   float fin[K / 16][8][4];
-  // the segment's results, written out together once it is done
-  float dq[kSeg][K];
-  float dk[kSeg][K];
-  float dv[kSeg][kBV];
-  float db[kSeg];
 };
 
 // One segment's inputs in flight: this thread's share of g_raw, k and q (key
@@ -500,18 +503,19 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
         if (cg == 0) sm.db[tt] = db;
       }
     };
-    // The two halves of the segment, the later first: each rebuilds its
-    // eight states S_{t-1} from the checkpoint into registers, then runs
-    // them in reverse.
+    // The parts of the segment, the latest first: each rebuilds its kPart
+    // states S_{t-1} from the checkpoint into registers, then runs them in
+    // reverse.
+    constexpr int kPart = 4;
     auto halves = [&](auto from_solve) {
 #pragma unroll
-      for (int half = 1; half >= 0; --half) {
-        const int base = half * (kSeg / 2);
+      for (int part = kSeg / kPart - 1; part >= 0; --part) {
+        const int base = part * kPart;
         float S[4] = {ck.x, ck.y, ck.z, ck.w};
         for (int tt = 0; tt < base && tt < n; ++tt) advance(tt, S);
-        float st[kSeg / 2][4];
+        float st[kPart][4];
 #pragma unroll
-        for (int j = 0; j < kSeg / 2; ++j) {
+        for (int j = 0; j < kPart; ++j) {
           if (base + j < n) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) st[j][i] = S[i];
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
           }
         }
 #pragma unroll
-        for (int j = kSeg / 2 - 1; j >= 0; --j)
+        for (int j = kPart - 1; j >= 0; --j)
           if (base + j < n) reverse(from_solve, base + j, st[j]);
       }
     };
