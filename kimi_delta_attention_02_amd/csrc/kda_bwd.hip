@@ -105,11 +105,20 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 // DPP broadcast of lane I of each group of four lanes (quad permutation
-// [I, I, I, I]).
+// [I, I, I, I]); quad_bcast_dyn takes an index that is a constant once its
+// caller's loop is unrolled.
 template <int I>
 __device__ __forceinline__ float quad_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
                                                                I * 0x55, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_bcast_dyn(int i, float x) {
+  switch (i) {
+    case 0: return quad_bcast<0>(x);
+    case 1: return quad_bcast<1>(x);
+    case 2: return quad_bcast<2>(x);
+    default: return quad_bcast<3>(x);
+  }
 }
 
 template <int K>
@@ -120,6 +129,8 @@ struct alignas(16) BwdSmem {
   // register per array serves all tokens.
   float beta[kSeg];
   float db[kSeg];
+  float rd[kSeg];  // sum over the tile's columns of r_t dL/do_t
+  float ar[kSeg];  // sum over the tile's columns of a_t r_t (the tile's part of dbeta_t)
   float u[kSeg][kBV];  // U = beta r from the forward's state pass (0 past the end)
   float v[kSeg][kBV];
   float dout[kSeg][kBV];
@@ -302,43 +313,55 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // (k / E)(s q E)^T, wavefront 2 % NW (k Suf) dS_in with Suf = gamma / E.
   auto products = [&]() {
     const int row = lane & 15, kq = lane >> 4;
+    // four accumulators per product, so that the dependent MFMA chains are
+    // a quarter as long
     if (w == 0 % NW) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-      for (int kb = 0; kb < K; kb += 4) {
-        const int key = kb + kq;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.k[row][key] * sm.E[row][key],
-                                                   sm.s0[key][row], acc, 0, 0, 0);
+      f32x4 acc[4] = {};
+#pragma unroll 2
+      for (int kb = 0; kb < K; kb += 16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int key = kb + 4 * c + kq;
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.k[row][key] * sm.E[row][key],
+                                                        sm.s0[key][row], acc[c], 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.ps[4 * kq + r][row] = acc[r];
+      for (int r = 0; r < 4; ++r) sm.ps[4 * kq + r][row] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
     }
     if (w == 1 % NW) {
-      f32x4 a1 = {0.0f, 0.0f, 0.0f, 0.0f}, a2 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-      for (int kb = 0; kb < K; kb += 4) {
-        const int key = kb + kq;
-        const float e = sm.E[row][key], kv = sm.k[row][key];
-        const float kh = kv * __builtin_amdgcn_rcpf(e);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, kv * e, a1, 0, 0, 0);
-        a2 = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, sm.q[row][key] * e, a2, 0, 0, 0);
+      f32x4 a1[2] = {}, a2[2] = {};
+#pragma unroll 4
+      for (int kb = 0; kb < K; kb += 8) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int key = kb + 4 * c + kq;
+          const float e = sm.E[row][key], kv = sm.k[row][key];
+          const float kh = kv * __builtin_amdgcn_rcpf(e);
+          a1[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, kv * e, a1[c], 0, 0, 0);
+          a2[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, sm.q[row][key] * e, a2[c], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sm.g1[4 * kq + r][row] = a1[r];
-        sm.g2[4 * kq + r][row] = a2[r];
+        sm.g1[4 * kq + r][row] = a1[0][r] + a1[1][r];
+        sm.g2[4 * kq + r][row] = a2[0][r] + a2[1][r];
       }
     }
     if (w == 2 % NW) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-      for (int kb = 0; kb < K; kb += 4) {
-        const int key = kb + kq;
-        const float ks = sm.k[row][key] * sm.E[kSeg - 1][key] * __builtin_amdgcn_rcpf(sm.E[row][key]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ks, sm.dsin[key][row], acc, 0, 0, 0);
+      f32x4 acc[4] = {};
+#pragma unroll 2
+      for (int kb = 0; kb < K; kb += 16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int key = kb + 4 * c + kq;
+          const float ks =
+              sm.k[row][key] * sm.E[kSeg - 1][key] * __builtin_amdgcn_rcpf(sm.E[row][key]);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ks, sm.dsin[key][row], acc[c], 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.kd[4 * kq + r][row] = acc[r];
+      for (int r = 0; r < 4; ++r) sm.kd[4 * kq + r][row] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
     }
   };
   // From the products, per (token t, column j) of the tile (L_tj = g1[j][t]
@@ -356,17 +379,40 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       sm.a[t][j] = yt;
     }
     __syncthreads();
-    if (tid < kBV) {
-      float y[kSeg];
+    // back substitution on wavefront 0: the four lanes of a quad share a
+    // column, lane s of it holding y_t for t = s, s + 4, s + 8, s + 12; a_m
+    // goes from its lane to the quad by a DPP broadcast
+    if (tid < 64) {
+      const int col = tid >> 2, s4 = tid & 3;
+      float y[4];
 #pragma unroll
-      for (int t = 0; t < kSeg; ++t) y[t] = sm.a[t][tid];
+      for (int i = 0; i < 4; ++i) y[i] = sm.a[s4 + 4 * i][col];
 #pragma unroll
       for (int m = kSeg - 1; m >= 0; --m) {
-        const float am = y[m];
-        sm.a[m][tid] = am;
+        const float am = quad_bcast_dyn(m & 3, y[m >> 2]);
+        if (s4 == (m & 3)) sm.a[m][col] = am;
         const float bam = sm.beta[m] * am;
 #pragma unroll
-        for (int t = 0; t < m; ++t) y[t] -= sm.g1[t][m] * bam;
+        for (int i = 0; i < 4; ++i) {
+          const int t = s4 + 4 * i;
+          y[i] -= (t < m ? sm.g1[t][m] : 0.0f) * bam;
+        }
+      }
+      // per token, the sums over the tile's columns of r_t dL/do_t and a_t r_t
+      // (this wavefront wrote a: its LDS accesses complete in order): lane l
+      // takes token l % 16 and columns 4 (l / 16) .. + 3, then the row swaps
+      // add the four column quarters
+      const int t = tid & 15, cq = 4 * (tid >> 4);
+      const float4 r4 = *reinterpret_cast<const float4*>(&sm.r[t][cq]);
+      const float4 a4 = *reinterpret_cast<const float4*>(&sm.a[t][cq]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&sm.dout[t][cq]);
+      float rdv = r4.x * d4.x + r4.y * d4.y + r4.z * d4.z + r4.w * d4.w;
+      float arv = a4.x * r4.x + a4.y * r4.y + a4.z * r4.z + a4.w * r4.w;
+      rdv = xor_sum<32>(xor_sum<16>(rdv));
+      arv = xor_sum<32>(xor_sum<16>(arv));
+      if (tid < kSeg) {
+        sm.rd[t] = rdv;
+        sm.ar[t] = arv;
       }
     }
   };
@@ -435,76 +481,89 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       solve();
       __syncthreads();
     }
-    // S_t = alpha_t S_{t-1} + k_t U_t^T, from the checkpoint
-    auto advance = [&](int tt, float S[4]) {
+    // S_t = Sd_t + k_t U_t^T with Sd_t = alpha_t S_{t-1}, from the
+    // checkpoint; Sd_t is also handed back
+    auto advance = [&](int tt, float S[4], float sd[4]) {
       const float a = sm.al[tt][kap], kv = sm.k[tt][kap];
       const float4 u = *reinterpret_cast<const float4*>(&sm.u[tt][c4]);
-      S[0] = a * S[0] + kv * u.x;
-      S[1] = a * S[1] + kv * u.y;
-      S[2] = a * S[2] + kv * u.z;
-      S[3] = a * S[3] + kv * u.w;
+      const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sd[i] = a * S[i];
+        S[i] = sd[i] + kv * uu[i];
+      }
     };
-    // The reverse step of token tt, given S_{t-1} (no global memory access):
-    // a_t and r_t from the solve, or (fallback) from one sum over the keys.
-    auto reverse = [&](auto from_solve, int tt, const float sp[4]) {
+    // The reverse step of token tt, given Sd_t (no global memory access):
+    // a_t, r_t and their column sums from the solve, or (fallback) from one
+    // sum over the keys.  With dS the gradient after the read, and beta
+    // factored out of the sums over the columns j:
+    //   dq = s (sum_j Sd d_j + beta k sum_j r_j d_j)
+    //   dk = beta (sum_j dS r_j - sum_j Sd a_j)
+    //   dg = sum_j (dS - k beta a_j) Sd,   dS <- alpha (dS - k beta a)
+    auto reverse = [&](auto from_solve, int tt, const float sd[4]) {
       const float a_ = sm.al[tt][kap], kv = sm.k[tt][kap], qv = sm.q[tt][kap];
       const float bt = sm.beta[tt];
       const float4 d4 = *reinterpret_cast<const float4*>(&sm.dout[tt][c4]);
       const float d[4] = {d4.x, d4.y, d4.z, d4.w};
-      float Sd[4], x[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Sd[i] = a_ * sp[i];
-        dS[i] += qv * d[i];  // the read o_t = s S_t^T q_t
-      }
+      for (int i = 0; i < 4; ++i) dS[i] += qv * d[i];  // the read o_t = s S_t^T q_t
+      float a[4], r[4], rd, ar;
       if constexpr (decltype(from_solve)::value) {
         const float4 a4 = *reinterpret_cast<const float4*>(&sm.a[tt][c4]);
         const float4 r4 = *reinterpret_cast<const float4*>(&sm.r[tt][c4]);
-        x[0] = a4.x; x[1] = a4.y; x[2] = a4.z; x[3] = a4.w;
-        x[4] = r4.x; x[5] = r4.y; x[6] = r4.z; x[7] = r4.w;
+        a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
+        r[0] = r4.x; r[1] = r4.y; r[2] = r4.z; r[3] = r4.w;
+        rd = sm.rd[tt];
+        ar = sm.ar[tt];
       } else {
+        float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           x[i] = kv * dS[i];
-          x[4 + i] = kv * Sd[i];
+          x[4 + i] = kv * sd[i];
         }
         key_sum8(x);  // a_t = dS^T k_t and the prediction Sd^T k_t, per column
         const float4 v4 = *reinterpret_cast<const float4*>(&sm.v[tt][c4]);
-        x[4] = v4.x - x[4];
-        x[5] = v4.y - x[5];
-        x[6] = v4.z - x[6];
-        x[7] = v4.w - x[7];
+        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+        rd = 0.0f;
+        ar = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] = x[i];
+          r[i] = vv[i] - x[4 + i];
+          rd += r[i] * d[i];
+          ar += a[i] * r[i];
+        }
+        rd = quad_sum(rd);
+        ar = quad_sum(ar);
       }
-      float dq = 0.0f, dk = 0.0f, dg = 0.0f, db = 0.0f;
-      const float bk = bt * kv;
+      const float kb = kv * bt;
+      float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float r = x[4 + i];
-        dq += (Sd[i] + bk * r) * d[i];
-        const float dr = bt * x[i];
-        db += x[i] * r;
-        dk += bt * dS[i] * r - Sd[i] * dr;
-        const float dsd = dS[i] - kv * dr;
-        dg += dsd * Sd[i];
+        s1 += sd[i] * d[i];
+        s2 += dS[i] * r[i];
+        s2 -= sd[i] * a[i];
+        const float dsd = dS[i] - kb * a[i];
+        s3 += dsd * sd[i];
         dS[i] = a_ * dsd;
-        x[i] = dr;
       }
-      dq = quad_sum(dq) * scale;
-      dk = quad_sum(dk);
-      dg = quad_sum(dg);
+      s1 = quad_sum(s1);
+      s2 = quad_sum(s2);
+      s3 = quad_sum(s3);
       if (cg == 0) {
-        sm.dq[tt][kap] = dq;
-        sm.dk[tt][kap] = dk;
-        sm.E[tt][kap] = dg;  // E is not read after the solve
+        sm.dq[tt][kap] = scale * (s1 + kb * rd);
+        sm.dk[tt][kap] = bt * s2;
+        sm.E[tt][kap] = s3;  // dg; E is not read after the solve
       }
       if (kap == 0) {
-        *reinterpret_cast<float4*>(&sm.dv[tt][c4]) = float4{x[0], x[1], x[2], x[3]};
-        db = quad_sum(db);
-        if (cg == 0) sm.db[tt] = db;
+        *reinterpret_cast<float4*>(&sm.dv[tt][c4]) =
+            float4{bt * a[0], bt * a[1], bt * a[2], bt * a[3]};
+        if (cg == 0) sm.db[tt] = ar;
       }
     };
     // The parts of the segment, the latest first: each rebuilds its kPart
-    // states S_{t-1} from the checkpoint into registers, then runs them in
+    // states Sd_t from the checkpoint into registers, then runs them in
     // reverse.
     constexpr int kPart = 4;
     auto halves = [&](auto from_solve) {
@@ -512,19 +571,14 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       for (int part = kSeg / kPart - 1; part >= 0; --part) {
         const int base = part * kPart;
         float S[4] = {ck.x, ck.y, ck.z, ck.w};
-        for (int tt = 0; tt < base && tt < n; ++tt) advance(tt, S);
-        float st[kPart][4];
+        float sd[kPart][4];
+        for (int tt = 0; tt < base && tt < n; ++tt) advance(tt, S, sd[0]);
 #pragma unroll
-        for (int j = 0; j < kPart; ++j) {
-          if (base + j < n) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st[j][i] = S[i];
-            advance(base + j, S);
-          }
-        }
+        for (int j = 0; j < kPart; ++j)
+          if (base + j < n) advance(base + j, S, sd[j]);
 #pragma unroll
         for (int j = kPart - 1; j >= 0; --j)
-          if (base + j < n) reverse(from_solve, base + j, st[j]);
+          if (base + j < n) reverse(from_solve, base + j, sd[j]);
       }
     };
     if (fallback)
