@@ -25,19 +25,27 @@
 // of every token in its workspace.  One workgroup per (sequence, value head,
 // 16-wide value tile) then walks the segments from the last.  Thread
 // 4 kappa + c holds key row kappa, value columns 4 c .. 4 c + 3 of the tile.
-// Per segment it stages the retain factors, k and q of the sixteen tokens in
-// LDS, rebuilds the sixteen states from the checkpoint in registers with
-// S_t = diag(alpha_t) S_{t-1} + k_t U_t^T (no reduction), then runs the
-// reverse recurrence with its tile of dS in registers.  Each reverse token
-// needs one sum over the keys, of dS^T k_t and of the prediction Sd_t^T k_t
-// together (the residual r_t is formed again from the latter): DPP row
-// rotations, row swaps and one LDS exchange across the wavefronts; sums over
-// the tile's columns are in-thread plus two lane exchanges.  The per-key
-// results (dq, dk, dg) and dbeta, summed over the value tiles (and the value
-// heads of a GVA group), are accumulated with fp32 atomics into zeroed
-// outputs, so their last bits depend on the order the tiles finish in.  A
-// last kernel applies the gate's chain rule and sums dt_bias and A_log over
-// the sequences.
+//
+// Inside a segment the reverse recurrence of dL/dS is the adjoint of the
+// forward's delta rule, dS_{t-1} = diag(alpha_t)(I - beta_t k_t k_t^T) G_t with
+// G_t = dS_t + s q_t do_t^T, so everything that couples the tokens through a
+// sum over the keys is a product over the segment.  With E_t the cumulative
+// retain factor from the segment start (per channel), Suf_t = E_15 / E_t,
+// L = strictly-lower[(k E)(k / E)^T] and M = upper[(k / E)(s q E)^T]:
+//   predictions  p = (k E) S_0 + L U,             r = v - p
+//   a_t = G_t^T k_t:  (I + L^T diag(beta)) A = M dL/do + (k Suf) dS_in
+// (dS_in: dL/dS entering the segment's reverse pass).  Three wavefronts form
+// the four products on fp32 MFMA, one wavefront back-substitutes, and the
+// token loop is then elementwise: the segment's states are rebuilt from the
+// checkpoint in registers, S_t = alpha_t S_{t-1} + k_t U_t^T, and each token
+// updates dS and forms its dq, dk, dg partial sums over the tile's columns.
+// Segments whose E leaves [2^-100, 2^100] (where k / E would lose range) take
+// the per-token sums over the keys instead (DPP and row swaps inside a
+// wavefront, an LDS exchange across them).  The per-key results (dq, dk, dg)
+// and dbeta, summed over the value tiles (and the value heads of a GVA group),
+// are accumulated with fp32 atomics into zeroed outputs, once per segment, so
+// their last bits depend on the order the tiles finish in.  A last kernel
+// applies the gate's chain rule and sums dt_bias and A_log over the sequences.
 // Arithmetic is fp32 throughout (bf16 inputs widened exactly).
 #include <type_traits>
 
