@@ -171,3 +171,42 @@ def test_bwd_growth_gate_none():
     d["g_raw"] = 0.15 * torch.randn(d["g_raw"].shape, generator=gen)
     got, ref = _run(d, dout, dST, "none")
     _compare(got, ref, "growth")
+
+
+@pytest.mark.timeout(600)
+def test_bwd_workload_prefill_all_heads():
+    """The backward at the size the benchmark times it (the prefill workload:
+    B = 4, T = 4096, H = HV = 16, K = V = 128, bf16, safe gate), one call on
+    the whole input.  The oracle recomputes every value head, one at a time
+    (all four sequences over their whole length, which bounds host memory),
+    so every gradient, including the sums over the sequences (A_log,
+    dt_bias), is compared element by element; the bar applies per head and
+    tensor."""
+    w = synth.WORKLOADS["prefill"]
+    d = synth.make_inputs(w)
+    gen = torch.Generator().manual_seed(77)
+    dout = torch.randn((w.B, w.T, w.HV, w.V), generator=gen)
+    g = L.to_dev(d)
+    print("bwd prefill: B=%d T=%d HV=%d K=%d" % (w.B, w.T, w.HV, w.K), flush=True)
+    got = kda.bwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"],
+                  gate=w.gate, lower_bound=w.lower_bound, dout=dout.to(L.DEV))
+    torch.cuda.synchronize()
+    got = {n: (t.cpu() if t is not None else None) for n, t in got.items()}
+    assert w.H == w.HV
+    ref_alog, ref_bias = np.zeros(w.HV), np.zeros((w.HV, w.K))
+    for hv in range(w.HV):
+        sl = slice(hv, hv + 1)
+        sub = lambda x, ax: x.narrow(ax, hv, 1) if x is not None else None
+        ref = oracle.default().kda_bwd(sub(d["q"], 2), sub(d["k"], 2), sub(d["v"], 2),
+                                       sub(d["g_raw"], 2), sub(d["beta"], 2), d["A_log"][sl],
+                                       d["dt_bias"][sl], w.gate, w.lower_bound, None,
+                                       dout[:, :, sl], None)
+        mine = {"dq": got["dq"][:, :, sl], "dk": got["dk"][:, :, sl], "dv": got["dv"][:, :, sl],
+                "dbeta": got["dbeta"][:, :, sl], "dg_raw": got["dg_raw"][:, :, sl]}
+        ref_alog[hv], ref_bias[hv] = ref["dA_log"][0], ref["ddt_bias"][0]
+        ref["dA_log"] = ref["ddt_bias"] = ref["dS0"] = None
+        _compare(mine, ref, "prefill head %d" % hv)
+    # the per-head sums over all tokens, as whole tensors (one scalar per head
+    # for A_log: its RMS over the heads, like every other gradient here)
+    _compare({"dA_log": got["dA_log"], "ddt_bias": got["ddt_bias"]},
+             {"dA_log": ref_alog, "ddt_bias": ref_bias}, "prefill per-head sums")
