@@ -278,18 +278,20 @@ kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void*
  * that read the same query/key head.
  *
  *   q, k, v, qkv_dtype, g_raw, beta, A_log, dt_bias, gate, lower_bound,
- *   initial_state        the forward's inputs, as kda_chunk_fwd (per-channel
- *                        gate only)
+ *   initial_state        the forward's inputs, as kda_chunk_fwd (a per-channel
+ *                        or, with KDA_GATE_PER_HEAD, a per-head gate)
  *   dout                 [B, T, HV, V]  float32, dL/do
  *   dfinal_state         [B, HV, K, V]  float32, dL/dS_T, or NULL for zero
  *   dq, dk               [B, T, H, K]   float32 outputs
  *   dv                   [B, T, HV, V]  float32 output
  *   dbeta                [B, T, HV]     float32 output
- *   dg_raw               [B, T, HV, K]  float32 output
+ *   dg_raw               [B, T, HV, K]  float32 output ([B, T, HV] with a
+ *                                       per-head gate: the sum over the key
+ *                                       channels the value is broadcast to)
  *   dA_log               [HV]           float32 output, or NULL to skip
- *   ddt_bias             [HV, K]        float32 output, or NULL to skip (with
- *                                       dt_bias NULL it is the gradient at a
- *                                       zero bias)
+ *   ddt_bias             [HV, K]        float32 output ([HV] with a per-head
+ *                                       gate), or NULL to skip (with dt_bias
+ *                                       NULL it is the gradient at a zero bias)
  *   dinitial_state       [B, HV, K, V]  float32 output (dL/dS_0), or NULL
  *   workspace            device scratch of at least kda_bwd_workspace_bytes(...)
  *                        bytes, 16-byte aligned, owned by the caller; it holds
@@ -301,8 +303,8 @@ kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void*
  * last bits can differ from run to run; dv and dinitial_state are written
  * once.  All pointers are device pointers; outputs must not alias inputs or
  * each other.
- * Supported: K == V in {32, 64, 128}; HV % H == 0; T >= 0; a per-channel gate
- * (KDA_GATE_PER_HEAD is KDA_ERR_UNSUPPORTED).  Arithmetic is fp32 throughout
+ * Supported: K == V in {32, 64, 128}; HV % H == 0; T >= 0; either gate
+ * layout.  Arithmetic is fp32 throughout
  * (bf16 inputs widened exactly; the forward pass that writes the segment
  * states is that of kda_chunk_fwd_split with chunk 16).  Several kernels run
  * in order on `stream`.  Returns KDA_ERR_WORKSPACE if the workspace is missing

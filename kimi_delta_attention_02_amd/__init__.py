@@ -219,10 +219,10 @@ def bwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_bound=-
         want_dinitial_state=None, workspace=None):
     """Gradients of the forward (kda_bwd) for dL/do = dout [B, T, HV, V] and
     dL/dS_T = dfinal_state (or zero).  Returns a dict of float32 tensors: dq,
-    dk [B, T, H, K], dv [B, T, HV, V], dbeta [B, T, HV], dg_raw [B, T, HV, K],
-    dA_log [HV] (None unless want_dA_log), ddt_bias [HV, K] (by default when
-    dt_bias is given), dS0 [B, HV, K, V] (by default when initial_state is
-    given)."""
+    dk [B, T, H, K], dv [B, T, HV, V], dbeta [B, T, HV], dg_raw [B, T, HV, K]
+    ([B, T, HV] for a per-head gate), dA_log [HV] (None unless want_dA_log),
+    ddt_bias [HV, K] or [HV] (by default when dt_bias is given), dS0
+    [B, HV, K, V] (by default when initial_state is given)."""
     lib = _lib.load()
     qkv = _qkv_dtype(q)
     dev, B, T, H, HV, K, V, per_head = _check_sequence_args(q, k, v, g_raw, beta, A_log, dt_bias,
@@ -231,13 +231,14 @@ def bwd(q, k, v, g_raw, beta, A_log, dt_bias=None, *, gate="safe", lower_bound=-
     if dfinal_state is not None:
         _need(dfinal_state, "dfinal_state", torch.float32, (B, HV, K, V), dev)
     f32 = dict(dtype=torch.float32, device=dev)
+    gk = () if per_head else (K,)  # a per-head gate has no key axis
     out = {"dq": torch.empty((B, T, H, K), **f32), "dk": torch.empty((B, T, H, K), **f32),
            "dv": torch.empty((B, T, HV, V), **f32), "dbeta": torch.empty((B, T, HV), **f32),
-           "dg_raw": torch.empty((B, T, HV, K), **f32)}
+           "dg_raw": torch.empty((B, T, HV) + gk, **f32)}
     out["dA_log"] = torch.empty((HV,), **f32) if want_dA_log else None
     if want_ddt_bias is None:
         want_ddt_bias = dt_bias is not None
-    out["ddt_bias"] = torch.empty((HV, K), **f32) if want_ddt_bias else None
+    out["ddt_bias"] = torch.empty((HV,) + gk, **f32) if want_ddt_bias else None
     if want_dinitial_state is None:
         want_dinitial_state = initial_state is not None
     out["dS0"] = torch.empty((B, HV, K, V), **f32) if want_dinitial_state else None

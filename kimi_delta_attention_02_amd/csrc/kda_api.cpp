@@ -34,7 +34,7 @@ hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, c
 size_t bwd_workspace_bytes(int B, int T, int HV, int K, int V);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                       const float* beta, const float* A_log, const float* dt_bias, int kind,
-                      float lower_bound, const float* S0, const float* dout, const float* dST,
+                      int per_head, float lower_bound, const float* S0, const float* dout, const float* dST,
                       float* dq, float* dk, float* dv, float* dbeta, float* dg_raw, float* dA_log,
                       float* ddt_bias, float* dS0, void* workspace, int B, int T, int H, int HV,
                       int K, hipStream_t stream);
@@ -303,7 +303,6 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, kda_dtype qkv_dt
                    void* workspace, size_t workspace_bytes, kda_stream_t stream) {
   kda_status st = check_gate(gate, lower_bound, A_log);
   if (st != KDA_OK) return st;
-  if (gate_per_head(gate)) return KDA_ERR_UNSUPPORTED;
   if (qkv_dtype != KDA_F32 && qkv_dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
   if (B < 0 || T < 0 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0) return KDA_ERR_INVALID_ARG;
   if ((long)B * HV > (1L << 26) || HV > 65535) return KDA_ERR_INVALID_ARG;
@@ -324,7 +323,7 @@ kda_status kda_bwd(const void* q, const void* k, const void* v, kda_dtype qkv_dt
   if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
   if (B == 0 && !dA_log && !ddt_bias) return KDA_OK;  // else those two sums are zero-filled
   return from_hip(kda::launch_bwd(q, k, v, qkv_dtype == KDA_BF16, g_raw, beta, A_log, dt_bias,
-                                  gate_base(gate), lower_bound, initial_state, dout, dfinal_state,
+                                  gate_base(gate), gate_per_head(gate), lower_bound, initial_state, dout, dfinal_state,
                                   dq, dk, dv, dbeta, dg_raw, dA_log, ddt_bias, dinitial_state,
                                   workspace, B, T, H, HV, K, reinterpret_cast<hipStream_t>(stream)));
 }

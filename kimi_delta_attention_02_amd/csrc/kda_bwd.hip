@@ -74,6 +74,7 @@ struct BwdParams {
   float* dA_log;
   float* ddt_bias;
   int B, T, H, HV, NC;
+  int per_head;  // one gate value per (token, value head): g_raw, dL/dg [B, T, HV], dt_bias [HV]
   float lower_bound;
 };
 
@@ -176,7 +177,7 @@ struct SegLoads {
   float4 u, ckpt;
 };
 
-template <int K, typename T, int GK>
+template <int K, typename T, int GK, bool PH>
 __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void bwd_segment_kernel(
     BwdParams p) {
   constexpr int V = K, NT = 4 * K, NW = NT / 64, NVT = V / kBV;
@@ -192,8 +193,11 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   const float scale = 1.0f / __builtin_sqrtf((float)K);
   const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
   const GateConsts gc = gate_consts(rate, p.lower_bound);
+  // PH: one gate value per (token, value head) (p.per_head)
+  constexpr int gK = PH ? 1 : K;  // gate stride
+  const int gc0 = PH ? 0 : kap;   // this thread's gate element
   const float bias = gate_bias_pre<GK>(
-      (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * K + kap] : 0.0f, gc);
+      (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * gK + gc0] : 0.0f, gc);
   const int town = tid / K, cown = tid % K;  // the layout of the results' write-out
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
@@ -205,13 +209,13 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   auto issue = [&](int seg, SegLoads<T, NVD>& L) {
     const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
     const long row0 = b * T_ + t0;
-    const float* gb = p.g_raw + (row0 * HV + hv) * K;
+    const float* gb = p.g_raw + (row0 * HV + hv) * gK;
     const T* kb = kg + (row0 * H + h) * K;
     const T* qb = qg + (row0 * H + h) * K;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = min(c4 + i, n - 1);
-      L.g[i] = gb[r * HV * K + kap];
+      L.g[i] = gb[r * HV * gK + gc0];
       L.k[i] = kb[r * H * K + kap];
       L.q[i] = qb[r * H * K + kap];
     }
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     const long row0 = b * T_ + t0;
     float* dqb = p.dq + (row0 * H + h) * K;
     float* dkb = p.dk + (row0 * H + h) * K;
-    float* dgb = p.dg + (row0 * HV + hv) * K;
+    float* dgb = p.dg + (row0 * HV + hv) * K;  // per-channel gate
     float vals[4][3];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -297,6 +301,18 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     }
     float4 dv4 = *reinterpret_cast<const float4*>(&sm.dv[(tid >> 2) & 15][4 * (tid & 3)]);
     const float dbv = sm.db[tid & 15];
+    // per-head gate: token tid / 4's dg summed over the key channels (the
+    // gate is one value broadcast over them)
+    float dgh = 0.0f;
+    if (PH && tid < 64) {
+      const int tt = tid >> 2;
+      float s0 = 0.0f, s1 = 0.0f;
+      for (int c = tid & 3; c < K; c += 8) {
+        s0 += sm.E[tt][c];
+        s1 += sm.E[tt][c + 4];
+      }
+      dgh = quad_sum(s0 + s1);
+    }
     __syncthreads();  // the next segment's staging overwrites E
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -304,9 +320,11 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       if (tt < n) {
         atomicAdd(dqb + tt * H * K + cown, vals[i][0]);
         atomicAdd(dkb + tt * H * K + cown, vals[i][1]);
-        atomicAdd(dgb + tt * HV * K + cown, vals[i][2]);
+        if (!PH) atomicAdd(dgb + tt * HV * K + cown, vals[i][2]);
       }
     }
+    if (PH && tid < 64 && (tid & 3) == 0 && (tid >> 2) < n)
+      atomicAdd(p.dg + row0 * HV + hv + (tid >> 2) * HV, dgh);
     if (tid < 64 && (tid >> 2) < n)
       *reinterpret_cast<float4*>(p.dv + (row0 * HV + hv) * V + v0 + (tid >> 2) * HV * V +
                                  4 * (tid & 3)) = dv4;
@@ -647,6 +665,51 @@ __global__ void bwd_gate_kernel(BwdParams p, int K, long rows) {
   }
 }
 
+// The per-head gate's chain rule: one thread per row (sequence, token) of
+// one value head, dL/dg -> dL/dg_raw in place, the dt_bias and A_log sums
+// reduced over the workgroup's rows before one atomic each.
+template <int GK>
+__global__ __launch_bounds__(256) void bwd_gate_head_kernel(BwdParams p, long rows) {
+  const int hv = blockIdx.y, tid = threadIdx.x;
+  const long r = (long)blockIdx.x * 256 + tid;
+  const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
+  const float bias = (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv] : 0.0f;
+  float dx = 0.0f, da = 0.0f;
+  if (r < rows) {
+    const long i = r * p.HV + hv;
+    const float dg = p.dg[i], x = p.g_raw[i] + bias;
+    dx = dg;
+    if constexpr (GK == KDA_GATE_SAFE) {
+      const float z = rate * x;
+      const float sg = __builtin_amdgcn_rcpf(1.0f + exp_f(-z));
+      const float d = p.lower_bound * sg * (1.0f - sg);
+      dx = dg * d * rate;
+      da = dg * d * z;
+    } else if constexpr (GK == KDA_GATE_STANDARD) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + exp_f(-x));
+      dx = -dg * rate * sg;
+      da = -dg * rate * softplus_f(x);
+    }
+    p.dg[i] = dx;
+  }
+  if (GK == KDA_GATE_NONE) return;  // neither dt_bias nor A_log enters this gate
+  __shared__ float red[2][256];
+  red[0][tid] = dx;
+  red[1][tid] = da;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) {
+      red[0][tid] += red[0][tid + st];
+      red[1][tid] += red[1][tid + st];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (p.ddt_bias) atomicAdd(p.ddt_bias + hv, red[0][0]);
+    if (p.dA_log) atomicAdd(p.dA_log + hv, red[1][0]);
+  }
+}
+
 hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
                         int per_head, float lower_bound, const float* S0, float* o, float* S_out,
@@ -675,21 +738,30 @@ template <int K, typename T, int GK>
 static hipError_t launch_bwd_kt(BwdParams p, hipStream_t stream) {
   const long nblk = (long)p.B * p.HV * (K / kBV);
   if (nblk > 0) {
-    hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK>), dim3((unsigned)nblk), dim3(4 * K), 0, stream,
-                       p);
+    if (p.per_head)
+      hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK, true>), dim3((unsigned)nblk), dim3(4 * K), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK, false>), dim3((unsigned)nblk), dim3(4 * K),
+                         0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long rows = (long)p.B * p.T;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_gate_kernel<GK>), dim3((unsigned)((rows + 63) / 64), (unsigned)p.HV),
-                     dim3(K), 0, stream, p, K, rows);
+  if (p.per_head)
+    hipLaunchKernelGGL((bwd_gate_head_kernel<GK>),
+                       dim3((unsigned)((rows + 255) / 256), (unsigned)p.HV), dim3(256), 0, stream,
+                       p, rows);
+  else
+    hipLaunchKernelGGL((bwd_gate_kernel<GK>), dim3((unsigned)((rows + 63) / 64), (unsigned)p.HV),
+                       dim3(K), 0, stream, p, K, rows);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                       const float* beta, const float* A_log, const float* dt_bias, int kind,
-                      float lower_bound, const float* S0, const float* dout, const float* dST,
+                      int per_head, float lower_bound, const float* S0, const float* dout, const float* dST,
                       float* dq, float* dk, float* dv, float* dbeta, float* dg_raw, float* dA_log,
                       float* ddt_bias, float* dS0, void* workspace, int B, int T, int H, int HV,
                       int K, hipStream_t stream) {
@@ -698,21 +770,22 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
   float* ckpt = reinterpret_cast<float*>(ws);
   void* split_ws = ws + align256((size_t)B * HV * NC * K * K * sizeof(float));
   hipError_t e;
-  const long nq = (long)B * T * H * K, ng = (long)B * T * HV * K;
+  const int gK = per_head ? 1 : K;  // gate values per (token, value head)
+  const long nq = (long)B * T * H * K, ng = (long)B * T * HV * gK;
   if ((e = zero(dq, nq, stream)) != hipSuccess || (e = zero(dk, nq, stream)) != hipSuccess ||
       (e = zero(dbeta, (long)B * T * HV, stream)) != hipSuccess ||
       (e = zero(dg_raw, ng, stream)) != hipSuccess || (e = zero(dA_log, HV, stream)) != hipSuccess ||
-      (e = zero(ddt_bias, (long)HV * K, stream)) != hipSuccess)
+      (e = zero(ddt_bias, (long)HV * gK, stream)) != hipSuccess)
     return e;
   if (T > 0) {
     // the states and U only (no o): the split skips its output stage
-    e = launch_split(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, 0, lower_bound, S0,
+    e = launch_split(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, per_head, lower_bound, S0,
                      nullptr, nullptr, ckpt, split_ws, B, T, H, HV, K, kSeg, stream);
     if (e != hipSuccess) return e;
   }
   const float* u = split_resolved_values(split_ws, (long)B * HV * NC, K, kSeg);
   BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, u, dq, dk, dv, dbeta,
-              dg_raw, dS0, dA_log, ddt_bias, B, T, H, HV, NC, lower_bound};
+              dg_raw, dS0, dA_log, ddt_bias, B, T, H, HV, NC, per_head, lower_bound};
 #define KDA_BWD_GATE(KK, TT)                                                       \
   switch (kind) {                                                                  \
     case KDA_GATE_SAFE: return launch_bwd_kt<KK, TT, KDA_GATE_SAFE>(p, stream);    \

@@ -111,7 +111,7 @@ int main() {
         g_last.workspace == P, "bwd sizes not forwarded");
   expect("bwd small ws", KDA_ERR_WORKSPACE, false, [&] {
     return bwd(KDA_GATE_SAFE, 64, 64, P, F, P, bneed - 1, 2, 4, 37); });
-  expect("bwd per-head", KDA_ERR_UNSUPPORTED, false, [&] {
+  expect("bwd per-head", KDA_OK, true, [&] {
     return bwd((kda_gate_kind)(KDA_GATE_SAFE | KDA_GATE_PER_HEAD), 64, 64, P, F, P, bneed, 2, 4, 37); });
   expect("bwd K=16", KDA_ERR_UNSUPPORTED, false, [&] { return bwd(KDA_GATE_SAFE, 16, 16, P, F, P, bneed, 2, 4, 37); });
   expect("bwd K!=V", KDA_ERR_UNSUPPORTED, false, [&] { return bwd(KDA_GATE_SAFE, 64, 32, P, F, P, bneed, 2, 4, 37); });

@@ -54,7 +54,7 @@ size_t bwd_workspace_bytes(int B, int T, int HV, int K, int V) {
   return (size_t)B * HV * (((size_t)T + 15) / 16) * K * V * sizeof(float) + 256;
 }
 hipError_t launch_bwd(const void*, const void*, const void*, int, const float*, const float*,
-                      const float*, const float*, int, float, const float*, const float*,
+                      const float*, const float*, int, int, float, const float*, const float*,
                       const float*, float*, float*, float*, float*, float*, float*, float*, float*,
                       void* workspace, int B, int T, int H, int HV, int K, hipStream_t) {
   record("bwd", B, T, H, HV, K, K, workspace);

@@ -286,7 +286,9 @@ def _bwd(lib, **kw):
 
 @needs_no_gpu
 @pytest.mark.parametrize("kw,status", [
-    (dict(gate=_lib.KDA_GATE_PER_HEAD | 1), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(gate=_lib.KDA_GATE_PER_HEAD | 3), _lib.KDA_ERR_INVALID_ARG),
+    (dict(gate=_lib.KDA_GATE_PER_HEAD | 1, g=P + 4, bias=P + 4, B=0, ws=None, wsb=0, dA=None,
+          dbias=None), _lib.KDA_OK),
     (dict(K=16, V=16), _lib.KDA_ERR_UNSUPPORTED),
     (dict(K=64, V=32), _lib.KDA_ERR_UNSUPPORTED),
     (dict(dq=None), _lib.KDA_ERR_INVALID_ARG),

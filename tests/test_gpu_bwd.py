@@ -141,10 +141,6 @@ def test_bwd_unsupported_and_invalid():
     with pytest.raises(kda.KDAError, match="UNSUPPORTED"):
         kda.bwd(d["q"], d["k"], d["v"], d["g_raw"], d["beta"], d["A_log"], d["dt_bias"],
                 dout=dout)
-    e = L.to_dev(synth.random_inputs(1, 8, 1, 1, 32, 32, seed=1, per_head_gate=True))
-    with pytest.raises(kda.KDAError, match="UNSUPPORTED"):
-        kda.bwd(e["q"], e["k"], e["v"], e["g_raw"], e["beta"], e["A_log"], e["dt_bias"],
-                dout=torch.zeros((1, 8, 1, 32), device=L.DEV))
 
 
 def test_bwd_strong_decay_takes_the_per_token_path():
@@ -210,3 +206,28 @@ def test_bwd_workload_prefill_all_heads():
     # for A_log: its RMS over the heads, like every other gradient here)
     _compare({"dA_log": got["dA_log"], "ddt_bias": got["ddt_bias"]},
              {"dA_log": ref_alog, "ddt_bias": ref_bias}, "prefill per-head sums")
+
+
+@pytest.mark.parametrize("gate", ["safe", "standard", "none"])
+def test_bwd_per_head_gate(gate):
+    """One gate value per (token, value head), broadcast over the key channels
+    (Gated DeltaNet's scalar gate): against the oracle run on the gate written
+    out per channel, whose g_raw and dt_bias gradients sum over the channels."""
+    d = synth.random_inputs(2, 37, 2, 4, 64, 64, seed=50, s0_std=0.3, per_head_gate=True)
+    if gate == "none":
+        d["g_raw"] = -0.2 * d["g_raw"].abs()
+    gen = torch.Generator().manual_seed(51)
+    dout = torch.randn((2, 37, 4, 64), generator=gen)
+    dST = torch.randn((2, 4, 64, 64), generator=gen)
+    g = L.to_dev(d)
+    got = kda.bwd(g["q"], g["k"], g["v"], g["g_raw"], g["beta"], g["A_log"], g["dt_bias"],
+                  gate=gate, lower_bound=-5.0, initial_state=g["S0"], dout=dout.to(L.DEV),
+                  dfinal_state=dST.to(L.DEV))
+    torch.cuda.synchronize()
+    assert got["dg_raw"].shape == (2, 37, 4) and got["ddt_bias"].shape == (4,)
+    e = L.per_channel_gate(d)
+    ref = oracle.default().kda_bwd(e["q"], e["k"], e["v"], e["g_raw"], e["beta"], e["A_log"],
+                                   e["dt_bias"], gate, -5.0, e["S0"], dout, dST)
+    ref["dg_raw"] = ref["dg_raw"].sum(axis=-1)
+    ref["ddt_bias"] = ref["ddt_bias"].sum(axis=-1)
+    _compare(got, ref, "per-head %s" % gate)
