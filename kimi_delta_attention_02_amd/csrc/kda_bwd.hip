@@ -113,6 +113,14 @@ __device__ __forceinline__ float quad_sum(float x) {
                                                                    0x4E, 0xF, 0xF, true));
 }
 
+// x, with the compiler unable to see its value: per-thread offsets derived
+// from it inside a phase of the segment loop are formed there, rather than
+// hoisted out of the loop (where they would hold registers through it)
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // DPP broadcast of lane I of each group of four lanes (quad permutation
 // [I, I, I, I]); quad_bcast_dyn takes an index that is a constant once its
 // caller's loop is unrolled.
@@ -133,9 +141,9 @@ __device__ __forceinline__ float quad_bcast_dyn(int i, float x) {
 template <int K>
 struct alignas(16) BwdSmem {
   static constexpr int KP = K + 4;  // row stride: the 16 rows of an MFMA operand read spread over the banks
-  // Everything the token loop reads or writes comes first, within the 64 KiB
-  // that a DS instruction's immediate offset reaches, so that one address
-  // register per array serves all tokens.
+  // Everything the chunked segment pass reads or writes comes first, within
+  // the 64 KiB that a DS instruction's immediate offset reaches, so that one
+  // address register per array serves every access.
   float beta[kSeg];
   float db[kSeg];
   float rd[kSeg];  // sum over the tile's columns of r_t dL/do_t
@@ -150,20 +158,20 @@ struct alignas(16) BwdSmem {
   float al[kSeg][KP];  // retain factors (1 for tokens past the end)
   float k[kSeg][KP];   // k (0 past the end)
   float q[kSeg][KP];   // s q (0 past the end)
-  float E[kSeg][KP];   // prod_{m <= t} alpha_m from the segment start; after the solve, dg
-  // the segment's results, written out together once it is done
-  float dq[kSeg][K];
-  float dk[kSeg][K];
-  // the segment's matrix products and their operands
+  float E[kSeg][KP];   // prod_{m <= t} alpha_m from the segment start; then dg (per-token pass, per-head gate)
+  float s0[K][kBV];    // the tile of the checkpoint S_0
+  float dsin[K][kBV];  // the tile of dL/dS entering the segment's reverse pass
+  // the segment's matrix products
   float ps[kSeg][kBV];   // (k E) S_0
   float kd[kSeg][kBV];   // (k Suf) dS_in
   float g1[kSeg][kSeg];  // (k / E)(k E)^T
   float g2[kSeg][kSeg];  // (k / E)(s q E)^T
-  float dsin[K][kBV];    // the tile of dL/dS entering the segment's reverse pass
-  float s0[K][kBV];      // the tile of the checkpoint S_0
-  // the per-token key sums of the fallback
+  // the per-token pass (segments outside the chunked form's range): its key
+  // sums and its results, written out together once the segment is done
   float red[2][K / 16][2][kBV];
   float fin[K / 16][8][4];
+  float dq[kSeg][K];
+  float dk[kSeg][K];
 };
 
 // One segment's inputs in flight: this thread's share of g_raw, k and q (key
@@ -284,20 +292,26 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     *reinterpret_cast<float4*>(&sm.s0[kap][c4]) = L.ckpt;
     return bad;
   };
-  // Add the finished segment's results to the outputs.
-  auto flush = [&](int seg) {
+  // Add the finished segment's results to the outputs: from LDS after the
+  // per-token pass, from the registers cq, ck, cg (lane l: tokens
+  // 4 (l / 16) + r, key 16 w + l % 16) after the chunked pass.
+  float cq[4], ckk[4], cgg[4];
+  auto flush = [&](int seg, bool chunked) {
+    const int tid = opaque(threadIdx.x), lane = tid & 63, town = tid / K, cown = tid % K;
     const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
     const long row0 = b * T_ + t0;
     float* dqb = p.dq + (row0 * H + h) * K;
     float* dkb = p.dk + (row0 * H + h) * K;
     float* dgb = p.dg + (row0 * HV + hv) * K;  // per-channel gate
     float vals[4][3];
+    if (!chunked) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = town + 4 * i;
-      vals[i][0] = sm.dq[tt][cown];
-      vals[i][1] = sm.dk[tt][cown];
-      vals[i][2] = sm.E[tt][cown];  // dg
+      for (int i = 0; i < 4; ++i) {
+        const int tt = town + 4 * i;
+        vals[i][0] = sm.dq[tt][cown];
+        vals[i][1] = sm.dk[tt][cown];
+        vals[i][2] = sm.E[tt][cown];  // dg
+      }
     }
     float4 dv4 = *reinterpret_cast<const float4*>(&sm.dv[(tid >> 2) & 15][4 * (tid & 3)]);
     const float dbv = sm.db[tid & 15];
@@ -314,13 +328,26 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       dgh = quad_sum(s0 + s1);
     }
     __syncthreads();  // the next segment's staging overwrites E
+    if (chunked) {
+      const int g4 = lane >> 4, key = 16 * (tid >> 6) + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = town + 4 * i;
-      if (tt < n) {
-        atomicAdd(dqb + tt * H * K + cown, vals[i][0]);
-        atomicAdd(dkb + tt * H * K + cown, vals[i][1]);
-        if (!PH) atomicAdd(dgb + tt * HV * K + cown, vals[i][2]);
+      for (int r = 0; r < 4; ++r) {
+        const int tt = 4 * g4 + r;
+        if (tt < n) {
+          atomicAdd(dqb + tt * H * K + key, cq[r]);
+          atomicAdd(dkb + tt * H * K + key, ckk[r]);
+          if (!PH) atomicAdd(dgb + tt * HV * K + key, cgg[r]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = town + 4 * i;
+        if (tt < n) {
+          atomicAdd(dqb + tt * H * K + cown, vals[i][0]);
+          atomicAdd(dkb + tt * H * K + cown, vals[i][1]);
+          if (!PH) atomicAdd(dgb + tt * HV * K + cown, vals[i][2]);
+        }
       }
     }
     if (PH && tid < 64 && (tid & 3) == 0 && (tid >> 2) < n)
@@ -338,6 +365,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // Wavefront 0 % NW forms (k E) S_0, wavefront 1 % NW both (k / E)(k E)^T and
   // (k / E)(s q E)^T, wavefront 2 % NW (k Suf) dS_in with Suf = gamma / E.
   auto products = [&]() {
+    const int tid = opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
     const int row = lane & 15, kq = lane >> 4;
     // four accumulators per product, so that the dependent MFMA chains are
     // a quarter as long
@@ -396,6 +424,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   //   y_t = kd_t + sum_{j>=t} M_tj dL/do_j
   // then a by back substitution, a_t = y_t - sum_{j>t} L_jt beta_j a_j.
   auto solve = [&]() {
+    const int tid = opaque(threadIdx.x);
     for (int e = tid; e < kSeg * kBV; e += NT) {
       const int t = e / kBV, j = e % kBV;
       float pt = sm.ps[t][j], yt = sm.kd[t][j];
@@ -487,18 +516,129 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     rb ^= 1;
   };
 
+  // The segment's gradients as products over the segment, with no per-token
+  // loop.  With W1 = lower[dL/do U^T] (m <= t), W2 = strictly-lower[dR U^T]
+  // (m < t), dR = diag(beta) A, Qt = s q E, Kt = k E, Kh = k / E, Ks = k Suf
+  // (the gradients with respect to each are marked d):
+  //   dQt = dL/do S_0^T + W1 Kh          dKt = -dR S_0^T - W2 Kh
+  //   dKh = W1^T Qt - W2^T Kt            dKs = U dS_in^T
+  //   dS_0 = diag(gamma) dS_in + Qt^T dL/do - Kt^T dR   (entering the earlier segment)
+  //   dq = s E dQt,  dk = E dKt + dKh / E + Suf dKs
+  //   dg_t = sum_{t' >= t} (dQt Qt + dKt Kt - dKh Kh - dKs Ks)_{t'}, plus, from
+  //          gamma = E_15, gamma sum_j dS_in S_0 + sum_t dKs Ks for every t.
+  // Wavefront w owns keys 16 w .. 16 w + 15.  Lane l: c16 = l % 16, g4 = l / 16;
+  // the MFMA accumulators hold rows 4 g4 + r of column c16.  W1 and W2 are formed
+  // in both orientations so that either serves as an A operand whose inner
+  // index in step r is 4 g4 + r (the lane's own accumulator entry r).
+  auto chunk_phase = [&]() {
+    const int tid = opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
+    const int c16 = lane & 15, g4 = lane >> 4, kb = 16 * w, key = kb + c16;
+    auto mfma = [](float a, float b, f32x4 c) {
+      return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    };
+    f32x4 w1t = {}, w1d = {}, w2t = {}, w2d = {};  // w?t: [t = c16][m = 4 g4 + r]; w?d: [t = 4 g4 + r][m = c16]
+    f32x4 dQ = {}, dKt = {}, dKs = {}, dKh = {}, dSn = {};
+    const float bc = sm.beta[c16];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int c = 4 * s4 + g4;
+      const float u_ = sm.u[c16][c], d_ = sm.dout[c16][c], r_ = bc * sm.a[c16][c];
+      const float s0v = sm.s0[key][c], dsv = sm.dsin[key][c];
+      w1t = mfma(u_, d_, w1t);
+      w1d = mfma(d_, u_, w1d);
+      w2t = mfma(u_, r_, w2t);
+      w2d = mfma(r_, u_, w2d);
+      dQ = mfma(d_, s0v, dQ);
+      dKt = mfma(-r_, s0v, dKt);
+      dKs = mfma(u_, dsv, dKs);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g4 + r;  // this step's inner index (a token)
+      const float e = sm.E[m][key], kv = sm.k[m][key];
+      const float kh = kv * __builtin_amdgcn_rcpf(e), kt = kv * e, qt = sm.q[m][key] * e;
+      dQ = mfma(m <= c16 ? w1t[r] : 0.0f, kh, dQ);
+      dKt = mfma(m < c16 ? -w2t[r] : 0.0f, kh, dKt);
+      dKh = mfma(c16 <= m ? w1d[r] : 0.0f, qt, dKh);
+      dKh = mfma(c16 < m ? -w2d[r] : 0.0f, kt, dKh);
+    }
+    // dS_0 for this wavefront's keys: rows key 16 w + 4 g4 + r, column c16
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int t = 4 * s4 + g4;
+      const float e = sm.E[t][key];
+      dSn = mfma(sm.q[t][key] * e, sm.dout[t][c16], dSn);
+      dSn = mfma(-sm.k[t][key] * e, sm.beta[t] * sm.a[t][c16], dSn);
+    }
+    // gamma's direct term for this lane's key: sum over the columns of
+    // dS_in S_0 (four columns per lane, then the four row groups)
+    const float gam = sm.E[kSeg - 1][key];
+    float gd = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gd += sm.dsin[key][4 * g4 + i] * sm.s0[key][4 * g4 + i];
+    float dGl[4], dql[4], dkl[4], ksks = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * g4 + r;
+      const float e = sm.E[t][key], kv = sm.k[t][key], sq = sm.q[t][key];
+      const float ie = __builtin_amdgcn_rcpf(e);
+      const float qt = sq * e, kt = kv * e, kh = kv * ie, ks = kv * gam * ie;
+      dql[r] = scale * e * dQ[r];
+      dkl[r] = e * dKt[r] + ie * dKh[r] + gam * ie * dKs[r];
+      dGl[r] = dQ[r] * qt + dKt[r] * kt - dKh[r] * kh - dKs[r] * ks;
+      ksks += dKs[r] * ks;
+    }
+    gd = xor_sum<32>(xor_sum<16>(gd));
+    ksks = xor_sum<32>(xor_sum<16>(ksks));
+    // the new dS entering the earlier segment (after every read of dS_in above)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int kr = kb + 4 * g4 + r;
+      sm.dsin[kr][c16] = dSn[r] + sm.E[kSeg - 1][kr] * sm.dsin[kr][c16];
+    }
+    // dg: the reverse cumulative sum over the tokens; gamma's terms belong to
+    // the last token (t = 15: row group 3, entry 3)
+    if (g4 == 3) dGl[3] += gam * gd + ksks;
+    float suf = dGl[3];
+    dGl[2] += suf;
+    suf = dGl[2];
+    dGl[1] += suf;
+    suf = dGl[1];
+    dGl[0] += suf;
+    const float tot = dGl[0];  // this row group's sum
+    // the sums of the later row groups (lanes 16, 32, 48 further)
+    const float n1 = __shfl_down(tot, 16), n2 = __shfl_down(tot, 32), n3 = __shfl_down(tot, 48);
+    const float later = (g4 < 1 ? n3 : 0.0f) + (g4 < 2 ? n2 : 0.0f) + (g4 < 3 ? n1 : 0.0f);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      cq[r] = dql[r];
+      ckk[r] = dkl[r];
+      cgg[r] = dGl[r] + later;
+      // a per-head gate sums dg over the keys in the flush: through E (this
+      // wavefront's keys only, every read of E above)
+      if (PH) sm.E[4 * g4 + r][key] = cgg[r];
+    }
+    if (w == 0) {  // dv = beta a and dbeta for the tile
+      const int t = lane >> 2, c = 4 * (lane & 3);
+      const float4 a4 = *reinterpret_cast<const float4*>(&sm.a[t][c]);
+      const float bt = sm.beta[t];
+      *reinterpret_cast<float4*>(&sm.dv[t][c]) = float4{bt * a4.x, bt * a4.y, bt * a4.z, bt * a4.w};
+      if (lane < kSeg) sm.db[lane] = sm.ar[lane];
+    }
+  };
+
   float dS[4];
   {
     const long o = ((long)hd * K + kap) * V + v0 + c4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dS[i] = p.dST ? p.dST[o + i] : 0.0f;
   }
+  *reinterpret_cast<float4*>(&sm.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
   SegLoads<T, NVD> L;
   if (NC > 0) issue(NC - 1, L);
   for (int seg = NC - 1; seg >= 0; --seg) {
     const int n = min(kSeg, T_ - seg * kSeg);
     const bool bad = stage(L, n);
-    *reinterpret_cast<float4*>(&sm.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
     const float4 ck = L.ckpt;
     const bool fallback = __syncthreads_or(bad);
     if (!fallback) {
@@ -607,20 +747,25 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
           if (base + j < n) reverse(from_solve, base + j, sd[j]);
       }
     };
-    if (fallback)
+    if (fallback) {  // dL/dS in registers for the per-token pass, in the LDS tile between segments
+      const float4 d0 = *reinterpret_cast<const float4*>(&sm.dsin[kap][c4]);
+      dS[0] = d0.x; dS[1] = d0.y; dS[2] = d0.z; dS[3] = d0.w;
       halves(std::false_type{});
-    else
-      halves(std::true_type{});
+      *reinterpret_cast<float4*>(&sm.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
+    } else {
+      chunk_phase();
+    }
     __syncthreads();  // the segment's results are in LDS; its inputs are no longer read
     // the next segment's loads go out before the atomics, so that waiting for
     // them does not wait for the atomics; unconditional (the last re-reads
     // segment 0) so that no earlier load stays live through the segment
     issue(max(seg - 1, 0), L);
-    flush(seg);
+    flush(seg, !fallback);
   }
+  __syncthreads();
   if (p.dS0)
     *reinterpret_cast<float4*>(p.dS0 + ((long)hd * K + kap) * V + v0 + c4) =
-        float4{dS[0], dS[1], dS[2], dS[3]};
+        *reinterpret_cast<const float4*>(&sm.dsin[kap][c4]);
 }
 
 // dg -> dg_raw in place (chain rule through the gate), and the sums of the
