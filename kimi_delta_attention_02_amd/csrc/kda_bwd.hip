@@ -65,6 +65,7 @@ struct BwdParams {
   const float* dST;   // dL/dS_T or null
   const float* ckpt;  // [B, HV, NC, K, V]: the state entering each 16-token segment
   const float* u;     // U = beta r of every token, as the split schedule's state pass left it
+  float* ops;         // [B, HV, NC, 3, 64, 4]: per segment, the value-independent operands (bwd_prep_kernel)
   float* dq;
   float* dk;
   float* dv;
@@ -84,6 +85,148 @@ constexpr int kBV = 16;   // value columns per workgroup
 __global__ void bwd_zero_kernel(float* p, long n) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.0f;
+}
+
+// Per (sequence, value head, segment), the matrices of the segment pass that
+// do not depend on the value tile, formed once instead of in each tile's
+// workgroup.  With E the cumulative retain factors from the segment start,
+// g1 = (k / E)(k E)^T, g2 = (k / E)(s q E)^T (sums over the keys) and
+// R = (I + L^T diag(beta))^{-1}, L[t][m] = g1[m][t] for m < t, lane
+// (c, g) = (l % 16, l / 16) of the segment's three 64 x 4 blocks holds, in
+// entry r:
+//   0: g1[4 g + r][c] if 4 g + r < c, else 0    (L as an MFMA A operand)
+//   1: g2[c][4 g + r] if 4 g + r >= c, else 0   (the upper part of g2, likewise)
+//   2: R[c][4 g + r]                            (R^T as an MFMA B operand)
+// for fp32 MFMA 16x16x4 steps whose inner index in step r is 4 g + r.  One
+// wavefront per segment.  Its g_raw, k and q rows go to LDS with coalesced
+// 16-byte loads; then lane (t, g) forms, key by key, the gate of token t,
+// E by a product scan over its 16-lane row (the tokens) and the products'
+// operands, for keys 16 j + 4 g + s (any order of the keys serves, as long
+// as both operands follow it).  R comes row by row (lane c, forward
+// substitution of R (I + L^T diag(beta)) = I) with the coupling in LDS.
+// Segments whose E leaves the chunked form's range are formed all the same;
+// the segment kernel does not read them.
+template <int K, typename T, bool PH>
+struct PrepSmem {
+  using Raw = typename In<T>::Raw1;
+  static constexpr int GS = PH ? 4 : K + 8;  // (the per-head gate is read straight from memory)
+                                             // row stride 32 mod 64 bytes
+  static constexpr int KS = (K * (int)sizeof(Raw) + 32) / (int)sizeof(Raw);  // likewise
+  alignas(16) float g[kSeg][GS];
+  alignas(16) Raw k[kSeg][KS];
+  alignas(16) Raw q[kSeg][KS];
+  alignas(16) float4 cpl[kSeg][kSeg / 4];  // cpl[t][m] = beta_t g1[m][t] for m < t
+};
+
+template <int K, typename T, int GK, bool PH>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  using Raw = typename In<T>::Raw1;
+  using Raw4 = typename In<T>::Raw4;
+  using S = PrepSmem<K, T, PH>;
+  __shared__ S sms[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  S& sm = sms[wv];
+  const long sid = (long)blockIdx.x * 4 + wv;  // (sequence, value head) * NC + segment
+  if (sid >= (long)p.B * p.HV * p.NC) return;  // no barrier below: only this wavefront's LDS
+  const int HV = p.HV, H = p.H, T_ = p.T;
+  const int seg = (int)(sid % p.NC);
+  const long hd = sid / p.NC, b = hd / HV;
+  const int hv = (int)(hd % HV), h = hv / (HV / H);
+  const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
+  const long row0 = b * T_ + t0;
+  // staging: rows past the end re-read the last (masked below)
+  constexpr int GU = PH ? 0 : kSeg * K / 4;  // float4 units of g
+  constexpr int RPU = 16 / (int)sizeof(Raw);  // elements per 16-byte unit of k or q
+  constexpr int KU = kSeg * K / RPU;
+  for (int u = lane; u < GU; u += 64) {
+    const int t = u / (K / 4), c = (u % (K / 4)) * 4;
+    *reinterpret_cast<float4*>(&sm.g[t][c]) = *reinterpret_cast<const float4*>(
+        p.g_raw + ((row0 + min(t, n - 1)) * HV + hv) * (long)K + c);
+  }
+  for (int u = lane; u < KU; u += 64) {
+    const int t = u / (K / RPU), c = (u % (K / RPU)) * RPU;
+    const long o = ((row0 + min(t, n - 1)) * H + h) * (long)K + c;
+    *reinterpret_cast<uint4*>(&sm.k[t][c]) = *reinterpret_cast<const uint4*>(static_cast<const Raw*>(p.k) + o);
+    *reinterpret_cast<uint4*>(&sm.q[t][c]) = *reinterpret_cast<const uint4*>(static_cast<const Raw*>(p.q) + o);
+  }
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const bool in = c16 < n;
+  const float scale = 1.0f / __builtin_sqrtf((float)K);
+  const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
+  const GateConsts gc = gate_consts(rate, p.lower_bound);
+  const float ghead = PH ? p.g_raw[(row0 + (in ? c16 : n - 1)) * HV + hv] : 0.0f;
+  const float bhead = PH ? gate_bias_pre<GK>((p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv] : 0.0f, gc)
+                         : 0.0f;
+  // a row-shifted product: lanes whose source lies outside the 16-lane row keep 1
+  auto shr_mul = [](float x, auto ctrl) {
+    return x * __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, x),
+                                             decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  f32x4 g1[2] = {}, g2t[2] = {};  // two chains each
+#pragma unroll 2
+  for (int j = 0; j < K / 16; ++j) {
+    const int kb = 16 * j + 4 * g4;  // this lane's four keys
+    float gv[4], kv[4], qv[4], bv[4];
+    if constexpr (!PH) {
+      const float4 g4v = *reinterpret_cast<const float4*>(&sm.g[c16][kb]);
+      gv[0] = g4v.x; gv[1] = g4v.y; gv[2] = g4v.z; gv[3] = g4v.w;
+      float4 b4 = float4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (p.dt_bias && GK != KDA_GATE_NONE) b4 = *reinterpret_cast<const float4*>(p.dt_bias + hv * K + kb);
+      bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
+    }
+    In<T>::unpack4(*reinterpret_cast<const Raw4*>(&sm.k[c16][kb]), kv);
+    In<T>::unpack4(*reinterpret_cast<const Raw4*>(&sm.q[c16][kb]), qv);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      float e = !in ? 1.0f
+                    : PH ? gate_alpha_pre<GK>(ghead, bhead, gc)
+                         : gate_alpha_pre<GK>(gv[s4], gate_bias_pre<GK>(bv[s4], gc), gc);
+      e = shr_mul(e, std::integral_constant<int, 0x111>{});
+      e = shr_mul(e, std::integral_constant<int, 0x112>{});
+      e = shr_mul(e, std::integral_constant<int, 0x114>{});
+      e = shr_mul(e, std::integral_constant<int, 0x118>{});
+      const float k_ = in ? kv[s4] : 0.0f, q_ = in ? scale * qv[s4] : 0.0f;
+      const float kh = k_ * __builtin_amdgcn_rcpf(e), kt = k_ * e, qt = q_ * e;
+      g1[s4 & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, kt, g1[s4 & 1], 0, 0, 0);
+      g2t[s4 & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt, kh, g2t[s4 & 1], 0, 0, 0);
+    }
+  }
+  // lane (c16, g4) entry r: g1[4 g4 + r][c16] and g2t = g2^T, i.e. g2[c16][4 g4 + r]
+  const float bt = in ? p.beta[(row0 + c16) * HV + hv] : 0.0f;  // beta of token c16
+  float lop[4], mop[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * g4 + r;
+    const float a = g1[0][r] + g1[1][r], c = g2t[0][r] + g2t[1][r];
+    lop[r] = m < c16 ? a : 0.0f;
+    mop[r] = m >= c16 ? c : 0.0f;
+  }
+  sm.cpl[c16][g4] = float4{bt * lop[0], bt * lop[1], bt * lop[2], bt * lop[3]};
+  // row c16 of R: R[c][t] = [t == c] - sum_{m < t} R[c][m] T[m][t], T[m][t] =
+  // cpl[t][m] (this wavefront's LDS accesses complete in order)
+  float x[kSeg];
+#pragma unroll
+  for (int t = 0; t < kSeg; ++t) {
+    float acc = t == c16 ? 1.0f : 0.0f;
+#pragma unroll
+    for (int m4 = 0; m4 < t; m4 += 4) {
+      const float4 tv = sm.cpl[t][m4 / 4];
+      acc -= x[m4] * tv.x;
+      if (m4 + 1 < t) acc -= x[m4 + 1] * tv.y;
+      if (m4 + 2 < t) acc -= x[m4 + 2] * tv.z;
+      if (m4 + 3 < t) acc -= x[m4 + 3] * tv.w;
+    }
+    x[t] = acc;
+  }
+  float rop[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    rop[r] = g4 == 0 ? x[r] : g4 == 1 ? x[4 + r] : g4 == 2 ? x[8 + r] : x[12 + r];
+  float4* o = reinterpret_cast<float4*>(p.ops + sid * (3 * 64 * 4)) + lane;
+  o[0] = float4{lop[0], lop[1], lop[2], lop[3]};
+  o[64] = float4{mop[0], mop[1], mop[2], mop[3]};
+  o[128] = float4{rop[0], rop[1], rop[2], rop[3]};
 }
 
 // x + the value N lanes further round its 16-lane row (DPP row rotation).
@@ -145,27 +288,29 @@ struct alignas(16) BwdSmem {
   // the 64 KiB that a DS instruction's immediate offset reaches, so that one
   // address register per array serves every access.
   float beta[kSeg];
-  float db[kSeg];
-  float rd[kSeg];  // sum over the tile's columns of r_t dL/do_t
-  float ar[kSeg];  // sum over the tile's columns of a_t r_t (the tile's part of dbeta_t)
+  float4 ops[3][64];  // the segment's value-independent operands (bwd_prep_kernel)
   float u[kSeg][kBV];  // U = beta r from the forward's state pass (0 past the end)
   float v[kSeg][kBV];
   float dout[kSeg][kBV];
   float a[kSeg][kBV];   // a_t = G_t^T k_t
   float r[kSeg][kBV];   // r_t = v_t - Sd_t^T k_t
-  float dv[kSeg][kBV];
+  float w1[kSeg][kSeg];  // W1[t][m] = (dL/do U^T)[t][m] for m <= t, else 0
+  float w2[kSeg][kSeg];  // W2[t][m] = (dR U^T)[t][m] for m < t, else 0
   // the segment's inputs per (token, key channel)
-  float al[kSeg][KP];  // retain factors (1 for tokens past the end)
   float k[kSeg][KP];   // k (0 past the end)
   float q[kSeg][KP];   // s q (0 past the end)
   float E[kSeg][KP];   // prod_{m <= t} alpha_m from the segment start; then dg (per-token pass, per-head gate)
   float s0[K][kBV];    // the tile of the checkpoint S_0
   float dsin[K][kBV];  // the tile of dL/dS entering the segment's reverse pass
-  // the segment's matrix products
-  float ps[kSeg][kBV];   // (k E) S_0
-  float kd[kSeg][kBV];   // (k Suf) dS_in
-  float g1[kSeg][kSeg];  // (k / E)(k E)^T
-  float g2[kSeg][kSeg];  // (k / E)(s q E)^T
+  union {
+    // chunked pass: partial products over the four quarters of the keys,
+    // (k E) S_0 in 0..3 and (k Suf) dS_in in 4..7; written after the
+    // staging, read before the next one
+    float part[8][kSeg][kBV];
+    // per-token pass: the retain factors, staged every segment (1 for tokens
+    // past the end)
+    float al[kSeg][KP];
+  };
   // the per-token pass (segments outside the chunked form's range): its key
   // sums and its results, written out together once the segment is done
   float red[2][K / 16][2][kBV];
@@ -177,12 +322,12 @@ struct alignas(16) BwdSmem {
 // One segment's inputs in flight: this thread's share of g_raw, k and q (key
 // channel kappa, tokens 4 c .. 4 c + 3), of v, dL/do, U and beta, and its own
 // row of the checkpoint.
-template <typename T, int NVD>
+template <typename T, int NVD, int NOPS>
 struct SegLoads {
   float g[4];
   typename In<T>::Raw1 k[4], q[4], v[NVD];
   float dout[NVD], beta;
-  float4 u, ckpt;
+  float4 u, ckpt, ops[NOPS];
 };
 
 template <int K, typename T, int GK, bool PH>
@@ -190,6 +335,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     BwdParams p) {
   constexpr int V = K, NT = 4 * K, NW = NT / 64, NVT = V / kBV;
   constexpr int NVD = (kSeg * kBV + NT - 1) / NT;  // v and dL/do elements each thread stages
+  constexpr int NOPS = (3 * 64 + NT - 1) / NT;     // float4s of the prep's operands each thread stages
   static_assert(kSeg * K / NT == 4 && NT >= 64, "thread layout");
   __shared__ BwdSmem<K> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -214,7 +360,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // Issue the loads of segment seg (rows past the end re-read the last
   // token, n >= 1).  Addresses are a base uniform over the workgroup plus a
   // 32-bit per-thread offset.
-  auto issue = [&](int seg, SegLoads<T, NVD>& L) {
+  auto issue = [&](int seg, SegLoads<T, NVD, NOPS>& L) {
     const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
     const long row0 = b * T_ + t0;
     const float* gb = p.g_raw + (row0 * HV + hv) * gK;
@@ -241,11 +387,14 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     L.beta = p.beta[row0 * HV + hv + min(tid & 15, n - 1) * HV];
     L.ckpt = *reinterpret_cast<const float4*>(p.ckpt + ((long)hd * NC + seg) * K * V + v0 +
                                               kap * V + c4);
+    const float4* ob = reinterpret_cast<const float4*>(p.ops + ((long)hd * NC + seg) * (3 * 64 * 4));
+#pragma unroll
+    for (int i = 0; i < NOPS; ++i) L.ops[i] = ob[min(tid + i * NT, 3 * 64 - 1)];
   };
   // Place them in LDS, tokens past the end as an identity (alpha = 1, k, q,
   // v, dL/do, U and beta zero), with the cumulative retain factors E.
   // Returns whether an E of this thread leaves [2^-100, 2^100] (or is NaN).
-  auto stage = [&](const SegLoads<T, NVD>& L, int n) {
+  auto stage = [&](const SegLoads<T, NVD, NOPS>& L, int n) {
     float al4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -290,6 +439,9 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     }
     if (tid < kSeg) sm.beta[tid] = tid < n ? L.beta : 0.0f;
     *reinterpret_cast<float4*>(&sm.s0[kap][c4]) = L.ckpt;
+#pragma unroll
+    for (int i = 0; i < NOPS; ++i)
+      if (tid + i * NT < 3 * 64) (&sm.ops[0][0])[tid + i * NT] = L.ops[i];
     return bad;
   };
   // Add the finished segment's results to the outputs: from LDS after the
@@ -313,8 +465,6 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
         vals[i][2] = sm.E[tt][cown];  // dg
       }
     }
-    float4 dv4 = *reinterpret_cast<const float4*>(&sm.dv[(tid >> 2) & 15][4 * (tid & 3)]);
-    const float dbv = sm.db[tid & 15];
     // per-head gate: token tid / 4's dg summed over the key channels (the
     // gate is one value broadcast over them)
     float dgh = 0.0f;
@@ -327,7 +477,9 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       }
       dgh = quad_sum(s0 + s1);
     }
-    __syncthreads();  // the next segment's staging overwrites E
+    // the next segment's staging overwrites E, which holds dg after the
+    // per-token pass and (per-head gate) the per-channel dg of either pass
+    if (PH || !chunked) __syncthreads();
     if (chunked) {
       const int g4 = lane >> 4, key = 16 * (tid >> 6) + (lane & 15);
 #pragma unroll
@@ -352,123 +504,113 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     }
     if (PH && tid < 64 && (tid & 3) == 0 && (tid >> 2) < n)
       atomicAdd(p.dg + row0 * HV + hv + (tid >> 2) * HV, dgh);
-    if (tid < 64 && (tid >> 2) < n)
-      *reinterpret_cast<float4*>(p.dv + (row0 * HV + hv) * V + v0 + (tid >> 2) * HV * V +
-                                 4 * (tid & 3)) = dv4;
-    if (tid < n) atomicAdd(p.dbeta + row0 * HV + hv + tid * HV, dbv);
   };
 
-  // The segment's per-token key sums as matrix products (16 x 16 outputs,
-  // fp32 MFMA 16x16x4, the key axis in steps of 4): lane l supplies the
-  // operands of row l % 16 (a token, or a value column of B) and key step
-  // position l / 16, and holds output rows 4 (l / 16) .. + 3 of column l % 16.
-  // Wavefront 0 % NW forms (k E) S_0, wavefront 1 % NW both (k / E)(k E)^T and
-  // (k / E)(s q E)^T, wavefront 2 % NW (k Suf) dS_in with Suf = gamma / E.
+  // The segment's per-token key sums that involve the value tile, as matrix
+  // products (16 x 16 outputs, fp32 MFMA 16x16x4, the key axis in steps of
+  // 4): lane l supplies the operands of row l % 16 (a token, or a value
+  // column of B) and key step position l / 16, and holds output rows
+  // 4 (l / 16) .. + 3 of column l % 16.  Eight tasks, product task / 4 over
+  // key quarter task % 4, spread over the wavefronts: (k E) S_0, then
+  // (k Suf) dS_in with Suf = gamma / E.
+  auto product = [&](auto PP, int task) {
+    constexpr int P = decltype(PP)::value;
+    const int lane = opaque(threadIdx.x) & 63, row = lane & 15, kq = lane >> 4;
+    const int k0 = (task & 3) * (K / 4);
+    // up to four accumulators, so that the dependent MFMA chains are short
+    f32x4 acc[4] = {};
+#pragma unroll
+    for (int st = 0; st < K / 16; ++st) {
+      const int key = k0 + 4 * st + kq;
+      const float kv = sm.k[row][key], e = sm.E[row][key];
+      float x, y;
+      if constexpr (P == 0) {
+        x = kv * e;
+        y = sm.s0[key][row];
+      } else {
+        x = kv * sm.E[kSeg - 1][key] * __builtin_amdgcn_rcpf(e);
+        y = sm.dsin[key][row];
+      }
+      acc[st & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc[st & 3], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      sm.part[task][4 * kq + r][row] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+  };
   auto products = [&]() {
-    const int tid = opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
-    const int row = lane & 15, kq = lane >> 4;
-    // four accumulators per product, so that the dependent MFMA chains are
-    // a quarter as long
-    if (w == 0 % NW) {
-      f32x4 acc[4] = {};
-#pragma unroll 2
-      for (int kb = 0; kb < K; kb += 16) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int key = kb + 4 * c + kq;
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.k[row][key] * sm.E[row][key],
-                                                        sm.s0[key][row], acc[c], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.ps[4 * kq + r][row] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
-    }
-    if (w == 1 % NW) {
-      f32x4 a1[2] = {}, a2[2] = {};
-#pragma unroll 4
-      for (int kb = 0; kb < K; kb += 8) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int key = kb + 4 * c + kq;
-          const float e = sm.E[row][key], kv = sm.k[row][key];
-          const float kh = kv * __builtin_amdgcn_rcpf(e);
-          a1[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, kv * e, a1[c], 0, 0, 0);
-          a2[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, sm.q[row][key] * e, a2[c], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sm.g1[4 * kq + r][row] = a1[0][r] + a1[1][r];
-        sm.g2[4 * kq + r][row] = a2[0][r] + a2[1][r];
-      }
-    }
-    if (w == 2 % NW) {
-      f32x4 acc[4] = {};
-#pragma unroll 2
-      for (int kb = 0; kb < K; kb += 16) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int key = kb + 4 * c + kq;
-          const float ks =
-              sm.k[row][key] * sm.E[kSeg - 1][key] * __builtin_amdgcn_rcpf(sm.E[row][key]);
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(ks, sm.dsin[key][row], acc[c], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.kd[4 * kq + r][row] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+    const int w = opaque(threadIdx.x) >> 6;
+#pragma unroll 1
+    for (int task = w; task < 8; task += NW) {
+      if (task < 4)
+        product(std::integral_constant<int, 0>{}, task);
+      else
+        product(std::integral_constant<int, 1>{}, task);
     }
   };
-  // From the products, per (token t, column j) of the tile (L_tj = g1[j][t]
-  // for j < t, M_tj = g2[t][j] for j >= t):
-  //   p_t = ps_t + sum_{j<t} L_tj U_j,   r_t = v_t - p_t
-  //   y_t = kd_t + sum_{j>=t} M_tj dL/do_j
-  // then a by back substitution, a_t = y_t - sum_{j>t} L_jt beta_j a_j.
+  // From the products and the prep's operands (L_tm = g1[m][t] for m < t,
+  // M_tm = g2[t][m] for m >= t, R = (I + L^T diag(beta))^{-1}):
+  //   wavefront 0:        P = (k E) S_0 + L U,  r = v - P
+  //   wavefront 1 % NW:   Y = (k Suf) dS_in + M dL/do,  a = R Y (formed as
+  //                       a^T = Y^T R^T), then W2 = strictly-lower[diag(beta) a U^T]
+  //   wavefront 2 % NW:   W1 = lower[dL/do U^T]
+  // The products over the tokens (or the tile's columns) are 16 x 16 x 16 on
+  // fp32 MFMA as above, the inner index in step r being 4 (l / 16) + r, so
+  // that an accumulator serves as the next product's operand in place.
   auto solve = [&]() {
-    const int tid = opaque(threadIdx.x);
-    for (int e = tid; e < kSeg * kBV; e += NT) {
-      const int t = e / kBV, j = e % kBV;
-      float pt = sm.ps[t][j], yt = sm.kd[t][j];
-      for (int m = 0; m < t; ++m) pt += sm.g1[m][t] * sm.u[m][j];
-      for (int m = t; m < kSeg; ++m) yt += sm.g2[t][m] * sm.dout[m][j];
-      sm.r[t][j] = sm.v[t][j] - pt;
-      sm.a[t][j] = yt;
+    const int tid = opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
+    const int c16 = lane & 15, g4 = lane >> 4;
+    auto mfma = [](float a, float b, f32x4 c) {
+      return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    };
+    auto part_sum = [&](int p0, int r) {
+      const int t = 4 * g4 + r;
+      return (sm.part[p0][t][c16] + sm.part[p0 + 1][t][c16]) +
+             (sm.part[p0 + 2][t][c16] + sm.part[p0 + 3][t][c16]);
+    };
+    if (w == 0) {
+      const float4 l4 = sm.ops[0][lane];
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = part_sum(0, r);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = mfma(lv[r], sm.u[4 * g4 + r][c16], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.r[4 * g4 + r][c16] = sm.v[4 * g4 + r][c16] - acc[r];
     }
-    __syncthreads();
-    // back substitution on wavefront 0: the four lanes of a quad share a
-    // column, lane s of it holding y_t for t = s, s + 4, s + 8, s + 12; a_m
-    // goes from its lane to the quad by a DPP broadcast
-    if (tid < 64) {
-      const int col = tid >> 2, s4 = tid & 3;
-      float y[4];
+    if (w == 1 % NW) {
+      const float4 m4 = sm.ops[1][lane], r4 = sm.ops[2][lane];
+      const float mv[4] = {m4.x, m4.y, m4.z, m4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+      f32x4 y;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = sm.a[s4 + 4 * i][col];
+      for (int r = 0; r < 4; ++r) y[r] = part_sum(4, r);
 #pragma unroll
-      for (int m = kSeg - 1; m >= 0; --m) {
-        const float am = quad_bcast_dyn(m & 3, y[m >> 2]);
-        if (s4 == (m & 3)) sm.a[m][col] = am;
-        const float bam = sm.beta[m] * am;
+      for (int r = 0; r < 4; ++r) y = mfma(mv[r], sm.dout[4 * g4 + r][c16], y);
+      // a^T[j][t] = sum_m Y[m][j] R[t][m]: Y's accumulator is Y^T's A operand
+      f32x4 at = {};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = s4 + 4 * i;
-          y[i] -= (t < m ? sm.g1[t][m] : 0.0f) * bam;
-        }
+      for (int r = 0; r < 4; ++r) at = mfma(y[r], rv[r], at);
+      // lane (c16, g4) holds a[c16][4 g4 + r]
+      *reinterpret_cast<float4*>(&sm.a[c16][4 * g4]) = float4{at[0], at[1], at[2], at[3]};
+      // W2[t][m] = sum_j beta_t a[t][j] U[m][j]
+      const float bc = sm.beta[c16];
+      const float4 u4 = *reinterpret_cast<const float4*>(&sm.u[c16][4 * g4]);
+      const float uv[4] = {u4.x, u4.y, u4.z, u4.w};
+      f32x4 acc2 = {};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc2 = mfma(bc * at[r], uv[r], acc2);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.w2[4 * g4 + r][c16] = c16 < 4 * g4 + r ? acc2[r] : 0.0f;
+    }
+    if (w == 2 % NW) {  // W1 = lower[dL/do U^T]
+      f32x4 acc = {};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int j = 4 * s4 + g4;
+        acc = mfma(sm.dout[c16][j], sm.u[c16][j], acc);
       }
-      // per token, the sums over the tile's columns of r_t dL/do_t and a_t r_t
-      // (this wavefront wrote a: its LDS accesses complete in order): lane l
-      // takes token l % 16 and columns 4 (l / 16) .. + 3, then the row swaps
-      // add the four column quarters
-      const int t = tid & 15, cq = 4 * (tid >> 4);
-      const float4 r4 = *reinterpret_cast<const float4*>(&sm.r[t][cq]);
-      const float4 a4 = *reinterpret_cast<const float4*>(&sm.a[t][cq]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&sm.dout[t][cq]);
-      float rdv = r4.x * d4.x + r4.y * d4.y + r4.z * d4.z + r4.w * d4.w;
-      float arv = a4.x * r4.x + a4.y * r4.y + a4.z * r4.z + a4.w * r4.w;
-      rdv = xor_sum<32>(xor_sum<16>(rdv));
-      arv = xor_sum<32>(xor_sum<16>(arv));
-      if (tid < kSeg) {
-        sm.rd[t] = rdv;
-        sm.ar[t] = arv;
-      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.w1[4 * g4 + r][c16] = c16 <= 4 * g4 + r ? acc[r] : 0.0f;
     }
   };
 
@@ -530,13 +672,23 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // the MFMA accumulators hold rows 4 g4 + r of column c16.  W1 and W2 are formed
   // in both orientations so that either serves as an A operand whose inner
   // index in step r is 4 g4 + r (the lane's own accumulator entry r).
-  auto chunk_phase = [&]() {
+  auto chunk_phase = [&](int seg) {
     const int tid = opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
     const int c16 = lane & 15, g4 = lane >> 4, kb = 16 * w, key = kb + c16;
     auto mfma = [](float a, float b, f32x4 c) {
       return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     };
-    f32x4 w1t = {}, w1d = {}, w2t = {}, w2d = {};  // w?t: [t = c16][m = 4 g4 + r]; w?d: [t = 4 g4 + r][m = c16]
+    // W1 and W2 (masked) in both orientations: w?t[r] = W?[c16][4 g4 + r],
+    // w?d[r] = W?[4 g4 + r][c16]
+    const float4 w1t = *reinterpret_cast<const float4*>(&sm.w1[c16][4 * g4]);
+    const float4 w2t = *reinterpret_cast<const float4*>(&sm.w2[c16][4 * g4]);
+    float w1d[4], w2d[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      w1d[r] = sm.w1[4 * g4 + r][c16];
+      w2d[r] = sm.w2[4 * g4 + r][c16];
+    }
+    const float w1tv[4] = {w1t.x, w1t.y, w1t.z, w1t.w}, w2tv[4] = {w2t.x, w2t.y, w2t.z, w2t.w};
     f32x4 dQ = {}, dKt = {}, dKs = {}, dKh = {}, dSn = {};
     const float bc = sm.beta[c16];
 #pragma unroll
@@ -544,10 +696,6 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       const int c = 4 * s4 + g4;
       const float u_ = sm.u[c16][c], d_ = sm.dout[c16][c], r_ = bc * sm.a[c16][c];
       const float s0v = sm.s0[key][c], dsv = sm.dsin[key][c];
-      w1t = mfma(u_, d_, w1t);
-      w1d = mfma(d_, u_, w1d);
-      w2t = mfma(u_, r_, w2t);
-      w2d = mfma(r_, u_, w2d);
       dQ = mfma(d_, s0v, dQ);
       dKt = mfma(-r_, s0v, dKt);
       dKs = mfma(u_, dsv, dKs);
@@ -557,10 +705,10 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       const int m = 4 * g4 + r;  // this step's inner index (a token)
       const float e = sm.E[m][key], kv = sm.k[m][key];
       const float kh = kv * __builtin_amdgcn_rcpf(e), kt = kv * e, qt = sm.q[m][key] * e;
-      dQ = mfma(m <= c16 ? w1t[r] : 0.0f, kh, dQ);
-      dKt = mfma(m < c16 ? -w2t[r] : 0.0f, kh, dKt);
-      dKh = mfma(c16 <= m ? w1d[r] : 0.0f, qt, dKh);
-      dKh = mfma(c16 < m ? -w2d[r] : 0.0f, kt, dKh);
+      dQ = mfma(w1tv[r], kh, dQ);
+      dKt = mfma(-w2tv[r], kh, dKt);
+      dKh = mfma(w1d[r], qt, dKh);
+      dKh = mfma(-w2d[r], kt, dKh);
     }
     // dS_0 for this wavefront's keys: rows key 16 w + 4 g4 + r, column c16
 #pragma unroll
@@ -618,12 +766,19 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       // wavefront's keys only, every read of E above)
       if (PH) sm.E[4 * g4 + r][key] = cgg[r];
     }
-    if (w == 0) {  // dv = beta a and dbeta for the tile
+    if (w == 0) {  // dv = beta a, and the tile's part of dbeta_t = a_t . r_t
       const int t = lane >> 2, c = 4 * (lane & 3);
+      const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
+      const long rw = (b * T_ + t0 + t) * HV + hv;
       const float4 a4 = *reinterpret_cast<const float4*>(&sm.a[t][c]);
+      const float4 r4 = *reinterpret_cast<const float4*>(&sm.r[t][c]);
       const float bt = sm.beta[t];
-      *reinterpret_cast<float4*>(&sm.dv[t][c]) = float4{bt * a4.x, bt * a4.y, bt * a4.z, bt * a4.w};
-      if (lane < kSeg) sm.db[lane] = sm.ar[lane];
+      const float arv = quad_sum(a4.x * r4.x + a4.y * r4.y + a4.z * r4.z + a4.w * r4.w);
+      if (t < n) {
+        *reinterpret_cast<float4*>(p.dv + rw * V + v0 + c) =
+            float4{bt * a4.x, bt * a4.y, bt * a4.z, bt * a4.w};
+        if ((lane & 3) == 0) atomicAdd(p.dbeta + rw, arv);
+      }
     }
   };
 
@@ -634,7 +789,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     for (int i = 0; i < 4; ++i) dS[i] = p.dST ? p.dST[o + i] : 0.0f;
   }
   *reinterpret_cast<float4*>(&sm.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
-  SegLoads<T, NVD> L;
+  SegLoads<T, NVD, NOPS> L;
   if (NC > 0) issue(NC - 1, L);
   for (int seg = NC - 1; seg >= 0; --seg) {
     const int n = min(kSeg, T_ - seg * kSeg);
@@ -660,49 +815,38 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       }
     };
     // The reverse step of token tt, given Sd_t (no global memory access):
-    // a_t, r_t and their column sums from the solve, or (fallback) from one
-    // sum over the keys.  With dS the gradient after the read, and beta
-    // factored out of the sums over the columns j:
+    // a_t and the prediction Sd_t^T k_t from one sum over the keys.  With dS
+    // the gradient after the read, and beta factored out of the sums over the
+    // columns j:
     //   dq = s (sum_j Sd d_j + beta k sum_j r_j d_j)
     //   dk = beta (sum_j dS r_j - sum_j Sd a_j)
     //   dg = sum_j (dS - k beta a_j) Sd,   dS <- alpha (dS - k beta a)
-    auto reverse = [&](auto from_solve, int tt, const float sd[4]) {
+    auto reverse = [&](int tt, const float sd[4]) {
       const float a_ = sm.al[tt][kap], kv = sm.k[tt][kap], qv = sm.q[tt][kap];
       const float bt = sm.beta[tt];
       const float4 d4 = *reinterpret_cast<const float4*>(&sm.dout[tt][c4]);
       const float d[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[i] += qv * d[i];  // the read o_t = s S_t^T q_t
-      float a[4], r[4], rd, ar;
-      if constexpr (decltype(from_solve)::value) {
-        const float4 a4 = *reinterpret_cast<const float4*>(&sm.a[tt][c4]);
-        const float4 r4 = *reinterpret_cast<const float4*>(&sm.r[tt][c4]);
-        a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
-        r[0] = r4.x; r[1] = r4.y; r[2] = r4.z; r[3] = r4.w;
-        rd = sm.rd[tt];
-        ar = sm.ar[tt];
-      } else {
-        float x[8];
+      float a[4], r[4], x[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = kv * dS[i];
-          x[4 + i] = kv * sd[i];
-        }
-        key_sum8(x);  // a_t = dS^T k_t and the prediction Sd^T k_t, per column
-        const float4 v4 = *reinterpret_cast<const float4*>(&sm.v[tt][c4]);
-        const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-        rd = 0.0f;
-        ar = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[i] = x[i];
-          r[i] = vv[i] - x[4 + i];
-          rd += r[i] * d[i];
-          ar += a[i] * r[i];
-        }
-        rd = quad_sum(rd);
-        ar = quad_sum(ar);
+      for (int i = 0; i < 4; ++i) {
+        x[i] = kv * dS[i];
+        x[4 + i] = kv * sd[i];
       }
+      key_sum8(x);  // a_t = dS^T k_t and the prediction Sd^T k_t, per column
+      const float4 v4 = *reinterpret_cast<const float4*>(&sm.v[tt][c4]);
+      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+      float rd = 0.0f, ar = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = x[i];
+        r[i] = vv[i] - x[4 + i];
+        rd += r[i] * d[i];
+        ar += a[i] * r[i];
+      }
+      rd = quad_sum(rd);
+      ar = quad_sum(ar);
       const float kb = kv * bt;
       float s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
@@ -720,19 +864,20 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       if (cg == 0) {
         sm.dq[tt][kap] = scale * (s1 + kb * rd);
         sm.dk[tt][kap] = bt * s2;
-        sm.E[tt][kap] = s3;  // dg; E is not read after the solve
+        sm.E[tt][kap] = s3;  // dg; E is not read again in this segment
       }
-      if (kap == 0) {
-        *reinterpret_cast<float4*>(&sm.dv[tt][c4]) =
+      if (kap == 0) {  // dv and the tile's part of dbeta, straight to the outputs
+        const long rw = (b * T_ + seg * kSeg + tt) * HV + hv;
+        *reinterpret_cast<float4*>(p.dv + rw * V + v0 + c4) =
             float4{bt * a[0], bt * a[1], bt * a[2], bt * a[3]};
-        if (cg == 0) sm.db[tt] = ar;
+        if (cg == 0) atomicAdd(p.dbeta + rw, ar);
       }
     };
     // The parts of the segment, the latest first: each rebuilds its kPart
     // states Sd_t from the checkpoint into registers, then runs them in
     // reverse.
     constexpr int kPart = 4;
-    auto halves = [&](auto from_solve) {
+    auto halves = [&]() {
 #pragma unroll
       for (int part = kSeg / kPart - 1; part >= 0; --part) {
         const int base = part * kPart;
@@ -744,16 +889,16 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
           if (base + j < n) advance(base + j, S, sd[j]);
 #pragma unroll
         for (int j = kPart - 1; j >= 0; --j)
-          if (base + j < n) reverse(from_solve, base + j, sd[j]);
+          if (base + j < n) reverse(base + j, sd[j]);
       }
     };
     if (fallback) {  // dL/dS in registers for the per-token pass, in the LDS tile between segments
       const float4 d0 = *reinterpret_cast<const float4*>(&sm.dsin[kap][c4]);
       dS[0] = d0.x; dS[1] = d0.y; dS[2] = d0.z; dS[3] = d0.w;
-      halves(std::false_type{});
+      halves();
       *reinterpret_cast<float4*>(&sm.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
     } else {
-      chunk_phase();
+      chunk_phase(seg);
     }
     __syncthreads();  // the segment's results are in LDS; its inputs are no longer read
     // the next segment's loads go out before the atomics, so that waiting for
@@ -865,11 +1010,13 @@ const float* split_resolved_values(const void* workspace, long chunks, int K, in
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace: the segment checkpoints [B, HV, NC, K, V], then the split
-// schedule's own workspace (which keeps U for the segment kernel).
+// Workspace: the segment checkpoints [B, HV, NC, K, V], the prep kernel's
+// operands [B, HV, NC, 3, 64, 4], then the split schedule's own workspace
+// (which keeps U for the segment kernel).
+static size_t ops_bytes(size_t segs) { return align256(segs * 3 * 64 * 4 * sizeof(float)); }
 size_t bwd_workspace_bytes(int B, int T, int HV, int K, int V) {
   const size_t nc = ((size_t)T + kSeg - 1) / kSeg;
-  return align256((size_t)B * HV * nc * K * V * sizeof(float)) +
+  return align256((size_t)B * HV * nc * K * V * sizeof(float)) + ops_bytes((size_t)B * HV * nc) +
          (size_t)B * HV * nc * split_workspace_bytes_per_chunk(K, V, kSeg);
 }
 
@@ -882,6 +1029,17 @@ static hipError_t zero(float* p, long n, hipStream_t stream) {
 template <int K, typename T, int GK>
 static hipError_t launch_bwd_kt(BwdParams p, hipStream_t stream) {
   const long nblk = (long)p.B * p.HV * (K / kBV);
+  const long nseg = (long)p.B * p.HV * p.NC;
+  if (nseg > 0) {
+    if (p.per_head)
+      hipLaunchKernelGGL((bwd_prep_kernel<K, T, GK, true>), dim3((unsigned)((nseg + 3) / 4)),
+                         dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<K, T, GK, false>), dim3((unsigned)((nseg + 3) / 4)),
+                         dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (nblk > 0) {
     if (p.per_head)
       hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK, true>), dim3((unsigned)nblk), dim3(4 * K), 0,
@@ -913,7 +1071,8 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
   const int NC = (T + kSeg - 1) / kSeg;
   char* ws = static_cast<char*>(workspace);
   float* ckpt = reinterpret_cast<float*>(ws);
-  void* split_ws = ws + align256((size_t)B * HV * NC * K * K * sizeof(float));
+  float* ops = reinterpret_cast<float*>(ws + align256((size_t)B * HV * NC * K * K * sizeof(float)));
+  void* split_ws = reinterpret_cast<char*>(ops) + ops_bytes((size_t)B * HV * NC);
   hipError_t e;
   const int gK = per_head ? 1 : K;  // gate values per (token, value head)
   const long nq = (long)B * T * H * K, ng = (long)B * T * HV * gK;
@@ -929,7 +1088,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
     if (e != hipSuccess) return e;
   }
   const float* u = split_resolved_values(split_ws, (long)B * HV * NC, K, kSeg);
-  BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, u, dq, dk, dv, dbeta,
+  BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, u, ops, dq, dk, dv, dbeta,
               dg_raw, dS0, dA_log, ddt_bias, B, T, H, HV, NC, per_head, lower_bound};
 #define KDA_BWD_GATE(KK, TT)                                                       \
   switch (kind) {                                                                  \
