@@ -63,9 +63,11 @@ struct BwdParams {
   const float* dt_bias;
   const float* dout;
   const float* dST;   // dL/dS_T or null
-  const float* ckpt;  // [B, HV, NC, K, V]: the state entering each 16-token segment
-  const float* u;     // U = beta r of every token, as the split schedule's state pass left it
+  const float* ckpt;  // [B, HV, NC, V, K]: the state entering each 16-token segment (column-major)
+  const float* u;     // [B, HV, NC, V / 16, 64, 4]: U = beta r of every token (MFMA accumulator order)
   float* ops;         // [B, HV, NC, 3, 64, 4]: per segment, the value-independent operands (bwd_prep_kernel)
+  float* eseg;        // [B, HV, NC, 16, K]: per segment, the cumulative retain factors E
+  int* segbad;        // [B, HV, NC]: 1 where some E leaves [2^-100, 2^100] (or is NaN)
   float* dq;
   float* dk;
   float* dv;
@@ -104,8 +106,9 @@ __global__ void bwd_zero_kernel(float* p, long n) {
 // operands, for keys 16 j + 4 g + s (any order of the keys serves, as long
 // as both operands follow it).  R comes row by row (lane c, forward
 // substitution of R (I + L^T diag(beta)) = I) with the coupling in LDS.
-// Segments whose E leaves the chunked form's range are formed all the same;
-// the segment kernel does not read them.
+// It also writes E itself (row-major, 16 x K per segment) and whether some
+// E leaves [2^-100, 2^100]; such segments are formed all the same, and the
+// segment kernel takes its per-token pass for them without reading them.
 template <int K, typename T, bool PH>
 struct PrepSmem {
   using Raw = typename In<T>::Raw1;
@@ -164,6 +167,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
                                              decltype(ctrl)::value, 0xF, 0xF, false));
   };
   f32x4 g1[2] = {}, g2t[2] = {};  // two chains each
+  bool bad = false;
+  float* eo = p.eseg + (sid * kSeg + c16) * K;
 #pragma unroll 2
   for (int j = 0; j < K / 16; ++j) {
     const int kb = 16 * j + 4 * g4;  // this lane's four keys
@@ -177,6 +182,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     }
     In<T>::unpack4(*reinterpret_cast<const Raw4*>(&sm.k[c16][kb]), kv);
     In<T>::unpack4(*reinterpret_cast<const Raw4*>(&sm.q[c16][kb]), qv);
+    float ev[4];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       float e = !in ? 1.0f
@@ -186,12 +192,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
       e = shr_mul(e, std::integral_constant<int, 0x112>{});
       e = shr_mul(e, std::integral_constant<int, 0x114>{});
       e = shr_mul(e, std::integral_constant<int, 0x118>{});
+      ev[s4] = e;
+      bad |= !(e >= 0x1p-100f && e <= 0x1p100f);
       const float k_ = in ? kv[s4] : 0.0f, q_ = in ? scale * qv[s4] : 0.0f;
       const float kh = k_ * __builtin_amdgcn_rcpf(e), kt = k_ * e, qt = q_ * e;
       g1[s4 & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, kt, g1[s4 & 1], 0, 0, 0);
       g2t[s4 & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt, kh, g2t[s4 & 1], 0, 0, 0);
     }
+    *reinterpret_cast<float4*>(eo + kb) = float4{ev[0], ev[1], ev[2], ev[3]};
   }
+  const bool anybad = __ballot(bad) != 0;
+  if (lane == 0) p.segbad[sid] = anybad ? 1 : 0;
   // lane (c16, g4) entry r: g1[4 g4 + r][c16] and g2t = g2^T, i.e. g2[c16][4 g4 + r]
   const float bt = in ? p.beta[(row0 + c16) * HV + hv] : 0.0f;  // beta of token c16
   float lop[4], mop[4];
@@ -319,15 +330,17 @@ struct alignas(16) BwdSmem {
   float dk[kSeg][K];
 };
 
-// One segment's inputs in flight: this thread's share of g_raw, k and q (key
-// channel kappa, tokens 4 c .. 4 c + 3), of v, dL/do, U and beta, and its own
-// row of the checkpoint.
+// One segment's inputs in flight: this thread's share of E, k and q (token
+// tid / (K / 4), four consecutive keys), of v, dL/do, U and beta, of the
+// prep's operands, its own row of the checkpoint, and the range flag.
 template <typename T, int NVD, int NOPS>
 struct SegLoads {
-  float g[4];
-  typename In<T>::Raw1 k[4], q[4], v[NVD];
+  float4 e;
+  typename In<T>::Raw4 k, q;
+  typename In<T>::Raw1 v[NVD];
   float dout[NVD], beta;
   float4 u, ckpt, ops[NOPS];
+  int bad;
 };
 
 template <int K, typename T, int GK, bool PH>
@@ -340,7 +353,10 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   __shared__ BwdSmem<K> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int kap = tid >> 2, cg = tid & 3, c4 = 4 * cg;
+  // (placing a head's value tiles on one XCD, so that their common reads
+  // share its L2, measured 2% slower: their atomics then meet there)
   const int vt = blockIdx.x % NVT, hd = blockIdx.x / NVT;
+  const int trow = tid / (K / 4), tcol = 4 * (tid % (K / 4));  // the staging layout of E, k, q
   const int HV = p.HV, H = p.H, T_ = p.T, NC = p.NC;
   const long b = hd / HV;
   const int hv = hd % HV, h = hv / (HV / H), v0 = vt * kBV;
@@ -363,16 +379,12 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   auto issue = [&](int seg, SegLoads<T, NVD, NOPS>& L) {
     const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
     const long row0 = b * T_ + t0;
-    const float* gb = p.g_raw + (row0 * HV + hv) * gK;
-    const T* kb = kg + (row0 * H + h) * K;
-    const T* qb = qg + (row0 * H + h) * K;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = min(c4 + i, n - 1);
-      L.g[i] = gb[r * HV * gK + gc0];
-      L.k[i] = kb[r * H * K + kap];
-      L.q[i] = qb[r * H * K + kap];
-    }
+    const long sg = (long)hd * NC + seg;
+    L.e = *reinterpret_cast<const float4*>(p.eseg + (sg * kSeg + trow) * K + tcol);
+    const int tr = min(trow, n - 1);
+    L.k = In<T>::raw4(kg, ((row0 + tr) * H + h) * K + tcol);
+    L.q = In<T>::raw4(qg, ((row0 + tr) * H + h) * K + tcol);
+    L.bad = p.segbad[sg];
     const T* vb = vg + (row0 * HV + hv) * V + v0;
     const float* db = p.dout + (row0 * HV + hv) * V + v0;
 #pragma unroll
@@ -385,8 +397,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     L.u = *reinterpret_cast<const float4*>(p.u + (((long)hd * NC + seg) * NVT + vt) * 256 +
                                            4 * (tid & 63));
     L.beta = p.beta[row0 * HV + hv + min(tid & 15, n - 1) * HV];
-    L.ckpt = *reinterpret_cast<const float4*>(p.ckpt + ((long)hd * NC + seg) * K * V + v0 +
-                                              kap * V + c4);
+    L.ckpt = *reinterpret_cast<const float4*>(p.ckpt + (sg * V + v0 + trow) * K + tcol);
     const float4* ob = reinterpret_cast<const float4*>(p.ops + ((long)hd * NC + seg) * (3 * 64 * 4));
 #pragma unroll
     for (int i = 0; i < NOPS; ++i) L.ops[i] = ob[min(tid + i * NT, 3 * 64 - 1)];
@@ -395,31 +406,17 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // v, dL/do, U and beta zero), with the cumulative retain factors E.
   // Returns whether an E of this thread leaves [2^-100, 2^100] (or is NaN).
   auto stage = [&](const SegLoads<T, NVD, NOPS>& L, int n) {
-    float al4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = c4 + i;
-      const bool in = tt < n;
-      al4[i] = in ? gate_alpha_pre<GK>(L.g[i], bias, gc) : 1.0f;
-      sm.al[tt][kap] = al4[i];
-      sm.k[tt][kap] = in ? In<T>::widen(L.k[i]) : 0.0f;
-      sm.q[tt][kap] = in ? scale * In<T>::widen(L.q[i]) : 0.0f;
-    }
-    // E: products over this thread's four tokens, then over the earlier
-    // groups of four (the other lanes of the quad)
-    float e4[4];
-    e4[0] = al4[0];
-    e4[1] = e4[0] * al4[1];
-    e4[2] = e4[1] * al4[2];
-    e4[3] = e4[2] * al4[3];
-    const float g0 = quad_bcast<0>(e4[3]), g1 = quad_bcast<1>(e4[3]), g2 = quad_bcast<2>(e4[3]);
-    const float ex = cg == 0 ? 1.0f : cg == 1 ? g0 : cg == 2 ? g0 * g1 : (g0 * g1) * g2;
-    bool bad = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float E = ex * e4[i];
-      sm.E[c4 + i][kap] = E;
-      bad |= !(E >= 0x1p-100f && E <= 0x1p100f);
+    {
+      const bool in = trow < n;
+      float kv[4], qv[4];
+      In<T>::unpack4(L.k, kv);
+      In<T>::unpack4(L.q, qv);
+      *reinterpret_cast<float4*>(&sm.E[trow][tcol]) = L.e;
+      *reinterpret_cast<float4*>(&sm.k[trow][tcol]) =
+          in ? float4{kv[0], kv[1], kv[2], kv[3]} : float4{0.0f, 0.0f, 0.0f, 0.0f};
+      *reinterpret_cast<float4*>(&sm.q[trow][tcol]) =
+          in ? float4{scale * qv[0], scale * qv[1], scale * qv[2], scale * qv[3]}
+             : float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
     for (int i = 0; i < NVD; ++i) {
@@ -438,11 +435,14 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       sm.u[r0 + 3][j] = r0 + 3 < n ? L.u.w : 0.0f;
     }
     if (tid < kSeg) sm.beta[tid] = tid < n ? L.beta : 0.0f;
-    *reinterpret_cast<float4*>(&sm.s0[kap][c4]) = L.ckpt;
+    sm.s0[tcol][trow] = L.ckpt.x;  // column trow of the tile, keys tcol .. tcol + 3
+    sm.s0[tcol + 1][trow] = L.ckpt.y;
+    sm.s0[tcol + 2][trow] = L.ckpt.z;
+    sm.s0[tcol + 3][trow] = L.ckpt.w;
 #pragma unroll
     for (int i = 0; i < NOPS; ++i)
       if (tid + i * NT < 3 * 64) (&sm.ops[0][0])[tid + i * NT] = L.ops[i];
-    return bad;
+    return L.bad != 0;
   };
   // Add the finished segment's results to the outputs: from LDS after the
   // per-token pass, from the registers cq, ck, cg (lane l: tokens
@@ -794,8 +794,8 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   for (int seg = NC - 1; seg >= 0; --seg) {
     const int n = min(kSeg, T_ - seg * kSeg);
     const bool bad = stage(L, n);
-    const float4 ck = L.ckpt;
-    const bool fallback = __syncthreads_or(bad);
+    const bool fallback = bad;  // uniform: one flag per segment
+    __syncthreads();
     if (!fallback) {
       products();
       __syncthreads();
@@ -881,6 +881,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
       for (int part = kSeg / kPart - 1; part >= 0; --part) {
         const int base = part * kPart;
+        const float4 ck = *reinterpret_cast<const float4*>(&sm.s0[kap][c4]);
         float S[4] = {ck.x, ck.y, ck.z, ck.w};
         float sd[kPart][4];
         for (int tt = 0; tt < base && tt < n; ++tt) advance(tt, S, sd[0]);
@@ -893,6 +894,16 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       }
     };
     if (fallback) {  // dL/dS in registers for the per-token pass, in the LDS tile between segments
+      {  // the per-token pass takes the retain factors themselves (1 past the end)
+        const float* gb = p.g_raw + ((b * T_ + seg * kSeg) * HV + hv) * gK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = c4 + i;
+          const float g = gb[min(tt, n - 1) * HV * gK + gc0];
+          sm.al[tt][kap] = tt < n ? gate_alpha_pre<GK>(g, bias, gc) : 1.0f;
+        }
+        __syncthreads();
+      }
       const float4 d0 = *reinterpret_cast<const float4*>(&sm.dsin[kap][c4]);
       dS[0] = d0.x; dS[1] = d0.y; dS[2] = d0.z; dS[3] = d0.w;
       halves();
@@ -1000,24 +1011,25 @@ __global__ __launch_bounds__(256) void bwd_gate_head_kernel(BwdParams p, long ro
   }
 }
 
-hipError_t launch_split(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
-                        const float* beta, const float* A_log, const float* dt_bias, int kind,
-                        int per_head, float lower_bound, const float* S0, float* o, float* S_out,
-                        float* h, void* workspace, int B, int T, int H, int HV, int K, int C,
-                        hipStream_t stream);
-size_t split_workspace_bytes_per_chunk(int K, int V, int C);
-const float* split_resolved_values(const void* workspace, long chunks, int K, int C);
+hipError_t launch_chunk_ckpt(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
+                             const float* beta, const float* A_log, const float* dt_bias, int kind,
+                             int per_head, float lower_bound, const float* S0, float* ckpt,
+                             float* u_out, int B, int T, int H, int HV, int K, hipStream_t stream);
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace: the segment checkpoints [B, HV, NC, K, V], the prep kernel's
-// operands [B, HV, NC, 3, 64, 4], then the split schedule's own workspace
-// (which keeps U for the segment kernel).
-static size_t ops_bytes(size_t segs) { return align256(segs * 3 * 64 * 4 * sizeof(float)); }
+// Workspace: the segment checkpoints [B, HV, NC, V, K] and U
+// [B, HV, NC, V / 16, 64, 4] from the forward in checkpoint mode, then the
+// prep kernel's operands [B, HV, NC, 3, 64, 4], its E [B, HV, NC, 16, K]
+// and range flags [B, HV, NC].
+static size_t prep_bytes(size_t segs, int K) {
+  return align256(segs * 3 * 64 * 4 * sizeof(float)) + align256(segs * kSeg * K * sizeof(float)) +
+         align256(segs * sizeof(int));
+}
 size_t bwd_workspace_bytes(int B, int T, int HV, int K, int V) {
-  const size_t nc = ((size_t)T + kSeg - 1) / kSeg;
-  return align256((size_t)B * HV * nc * K * V * sizeof(float)) + ops_bytes((size_t)B * HV * nc) +
-         (size_t)B * HV * nc * split_workspace_bytes_per_chunk(K, V, kSeg);
+  const size_t segs = (size_t)B * HV * (((size_t)T + kSeg - 1) / kSeg);
+  return align256(segs * K * V * sizeof(float)) + align256(segs * kSeg * V * sizeof(float)) +
+         prep_bytes(segs, K);
 }
 
 static hipError_t zero(float* p, long n, hipStream_t stream) {
@@ -1070,9 +1082,12 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
                       int K, hipStream_t stream) {
   const int NC = (T + kSeg - 1) / kSeg;
   char* ws = static_cast<char*>(workspace);
+  const size_t segs = (size_t)B * HV * NC;
   float* ckpt = reinterpret_cast<float*>(ws);
-  float* ops = reinterpret_cast<float*>(ws + align256((size_t)B * HV * NC * K * K * sizeof(float)));
-  void* split_ws = reinterpret_cast<char*>(ops) + ops_bytes((size_t)B * HV * NC);
+  float* u = reinterpret_cast<float*>(ws + align256(segs * K * K * sizeof(float)));
+  float* ops = reinterpret_cast<float*>(reinterpret_cast<char*>(u) + align256(segs * kSeg * K * sizeof(float)));
+  float* eseg = reinterpret_cast<float*>(reinterpret_cast<char*>(ops) + align256(segs * 3 * 64 * 4 * sizeof(float)));
+  int* segbad = reinterpret_cast<int*>(reinterpret_cast<char*>(eseg) + align256(segs * kSeg * K * sizeof(float)));
   hipError_t e;
   const int gK = per_head ? 1 : K;  // gate values per (token, value head)
   const long nq = (long)B * T * H * K, ng = (long)B * T * HV * gK;
@@ -1082,13 +1097,12 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
       (e = zero(ddt_bias, (long)HV * gK, stream)) != hipSuccess)
     return e;
   if (T > 0) {
-    // the states and U only (no o): the split skips its output stage
-    e = launch_split(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, per_head, lower_bound, S0,
-                     nullptr, nullptr, ckpt, split_ws, B, T, H, HV, K, kSeg, stream);
+    // the forward in checkpoint mode: every segment's entry state and U, no o
+    e = launch_chunk_ckpt(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, per_head, lower_bound, S0,
+                          ckpt, u, B, T, H, HV, K, stream);
     if (e != hipSuccess) return e;
   }
-  const float* u = split_resolved_values(split_ws, (long)B * HV * NC, K, kSeg);
-  BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, u, ops, dq, dk, dv, dbeta,
+  BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, u, ops, eseg, segbad, dq, dk, dv, dbeta,
               dg_raw, dS0, dA_log, ddt_bias, B, T, H, HV, NC, per_head, lower_bound};
 #define KDA_BWD_GATE(KK, TT)                                                       \
   switch (kind) {                                                                  \

@@ -71,6 +71,12 @@ struct ChunkParams {
   const float* S0;
   float* o;
   float* S_out;
+  // checkpoint mode (the backward's forward pass; no o): the state entering
+  // every 16-token block, [B, HV, NC, V, K] (each state column-major), and
+  // U = beta r of every block, [B, HV, NC, V / 16, 64, 4] (per 16-wide column
+  // block, lane l of 64 holding rows 4 (l / 16) .. + 3 of column l % 16)
+  float* ckpt;
+  float* u_out;
   int B, T, H, HV, kind;
   int G;  // value heads per XCD group (a divisor of HV / H)
   float lower_bound;
@@ -420,9 +426,12 @@ __device__ __forceinline__ VR buffer_load_v(__amdgpu_buffer_rsrc_t r, uint32_t o
 // GS: per-head gate (g_raw [B, T, HV], dt_bias [HV]), one decay shared by all
 // key channels, so the prep computes one gate and one product scan per token
 // pair instead of four.
-template <int K, typename T, int GK, bool GS>
+template <int K, typename T, int GK, bool GS, bool CK>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
-  constexpr bool F32 = std::is_same<T, float>::value;
+  // F32: every product on fp32 MFMA (fp32 inputs, and checkpoint mode, whose
+  // states feed the backward's fp32 arithmetic); otherwise hi/lo bf16 operands
+  constexpr bool F32IN = std::is_same<T, float>::value;
+  constexpr bool F32 = F32IN || CK;
   constexpr int V = K;
   constexpr int BV = V < 32 ? V : 32;
   constexpr int NCB = BV / 16, NKB = K / 16, NVT = V / BV;
@@ -638,11 +647,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
         };
         {  // v tile, transposed for the chain waves (padding rows: 0)
           const VRaw x = it * kTok + vtt < T_ ? cur.v : VRaw{};
-          if constexpr (F32 && VPT == 1) {
+          if constexpr (F32IN && VPT == 1) {
             B.vT[vc][vtt] = __uint_as_float(x);
-          } else if constexpr (F32) {
+          } else if constexpr (F32IN) {
             B.vT[vc][vtt] = __uint_as_float(x.x);
             B.vT[vc + 1][vtt] = __uint_as_float(x.y);
+          } else if constexpr (F32 && VPT == 1) {  // bf16 inputs on the fp32 path: widened
+            B.vT[vc][vtt] = bf16_bits_to_f32((uint16_t)x);
+          } else if constexpr (F32) {
+            B.vT[vc][vtt] = bf16_bits_to_f32((uint16_t)(x & 0xffffu));
+            B.vT[vc + 1][vtt] = bf16_bits_to_f32((uint16_t)(x >> 16));
           } else if constexpr (VPT == 1) {
             B.vT[vc][vtt] = x;
           } else {
@@ -684,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
       for (int e = lane; e < kTok * kRS; e += 64) sm.xd[e] = 0.0f;
     for (int it = 0; it < NT + 3; ++it) {
       const int ti = it - 1;
-      if constexpr (!F32) {
+      if constexpr (!F32 && !CK) {
         if (w == kAqkWave) {
           const int g = lane >> 4;
           if (!skip_o) {  // O of block it - 3
@@ -737,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           const int j = lane & 15;
           if (w == kAqkWave) {
-            if constexpr (F32) {
+            if constexpr (F32 && !CK) {
               kprod(acc, B.qh, 0, B.ki, 0, lane);
   #pragma unroll
               for (int r = 0; r < 4; ++r) {
@@ -865,6 +879,18 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
         const Ops& B = sm.blk[tc % 3];
         typename SM::Chain& C = sm.chain[cb];
         const int t0 = tc * kTok;
+        // checkpoint mode: this block's entry state (column vcol, keys
+        // 16 kb + 4 (lane / 16) .. + 3) and where its U goes
+        float* ublk = nullptr;
+        if constexpr (CK) {
+          const long blk = (long)hd * NT + tc;
+          float* ck = p.ckpt + (blk * V + vcol) * K + 4 * (lane >> 4);
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            *reinterpret_cast<float4*>(ck + 16 * kb) =
+                float4{sacc[kb][0], sacc[kb][1], sacc[kb][2], sacc[kb][3]};
+          ublk = p.u_out + ((blk * (V / 16) + vcol / 16) * 64 + lane) * 4;
+        }
         if (B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3]) {
           // ---- token-by-token recurrence (exact, slow path); the wave owns all
           // key rows of its columns, so both reductions stay in the wavefront
@@ -891,6 +917,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
             const float rr = p.beta[row * HV + hv] * (In<T>::at(vg, (row * HV + hv) * V + vcol) - part);
+            if constexpr (CK)  // U of token tt: row tt of the block, lane (tt / 4) * 16 + column
+              if ((lane >> 4) == (tt >> 2)) ublk[tt & 3] = rr;
             float op = 0.0f;
   #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -904,7 +932,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             }
             op += __shfl_xor(op, 16);
             op += __shfl_xor(op, 32);
-            if (lane < 16) p.o[(row * HV + hv) * V + vcol] = scale * op;
+            if (!CK && lane < 16) p.o[(row * HV + hv) * V + vcol] = scale * op;
           }
         } else {
           const int g = lane >> 4;
@@ -925,7 +953,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             }
           }
           f32x4 pk = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (F32)
+          if constexpr (F32 && CK)
+            kprod(pk, B.kh, 0, C.st[tc & 1], 0, lane);        // K_hat S (no output)
+          else if constexpr (F32)
             kprod2(pk, qs, B.kh, B.qh, C.st[tc & 1], lane);  // K_hat S and Q_hat S
           else if constexpr (kRegB) {  // K_hat S, the state from registers
             const int row = lane & 15;
@@ -957,22 +987,26 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             for (int r = 0; r < 4; ++r) put_tok(C.f.eb, lane & 15, 4 * g + r, e[r]);
             wave_lds_sync();
             tprod(u, sm.akk[tc & 1], 0, C.f.eb, lane);
+            if constexpr (CK) *reinterpret_cast<float4*>(ublk) = float4{u[0], u[1], u[2], u[3]};
 #pragma unroll
             for (int r = 0; r < 4; ++r) put_tok(C.f.u, lane & 15, 4 * g + r, u[r]);
             wave_lds_sync();
-            tprod(ov, sm.aqk[tc & 1], 0, C.f.u, lane);
+            if constexpr (!CK) tprod(ov, sm.aqk[tc & 1], 0, C.f.u, lane);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) tprod(sacc[kb], B.keT, 16 * kb, C.f.u, lane);
+            if constexpr (!CK) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = t0 + 4 * g + r;
-              if (t < T_) p.o[((b * T_ + t) * HV + hv) * V + vcol] = ov[r];
+              for (int r = 0; r < 4; ++r) {
+                const int t = t0 + 4 * g + r;
+                if (t < T_) p.o[((b * T_ + t) * HV + hv) * V + vcol] = ov[r];
+              }
             }
           } else {
             // Ebar, U stay in registers: accumulator layout = B operand layout
             bf16x4 eh, el, uh, ul;
             split4(e, eh, el);
             tprod_reg(u, sm.akk[tc & 1].c, eh, el, lane);  // U = (I + R)^{-1} Ebar
+            if constexpr (CK) *reinterpret_cast<float4*>(ublk) = float4{u[0], u[1], u[2], u[3]};
             const float uu[4] = {u[0], u[1], u[2], u[3]};
             split4(uu, uh, ul);
             {  // U to the output wave
@@ -1008,7 +1042,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   }
 }
 
-template <int K, typename T, int GK, bool GS>
+template <int K, typename T, int GK, bool GS, bool CK = false>
 static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   constexpr int BV = K < 32 ? K : 32;
   constexpr int NVT = K / BV;
@@ -1019,12 +1053,12 @@ static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   if (lds < 84 * 1024) lds = 84 * 1024;
   // the dynamic LDS limit above 64 KiB is raised on every launch (a host-side
   // attribute of the function: cheap, and it leaves the library stateless)
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK, GS>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_fwd_kernel<K, T, GK, GS, CK>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int nheads = p.B * p.HV;
   const long blocks = (long)((nheads / p.G + 7) / 8) * 8 * p.G * NVT;
-  hipLaunchKernelGGL((chunk_fwd_kernel<K, T, GK, GS>), dim3((unsigned)blocks), dim3(kThreads), lds,
+  hipLaunchKernelGGL((chunk_fwd_kernel<K, T, GK, GS, CK>), dim3((unsigned)blocks), dim3(kThreads), lds,
                      stream, p);
   return hipGetLastError();
 }
@@ -1033,8 +1067,8 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
                         int per_head, float lower_bound, const float* S0, float* o, float* S_out,
                         int B, int T, int H, int HV, int K, hipStream_t stream) {
-  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, B, T, H, HV, kind, 1,
-                lower_bound};
+  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, nullptr, nullptr, B, T, H, HV,
+                kind, 1, lower_bound};
   // The value heads of one query/key head share an XCD (and their q, k reads
   // its L2) when that keeps the eight XCDs evenly loaded.
   const int Gq = HV / H;
@@ -1057,6 +1091,38 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
 #undef KDA_CHUNK_CASE
 #undef KDA_CHUNK_GATE
 #undef KDA_CHUNK_GS
+  return hipErrorInvalidValue;
+}
+
+// The forward pass of the backward: the same kernel in checkpoint mode, which
+// writes the state entering every 16-token block and U of every block (see
+// ChunkParams) instead of o; K in {32, 64, 128}.
+hipError_t launch_chunk_ckpt(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
+                             const float* beta, const float* A_log, const float* dt_bias, int kind,
+                             int per_head, float lower_bound, const float* S0, float* ckpt,
+                             float* u_out, int B, int T, int H, int HV, int K, hipStream_t stream) {
+  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, nullptr, nullptr, ckpt, u_out, B, T, H, HV,
+                kind, 1, lower_bound};
+  const int Gq = HV / H;
+  p.G = (B * HV / Gq) % 8 == 0 ? Gq : 1;
+#define KDA_CKPT_GS(KK, TT, GG)                                            \
+  return per_head ? launch_chunk_kt<KK, TT, GG, true, true>(p, stream)     \
+                  : launch_chunk_kt<KK, TT, GG, false, true>(p, stream);
+#define KDA_CKPT_GATE(KK, TT)                                      \
+  switch (kind) {                                                  \
+    case KDA_GATE_SAFE: KDA_CKPT_GS(KK, TT, KDA_GATE_SAFE)         \
+    case KDA_GATE_STANDARD: KDA_CKPT_GS(KK, TT, KDA_GATE_STANDARD) \
+    default: KDA_CKPT_GS(KK, TT, KDA_GATE_NONE)                    \
+  }
+#define KDA_CKPT_CASE(KK)                     \
+  if (K == KK) {                              \
+    if (bf16) { KDA_CKPT_GATE(KK, uint16_t) } \
+    else { KDA_CKPT_GATE(KK, float) }         \
+  }
+  KDA_CKPT_CASE(32) KDA_CKPT_CASE(64) KDA_CKPT_CASE(128)
+#undef KDA_CKPT_CASE
+#undef KDA_CKPT_GATE
+#undef KDA_CKPT_GS
   return hipErrorInvalidValue;
 }
 
