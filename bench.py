@@ -17,9 +17,10 @@ forward runs the prefill shape with one gate per (token, value head)
 ("head_gate" object), and the one-sequence long shard (T=65536, 8 value heads)
 runs through both the fused chunk kernel and the three-stage split schedule
 ("split" object).  The backward pass (kda_bwd) runs on the prefill shape
-("backward" object): its roofline covers the segment phase, the call's time
-minus that of the chunk-16 split forward it starts with, against the fp32
-vector peak.
+("backward" object): its roofline covers the whole call (the forward pass
+that writes the segment checkpoints, the prep, segment and gate kernels),
+its algorithmic FLOPs against the fp32 MFMA peak, on which all of its
+products run.
 
 Prints ONE JSON line (rank 0).  Inputs are synthetic, seeded, resident in
 HBM before timing starts.  `roofline` covers the chunk kernel: algorithmic
@@ -44,6 +45,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+FP32_MFMA_PEAK_TFLOPS = 157.3
 
 
 def chunk_bytes(w):
@@ -72,12 +74,18 @@ def chunk_flops(w, C=BLOCK):
 
 
 def bwd_flops(w):
-    """Arithmetic of the backward's segment phase per token and value head,
+    """Arithmetic of the backward's reverse pass per token and value head,
     an FMA counted as two: the state rebuilt from its segment checkpoint
     (Sd = alpha S, Sd^T k, S = Sd + beta k r^T: 5 K V) and the reverse step
     (dS += s q do^T, S_t do, dS^T k, beta dS r - Sd dr, dS - k dr^T,
     rowsum(dSd Sd), alpha dSd: 15 K V)."""
     return 20 * w.K * w.V * w.B * w.T * w.HV
+
+
+def bwd_call_flops(w):
+    """A whole backward call: the forward pass that writes the checkpoints,
+    at its 16-token block, plus the reverse pass."""
+    return chunk_flops(w, 16) + bwd_flops(w)
 
 
 def bwd_bytes(w):
@@ -498,8 +506,8 @@ def main():
         result["recurrent"] = rec
         del gd, st
 
-    # Backward pass on the prefill shape: kda_bwd (the split forward at chunk
-    # 16 writing segment checkpoints, then the segment and gate kernels).
+    # Backward pass on the prefill shape: kda_bwd (the forward in checkpoint
+    # mode, then the prep, segment and gate kernels), timed as whole calls.
     if not args.no_bwd:
         wb = synth.WORKLOADS["prefill"]
         db = synth.make_inputs(wb)
@@ -508,10 +516,6 @@ def main():
         dout = torch.randn((wb.B, wb.T, wb.HV, wb.V), generator=gen).to(dev)
         wsb = torch.empty(kda.bwd_workspace_bytes(wb.B, wb.T, wb.H, wb.HV, wb.K, wb.V),
                           dtype=torch.uint8, device=dev)
-        nc16 = (wb.T + 15) // 16
-        hb = torch.empty((wb.B, wb.HV, nc16, wb.K, wb.V), dtype=torch.float32, device=dev)
-        wss = torch.empty(kda.chunk_fwd_split_workspace_bytes(wb.B, wb.T, wb.H, wb.HV, wb.K, wb.V,
-                                                              16), dtype=torch.uint8, device=dev)
         argsb = (gb["q"], gb["k"], gb["v"], gb["g_raw"], gb["beta"], gb["A_log"], gb["dt_bias"])
 
         def timed(fn, n):
@@ -529,29 +533,22 @@ def main():
         n_b = max(1, min(args.steps, 5))
         bwd_ms = timed(lambda: kda.bwd(*argsb, gate=wb.gate, lower_bound=wb.lower_bound,
                                        initial_state=gb["S0"], dout=dout, workspace=wsb), n_b)
-        # the states-only split forward at chunk 16: what kda_bwd runs first
-        fwd16_ms = timed(lambda: kda.chunk_fwd_split(*argsb, gate=wb.gate,
-                                                     lower_bound=wb.lower_bound, chunk_size=16,
-                                                     initial_state=gb["S0"], h=hb, output_o=False,
-                                                     output_final_state=False, workspace=wss), n_b)
-        seg_ms = bwd_ms - fwd16_ms
-        fl = bwd_flops(wb)
+        fl = bwd_call_flops(wb)
         result["backward"] = {
             "workload": wb.name, "B": wb.B, "T": wb.T, "H": wb.H, "HV": wb.HV, "K": wb.K,
             "gate": wb.gate, "dtype": wb.dtype, "calls": n_b, "ms_per_call": bwd_ms,
             "value": wb.B * wb.T / (bwd_ms * 1e-3), "unit": "tokens/s",
             "algorithmic_bytes": bwd_bytes(wb),
             "hbm_frac_whole_call": bwd_bytes(wb) / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "split_forward_chunk16_ms": fwd16_ms,
-            "roofline": {"bound": "alu", "achieved": fl / (seg_ms * 1e-3) / 1e12,
-                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": fl / (seg_ms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+            "roofline": {"bound": "mfma", "achieved": fl / (bwd_ms * 1e-3) / 1e12,
+                         "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": fl / (bwd_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS,
                          "traffic": measured_traffic("bwd_prefill"), "flops_per_launch": fl,
-                         "launch_ms": seg_ms,
-                         "kernel": "bwd_segment_kernel<128, bf16, safe gate> (with the gate and "
-                                   "zero-fill kernels: the call minus its states-only split "
-                                   "forward at chunk 16)"}}
-        del gb, dout, wsb, hb, wss
+                         "launch_ms": bwd_ms,
+                         "kernel": "kda_bwd, whole call (checkpoint-mode chunk forward, "
+                                   "bwd_prep_kernel, bwd_segment_kernel<128, bf16, safe gate>, "
+                                   "gate and zero-fill kernels)"}}
+        del gb, dout, wsb
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4

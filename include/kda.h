@@ -294,10 +294,11 @@ kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void*
  *                                       NULL it is the gradient at a zero bias)
  *   dinitial_state       [B, HV, K, V]  float32 output (dL/dS_0), or NULL
  *   workspace            device scratch of at least kda_bwd_workspace_bytes(...)
- *                        bytes, 16-byte aligned, owned by the caller; it holds
- *                        the state entering every 16-token segment, written by
- *                        the split schedule's forward, and that schedule's own
- *                        scratch; its contents are meaningless afterwards
+ *                        bytes, 16-byte aligned, owned by the caller; per
+ *                        16-token segment it holds the entering K x V state
+ *                        and U = beta r (written by the forward pass), and
+ *                        the segment's cumulative decays and three 16 x 16
+ *                        matrices; its contents are meaningless afterwards
  * Every output is overwritten (none needs initialising).  dq, dk, dg_raw,
  * dbeta, dA_log and ddt_bias are sums accumulated with fp32 atomics, so their
  * last bits can differ from run to run; dv and dinitial_state are written
@@ -306,8 +307,8 @@ kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void*
  * Supported: K == V in {32, 64, 128}; HV % H == 0; T >= 0; either gate
  * layout.  Arithmetic is fp32 throughout
  * (bf16 inputs widened exactly; the forward pass that writes the segment
- * states is that of kda_chunk_fwd_split with chunk 16).  Several kernels run
- * in order on `stream`.  Returns KDA_ERR_WORKSPACE if the workspace is missing
+ * states is kda_chunk_fwd's kernel on its fp32 products).  Several kernels
+ * run in order on `stream`.  Returns KDA_ERR_WORKSPACE if the workspace is missing
  * or too small.
  */
 size_t kda_bwd_workspace_bytes(int B, int T, int H, int HV, int K, int V);

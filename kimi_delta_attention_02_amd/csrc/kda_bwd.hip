@@ -19,12 +19,17 @@
 // sequence for the last two), and under GVA sums of dq, dk over the value
 // heads that share a query/key head.
 //
-// Schedule.  The states S_{t-1} the reverse pass needs come from checkpoints:
-// the split schedule (kda_split.hip, chunk 16, without its output stage)
-// writes the state entering every 16-token segment and leaves U_t = beta_t r_t
-// of every token in its workspace.  One workgroup per (sequence, value head,
-// 16-wide value tile) then walks the segments from the last.  Thread
-// 4 kappa + c holds key row kappa, value columns 4 c .. 4 c + 3 of the tile.
+// Schedule, four launches after the zero fills:
+//  1. the fused chunk kernel in checkpoint mode (kda_chunk.hip) writes the
+//     state entering every 16-token segment and U_t = beta_t r_t of every
+//     token, on its fp32 path whatever the input type;
+//  2. bwd_prep_kernel forms, once per (sequence, value head, segment), the
+//     matrices below that do not depend on the value tile, and E;
+//  3. bwd_segment_kernel: one workgroup per (sequence, value head, 16-wide
+//     value tile) walks the segments from the last, carrying dL/dS of its
+//     tile in LDS;
+//  4. the gate kernel applies the gate's chain rule and sums dt_bias and
+//     A_log over the sequences.
 //
 // Inside a segment the reverse recurrence of dL/dS is the adjoint of the
 // forward's delta rule, dS_{t-1} = diag(alpha_t)(I - beta_t k_t k_t^T) G_t with
@@ -34,19 +39,17 @@
 // L = strictly-lower[(k E)(k / E)^T] and M = upper[(k / E)(s q E)^T]:
 //   predictions  p = (k E) S_0 + L U,             r = v - p
 //   a_t = G_t^T k_t:  (I + L^T diag(beta)) A = M dL/do + (k Suf) dS_in
-// (dS_in: dL/dS entering the segment's reverse pass).  Three wavefronts form
-// the four products on fp32 MFMA, one wavefront back-substitutes, and the
-// token loop is then elementwise: the segment's states are rebuilt from the
-// checkpoint in registers, S_t = alpha_t S_{t-1} + k_t U_t^T, and each token
-// updates dS and forms its dq, dk, dg partial sums over the tile's columns.
-// Segments whose E leaves [2^-100, 2^100] (where k / E would lose range) take
-// the per-token sums over the keys instead (DPP and row swaps inside a
-// wavefront, an LDS exchange across them).  The per-key results (dq, dk, dg)
-// and dbeta, summed over the value tiles (and the value heads of a GVA group),
-// are accumulated with fp32 atomics into zeroed outputs, once per segment, so
-// their last bits depend on the order the tiles finish in.  A last kernel
-// applies the gate's chain rule and sums dt_bias and A_log over the sequences.
-// Arithmetic is fp32 throughout (bf16 inputs widened exactly).
+// (dS_in: dL/dS entering the segment's reverse pass), and dq, dk, dg and the
+// dS_in of the earlier segment are products over the segment as well (see
+// chunk_phase).  All of it runs on fp32 MFMA 16x16x4.  Segments whose E
+// leaves [2^-100, 2^100] (where k / E would lose range) take a per-token pass
+// instead: the states rebuilt from the checkpoint in registers, the sums over
+// the keys by DPP and row swaps inside a wavefront and an LDS exchange across
+// them.  The per-key results (dq, dk, dg) and dbeta, summed over the value
+// tiles (and the value heads of a GVA group), are accumulated with fp32
+// atomics into zeroed outputs, once per segment, so their last bits depend on
+// the order the tiles finish in.  Arithmetic is fp32 throughout (bf16 inputs
+// widened exactly).
 #include <type_traits>
 
 #include "kda_device.h"

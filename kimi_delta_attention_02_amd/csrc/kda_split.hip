@@ -1029,14 +1029,6 @@ static size_t image_bytes(int K, int C) {
   return 0;
 }
 
-// Where the state pass leaves U (the resolved values beta_t r_t of every
-// token) in a workspace laid out for B * HV * NC chunks: per (b, hv, chunk)
-// and 16-wide column block cb, one 16 x 16 fragment (frag_index) for C = 16.
-const float* split_resolved_values(const void* workspace, long chunks, int K, int C) {
-  return reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
-                                        chunks * image_bytes(K, C));
-}
-
 size_t split_workspace_bytes_per_chunk(int K, int V, int C) {
   return image_bytes(K, C) + ((size_t)C * V + (size_t)K * V) * sizeof(float);
 }
