@@ -278,59 +278,54 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// DPP broadcast of lane I of each group of four lanes (quad permutation
-// [I, I, I, I]); quad_bcast_dyn takes an index that is a constant once its
-// caller's loop is unrolled.
-template <int I>
-__device__ __forceinline__ float quad_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               I * 0x55, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float quad_bcast_dyn(int i, float x) {
-  switch (i) {
-    case 0: return quad_bcast<0>(x);
-    case 1: return quad_bcast<1>(x);
-    case 2: return quad_bcast<2>(x);
-    default: return quad_bcast<3>(x);
-  }
-}
+constexpr int kTiles = 2;  // value tiles per workgroup
+
+// One value tile's arrays.  Each wavefront touches only its own tile's, from
+// one base address: within the tile every offset fits a DS instruction's
+// 64 KiB immediate range.
+template <int K>
+struct alignas(16) BwdTile {
+  float u[kSeg][kBV];  // U = beta r from the forward (0 past the end)
+  float v[kSeg][kBV];
+  float dout[kSeg][kBV];
+  float a[kSeg][kBV];    // a_t = G_t^T k_t
+  float r[kSeg][kBV];    // r_t = v_t - Sd_t^T k_t
+  float w1[kSeg][kSeg];  // W1[t][m] = (dL/do U^T)[t][m] for m <= t, else 0
+  float w2[kSeg][kSeg];  // W2[t][m] = (dR U^T)[t][m] for m < t, else 0
+  float s0[K][kBV];      // the tile of the checkpoint S_0
+  float dsin[K][kBV];    // the tile of dL/dS entering the segment's reverse pass
+  // chunked pass: partial products over the four quarters of the keys,
+  // (k E) S_0 in 0..3 and (k Suf) dS_in in 4..7; written after the staging,
+  // read before the next one
+  float part[8][kSeg][kBV];
+  // per-token pass: its key sums across the wavefronts
+  float red[2][K / 16][2][kBV];
+  float fin[K / 16][8][4];
+};
 
 template <int K>
 struct alignas(16) BwdSmem {
   static constexpr int KP = K + 4;  // row stride: the 16 rows of an MFMA operand read spread over the banks
-  // Everything the chunked segment pass reads or writes comes first, within
-  // the 64 KiB that a DS instruction's immediate offset reaches, so that one
-  // address register per array serves every access.
   float beta[kSeg];
   float4 ops[3][64];  // the segment's value-independent operands (bwd_prep_kernel)
-  float u[kSeg][kBV];  // U = beta r from the forward's state pass (0 past the end)
-  float v[kSeg][kBV];
-  float dout[kSeg][kBV];
-  float a[kSeg][kBV];   // a_t = G_t^T k_t
-  float r[kSeg][kBV];   // r_t = v_t - Sd_t^T k_t
-  float w1[kSeg][kSeg];  // W1[t][m] = (dL/do U^T)[t][m] for m <= t, else 0
-  float w2[kSeg][kSeg];  // W2[t][m] = (dR U^T)[t][m] for m < t, else 0
   // the segment's inputs per (token, key channel)
   float k[kSeg][KP];   // k (0 past the end)
   float q[kSeg][KP];   // s q (0 past the end)
-  float E[kSeg][KP];   // prod_{m <= t} alpha_m from the segment start; then dg (per-token pass, per-head gate)
-  float s0[K][kBV];    // the tile of the checkpoint S_0
-  float dsin[K][kBV];  // the tile of dL/dS entering the segment's reverse pass
+  float E[kSeg][KP];   // prod_{m <= t} alpha_m from the segment start
+  float al[kSeg][KP];  // the retain factors (per-token pass; 1 past the end)
+  BwdTile<K> tile[kTiles];
   union {
-    // chunked pass: partial products over the four quarters of the keys,
-    // (k E) S_0 in 0..3 and (k Suf) dS_in in 4..7; written after the
-    // staging, read before the next one
-    float part[8][kSeg][kBV];
-    // per-token pass: the retain factors, staged every segment (1 for tokens
-    // past the end)
-    float al[kSeg][KP];
+    // chunked pass: each wavefront of tile 1 hands its results (dq, dk, dg:
+    // entry r of lane l) to the wavefront of tile 0 that owns the same keys
+    float xch[K / 16][3][4][64];
+    // per-token pass: its results, the tiles summed, written out together
+    // once the segment is done
+    struct {
+      float dq[kSeg][K];
+      float dk[kSeg][K];
+      float dg[kSeg][K];
+    } fb;
   };
-  // the per-token pass (segments outside the chunked form's range): its key
-  // sums and its results, written out together once the segment is done
-  float red[2][K / 16][2][kBV];
-  float fin[K / 16][8][4];
-  float dq[kSeg][K];
-  float dk[kSeg][K];
 };
 
 // One segment's inputs in flight: this thread's share of E, k and q (token
@@ -347,31 +342,32 @@ struct SegLoads {
 };
 
 template <int K, typename T, int GK, bool PH>
-__global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void bwd_segment_kernel(
-    BwdParams p) {
-  constexpr int V = K, NT = 4 * K, NW = NT / 64, NVT = V / kBV;
-  constexpr int NVD = (kSeg * kBV + NT - 1) / NT;  // v and dL/do elements each thread stages
-  constexpr int NOPS = (3 * 64 + NT - 1) / NT;     // float4s of the prep's operands each thread stages
-  static_assert(kSeg * K / NT == 4 && NT >= 64, "thread layout");
+__global__ __launch_bounds__(4 * K * kTiles) __attribute__((amdgpu_waves_per_eu(4))) void
+bwd_segment_kernel(BwdParams p) {
+  // NTH threads per value tile (4 per key row), NWH wavefronts; the
+  // workgroup's kTiles tiles are adjacent 16-wide column blocks
+  constexpr int V = K, NTH = 4 * K, NWH = NTH / 64, NT = NTH * kTiles, NVT = V / kBV;
+  constexpr int NVD = (kSeg * kBV + NTH - 1) / NTH;  // v and dL/do elements each thread stages
+  constexpr int NOPS = (3 * 64 + NT - 1) / NT;       // float4s of the prep's operands each thread stages
+  static_assert(kSeg * K / NTH == 4 && NTH >= 64 && (NTH & (NTH - 1)) == 0, "thread layout");
+  static_assert(NVT % kTiles == 0, "value tiles per workgroup");
   __shared__ BwdSmem<K> sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int gtid = threadIdx.x, tile = gtid / NTH;
+  const int tid = gtid & (NTH - 1), lane = tid & 63, w = tid >> 6;  // within the tile
   const int kap = tid >> 2, cg = tid & 3, c4 = 4 * cg;
+  BwdTile<K>& ts = sm.tile[tile];
   // (placing a head's value tiles on one XCD, so that their common reads
   // share its L2, measured 2% slower: their atomics then meet there)
-  const int vt = blockIdx.x % NVT, hd = blockIdx.x / NVT;
-  const int trow = tid / (K / 4), tcol = 4 * (tid % (K / 4));  // the staging layout of E, k, q
+  const int vt = blockIdx.x % (NVT / kTiles), hd = blockIdx.x / (NVT / kTiles);
+  const int trow = tid / (K / 4), tcol = 4 * (tid % (K / 4));  // the staging layout of E, k, q, S_0
   const int HV = p.HV, H = p.H, T_ = p.T, NC = p.NC;
   const long b = hd / HV;
-  const int hv = hd % HV, h = hv / (HV / H), v0 = vt * kBV;
+  const int hv = hd % HV, h = hv / (HV / H), v0 = (vt * kTiles + tile) * kBV;
   const float scale = 1.0f / __builtin_sqrtf((float)K);
   const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
   const GateConsts gc = gate_consts(rate, p.lower_bound);
   // PH: one gate value per (token, value head) (p.per_head)
   constexpr int gK = PH ? 1 : K;  // gate stride
-  const int gc0 = PH ? 0 : kap;   // this thread's gate element
-  const float bias = gate_bias_pre<GK>(
-      (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * gK + gc0] : 0.0f, gc);
-  const int town = tid / K, cown = tid % K;  // the layout of the results' write-out
   const T* qg = static_cast<const T*>(p.q);
   const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
@@ -380,36 +376,45 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // token, n >= 1).  Addresses are a base uniform over the workgroup plus a
   // 32-bit per-thread offset.
   auto issue = [&](int seg, SegLoads<T, NVD, NOPS>& L) {
+    const int gtid = opaque(threadIdx.x), tid = gtid & (NTH - 1);
+    const int trow = tid / (K / 4), tcol = 4 * (tid % (K / 4));
+    const int v0 = (vt * kTiles + opaque(threadIdx.x) / NTH) * kBV;
+    const int tile = opaque(threadIdx.x) / NTH;
     const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
     const long row0 = b * T_ + t0;
     const long sg = (long)hd * NC + seg;
-    L.e = *reinterpret_cast<const float4*>(p.eseg + (sg * kSeg + trow) * K + tcol);
-    const int tr = min(trow, n - 1);
-    L.k = In<T>::raw4(kg, ((row0 + tr) * H + h) * K + tcol);
-    L.q = In<T>::raw4(qg, ((row0 + tr) * H + h) * K + tcol);
+    if (tile == 0) {  // E, k and q serve both tiles
+      L.e = *reinterpret_cast<const float4*>(p.eseg + (sg * kSeg + trow) * K + tcol);
+      const int tr = min(trow, n - 1);
+      L.k = In<T>::raw4(kg, ((row0 + tr) * H + h) * K + tcol);
+      L.q = In<T>::raw4(qg, ((row0 + tr) * H + h) * K + tcol);
+    }
     L.bad = p.segbad[sg];
     const T* vb = vg + (row0 * HV + hv) * V + v0;
     const float* db = p.dout + (row0 * HV + hv) * V + v0;
 #pragma unroll
     for (int i = 0; i < NVD; ++i) {  // elements past the tile re-read its first ones
-      const int e = (tid + i * NT) % (kSeg * kBV);
+      const int e = (tid + i * NTH) % (kSeg * kBV);
       const int o = min(e / kBV, n - 1) * HV * V + e % kBV;
       L.v[i] = vb[o];
       L.dout[i] = db[o];
     }
-    L.u = *reinterpret_cast<const float4*>(p.u + (((long)hd * NC + seg) * NVT + vt) * 256 +
-                                           4 * (tid & 63));
+    L.u = *reinterpret_cast<const float4*>(p.u + (sg * NVT + v0 / kBV) * 256 + 4 * (tid & 63));
     L.beta = p.beta[row0 * HV + hv + min(tid & 15, n - 1) * HV];
     L.ckpt = *reinterpret_cast<const float4*>(p.ckpt + (sg * V + v0 + trow) * K + tcol);
     const float4* ob = reinterpret_cast<const float4*>(p.ops + ((long)hd * NC + seg) * (3 * 64 * 4));
 #pragma unroll
-    for (int i = 0; i < NOPS; ++i) L.ops[i] = ob[min(tid + i * NT, 3 * 64 - 1)];
+    for (int i = 0; i < NOPS; ++i) L.ops[i] = ob[min(gtid + i * NT, 3 * 64 - 1)];
   };
   // Place them in LDS, tokens past the end as an identity (alpha = 1, k, q,
   // v, dL/do, U and beta zero), with the cumulative retain factors E.
   // Returns whether an E of this thread leaves [2^-100, 2^100] (or is NaN).
   auto stage = [&](const SegLoads<T, NVD, NOPS>& L, int n) {
-    {
+    const int gtid = opaque(threadIdx.x), tid = gtid & (NTH - 1);
+    const int trow = tid / (K / 4), tcol = 4 * (tid % (K / 4));
+    BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
+    const int tile = opaque(threadIdx.x) / NTH;
+    if (tile == 0) {
       const bool in = trow < n;
       float kv[4], qv[4];
       In<T>::unpack4(L.k, kv);
@@ -423,68 +428,52 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     }
 #pragma unroll
     for (int i = 0; i < NVD; ++i) {
-      const int e = tid + i * NT;
+      const int e = tid + i * NTH;
       if (e < kSeg * kBV) {
         const bool in = e / kBV < n;
-        sm.v[e / kBV][e % kBV] = in ? In<T>::widen(L.v[i]) : 0.0f;
-        sm.dout[e / kBV][e % kBV] = in ? L.dout[i] : 0.0f;
+        ts.v[e / kBV][e % kBV] = in ? In<T>::widen(L.v[i]) : 0.0f;
+        ts.dout[e / kBV][e % kBV] = in ? L.dout[i] : 0.0f;
       }
     }
     if (tid < 64) {  // U: one 16 x 16 fragment, lane l holding rows 4 (l / 16) + r of column l % 16
       const int r0 = 4 * (tid >> 4), j = tid & 15;
-      sm.u[r0][j] = r0 < n ? L.u.x : 0.0f;
-      sm.u[r0 + 1][j] = r0 + 1 < n ? L.u.y : 0.0f;
-      sm.u[r0 + 2][j] = r0 + 2 < n ? L.u.z : 0.0f;
-      sm.u[r0 + 3][j] = r0 + 3 < n ? L.u.w : 0.0f;
+      ts.u[r0][j] = r0 < n ? L.u.x : 0.0f;
+      ts.u[r0 + 1][j] = r0 + 1 < n ? L.u.y : 0.0f;
+      ts.u[r0 + 2][j] = r0 + 2 < n ? L.u.z : 0.0f;
+      ts.u[r0 + 3][j] = r0 + 3 < n ? L.u.w : 0.0f;
     }
-    if (tid < kSeg) sm.beta[tid] = tid < n ? L.beta : 0.0f;
-    sm.s0[tcol][trow] = L.ckpt.x;  // column trow of the tile, keys tcol .. tcol + 3
-    sm.s0[tcol + 1][trow] = L.ckpt.y;
-    sm.s0[tcol + 2][trow] = L.ckpt.z;
-    sm.s0[tcol + 3][trow] = L.ckpt.w;
+    if (gtid < kSeg) sm.beta[gtid] = gtid < n ? L.beta : 0.0f;
+    ts.s0[tcol][trow] = L.ckpt.x;  // column trow of the tile, keys tcol .. tcol + 3
+    ts.s0[tcol + 1][trow] = L.ckpt.y;
+    ts.s0[tcol + 2][trow] = L.ckpt.z;
+    ts.s0[tcol + 3][trow] = L.ckpt.w;
 #pragma unroll
     for (int i = 0; i < NOPS; ++i)
-      if (tid + i * NT < 3 * 64) (&sm.ops[0][0])[tid + i * NT] = L.ops[i];
+      if (gtid + i * NT < 3 * 64) (&sm.ops[0][0])[gtid + i * NT] = L.ops[i];
     return L.bad != 0;
   };
-  // Add the finished segment's results to the outputs: from LDS after the
-  // per-token pass, from the registers cq, ck, cg (lane l: tokens
-  // 4 (l / 16) + r, key 16 w + l % 16) after the chunked pass.
+  // Add the finished segment's results to the outputs.  After the chunked
+  // pass they are in the registers cq, ck, cg (lane l: tokens 4 (l / 16) + r,
+  // key 16 w + l % 16) of both tiles: tile 0 adds tile 1's, handed over in
+  // LDS, and issues one atomic per element.  After the per-token pass they are
+  // in LDS, the tiles already summed.
   float cq[4], ckk[4], cgg[4];
   auto flush = [&](int seg, bool chunked) {
-    const int tid = opaque(threadIdx.x), lane = tid & 63, town = tid / K, cown = tid % K;
+    const int gtid = opaque(threadIdx.x), tid = gtid & (NTH - 1), lane = tid & 63;
     const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
     const long row0 = b * T_ + t0;
     float* dqb = p.dq + (row0 * H + h) * K;
     float* dkb = p.dk + (row0 * H + h) * K;
     float* dgb = p.dg + (row0 * HV + hv) * K;  // per-channel gate
-    float vals[4][3];
-    if (!chunked) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tt = town + 4 * i;
-        vals[i][0] = sm.dq[tt][cown];
-        vals[i][1] = sm.dk[tt][cown];
-        vals[i][2] = sm.E[tt][cown];  // dg
-      }
-    }
-    // per-head gate: token tid / 4's dg summed over the key channels (the
-    // gate is one value broadcast over them)
-    float dgh = 0.0f;
-    if (PH && tid < 64) {
-      const int tt = tid >> 2;
-      float s0 = 0.0f, s1 = 0.0f;
-      for (int c = tid & 3; c < K; c += 8) {
-        s0 += sm.E[tt][c];
-        s1 += sm.E[tt][c + 4];
-      }
-      dgh = quad_sum(s0 + s1);
-    }
-    // the next segment's staging overwrites E, which holds dg after the
-    // per-token pass and (per-head gate) the per-channel dg of either pass
-    if (PH || !chunked) __syncthreads();
     if (chunked) {
-      const int g4 = lane >> 4, key = 16 * (tid >> 6) + (lane & 15);
+      if (gtid >= NTH) return;  // tile 1 handed its results over
+      const int w = tid >> 6, g4 = lane >> 4, c16 = lane & 15, key = 16 * w + c16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        cq[r] += sm.xch[w][0][r][lane];
+        ckk[r] += sm.xch[w][1][r][lane];
+        cgg[r] += sm.xch[w][2][r][lane];
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tt = 4 * g4 + r;
@@ -494,19 +483,34 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
           if (!PH) atomicAdd(dgb + tt * HV * K + key, cgg[r]);
         }
       }
-    } else {
+      if (PH) {  // per-head gate: dg summed over this wavefront's 16 keys, one atomic per token
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tt = town + 4 * i;
-        if (tt < n) {
-          atomicAdd(dqb + tt * H * K + cown, vals[i][0]);
-          atomicAdd(dkb + tt * H * K + cown, vals[i][1]);
-          if (!PH) atomicAdd(dgb + tt * HV * K + cown, vals[i][2]);
+        for (int r = 0; r < 4; ++r) {
+          float x = cgg[r];
+          x = ror_add<8>(x);
+          x = ror_add<4>(x);
+          x = ror_add<2>(x);
+          x = ror_add<1>(x);
+          if (c16 == 0 && 4 * g4 + r < n) atomicAdd(p.dg + (row0 + 4 * g4 + r) * HV + hv, x);
         }
       }
+    } else {
+      for (int e = gtid; e < kSeg * K; e += NT) {
+        const int tt = e / K, c = e % K;
+        if (tt < n) {
+          atomicAdd(dqb + tt * H * K + c, sm.fb.dq[tt][c]);
+          atomicAdd(dkb + tt * H * K + c, sm.fb.dk[tt][c]);
+          if (!PH) atomicAdd(dgb + tt * HV * K + c, sm.fb.dg[tt][c]);
+        }
+      }
+      if (PH && gtid < 64) {  // per-head gate: token gtid / 4's dg summed over the key channels
+        const int tt = gtid >> 2;
+        float x = 0.0f;
+        for (int c = gtid & 3; c < K; c += 4) x += sm.fb.dg[tt][c];
+        x = quad_sum(x);
+        if ((gtid & 3) == 0 && tt < n) atomicAdd(p.dg + (row0 + tt) * HV + hv, x);
+      }
     }
-    if (PH && tid < 64 && (tid & 3) == 0 && (tid >> 2) < n)
-      atomicAdd(p.dg + row0 * HV + hv + (tid >> 2) * HV, dgh);
   };
 
   // The segment's per-token key sums that involve the value tile, as matrix
@@ -518,6 +522,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // (k Suf) dS_in with Suf = gamma / E.
   auto product = [&](auto PP, int task) {
     constexpr int P = decltype(PP)::value;
+    BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
     const int lane = opaque(threadIdx.x) & 63, row = lane & 15, kq = lane >> 4;
     const int k0 = (task & 3) * (K / 4);
     // up to four accumulators, so that the dependent MFMA chains are short
@@ -529,21 +534,21 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       float x, y;
       if constexpr (P == 0) {
         x = kv * e;
-        y = sm.s0[key][row];
+        y = ts.s0[key][row];
       } else {
         x = kv * sm.E[kSeg - 1][key] * __builtin_amdgcn_rcpf(e);
-        y = sm.dsin[key][row];
+        y = ts.dsin[key][row];
       }
       acc[st & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc[st & 3], 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      sm.part[task][4 * kq + r][row] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
+      ts.part[task][4 * kq + r][row] = (acc[0][r] + acc[1][r]) + (acc[2][r] + acc[3][r]);
   };
   auto products = [&]() {
-    const int w = opaque(threadIdx.x) >> 6;
+    const int w = (opaque(threadIdx.x) & (NTH - 1)) >> 6;
 #pragma unroll 1
-    for (int task = w; task < 8; task += NW) {
+    for (int task = w; task < 8; task += NWH) {
       if (task < 4)
         product(std::integral_constant<int, 0>{}, task);
       else
@@ -553,22 +558,23 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // From the products and the prep's operands (L_tm = g1[m][t] for m < t,
   // M_tm = g2[t][m] for m >= t, R = (I + L^T diag(beta))^{-1}):
   //   wavefront 0:        P = (k E) S_0 + L U,  r = v - P
-  //   wavefront 1 % NW:   Y = (k Suf) dS_in + M dL/do,  a = R Y (formed as
+  //   wavefront 1 % NWH:   Y = (k Suf) dS_in + M dL/do,  a = R Y (formed as
   //                       a^T = Y^T R^T), then W2 = strictly-lower[diag(beta) a U^T]
-  //   wavefront 2 % NW:   W1 = lower[dL/do U^T]
+  //   wavefront 2 % NWH:   W1 = lower[dL/do U^T]
   // The products over the tokens (or the tile's columns) are 16 x 16 x 16 on
   // fp32 MFMA as above, the inner index in step r being 4 (l / 16) + r, so
   // that an accumulator serves as the next product's operand in place.
   auto solve = [&]() {
-    const int tid = opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
+    BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
+    const int tid = opaque(threadIdx.x) & (NTH - 1), lane = tid & 63, w = tid >> 6;
     const int c16 = lane & 15, g4 = lane >> 4;
     auto mfma = [](float a, float b, f32x4 c) {
       return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     };
     auto part_sum = [&](int p0, int r) {
       const int t = 4 * g4 + r;
-      return (sm.part[p0][t][c16] + sm.part[p0 + 1][t][c16]) +
-             (sm.part[p0 + 2][t][c16] + sm.part[p0 + 3][t][c16]);
+      return (ts.part[p0][t][c16] + ts.part[p0 + 1][t][c16]) +
+             (ts.part[p0 + 2][t][c16] + ts.part[p0 + 3][t][c16]);
     };
     if (w == 0) {
       const float4 l4 = sm.ops[0][lane];
@@ -577,43 +583,43 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = part_sum(0, r);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc = mfma(lv[r], sm.u[4 * g4 + r][c16], acc);
+      for (int r = 0; r < 4; ++r) acc = mfma(lv[r], ts.u[4 * g4 + r][c16], acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.r[4 * g4 + r][c16] = sm.v[4 * g4 + r][c16] - acc[r];
+      for (int r = 0; r < 4; ++r) ts.r[4 * g4 + r][c16] = ts.v[4 * g4 + r][c16] - acc[r];
     }
-    if (w == 1 % NW) {
+    if (w == 1 % NWH) {
       const float4 m4 = sm.ops[1][lane], r4 = sm.ops[2][lane];
       const float mv[4] = {m4.x, m4.y, m4.z, m4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
       f32x4 y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[r] = part_sum(4, r);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y = mfma(mv[r], sm.dout[4 * g4 + r][c16], y);
+      for (int r = 0; r < 4; ++r) y = mfma(mv[r], ts.dout[4 * g4 + r][c16], y);
       // a^T[j][t] = sum_m Y[m][j] R[t][m]: Y's accumulator is Y^T's A operand
       f32x4 at = {};
 #pragma unroll
       for (int r = 0; r < 4; ++r) at = mfma(y[r], rv[r], at);
       // lane (c16, g4) holds a[c16][4 g4 + r]
-      *reinterpret_cast<float4*>(&sm.a[c16][4 * g4]) = float4{at[0], at[1], at[2], at[3]};
+      *reinterpret_cast<float4*>(&ts.a[c16][4 * g4]) = float4{at[0], at[1], at[2], at[3]};
       // W2[t][m] = sum_j beta_t a[t][j] U[m][j]
       const float bc = sm.beta[c16];
-      const float4 u4 = *reinterpret_cast<const float4*>(&sm.u[c16][4 * g4]);
+      const float4 u4 = *reinterpret_cast<const float4*>(&ts.u[c16][4 * g4]);
       const float uv[4] = {u4.x, u4.y, u4.z, u4.w};
       f32x4 acc2 = {};
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc2 = mfma(bc * at[r], uv[r], acc2);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.w2[4 * g4 + r][c16] = c16 < 4 * g4 + r ? acc2[r] : 0.0f;
+      for (int r = 0; r < 4; ++r) ts.w2[4 * g4 + r][c16] = c16 < 4 * g4 + r ? acc2[r] : 0.0f;
     }
-    if (w == 2 % NW) {  // W1 = lower[dL/do U^T]
+    if (w == 2 % NWH) {  // W1 = lower[dL/do U^T]
       f32x4 acc = {};
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const int j = 4 * s4 + g4;
-        acc = mfma(sm.dout[c16][j], sm.u[c16][j], acc);
+        acc = mfma(ts.dout[c16][j], ts.u[c16][j], acc);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.w1[4 * g4 + r][c16] = c16 <= 4 * g4 + r ? acc[r] : 0.0f;
+      for (int r = 0; r < 4; ++r) ts.w1[4 * g4 + r][c16] = c16 <= 4 * g4 + r ? acc[r] : 0.0f;
     }
   };
 
@@ -628,9 +634,12 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // wavefronts, and the totals come back through a slot of the wavefront's
   // own (no further barrier).  The partials are double-buffered: one barrier
   // per call.
-  static_assert(NW == 8 || NW == 4 || NW == 2, "wavefronts per workgroup");
+  static_assert(NWH == 8 || NWH == 4 || NWH == 2, "wavefronts per tile");
   int rb = 0;
   auto key_sum8 = [&](float x[8]) {
+    const int tid = opaque(threadIdx.x) & (NTH - 1), lane = tid & 63, w = tid >> 6, cg = tid & 3,
+              c4 = 4 * cg;
+    BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       x[i] = ror_add<4>(x[i]);
@@ -639,23 +648,23 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       x[i] = xor_sum<32>(x[i]);
     }
     if (lane < 4) {
-      *reinterpret_cast<float4*>(&sm.red[rb][w][0][c4]) = float4{x[0], x[1], x[2], x[3]};
-      *reinterpret_cast<float4*>(&sm.red[rb][w][1][c4]) = float4{x[4], x[5], x[6], x[7]};
+      *reinterpret_cast<float4*>(&ts.red[rb][w][0][c4]) = float4{x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<float4*>(&ts.red[rb][w][1][c4]) = float4{x[4], x[5], x[6], x[7]};
     }
     __syncthreads();
     const int grp = lane >> 3;  // pair group: quantity grp / 4, columns 4 (grp % 4) ..
     float4 t = *reinterpret_cast<const float4*>(
-        &sm.red[rb][lane & (NW - 1)][grp >> 2][4 * (grp & 3)]);
-    if (NW < 8 && (lane & 7) >= NW) t = float4{0.0f, 0.0f, 0.0f, 0.0f};
+        &ts.red[rb][lane & (NWH - 1)][grp >> 2][4 * (grp & 3)]);
+    if (NWH < 8 && (lane & 7) >= NWH) t = float4{0.0f, 0.0f, 0.0f, 0.0f};
     t.x = oct_sum(t.x);
     t.y = oct_sum(t.y);
     t.z = oct_sum(t.z);
     t.w = oct_sum(t.w);
-    if ((lane & 7) == 0) *reinterpret_cast<float4*>(&sm.fin[w][grp][0]) = t;
+    if ((lane & 7) == 0) *reinterpret_cast<float4*>(&ts.fin[w][grp][0]) = t;
     // the slot is read back by the same wavefront: LDS accesses of one
     // wavefront complete in order
-    const float4 a = *reinterpret_cast<const float4*>(&sm.fin[w][cg][0]);
-    const float4 z = *reinterpret_cast<const float4*>(&sm.fin[w][4 + cg][0]);
+    const float4 a = *reinterpret_cast<const float4*>(&ts.fin[w][cg][0]);
+    const float4 z = *reinterpret_cast<const float4*>(&ts.fin[w][4 + cg][0]);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = z.x; x[5] = z.y; x[6] = z.z; x[7] = z.w;
     rb ^= 1;
@@ -676,20 +685,22 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
   // in both orientations so that either serves as an A operand whose inner
   // index in step r is 4 g4 + r (the lane's own accumulator entry r).
   auto chunk_phase = [&](int seg) {
-    const int tid = opaque(threadIdx.x), lane = tid & 63, w = tid >> 6;
+    BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
+    const int v0 = (vt * kTiles + opaque(threadIdx.x) / NTH) * kBV;
+    const int tid = opaque(threadIdx.x) & (NTH - 1), lane = tid & 63, w = tid >> 6;
     const int c16 = lane & 15, g4 = lane >> 4, kb = 16 * w, key = kb + c16;
     auto mfma = [](float a, float b, f32x4 c) {
       return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     };
     // W1 and W2 (masked) in both orientations: w?t[r] = W?[c16][4 g4 + r],
     // w?d[r] = W?[4 g4 + r][c16]
-    const float4 w1t = *reinterpret_cast<const float4*>(&sm.w1[c16][4 * g4]);
-    const float4 w2t = *reinterpret_cast<const float4*>(&sm.w2[c16][4 * g4]);
+    const float4 w1t = *reinterpret_cast<const float4*>(&ts.w1[c16][4 * g4]);
+    const float4 w2t = *reinterpret_cast<const float4*>(&ts.w2[c16][4 * g4]);
     float w1d[4], w2d[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      w1d[r] = sm.w1[4 * g4 + r][c16];
-      w2d[r] = sm.w2[4 * g4 + r][c16];
+      w1d[r] = ts.w1[4 * g4 + r][c16];
+      w2d[r] = ts.w2[4 * g4 + r][c16];
     }
     const float w1tv[4] = {w1t.x, w1t.y, w1t.z, w1t.w}, w2tv[4] = {w2t.x, w2t.y, w2t.z, w2t.w};
     f32x4 dQ = {}, dKt = {}, dKs = {}, dKh = {}, dSn = {};
@@ -697,8 +708,8 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int c = 4 * s4 + g4;
-      const float u_ = sm.u[c16][c], d_ = sm.dout[c16][c], r_ = bc * sm.a[c16][c];
-      const float s0v = sm.s0[key][c], dsv = sm.dsin[key][c];
+      const float u_ = ts.u[c16][c], d_ = ts.dout[c16][c], r_ = bc * ts.a[c16][c];
+      const float s0v = ts.s0[key][c], dsv = ts.dsin[key][c];
       dQ = mfma(d_, s0v, dQ);
       dKt = mfma(-r_, s0v, dKt);
       dKs = mfma(u_, dsv, dKs);
@@ -718,15 +729,15 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     for (int s4 = 0; s4 < 4; ++s4) {
       const int t = 4 * s4 + g4;
       const float e = sm.E[t][key];
-      dSn = mfma(sm.q[t][key] * e, sm.dout[t][c16], dSn);
-      dSn = mfma(-sm.k[t][key] * e, sm.beta[t] * sm.a[t][c16], dSn);
+      dSn = mfma(sm.q[t][key] * e, ts.dout[t][c16], dSn);
+      dSn = mfma(-sm.k[t][key] * e, sm.beta[t] * ts.a[t][c16], dSn);
     }
     // gamma's direct term for this lane's key: sum over the columns of
     // dS_in S_0 (four columns per lane, then the four row groups)
     const float gam = sm.E[kSeg - 1][key];
     float gd = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gd += sm.dsin[key][4 * g4 + i] * sm.s0[key][4 * g4 + i];
+    for (int i = 0; i < 4; ++i) gd += ts.dsin[key][4 * g4 + i] * ts.s0[key][4 * g4 + i];
     float dGl[4], dql[4], dkl[4], ksks = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -745,7 +756,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int kr = kb + 4 * g4 + r;
-      sm.dsin[kr][c16] = dSn[r] + sm.E[kSeg - 1][kr] * sm.dsin[kr][c16];
+      ts.dsin[kr][c16] = dSn[r] + sm.E[kSeg - 1][kr] * ts.dsin[kr][c16];
     }
     // dg: the reverse cumulative sum over the tokens; gamma's terms belong to
     // the last token (t = 15: row group 3, entry 3)
@@ -765,16 +776,21 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       cq[r] = dql[r];
       ckk[r] = dkl[r];
       cgg[r] = dGl[r] + later;
-      // a per-head gate sums dg over the keys in the flush: through E (this
-      // wavefront's keys only, every read of E above)
-      if (PH) sm.E[4 * g4 + r][key] = cgg[r];
+    }
+    if (opaque(threadIdx.x) >= NTH) {  // tile 1: to the wavefront of tile 0 with the same keys
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sm.xch[w][0][r][lane] = cq[r];
+        sm.xch[w][1][r][lane] = ckk[r];
+        sm.xch[w][2][r][lane] = cgg[r];
+      }
     }
     if (w == 0) {  // dv = beta a, and the tile's part of dbeta_t = a_t . r_t
       const int t = lane >> 2, c = 4 * (lane & 3);
       const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
       const long rw = (b * T_ + t0 + t) * HV + hv;
-      const float4 a4 = *reinterpret_cast<const float4*>(&sm.a[t][c]);
-      const float4 r4 = *reinterpret_cast<const float4*>(&sm.r[t][c]);
+      const float4 a4 = *reinterpret_cast<const float4*>(&ts.a[t][c]);
+      const float4 r4 = *reinterpret_cast<const float4*>(&ts.r[t][c]);
       const float bt = sm.beta[t];
       const float arv = quad_sum(a4.x * r4.x + a4.y * r4.y + a4.z * r4.z + a4.w * r4.w);
       if (t < n) {
@@ -791,7 +807,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
 #pragma unroll
     for (int i = 0; i < 4; ++i) dS[i] = p.dST ? p.dST[o + i] : 0.0f;
   }
-  *reinterpret_cast<float4*>(&sm.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
+  *reinterpret_cast<float4*>(&ts.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
   SegLoads<T, NVD, NOPS> L;
   if (NC > 0) issue(NC - 1, L);
   for (int seg = NC - 1; seg >= 0; --seg) {
@@ -808,8 +824,10 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     // S_t = Sd_t + k_t U_t^T with Sd_t = alpha_t S_{t-1}, from the
     // checkpoint; Sd_t is also handed back
     auto advance = [&](int tt, float S[4], float sd[4]) {
+      const int tid = opaque(threadIdx.x) & (NTH - 1), kap = tid >> 2, c4 = 4 * (tid & 3);
+      BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
       const float a = sm.al[tt][kap], kv = sm.k[tt][kap];
-      const float4 u = *reinterpret_cast<const float4*>(&sm.u[tt][c4]);
+      const float4 u = *reinterpret_cast<const float4*>(&ts.u[tt][c4]);
       const float uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -825,9 +843,12 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     //   dk = beta (sum_j dS r_j - sum_j Sd a_j)
     //   dg = sum_j (dS - k beta a_j) Sd,   dS <- alpha (dS - k beta a)
     auto reverse = [&](int tt, const float sd[4]) {
+      const int tid = opaque(threadIdx.x) & (NTH - 1), kap = tid >> 2, cg = tid & 3, c4 = 4 * cg;
+      BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
+      const int v0 = (vt * kTiles + opaque(threadIdx.x) / NTH) * kBV;
       const float a_ = sm.al[tt][kap], kv = sm.k[tt][kap], qv = sm.q[tt][kap];
       const float bt = sm.beta[tt];
-      const float4 d4 = *reinterpret_cast<const float4*>(&sm.dout[tt][c4]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&ts.dout[tt][c4]);
       const float d[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[i] += qv * d[i];  // the read o_t = s S_t^T q_t
@@ -838,7 +859,7 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
         x[4 + i] = kv * sd[i];
       }
       key_sum8(x);  // a_t = dS^T k_t and the prediction Sd^T k_t, per column
-      const float4 v4 = *reinterpret_cast<const float4*>(&sm.v[tt][c4]);
+      const float4 v4 = *reinterpret_cast<const float4*>(&ts.v[tt][c4]);
       const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
       float rd = 0.0f, ar = 0.0f;
 #pragma unroll
@@ -864,10 +885,10 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       s1 = quad_sum(s1);
       s2 = quad_sum(s2);
       s3 = quad_sum(s3);
-      if (cg == 0) {
-        sm.dq[tt][kap] = scale * (s1 + kb * rd);
-        sm.dk[tt][kap] = bt * s2;
-        sm.E[tt][kap] = s3;  // dg; E is not read again in this segment
+      if (cg == 0) {  // both tiles add into the zeroed results: 0 + x + y, exact in either order
+        atomicAdd(&sm.fb.dq[tt][kap], scale * (s1 + kb * rd));
+        atomicAdd(&sm.fb.dk[tt][kap], bt * s2);
+        atomicAdd(&sm.fb.dg[tt][kap], s3);
       }
       if (kap == 0) {  // dv and the tile's part of dbeta, straight to the outputs
         const long rw = (b * T_ + seg * kSeg + tt) * HV + hv;
@@ -881,10 +902,12 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     // reverse.
     constexpr int kPart = 4;
     auto halves = [&]() {
+      const int tid = opaque(threadIdx.x) & (NTH - 1), kap = tid >> 2, c4 = 4 * (tid & 3);
+      BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
 #pragma unroll
       for (int part = kSeg / kPart - 1; part >= 0; --part) {
         const int base = part * kPart;
-        const float4 ck = *reinterpret_cast<const float4*>(&sm.s0[kap][c4]);
+        const float4 ck = *reinterpret_cast<const float4*>(&ts.s0[kap][c4]);
         float S[4] = {ck.x, ck.y, ck.z, ck.w};
         float sd[kPart][4];
         for (int tt = 0; tt < base && tt < n; ++tt) advance(tt, S, sd[0]);
@@ -897,20 +920,32 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
       }
     };
     if (fallback) {  // dL/dS in registers for the per-token pass, in the LDS tile between segments
+      const int gtid = opaque(threadIdx.x), tid = gtid & (NTH - 1), kap = tid >> 2, c4 = 4 * (tid & 3);
+      BwdTile<K>& ts = sm.tile[gtid / NTH];
       {  // the per-token pass takes the retain factors themselves (1 past the end)
+        const int gc0 = PH ? 0 : kap;  // this thread's gate element
+        const float bias = gate_bias_pre<GK>(
+            (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * gK + gc0] : 0.0f, gc);
         const float* gb = p.g_raw + ((b * T_ + seg * kSeg) * HV + hv) * gK;
+        if (gtid < NTH) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tt = c4 + i;
-          const float g = gb[min(tt, n - 1) * HV * gK + gc0];
-          sm.al[tt][kap] = tt < n ? gate_alpha_pre<GK>(g, bias, gc) : 1.0f;
+          for (int i = 0; i < 4; ++i) {
+            const int tt = c4 + i;
+            const float g = gb[min(tt, n - 1) * HV * gK + gc0];
+            sm.al[tt][kap] = tt < n ? gate_alpha_pre<GK>(g, bias, gc) : 1.0f;
+          }
+        }
+        for (int e = gtid; e < kSeg * K; e += NT) {
+          (&sm.fb.dq[0][0])[e] = 0.0f;
+          (&sm.fb.dk[0][0])[e] = 0.0f;
+          (&sm.fb.dg[0][0])[e] = 0.0f;
         }
         __syncthreads();
       }
-      const float4 d0 = *reinterpret_cast<const float4*>(&sm.dsin[kap][c4]);
+      const float4 d0 = *reinterpret_cast<const float4*>(&ts.dsin[kap][c4]);
       dS[0] = d0.x; dS[1] = d0.y; dS[2] = d0.z; dS[3] = d0.w;
       halves();
-      *reinterpret_cast<float4*>(&sm.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
+      *reinterpret_cast<float4*>(&ts.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
     } else {
       chunk_phase(seg);
     }
@@ -922,9 +957,12 @@ __global__ __launch_bounds__(4 * K) __attribute__((amdgpu_waves_per_eu(4))) void
     flush(seg, !fallback);
   }
   __syncthreads();
-  if (p.dS0)
-    *reinterpret_cast<float4*>(p.dS0 + ((long)hd * K + kap) * V + v0 + c4) =
-        *reinterpret_cast<const float4*>(&sm.dsin[kap][c4]);
+  if (p.dS0) {  // (the thread's layout formed anew: nothing of it stays live through the loop)
+    const int g = opaque(threadIdx.x), t = g & (NTH - 1), kr = t >> 2, cc = 4 * (t & 3);
+    const int vc = (vt * kTiles + g / NTH) * kBV + cc;
+    *reinterpret_cast<float4*>(p.dS0 + ((long)hd * K + kr) * V + vc) =
+        *reinterpret_cast<const float4*>(&sm.tile[g / NTH].dsin[kr][cc]);
+  }
 }
 
 // dg -> dg_raw in place (chain rule through the gate), and the sums of the
@@ -1043,7 +1081,7 @@ static hipError_t zero(float* p, long n, hipStream_t stream) {
 
 template <int K, typename T, int GK>
 static hipError_t launch_bwd_kt(BwdParams p, hipStream_t stream) {
-  const long nblk = (long)p.B * p.HV * (K / kBV);
+  const long nblk = (long)p.B * p.HV * (K / kBV / kTiles);
   const long nseg = (long)p.B * p.HV * p.NC;
   if (nseg > 0) {
     if (p.per_head)
@@ -1057,11 +1095,11 @@ static hipError_t launch_bwd_kt(BwdParams p, hipStream_t stream) {
   }
   if (nblk > 0) {
     if (p.per_head)
-      hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK, true>), dim3((unsigned)nblk), dim3(4 * K), 0,
-                         stream, p);
+      hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK, true>), dim3((unsigned)nblk),
+                         dim3(4 * K * kTiles), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK, false>), dim3((unsigned)nblk), dim3(4 * K),
-                         0, stream, p);
+      hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK, false>), dim3((unsigned)nblk),
+                         dim3(4 * K * kTiles), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
