@@ -66,7 +66,7 @@ struct BwdParams {
   const float* dt_bias;
   const float* dout;
   const float* dST;   // dL/dS_T or null
-  const float* ckpt;  // [B, HV, NC, V, K]: the state entering each 16-token segment (column-major)
+  const float* ckpt;  // [B, HV, NC, K / 4, V, 4]: the state entering each 16-token segment, by key quads
   const float* u;     // [B, HV, NC, V / 16, 64, 4]: U = beta r of every token (MFMA accumulator order)
   float* ops;         // [B, HV, NC, 3, 64, 4]: per segment, the value-independent operands (bwd_prep_kernel)
   float* eseg;        // [B, HV, NC, 16, K]: per segment, the cumulative retain factors E
@@ -280,24 +280,30 @@ __device__ __forceinline__ int opaque(int x) {
 
 constexpr int kTiles = 2;  // value tiles per workgroup
 
+// Row stride of the tile's 16-wide arrays: 20 floats place the 16 rows of a
+// column read, and the 16 columns of a row read by 16 lanes at stride one
+// row, on distinct banks (a stride of 16 put every fourth row on the same
+// ones), and keeps each row 16-byte aligned for the float4 accesses.
+constexpr int kTS = kBV + 4;
+
 // One value tile's arrays.  Each wavefront touches only its own tile's, from
 // one base address: within the tile every offset fits a DS instruction's
 // 64 KiB immediate range.
 template <int K>
 struct alignas(16) BwdTile {
-  float u[kSeg][kBV];  // U = beta r from the forward (0 past the end)
-  float v[kSeg][kBV];
-  float dout[kSeg][kBV];
-  float a[kSeg][kBV];    // a_t = G_t^T k_t
-  float r[kSeg][kBV];    // r_t = v_t - Sd_t^T k_t
-  float w1[kSeg][kSeg];  // W1[t][m] = (dL/do U^T)[t][m] for m <= t, else 0
-  float w2[kSeg][kSeg];  // W2[t][m] = (dR U^T)[t][m] for m < t, else 0
-  float s0[K][kBV];      // the tile of the checkpoint S_0
-  float dsin[K][kBV];    // the tile of dL/dS entering the segment's reverse pass
+  float u[kSeg][kTS];  // U = beta r from the forward (0 past the end)
+  float v[kSeg][kTS];
+  float dout[kSeg][kTS];
+  float a[kSeg][kTS];    // a_t = G_t^T k_t
+  float r[kSeg][kTS];    // r_t = v_t - Sd_t^T k_t
+  float w1[kSeg][kTS];   // W1[t][m] = (dL/do U^T)[t][m] for m <= t, else 0
+  float w2[kSeg][kTS];   // W2[t][m] = (dR U^T)[t][m] for m < t, else 0
+  float s0[K][kTS];      // the tile of the checkpoint S_0
+  float dsin[K][kTS];    // the tile of dL/dS entering the segment's reverse pass
   // chunked pass: partial products over the four quarters of the keys,
   // (k E) S_0 in 0..3 and (k Suf) dS_in in 4..7; written after the staging,
   // read before the next one
-  float part[8][kSeg][kBV];
+  float part[8][kSeg][kTS];
   // per-token pass: its key sums across the wavefronts
   float red[2][K / 16][2][kBV];
   float fin[K / 16][8][4];
@@ -330,7 +336,7 @@ struct alignas(16) BwdSmem {
 
 // One segment's inputs in flight: this thread's share of E, k and q (token
 // tid / (K / 4), four consecutive keys), of v, dL/do, U and beta, of the
-// prep's operands, its own row of the checkpoint, and the range flag.
+// prep's operands, four keys of one column of the checkpoint, and the range flag.
 template <typename T, int NVD, int NOPS>
 struct SegLoads {
   float4 e;
@@ -401,7 +407,8 @@ bwd_segment_kernel(BwdParams p) {
     }
     L.u = *reinterpret_cast<const float4*>(p.u + (sg * NVT + v0 / kBV) * 256 + 4 * (tid & 63));
     L.beta = p.beta[row0 * HV + hv + min(tid & 15, n - 1) * HV];
-    L.ckpt = *reinterpret_cast<const float4*>(p.ckpt + (sg * V + v0 + trow) * K + tcol);
+    // keys 4 (tid / 16) .. + 3 of column v0 + tid % 16: 16 lanes read 256 contiguous bytes
+    L.ckpt = *reinterpret_cast<const float4*>(p.ckpt + sg * K * V + ((tid >> 4) * V + v0 + (tid & 15)) * 4);
     const float4* ob = reinterpret_cast<const float4*>(p.ops + ((long)hd * NC + seg) * (3 * 64 * 4));
 #pragma unroll
     for (int i = 0; i < NOPS; ++i) L.ops[i] = ob[min(gtid + i * NT, 3 * 64 - 1)];
@@ -443,10 +450,13 @@ bwd_segment_kernel(BwdParams p) {
       ts.u[r0 + 3][j] = r0 + 3 < n ? L.u.w : 0.0f;
     }
     if (gtid < kSeg) sm.beta[gtid] = gtid < n ? L.beta : 0.0f;
-    ts.s0[tcol][trow] = L.ckpt.x;  // column trow of the tile, keys tcol .. tcol + 3
-    ts.s0[tcol + 1][trow] = L.ckpt.y;
-    ts.s0[tcol + 2][trow] = L.ckpt.z;
-    ts.s0[tcol + 3][trow] = L.ckpt.w;
+    {  // column tid % 16 of the tile, keys 4 (tid / 16) .. + 3
+      const int kr = 4 * (tid >> 4), cc = tid & 15;
+      ts.s0[kr][cc] = L.ckpt.x;
+      ts.s0[kr + 1][cc] = L.ckpt.y;
+      ts.s0[kr + 2][cc] = L.ckpt.z;
+      ts.s0[kr + 3][cc] = L.ckpt.w;
+    }
 #pragma unroll
     for (int i = 0; i < NOPS; ++i)
       if (gtid + i * NT < 3 * 64) (&sm.ops[0][0])[gtid + i * NT] = L.ops[i];
@@ -725,19 +735,21 @@ bwd_segment_kernel(BwdParams p) {
       dKh = mfma(-w2d[r], kt, dKh);
     }
     // dS_0 for this wavefront's keys: rows key 16 w + 4 g4 + r, column c16
+    // (the inner index of step s4 is token 4 g4 + s4: the 16 lanes of a
+    // row group read one row of dL/do and a)
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const int t = 4 * s4 + g4;
+      const int t = 4 * g4 + s4;
       const float e = sm.E[t][key];
       dSn = mfma(sm.q[t][key] * e, ts.dout[t][c16], dSn);
       dSn = mfma(-sm.k[t][key] * e, sm.beta[t] * ts.a[t][c16], dSn);
     }
     // gamma's direct term for this lane's key: sum over the columns of
-    // dS_in S_0 (four columns per lane, then the four row groups)
+    // dS_in S_0 (columns g4 + 4 i per lane, then the four row groups)
     const float gam = sm.E[kSeg - 1][key];
     float gd = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gd += ts.dsin[key][4 * g4 + i] * ts.s0[key][4 * g4 + i];
+    for (int i = 0; i < 4; ++i) gd += ts.dsin[key][g4 + 4 * i] * ts.s0[key][g4 + 4 * i];
     float dGl[4], dql[4], dkl[4], ksks = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

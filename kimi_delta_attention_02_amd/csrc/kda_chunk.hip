@@ -72,7 +72,8 @@ struct ChunkParams {
   float* o;
   float* S_out;
   // checkpoint mode (the backward's forward pass; no o): the state entering
-  // every 16-token block, [B, HV, NC, V, K] (each state column-major), and
+  // every 16-token block, [B, HV, NC, K / 4, V, 4] (each state by key quads:
+  // keys 4 i .. 4 i + 3 of every column together), and
   // U = beta r of every block, [B, HV, NC, V / 16, 64, 4] (per 16-wide column
   // block, lane l of 64 holding rows 4 (l / 16) .. + 3 of column l % 16)
   float* ckpt;
@@ -880,14 +881,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
         typename SM::Chain& C = sm.chain[cb];
         const int t0 = tc * kTok;
         // checkpoint mode: this block's entry state (column vcol, keys
-        // 16 kb + 4 (lane / 16) .. + 3) and where its U goes
+        // 16 kb + 4 (lane / 16) .. + 3), stored by key quads ([K / 4][V][4]:
+        // the 16 columns of a row group are 256 contiguous bytes), and where
+        // its U goes
         float* ublk = nullptr;
         if constexpr (CK) {
           const long blk = (long)hd * NT + tc;
-          float* ck = p.ckpt + (blk * V + vcol) * K + 4 * (lane >> 4);
+          float* ck = p.ckpt + blk * K * V + ((lane >> 4) * V + vcol) * 4;
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            *reinterpret_cast<float4*>(ck + 16 * kb) =
+            *reinterpret_cast<float4*>(ck + 16 * kb * V) =
                 float4{sacc[kb][0], sacc[kb][1], sacc[kb][2], sacc[kb][3]};
           ublk = p.u_out + ((blk * (V / 16) + vcol / 16) * 64 + lane) * 4;
         }
