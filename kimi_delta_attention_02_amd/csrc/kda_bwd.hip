@@ -694,25 +694,31 @@ bwd_segment_kernel(BwdParams p) {
   // the MFMA accumulators hold rows 4 g4 + r of column c16.  W1 and W2 are formed
   // in both orientations so that either serves as an A operand whose inner
   // index in step r is 4 g4 + r (the lane's own accumulator entry r).
-  auto chunk_phase = [&](int seg) {
-    BwdTile<K>& ts = sm.tile[opaque(threadIdx.x) / NTH];
-    const int v0 = (vt * kTiles + opaque(threadIdx.x) / NTH) * kBV;
+  auto chunk_phase = [&](int seg, auto FIRST) {
+    constexpr bool kFirst = decltype(FIRST)::value;  // the workgroup's first value tile
+    static_assert(kTiles == 2, "the products with W1 and W2 are split between two tiles");
+    BwdTile<K>& ts = sm.tile[kFirst ? 0 : 1];
+    const int v0 = (vt * kTiles + (kFirst ? 0 : 1)) * kBV;
     const int tid = opaque(threadIdx.x) & (NTH - 1), lane = tid & 63, w = tid >> 6;
     const int c16 = lane & 15, g4 = lane >> 4, kb = 16 * w, key = kb + c16;
     auto mfma = [](float a, float b, f32x4 c) {
       return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     };
-    // W1 and W2 (masked) in both orientations: w?t[r] = W?[c16][4 g4 + r],
-    // w?d[r] = W?[4 g4 + r][c16]
-    const float4 w1t = *reinterpret_cast<const float4*>(&ts.w1[c16][4 * g4]);
-    const float4 w2t = *reinterpret_cast<const float4*>(&ts.w2[c16][4 * g4]);
-    float w1d[4], w2d[4];
+    // W1 and W2 enter the gradients linearly, so their products need them
+    // only summed over the two tiles, and each runs in one tile: the first
+    // takes W1's (into dQt and dKh), the second -W2's (into dKt and dKh).
+    // W (masked) in both orientations: wt[r] = W[c16][4 g4 + r],
+    // wd[r] = W[4 g4 + r][c16].
+    const float(*wa)[kTS] = kFirst ? sm.tile[0].w1 : sm.tile[0].w2;
+    const float(*wb)[kTS] = kFirst ? sm.tile[1].w1 : sm.tile[1].w2;
+    const float4 wta = *reinterpret_cast<const float4*>(&wa[c16][4 * g4]);
+    const float4 wtb = *reinterpret_cast<const float4*>(&wb[c16][4 * g4]);
+    const float sg = kFirst ? 1.0f : -1.0f;
+    const float wt[4] = {sg * (wta.x + wtb.x), sg * (wta.y + wtb.y), sg * (wta.z + wtb.z),
+                         sg * (wta.w + wtb.w)};
+    float wd[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      w1d[r] = ts.w1[4 * g4 + r][c16];
-      w2d[r] = ts.w2[4 * g4 + r][c16];
-    }
-    const float w1tv[4] = {w1t.x, w1t.y, w1t.z, w1t.w}, w2tv[4] = {w2t.x, w2t.y, w2t.z, w2t.w};
+    for (int r = 0; r < 4; ++r) wd[r] = sg * (wa[4 * g4 + r][c16] + wb[4 * g4 + r][c16]);
     f32x4 dQ = {}, dKt = {}, dKs = {}, dKh = {}, dSn = {};
     const float bc = sm.beta[c16];
 #pragma unroll
@@ -728,11 +734,14 @@ bwd_segment_kernel(BwdParams p) {
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g4 + r;  // this step's inner index (a token)
       const float e = sm.E[m][key], kv = sm.k[m][key];
-      const float kh = kv * __builtin_amdgcn_rcpf(e), kt = kv * e, qt = sm.q[m][key] * e;
-      dQ = mfma(w1tv[r], kh, dQ);
-      dKt = mfma(-w2tv[r], kh, dKt);
-      dKh = mfma(w1d[r], qt, dKh);
-      dKh = mfma(-w2d[r], kt, dKh);
+      const float kh = kv * __builtin_amdgcn_rcpf(e);
+      if constexpr (kFirst) {
+        dQ = mfma(wt[r], kh, dQ);
+        dKh = mfma(wd[r], sm.q[m][key] * e, dKh);
+      } else {
+        dKt = mfma(wt[r], kh, dKt);
+        dKh = mfma(wd[r], kv * e, dKh);
+      }
     }
     // dS_0 for this wavefront's keys: rows key 16 w + 4 g4 + r, column c16
     // (the inner index of step s4 is token 4 g4 + s4: the 16 lanes of a
@@ -789,7 +798,7 @@ bwd_segment_kernel(BwdParams p) {
       ckk[r] = dkl[r];
       cgg[r] = dGl[r] + later;
     }
-    if (opaque(threadIdx.x) >= NTH) {  // tile 1: to the wavefront of tile 0 with the same keys
+    if constexpr (!kFirst) {  // to the wavefront of the first tile with the same keys
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         sm.xch[w][0][r][lane] = cq[r];
@@ -958,8 +967,10 @@ bwd_segment_kernel(BwdParams p) {
       dS[0] = d0.x; dS[1] = d0.y; dS[2] = d0.z; dS[3] = d0.w;
       halves();
       *reinterpret_cast<float4*>(&ts.dsin[kap][c4]) = float4{dS[0], dS[1], dS[2], dS[3]};
+    } else if (__builtin_amdgcn_readfirstlane(threadIdx.x) < NTH) {  // (uniform per wavefront)
+      chunk_phase(seg, std::true_type{});
     } else {
-      chunk_phase(seg);
+      chunk_phase(seg, std::false_type{});
     }
     __syncthreads();  // the segment's results are in LDS; its inputs are no longer read
     // the next segment's loads go out before the atomics, so that waiting for
