@@ -835,6 +835,9 @@ bwd_segment_kernel(BwdParams p) {
     const int n = min(kSeg, T_ - seg * kSeg);
     const bool bad = stage(L, n);
     const bool fallback = bad;  // uniform: one flag per segment
+    // the next segment's loads go out at once, so that the whole segment
+    // hides their latency; unconditional (the last re-reads segment 0)
+    issue(max(seg - 1, 0), L);
     __syncthreads();
     if (!fallback) {
       products();
@@ -973,10 +976,6 @@ bwd_segment_kernel(BwdParams p) {
       chunk_phase(seg, std::false_type{});
     }
     __syncthreads();  // the segment's results are in LDS; its inputs are no longer read
-    // the next segment's loads go out before the atomics, so that waiting for
-    // them does not wait for the atomics; unconditional (the last re-reads
-    // segment 0) so that no earlier load stays live through the segment
-    issue(max(seg - 1, 0), L);
     flush(seg, !fallback);
   }
   __syncthreads();
