@@ -50,6 +50,8 @@
 // atomics into zeroed outputs, once per segment, so their last bits depend on
 // the order the tiles finish in.  Arithmetic is fp32 throughout (bf16 inputs
 // widened exactly).
+#include <algorithm>
+#include <cstdint>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -87,9 +89,23 @@ struct BwdParams {
 constexpr int kSeg = 16;  // tokens per segment (the checkpoint spacing)
 constexpr int kBV = 16;   // value columns per workgroup
 
-__global__ void bwd_zero_kernel(float* p, long n) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
+// The buffers the backward accumulates into, zeroed by one launch.
+constexpr int kZeroBufs = 6;
+struct ZeroList {
+  float* p[kZeroBufs];  // NULL: skipped
+  long n[kZeroBufs];
+};
+__global__ void bwd_zero_kernel(ZeroList z) {
+  const long stride = (long)gridDim.x * blockDim.x, t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int j = 0; j < kZeroBufs; ++j) {
+    float* p = z.p[j];
+    const long n = z.n[j];
+    if (!p) continue;
+    // 16-byte stores where the buffer is 16-byte aligned, its tail element by element
+    const long n4 = (reinterpret_cast<uintptr_t>(p) & 15) == 0 ? n / 4 : 0;
+    for (long i = t; i < n4; i += stride) reinterpret_cast<float4*>(p)[i] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (long i = 4 * n4 + t; i < n; i += stride) p[i] = 0.0f;
+  }
 }
 
 // Per (sequence, value head, segment), the matrices of the segment pass that
@@ -997,24 +1013,36 @@ __global__ void bwd_gate_kernel(BwdParams p, int K, long rows) {
   const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
   const float bias = (p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv * K + c] : 0.0f;
   float sb = 0.0f, sa = 0.0f;
-  for (long r = r0; r < r1; ++r) {
-    const long i = (r * p.HV + hv) * K + c;
-    const float dg = p.dg[i], x = p.g_raw[i] + bias;
-    float dx = dg, da = 0.0f;
-    if constexpr (GK == KDA_GATE_SAFE) {  // g = L sigma(rate x)
-      const float z = rate * x;
-      const float sg = __builtin_amdgcn_rcpf(1.0f + exp_f(-z));
-      const float d = p.lower_bound * sg * (1.0f - sg);
-      dx = dg * d * rate;
-      da = dg * d * z;
-    } else if constexpr (GK == KDA_GATE_STANDARD) {  // g = -rate softplus(x)
-      const float sg = __builtin_amdgcn_rcpf(1.0f + exp_f(-x));
-      dx = -dg * rate * sg;
-      da = -dg * rate * softplus_f(x);
+  constexpr int kRB = 8;  // rows whose loads are in flight together
+  for (long rb = r0; rb < r1; rb += kRB) {
+    float dgv[kRB], xv[kRB];
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) {  // (rows past the block re-read its last one)
+      const long i = ((rb + j < r1 ? rb + j : r1 - 1) * p.HV + hv) * K + c;
+      dgv[j] = p.dg[i];
+      xv[j] = p.g_raw[i];
     }
-    p.dg[i] = dx;
-    sb += dx;
-    sa += da;
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) {
+      if (rb + j >= r1) break;
+      const long i = ((rb + j) * p.HV + hv) * K + c;
+      const float dg = dgv[j], x = xv[j] + bias;
+      float dx = dg, da = 0.0f;
+      if constexpr (GK == KDA_GATE_SAFE) {  // g = L sigma(rate x)
+        const float z = rate * x;
+        const float sg = __builtin_amdgcn_rcpf(1.0f + exp_f(-z));
+        const float d = p.lower_bound * sg * (1.0f - sg);
+        dx = dg * d * rate;
+        da = dg * d * z;
+      } else if constexpr (GK == KDA_GATE_STANDARD) {  // g = -rate softplus(x)
+        const float sg = __builtin_amdgcn_rcpf(1.0f + exp_f(-x));
+        dx = -dg * rate * sg;
+        da = -dg * rate * softplus_f(x);
+      }
+      p.dg[i] = dx;
+      sb += dx;
+      sa += da;
+    }
   }
   if (GK == KDA_GATE_NONE) return;  // neither dt_bias nor A_log enters this gate
   if (p.ddt_bias) atomicAdd(p.ddt_bias + hv * K + c, sb);
@@ -1095,9 +1123,13 @@ size_t bwd_workspace_bytes(int B, int T, int HV, int K, int V) {
          prep_bytes(segs, K);
 }
 
-static hipError_t zero(float* p, long n, hipStream_t stream) {
-  if (!p || n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+static hipError_t zero(const ZeroList& z, hipStream_t stream) {
+  long total = 0;
+  for (int j = 0; j < kZeroBufs; ++j) total += z.p[j] ? z.n[j] : 0;
+  if (total == 0) return hipSuccess;
+  // enough 256-thread workgroups for a few 16-byte stores each, at most 8 per CU
+  const long blocks = std::min<long>(2048, (total / 4 + 255) / 256 + 1);
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, z);
   return hipGetLastError();
 }
 
@@ -1154,11 +1186,9 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
   hipError_t e;
   const int gK = per_head ? 1 : K;  // gate values per (token, value head)
   const long nq = (long)B * T * H * K, ng = (long)B * T * HV * gK;
-  if ((e = zero(dq, nq, stream)) != hipSuccess || (e = zero(dk, nq, stream)) != hipSuccess ||
-      (e = zero(dbeta, (long)B * T * HV, stream)) != hipSuccess ||
-      (e = zero(dg_raw, ng, stream)) != hipSuccess || (e = zero(dA_log, HV, stream)) != hipSuccess ||
-      (e = zero(ddt_bias, (long)HV * gK, stream)) != hipSuccess)
-    return e;
+  const ZeroList zl{{dq, dk, dbeta, dg_raw, dA_log, ddt_bias},
+                    {nq, nq, (long)B * T * HV, ng, (long)HV, (long)HV * gK}};
+  if ((e = zero(zl, stream)) != hipSuccess) return e;
   if (T > 0) {
     // the forward in checkpoint mode: every segment's entry state and U, no o
     e = launch_chunk_ckpt(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, per_head, lower_bound, S0,
