@@ -19,16 +19,16 @@
 // sequence for the last two), and under GVA sums of dq, dk over the value
 // heads that share a query/key head.
 //
-// Schedule, four launches after the zero fills:
+// Schedule, three launches after the zero fill:
 //  1. the fused chunk kernel in checkpoint mode (kda_chunk.hip) writes the
 //     state entering every 16-token segment and U_t = beta_t r_t of every
-//     token, on its fp32 path whatever the input type;
-//  2. bwd_prep_kernel forms, once per (sequence, value head, segment), the
-//     matrices below that do not depend on the value tile, and E;
-//  3. bwd_segment_kernel: one workgroup per (sequence, value head, 16-wide
+//     token, on its fp32 path whatever the input type, and once per
+//     (sequence, value head, segment) E and the matrices below that do not
+//     depend on the value tile;
+//  2. bwd_segment_kernel: one workgroup per (sequence, value head, 16-wide
 //     value tile) walks the segments from the last, carrying dL/dS of its
 //     tile in LDS;
-//  4. the gate kernel applies the gate's chain rule and sums dt_bias and
+//  3. the gate kernel applies the gate's chain rule and sums dt_bias and
 //     A_log over the sequences.
 //
 // Inside a segment the reverse recurrence of dL/dS is the adjoint of the
@@ -70,9 +70,9 @@ struct BwdParams {
   const float* dST;   // dL/dS_T or null
   const float* ckpt;  // [B, HV, NC, K / 4, V, 4]: the state entering each 16-token segment, by key quads
   const float* u;     // [B, HV, NC, V / 16, 64, 4]: U = beta r of every token (MFMA accumulator order)
-  float* ops;         // [B, HV, NC, 3, 64, 4]: per segment, the value-independent operands (bwd_prep_kernel)
+  float* ops;         // [B, HV, NC, 3, 64, 4]: per segment, the value-independent operands (the checkpoint forward)
   float* eseg;        // [B, HV, NC, 16, K]: per segment, the cumulative retain factors E
-  int* segbad;        // [B, HV, NC]: 1 where some E leaves [2^-100, 2^100] (or is NaN)
+  int* segbad;        // [B, HV, NC]: nonzero where the forward ran the segment token by token
   float* dq;
   float* dk;
   float* dv;
@@ -106,157 +106,6 @@ __global__ void bwd_zero_kernel(ZeroList z) {
     for (long i = t; i < n4; i += stride) reinterpret_cast<float4*>(p)[i] = float4{0.0f, 0.0f, 0.0f, 0.0f};
     for (long i = 4 * n4 + t; i < n; i += stride) p[i] = 0.0f;
   }
-}
-
-// Per (sequence, value head, segment), the matrices of the segment pass that
-// do not depend on the value tile, formed once instead of in each tile's
-// workgroup.  With E the cumulative retain factors from the segment start,
-// g1 = (k / E)(k E)^T, g2 = (k / E)(s q E)^T (sums over the keys) and
-// R = (I + L^T diag(beta))^{-1}, L[t][m] = g1[m][t] for m < t, lane
-// (c, g) = (l % 16, l / 16) of the segment's three 64 x 4 blocks holds, in
-// entry r:
-//   0: g1[4 g + r][c] if 4 g + r < c, else 0    (L as an MFMA A operand)
-//   1: g2[c][4 g + r] if 4 g + r >= c, else 0   (the upper part of g2, likewise)
-//   2: R[c][4 g + r]                            (R^T as an MFMA B operand)
-// for fp32 MFMA 16x16x4 steps whose inner index in step r is 4 g + r.  One
-// wavefront per segment.  Its g_raw, k and q rows go to LDS with coalesced
-// 16-byte loads; then lane (t, g) forms, key by key, the gate of token t,
-// E by a product scan over its 16-lane row (the tokens) and the products'
-// operands, for keys 16 j + 4 g + s (any order of the keys serves, as long
-// as both operands follow it).  R comes row by row (lane c, forward
-// substitution of R (I + L^T diag(beta)) = I) with the coupling in LDS.
-// It also writes E itself (row-major, 16 x K per segment) and whether some
-// E leaves [2^-100, 2^100]; such segments are formed all the same, and the
-// segment kernel takes its per-token pass for them without reading them.
-template <int K, typename T, bool PH>
-struct PrepSmem {
-  using Raw = typename In<T>::Raw1;
-  static constexpr int GS = PH ? 4 : K + 8;  // (the per-head gate is read straight from memory)
-                                             // row stride 32 mod 64 bytes
-  static constexpr int KS = (K * (int)sizeof(Raw) + 32) / (int)sizeof(Raw);  // likewise
-  alignas(16) float g[kSeg][GS];
-  alignas(16) Raw k[kSeg][KS];
-  alignas(16) Raw q[kSeg][KS];
-  alignas(16) float4 cpl[kSeg][kSeg / 4];  // cpl[t][m] = beta_t g1[m][t] for m < t
-};
-
-template <int K, typename T, int GK, bool PH>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-  using Raw = typename In<T>::Raw1;
-  using Raw4 = typename In<T>::Raw4;
-  using S = PrepSmem<K, T, PH>;
-  __shared__ S sms[4];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  S& sm = sms[wv];
-  const long sid = (long)blockIdx.x * 4 + wv;  // (sequence, value head) * NC + segment
-  if (sid >= (long)p.B * p.HV * p.NC) return;  // no barrier below: only this wavefront's LDS
-  const int HV = p.HV, H = p.H, T_ = p.T;
-  const int seg = (int)(sid % p.NC);
-  const long hd = sid / p.NC, b = hd / HV;
-  const int hv = (int)(hd % HV), h = hv / (HV / H);
-  const int t0 = seg * kSeg, n = min(kSeg, T_ - t0);
-  const long row0 = b * T_ + t0;
-  // staging: rows past the end re-read the last (masked below)
-  constexpr int GU = PH ? 0 : kSeg * K / 4;  // float4 units of g
-  constexpr int RPU = 16 / (int)sizeof(Raw);  // elements per 16-byte unit of k or q
-  constexpr int KU = kSeg * K / RPU;
-  for (int u = lane; u < GU; u += 64) {
-    const int t = u / (K / 4), c = (u % (K / 4)) * 4;
-    *reinterpret_cast<float4*>(&sm.g[t][c]) = *reinterpret_cast<const float4*>(
-        p.g_raw + ((row0 + min(t, n - 1)) * HV + hv) * (long)K + c);
-  }
-  for (int u = lane; u < KU; u += 64) {
-    const int t = u / (K / RPU), c = (u % (K / RPU)) * RPU;
-    const long o = ((row0 + min(t, n - 1)) * H + h) * (long)K + c;
-    *reinterpret_cast<uint4*>(&sm.k[t][c]) = *reinterpret_cast<const uint4*>(static_cast<const Raw*>(p.k) + o);
-    *reinterpret_cast<uint4*>(&sm.q[t][c]) = *reinterpret_cast<const uint4*>(static_cast<const Raw*>(p.q) + o);
-  }
-  const int c16 = lane & 15, g4 = lane >> 4;
-  const bool in = c16 < n;
-  const float scale = 1.0f / __builtin_sqrtf((float)K);
-  const float rate = GK != KDA_GATE_NONE ? exp_f(p.A_log[hv]) : 1.0f;
-  const GateConsts gc = gate_consts(rate, p.lower_bound);
-  const float ghead = PH ? p.g_raw[(row0 + (in ? c16 : n - 1)) * HV + hv] : 0.0f;
-  const float bhead = PH ? gate_bias_pre<GK>((p.dt_bias && GK != KDA_GATE_NONE) ? p.dt_bias[hv] : 0.0f, gc)
-                         : 0.0f;
-  // a row-shifted product: lanes whose source lies outside the 16-lane row keep 1
-  auto shr_mul = [](float x, auto ctrl) {
-    return x * __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                             __builtin_bit_cast(int, 1.0f), __builtin_bit_cast(int, x),
-                                             decltype(ctrl)::value, 0xF, 0xF, false));
-  };
-  f32x4 g1[2] = {}, g2t[2] = {};  // two chains each
-  bool bad = false;
-  float* eo = p.eseg + (sid * kSeg + c16) * K;
-#pragma unroll 2
-  for (int j = 0; j < K / 16; ++j) {
-    const int kb = 16 * j + 4 * g4;  // this lane's four keys
-    float gv[4], kv[4], qv[4], bv[4];
-    if constexpr (!PH) {
-      const float4 g4v = *reinterpret_cast<const float4*>(&sm.g[c16][kb]);
-      gv[0] = g4v.x; gv[1] = g4v.y; gv[2] = g4v.z; gv[3] = g4v.w;
-      float4 b4 = float4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (p.dt_bias && GK != KDA_GATE_NONE) b4 = *reinterpret_cast<const float4*>(p.dt_bias + hv * K + kb);
-      bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
-    }
-    In<T>::unpack4(*reinterpret_cast<const Raw4*>(&sm.k[c16][kb]), kv);
-    In<T>::unpack4(*reinterpret_cast<const Raw4*>(&sm.q[c16][kb]), qv);
-    float ev[4];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      float e = !in ? 1.0f
-                    : PH ? gate_alpha_pre<GK>(ghead, bhead, gc)
-                         : gate_alpha_pre<GK>(gv[s4], gate_bias_pre<GK>(bv[s4], gc), gc);
-      e = shr_mul(e, std::integral_constant<int, 0x111>{});
-      e = shr_mul(e, std::integral_constant<int, 0x112>{});
-      e = shr_mul(e, std::integral_constant<int, 0x114>{});
-      e = shr_mul(e, std::integral_constant<int, 0x118>{});
-      ev[s4] = e;
-      bad |= !(e >= 0x1p-100f && e <= 0x1p100f);
-      const float k_ = in ? kv[s4] : 0.0f, q_ = in ? scale * qv[s4] : 0.0f;
-      const float kh = k_ * __builtin_amdgcn_rcpf(e), kt = k_ * e, qt = q_ * e;
-      g1[s4 & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(kh, kt, g1[s4 & 1], 0, 0, 0);
-      g2t[s4 & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qt, kh, g2t[s4 & 1], 0, 0, 0);
-    }
-    *reinterpret_cast<float4*>(eo + kb) = float4{ev[0], ev[1], ev[2], ev[3]};
-  }
-  const bool anybad = __ballot(bad) != 0;
-  if (lane == 0) p.segbad[sid] = anybad ? 1 : 0;
-  // lane (c16, g4) entry r: g1[4 g4 + r][c16] and g2t = g2^T, i.e. g2[c16][4 g4 + r]
-  const float bt = in ? p.beta[(row0 + c16) * HV + hv] : 0.0f;  // beta of token c16
-  float lop[4], mop[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = 4 * g4 + r;
-    const float a = g1[0][r] + g1[1][r], c = g2t[0][r] + g2t[1][r];
-    lop[r] = m < c16 ? a : 0.0f;
-    mop[r] = m >= c16 ? c : 0.0f;
-  }
-  sm.cpl[c16][g4] = float4{bt * lop[0], bt * lop[1], bt * lop[2], bt * lop[3]};
-  // row c16 of R: R[c][t] = [t == c] - sum_{m < t} R[c][m] T[m][t], T[m][t] =
-  // cpl[t][m] (this wavefront's LDS accesses complete in order)
-  float x[kSeg];
-#pragma unroll
-  for (int t = 0; t < kSeg; ++t) {
-    float acc = t == c16 ? 1.0f : 0.0f;
-#pragma unroll
-    for (int m4 = 0; m4 < t; m4 += 4) {
-      const float4 tv = sm.cpl[t][m4 / 4];
-      acc -= x[m4] * tv.x;
-      if (m4 + 1 < t) acc -= x[m4 + 1] * tv.y;
-      if (m4 + 2 < t) acc -= x[m4 + 2] * tv.z;
-      if (m4 + 3 < t) acc -= x[m4 + 3] * tv.w;
-    }
-    x[t] = acc;
-  }
-  float rop[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    rop[r] = g4 == 0 ? x[r] : g4 == 1 ? x[4 + r] : g4 == 2 ? x[8 + r] : x[12 + r];
-  float4* o = reinterpret_cast<float4*>(p.ops + sid * (3 * 64 * 4)) + lane;
-  o[0] = float4{lop[0], lop[1], lop[2], lop[3]};
-  o[64] = float4{mop[0], mop[1], mop[2], mop[3]};
-  o[128] = float4{rop[0], rop[1], rop[2], rop[3]};
 }
 
 // x + the value N lanes further round its 16-lane row (DPP row rotation).
@@ -329,7 +178,7 @@ template <int K>
 struct alignas(16) BwdSmem {
   static constexpr int KP = K + 4;  // row stride: the 16 rows of an MFMA operand read spread over the banks
   float beta[kSeg];
-  float4 ops[3][64];  // the segment's value-independent operands (bwd_prep_kernel)
+  float4 ops[3][64];  // the segment's value-independent operands (the checkpoint forward)
   // the segment's inputs per (token, key channel)
   float k[kSeg][KP];   // k (0 past the end)
   float q[kSeg][KP];   // s q (0 past the end)
@@ -1105,14 +954,15 @@ __global__ __launch_bounds__(256) void bwd_gate_head_kernel(BwdParams p, long ro
 hipError_t launch_chunk_ckpt(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                              const float* beta, const float* A_log, const float* dt_bias, int kind,
                              int per_head, float lower_bound, const float* S0, float* ckpt,
-                             float* u_out, int B, int T, int H, int HV, int K, hipStream_t stream);
+                             float* u_out, float* eseg, float* ops, int* segbad, int B, int T, int H,
+                             int HV, int K, hipStream_t stream);
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace: the segment checkpoints [B, HV, NC, V, K] and U
-// [B, HV, NC, V / 16, 64, 4] from the forward in checkpoint mode, then the
-// prep kernel's operands [B, HV, NC, 3, 64, 4], its E [B, HV, NC, 16, K]
-// and range flags [B, HV, NC].
+// Workspace, all written by the forward in checkpoint mode: the segment
+// checkpoints [B, HV, NC, K / 4, V, 4] and U [B, HV, NC, V / 16, 64, 4], then
+// the per-segment operands [B, HV, NC, 3, 64, 4], E [B, HV, NC, 16, K] and
+// range flags [B, HV, NC].
 static size_t prep_bytes(size_t segs, int K) {
   return align256(segs * 3 * 64 * 4 * sizeof(float)) + align256(segs * kSeg * K * sizeof(float)) +
          align256(segs * sizeof(int));
@@ -1136,17 +986,6 @@ static hipError_t zero(const ZeroList& z, hipStream_t stream) {
 template <int K, typename T, int GK>
 static hipError_t launch_bwd_kt(BwdParams p, hipStream_t stream) {
   const long nblk = (long)p.B * p.HV * (K / kBV / kTiles);
-  const long nseg = (long)p.B * p.HV * p.NC;
-  if (nseg > 0) {
-    if (p.per_head)
-      hipLaunchKernelGGL((bwd_prep_kernel<K, T, GK, true>), dim3((unsigned)((nseg + 3) / 4)),
-                         dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((bwd_prep_kernel<K, T, GK, false>), dim3((unsigned)((nseg + 3) / 4)),
-                         dim3(256), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   if (nblk > 0) {
     if (p.per_head)
       hipLaunchKernelGGL((bwd_segment_kernel<K, T, GK, true>), dim3((unsigned)nblk),
@@ -1192,7 +1031,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
   if (T > 0) {
     // the forward in checkpoint mode: every segment's entry state and U, no o
     e = launch_chunk_ckpt(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, per_head, lower_bound, S0,
-                          ckpt, u, B, T, H, HV, K, stream);
+                          ckpt, u, eseg, ops, segbad, B, T, H, HV, K, stream);
     if (e != hipSuccess) return e;
   }
   BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, u, ops, eseg, segbad, dq, dk, dv, dbeta,

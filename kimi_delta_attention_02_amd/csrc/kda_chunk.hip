@@ -78,6 +78,19 @@ struct ChunkParams {
   // block, lane l of 64 holding rows 4 (l / 16) .. + 3 of column l % 16)
   float* ckpt;
   float* u_out;
+  // checkpoint mode, also: the backward's value-independent operands of every
+  // block, written by the workgroup of the head's first value tile:
+  //   eseg   [B, HV, NC, 16, K]  E = prod_{m <= t} alpha_m from the block start
+  //                              (row-major; past the end it stays at the last token's)
+  //   ops    [B, HV, NC, 3, 64, 4]: lane (c, g) = (l % 16, l / 16), entry r, of
+  //            0: P[c][4 g + r] if 4 g + r < c, else 0, P = (k E)(k / E)^T
+  //            1: s ((q E)(k / E)^T)[4 g + r][c] if 4 g + r >= c, else 0 (A^T)
+  //            2: (I + R)^{-1}[4 g + r][c], R = diag(beta) strictly-lower[P]
+  //   segbad [B, HV, NC]  nonzero where the block runs token by token (its
+  //                        ops are then not written)
+  float* eseg;
+  float* ops;
+  int* segbad;
   int B, T, H, HV, kind;
   int G;  // value heads per XCD group (a divisor of HV / H)
   float lower_bound;
@@ -191,6 +204,9 @@ struct alignas(16) Smem {
     ChainScratch<F32> f;
   } chain[BV / 16];
   UHandoff<F32, BV / 16> uo;
+  // checkpoint mode: the unscaled coupling P of the last two blocks (masked
+  // strictly lower), handed from the inverse wave to the A wave
+  alignas(16) float pl[F32 ? 2 : 1][F32 ? kTok * kRS : 4];
 };
 
 // ------------------------------------------------------------ MFMA tiles
@@ -627,6 +643,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             ig[c] = ig[0];
           }
           if (tp == 0) *reinterpret_cast<float4*>(&B.gam[c0]) = float4{gam[0], gam[1], gam[2], gam[3]};
+          if constexpr (CK) {  // the head's first value tile hands E to the backward
+            if (v0 == 0) {
+              float* eb = p.eseg + ((long)hd * NT + it) * (kTok * K) + c0;
+  #pragma unroll
+              for (int j = 0; j < 2; ++j)
+                *reinterpret_cast<float4*>(eb + (2 * tp + j) * K) = float4{E[j][0], E[j][1], E[j][2], E[j][3]};
+            }
+          }
           float ke[2][4];
   #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -767,6 +791,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               const int i = 4 * (lane >> 4) + r;
               sm.r[i * kRS + j] = j < i ? B.beta[i] * acc[r] : 0.0f;
             }
+            if constexpr (CK) {  // P itself, for the backward's operands (the A wave writes them)
+              if (v0 == 0) {
+  #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const int i = 4 * (lane >> 4) + r;
+                  sm.pl[ti & 1][i * kRS + j] = j < i ? acc[r] : 0.0f;
+                }
+              }
+            }
             wave_lds_sync();
             // (I + R)^{-1} in fp32.  With X_d the inverse of I + R's two 8 x 8
             // diagonal blocks and N = R's lower-left 8 x 8 block,
@@ -816,6 +849,33 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
                 *reinterpret_cast<bf16x4*>(&sm.akk[ti & 1].c[row * kCat + 16 + 4 * kk]) = yl;
               }
             }
+          }
+        }
+      }
+      if constexpr (CK) {
+        // The A wave of the head's first value tile writes the backward's
+        // operands of the chain's block (its E came from the prep, P and the
+        // inverse from the inverse wave, one step earlier), and whether the
+        // block runs token by token.
+        const int tc = it - 2;
+        if (w == kAqkWave && v0 == 0 && tc >= 0 && tc < NT) {
+          const Ops& B = sm.blk[tc % 3];
+          const bool bad = (B.flag[0] | B.flag[1] | B.flag[2] | B.flag[3]) != 0;
+          const long blk = (long)hd * NT + tc;
+          if (lane == 0) p.segbad[blk] = bad ? 1 : 0;
+          if (!bad) {
+            const int c = lane & 15, g = lane >> 4;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            kprod(acc, B.qh, 0, B.ki, 0, lane);  // lane l, r: ((q E)(k / E)^T)[4 g + r][c]
+            float4* ob = reinterpret_cast<float4*>(p.ops + blk * (3 * 64 * 4)) + lane;
+            ob[0] = *reinterpret_cast<const float4*>(&sm.pl[tc & 1][c * kRS + 4 * g]);
+            float m[4];
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) m[r] = 4 * g + r >= c ? scale * acc[r] : 0.0f;
+            ob[64] = float4{m[0], m[1], m[2], m[3]};
+            const float* X = sm.akk[tc & 1].c;  // X[i][j] at i * 17 + j
+            ob[128] = float4{X[(4 * g) * 17 + c], X[(4 * g + 1) * 17 + c], X[(4 * g + 2) * 17 + c],
+                             X[(4 * g + 3) * 17 + c]};
           }
         }
       }
@@ -1049,7 +1109,7 @@ template <int K, typename T, int GK, bool GS, bool CK = false>
 static hipError_t launch_chunk_kt(const ChunkParams& p, hipStream_t stream) {
   constexpr int BV = K < 32 ? K : 32;
   constexpr int NVT = K / BV;
-  using SM = Smem<std::is_same<T, float>::value, K, BV>;
+  using SM = Smem<std::is_same<T, float>::value || CK, K, BV>;  // the kernel's own layout
   // More than half of the CU's 160 KiB of LDS per workgroup keeps one
   // workgroup per CU, so the B*HV*NVT workgroups spread over all CUs.
   size_t lds = sizeof(SM);
@@ -1070,7 +1130,8 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
                         const float* beta, const float* A_log, const float* dt_bias, int kind,
                         int per_head, float lower_bound, const float* S0, float* o, float* S_out,
                         int B, int T, int H, int HV, int K, hipStream_t stream) {
-  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, nullptr, nullptr, B, T, H, HV,
+  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, o, S_out, nullptr, nullptr, nullptr, nullptr,
+                nullptr, B, T, H, HV,
                 kind, 1, lower_bound};
   // The value heads of one query/key head share an XCD (and their q, k reads
   // its L2) when that keeps the eight XCDs evenly loaded.
@@ -1098,13 +1159,16 @@ hipError_t launch_chunk(const void* q, const void* k, const void* v, int bf16, c
 }
 
 // The forward pass of the backward: the same kernel in checkpoint mode, which
-// writes the state entering every 16-token block and U of every block (see
-// ChunkParams) instead of o; K in {32, 64, 128}.
+// writes the state entering every 16-token block, U of every block and the
+// backward's per-block operands (see ChunkParams) instead of o; K in
+// {32, 64, 128}.
 hipError_t launch_chunk_ckpt(const void* q, const void* k, const void* v, int bf16, const float* g_raw,
                              const float* beta, const float* A_log, const float* dt_bias, int kind,
                              int per_head, float lower_bound, const float* S0, float* ckpt,
-                             float* u_out, int B, int T, int H, int HV, int K, hipStream_t stream) {
-  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, nullptr, nullptr, ckpt, u_out, B, T, H, HV,
+                             float* u_out, float* eseg, float* ops, int* segbad, int B, int T, int H,
+                             int HV, int K, hipStream_t stream) {
+  ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, nullptr, nullptr, ckpt, u_out, eseg, ops,
+                segbad, B, T, H, HV,
                 kind, 1, lower_bound};
   const int Gq = HV / H;
   p.G = (B * HV / Gq) % 8 == 0 ? Gq : 1;
