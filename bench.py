@@ -546,7 +546,7 @@ def main():
                          "traffic": measured_traffic("bwd_prefill"), "flops_per_launch": fl,
                          "launch_ms": bwd_ms,
                          "kernel": "kda_bwd, whole call (checkpoint-mode chunk forward, "
-                                   "bwd_prep_kernel, bwd_segment_kernel<128, bf16, safe gate>, "
+                                   "bwd_segment_kernel<128, bf16, safe gate>, "
                                    "gate and zero-fill kernels)"}}
         del gb, dout, wsb
 
