@@ -179,11 +179,23 @@ struct alignas(16) BwdSmem {
   static constexpr int KP = K + 4;  // row stride: the 16 rows of an MFMA operand read spread over the banks
   float beta[kSeg];
   float4 ops[3][64];  // the segment's value-independent operands (the checkpoint forward)
-  // the segment's inputs per (token, key channel)
-  float k[kSeg][KP];   // k (0 past the end)
-  float q[kSeg][KP];   // s q (0 past the end)
-  float E[kSeg][KP];   // prod_{m <= t} alpha_m from the segment start
-  float al[kSeg][KP];  // the retain factors (per-token pass; 1 past the end)
+  // the segment's inputs per (token, key channel).  A segment takes either the
+  // chunked pass, which reads the per-key operands formed once at the staging,
+  // or the per-token pass, which reads k, s q and the retain factors: each pair
+  // shares its LDS, and the staging writes the one the segment's pass reads.
+  float E[kSeg][KP];  // prod_{m <= t} alpha_m from the segment start
+  union {
+    float ke[kSeg][KP];  // chunked: k E (0 past the end)
+    float k[kSeg][KP];   // per-token: k (0 past the end)
+  };
+  union {
+    float qe[kSeg][KP];  // chunked: s q E (0 past the end)
+    float q[kSeg][KP];   // per-token: s q (0 past the end)
+  };
+  union {
+    float kh[kSeg][KP];  // chunked: k / E (0 past the end)
+    float al[kSeg][KP];  // per-token: the retain factors (1 past the end)
+  };
   BwdTile<K> tile[kTiles];
   union {
     // chunked pass: each wavefront of tile 1 hands its results (dq, dk, dg:
@@ -291,12 +303,28 @@ bwd_segment_kernel(BwdParams p) {
       float kv[4], qv[4];
       In<T>::unpack4(L.k, kv);
       In<T>::unpack4(L.q, qv);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kv[c] = in ? kv[c] : 0.0f;
+        qv[c] = in ? scale * qv[c] : 0.0f;
+      }
       *reinterpret_cast<float4*>(&sm.E[trow][tcol]) = L.e;
-      *reinterpret_cast<float4*>(&sm.k[trow][tcol]) =
-          in ? float4{kv[0], kv[1], kv[2], kv[3]} : float4{0.0f, 0.0f, 0.0f, 0.0f};
-      *reinterpret_cast<float4*>(&sm.q[trow][tcol]) =
-          in ? float4{scale * qv[0], scale * qv[1], scale * qv[2], scale * qv[3]}
-             : float4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (L.bad == 0) {  // chunked pass: the per-key operands (uniform branch)
+        const float e[4] = {L.e.x, L.e.y, L.e.z, L.e.w};
+        float ke[4], qe[4], kh[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          ke[c] = kv[c] * e[c];
+          qe[c] = qv[c] * e[c];
+          kh[c] = kv[c] * __builtin_amdgcn_rcpf(e[c]);
+        }
+        *reinterpret_cast<float4*>(&sm.ke[trow][tcol]) = float4{ke[0], ke[1], ke[2], ke[3]};
+        *reinterpret_cast<float4*>(&sm.qe[trow][tcol]) = float4{qe[0], qe[1], qe[2], qe[3]};
+        *reinterpret_cast<float4*>(&sm.kh[trow][tcol]) = float4{kh[0], kh[1], kh[2], kh[3]};
+      } else {
+        *reinterpret_cast<float4*>(&sm.k[trow][tcol]) = float4{kv[0], kv[1], kv[2], kv[3]};
+        *reinterpret_cast<float4*>(&sm.q[trow][tcol]) = float4{qv[0], qv[1], qv[2], qv[3]};
+      }
     }
 #pragma unroll
     for (int i = 0; i < NVD; ++i) {
@@ -405,13 +433,12 @@ bwd_segment_kernel(BwdParams p) {
 #pragma unroll
     for (int st = 0; st < K / 16; ++st) {
       const int key = k0 + 4 * st + kq;
-      const float kv = sm.k[row][key], e = sm.E[row][key];
       float x, y;
       if constexpr (P == 0) {
-        x = kv * e;
+        x = sm.ke[row][key];
         y = ts.s0[key][row];
       } else {
-        x = kv * sm.E[kSeg - 1][key] * __builtin_amdgcn_rcpf(e);
+        x = sm.kh[row][key] * sm.E[kSeg - 1][key];
         y = ts.dsin[key][row];
       }
       acc[st & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc[st & 3], 0, 0, 0);
@@ -598,14 +625,13 @@ bwd_segment_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g4 + r;  // this step's inner index (a token)
-      const float e = sm.E[m][key], kv = sm.k[m][key];
-      const float kh = kv * __builtin_amdgcn_rcpf(e);
+      const float kh = sm.kh[m][key];
       if constexpr (kFirst) {
         dQ = mfma(wt[r], kh, dQ);
-        dKh = mfma(wd[r], sm.q[m][key] * e, dKh);
+        dKh = mfma(wd[r], sm.qe[m][key], dKh);
       } else {
         dKt = mfma(wt[r], kh, dKt);
-        dKh = mfma(wd[r], kv * e, dKh);
+        dKh = mfma(wd[r], sm.ke[m][key], dKh);
       }
     }
     // dS_0 for this wavefront's keys: rows key 16 w + 4 g4 + r, column c16
@@ -614,9 +640,8 @@ bwd_segment_kernel(BwdParams p) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int t = 4 * g4 + s4;
-      const float e = sm.E[t][key];
-      dSn = mfma(sm.q[t][key] * e, ts.dout[t][c16], dSn);
-      dSn = mfma(-sm.k[t][key] * e, sm.beta[t] * ts.a[t][c16], dSn);
+      dSn = mfma(sm.qe[t][key], ts.dout[t][c16], dSn);
+      dSn = mfma(-sm.ke[t][key], sm.beta[t] * ts.a[t][c16], dSn);
     }
     // gamma's direct term for this lane's key: sum over the columns of
     // dS_in S_0 (columns g4 + 4 i per lane, then the four row groups)
@@ -628,9 +653,8 @@ bwd_segment_kernel(BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * g4 + r;
-      const float e = sm.E[t][key], kv = sm.k[t][key], sq = sm.q[t][key];
-      const float ie = __builtin_amdgcn_rcpf(e);
-      const float qt = sq * e, kt = kv * e, kh = kv * ie, ks = kv * gam * ie;
+      const float e = sm.E[t][key], ie = __builtin_amdgcn_rcpf(e);
+      const float qt = sm.qe[t][key], kt = sm.ke[t][key], kh = sm.kh[t][key], ks = kh * gam;
       dql[r] = scale * e * dQ[r];
       dkl[r] = e * dKt[r] + ie * dKh[r] + gam * ie * dKs[r];
       dGl[r] = dQ[r] * qt + dKt[r] * kt - dKh[r] * kh - dKs[r] * ks;
