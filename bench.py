@@ -425,43 +425,46 @@ def main():
                                  "hbm_roofline is the same step on a 1 GiB state"},
         }
 
-        # The same steps with twice the sequences (a 1 GiB state, read with
-        # non-temporal loads): the step as HBM alone streams it.
+        # The same steps with two and four times the sequences (1 and 2 GiB
+        # states, read with non-temporal loads): the step as HBM alone streams it.
         import dataclasses
 
-        wl = dataclasses.replace(wd, B=2 * wd.B)
-        st2 = torch.cat([st, st])
-        q2, k2, v2, g2, b2 = (torch.cat([x, x], 1) for x in (qs, ks, vs, gs, bs))
-        o2 = torch.empty((wl.B, wl.HV, wl.V), dtype=torch.float32, device=dev)
         nl = 32
+        for rep, key in ((2, "large_state"), (4, "xl_state")):
+            wl = dataclasses.replace(wd, B=rep * wd.B)
+            st2 = torch.cat([st] * rep)
+            q2, k2, v2, g2, b2 = (torch.cat([x] * rep, 1) for x in (qs, ks, vs, gs, bs))
+            o2 = torch.empty((wl.B, wl.HV, wl.V), dtype=torch.float32, device=dev)
 
-        def lstep(t):
-            kda.recurrent_step(q2[t], k2[t], v2[t], g2[t], b2[t], A_log, dtb, st2, gate=wl.gate,
-                               lower_bound=wl.lower_bound, o=o2)
+            def lstep(t):
+                kda.recurrent_step(q2[t], k2[t], v2[t], g2[t], b2[t], A_log, dtb, st2, gate=wl.gate,
+                                   lower_bound=wl.lower_bound, o=o2)
 
-        for t in range(4):
-            lstep(t)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for t in range(nl):
-            lstep(t)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        lms = e0.elapsed_time(e1) / nl
-        lgbs = decode_bytes(wl) / (lms * 1e-3) / 1e9
-        result["decode"]["hbm_roofline"] = {
-            "bound": "hbm", "achieved": lgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": lgbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": decode_bytes(wl),
-            "kernel": "decode_step_kernel<128, 128, bf16, non-temporal loads>",
-            "note": "the decode step with twice the sequences (1 GiB state, beyond the "
-                    "last-level cache): HBM alone"}
-        result["decode"]["large_state"] = {
-            "B": wl.B, "state_mib": wl.B * wl.HV * wl.K * wl.V * 4 >> 20, "steps": nl,
-            "ms_per_token_step": lms, "value": wl.B / (lms * 1e-3), "unit": "tokens/s",
-            "roofline": {"bound": "hbm", "achieved": lgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": lgbs / HBM_PEAK_GBS, "traffic": None,
-                         "bytes_per_launch": decode_bytes(wl)}}
-        del q2, k2, v2, g2, b2, o2, st2
+            for t in range(4):
+                lstep(t)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for t in range(nl):
+                lstep(t)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            lms = e0.elapsed_time(e1) / nl
+            lgbs = decode_bytes(wl) / (lms * 1e-3) / 1e9
+            mib = wl.B * wl.HV * wl.K * wl.V * 4 >> 20
+            if key == "large_state":
+                result["decode"]["hbm_roofline"] = {
+                    "bound": "hbm", "achieved": lgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": lgbs / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": decode_bytes(wl),
+                    "kernel": "decode_step_kernel<128, 128, bf16, non-temporal loads>",
+                    "note": "the decode step with twice the sequences (1 GiB state, beyond the "
+                            "last-level cache): HBM alone; xl_state has it at 2 GiB"}
+            result["decode"][key] = {
+                "B": wl.B, "state_mib": mib, "steps": nl,
+                "ms_per_token_step": lms, "value": wl.B / (lms * 1e-3), "unit": "tokens/s",
+                "roofline": {"bound": "hbm", "achieved": lgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": lgbs / HBM_PEAK_GBS, "traffic": None,
+                             "bytes_per_launch": decode_bytes(wl)}}
+            del q2, k2, v2, g2, b2, o2, st2
         del qs, ks, vs, gs, bs, od, st
 
         # The fused multi-token recurrent forward on the same workload: the 256
