@@ -295,10 +295,11 @@ kda_status kda_chunk_fwd_split_noalloc(const void* q, const void* k, const void*
  *   dinitial_state       [B, HV, K, V]  float32 output (dL/dS_0), or NULL
  *   workspace            device scratch of at least kda_bwd_workspace_bytes(...)
  *                        bytes, 16-byte aligned, owned by the caller; per
- *                        16-token segment it holds the entering K x V state
- *                        and U = beta r (written by the forward pass), and
- *                        the segment's cumulative decays and three 16 x 16
- *                        matrices; its contents are meaningless afterwards
+ *                        16-token segment it holds the entering K x V state,
+ *                        U = beta r, the segment's cumulative decays, three
+ *                        16 x 16 matrices and a range flag, all written by
+ *                        the forward pass the call runs first; its contents
+ *                        are meaningless afterwards
  * Every output is overwritten (none needs initialising).  dq, dk, dg_raw,
  * dbeta, dA_log and ddt_bias are sums accumulated with fp32 atomics, so their
  * last bits can differ from run to run; dv and dinitial_state are written
