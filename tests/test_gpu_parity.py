@@ -36,6 +36,24 @@ def test_gate_matches_oracle(gate, chunk):
     assert err <= bound, (err, bound)
 
 
+@pytest.mark.parametrize("K", [5, 32])
+@pytest.mark.parametrize("chunk", [0, 16])
+def test_gate_in_place_both_layouts(K, chunk):
+    """g_out aliasing g_raw, for a K that takes the per-channel layout (5) and
+    one that takes the four-channel one (32); T = 150 leaves ragged chunks."""
+    d = synth.random_inputs(2, 150, 2, 6, K, K, seed=11, g_std=3.0)
+    g = L.to_dev(d)
+    ref = oracle.default().gate(d["g_raw"], d["A_log"], d["dt_bias"], "safe", -5.0)
+    if chunk:
+        T = ref.shape[1]
+        ref = np.concatenate([np.cumsum(ref[:, s:s + chunk], axis=1) for s in range(0, T, chunk)], 1)
+    buf = g["g_raw"].clone()
+    got = kda.gate(buf, g["A_log"], g["dt_bias"], gate="safe", lower_bound=-5.0, chunk_size=chunk, out=buf)
+    assert got.data_ptr() == buf.data_ptr()
+    err = np.abs(buf.cpu().double().numpy() - ref).max()
+    assert err <= 2e-6 * max(1.0, np.abs(ref).max()), err
+
+
 def test_gate_printed_default_value():
     """Defaults table of the gate section: g ~ -0.09, exp(g) ~ 0.91."""
     g_raw = torch.zeros((1, 1, 1, 1), device=L.DEV)
