@@ -186,7 +186,8 @@ struct ChainScratch<false> {};
 // wave, per lane the hi and lo words of its four accumulator-layout values.
 template <bool F32, int NCB>
 struct UHandoff {
-  uint4 u[NCB][2][64];  // [column block][block parity][lane]
+  uint4 u[NCB][2][64];   // U hi/lo: [column block][block parity][lane]
+  f32x4 qs[NCB][2][64];  // Q_hat S of the block (K a multiple of 32), likewise
 };
 template <int NCB>
 struct UHandoff<true, NCB> {};
@@ -477,6 +478,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   constexpr int V = K;
   constexpr int BV = V < 32 ? V : 32;
   constexpr int NCB = BV / 16, NKB = K / 16, NVT = V / BV;
+  // bf16 with K a multiple of 32: the chain forms Q_hat S beside K_hat S from
+  // the hi/lo state in its registers and hands it to the A wave, so no copy
+  // of the state goes through LDS
+  constexpr bool kChainQS = !F32 && K % 32 == 0;
   using SM = Smem<F32, K, BV>;
   using Ops = BlockOps<F32, K, BV>;
   typedef typename In<T>::Raw4 Raw4;
@@ -760,7 +765,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               const uint4 uu = sm.uo.u[cb][(it - 3) & 1][lane];
               const bf16x4 uh = __builtin_bit_cast(bf16x4, uint2{uu.x, uu.y});
               const bf16x4 ul = __builtin_bit_cast(bf16x4, uint2{uu.z, uu.w});
-              f32x4 acc = qsv[cb];
+              f32x4 acc = kChainQS ? sm.uo.qs[cb][(it - 3) & 1][lane] * scale : qsv[cb];
               acc = mfma16(ah_o, uh, acc);
               acc = mfma16(ah_o, ul, acc);
               acc = mfma16(al_o, uh, acc);
@@ -772,7 +777,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           ah_o = ah_n;
           al_o = al_n;
           skip_o = skip_n;
-          if (!skip_o) {  // s Q_hat S of block it - 2
+          if (!kChainQS && !skip_o) {  // s Q_hat S of block it - 2 (otherwise the chain's)
             const Ops& B2 = sm.blk[(it - 2) % 3];
   #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
@@ -935,9 +940,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
           split2_bf16(sacc[2 * q + 1][2], sacc[2 * q + 1][3], h.w, l.w);
           sh[q] = __builtin_bit_cast(bf16x8, h);
           sl[q] = __builtin_bit_cast(bf16x8, l);
-          const int o = row * RowOp<F32, 16, K>::LD + row_pos<K>(row, 32 * q + 8 * (lane >> 4));
-          *reinterpret_cast<uint4*>(st.hi + o) = h;
-          *reinterpret_cast<uint4*>(st.lo + o) = l;
+          (void)row;
+          (void)st;  // the state's only readers are this wave's registers
         }
       } else {
   #pragma unroll
@@ -1053,10 +1057,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
               const int o = row * RowOp<F32, kTok, K>::LD + row_pos<K>(row, 32 * q + 8 * (lane >> 4));
               const bf16x8 ah = *reinterpret_cast<const bf16x8*>(B.kh.hi + o);
               const bf16x8 al = *reinterpret_cast<const bf16x8*>(B.kh.lo + o);
+              const bf16x8 qh = *reinterpret_cast<const bf16x8*>(B.qh.hi + o);
+              const bf16x8 ql = *reinterpret_cast<const bf16x8*>(B.qh.lo + o);
               pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh[q], pk, 0, 0, 0);
+              qs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, sh[q], qs, 0, 0, 0);
               pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl[q], pk, 0, 0, 0);
+              qs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, sl[q], qs, 0, 0, 0);
               pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, sh[q], pk, 0, 0, 0);
+              qs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, sh[q], qs, 0, 0, 0);
             }
+            // Q_hat S goes to the A wave, which forms this block's outputs next step
+            if constexpr (!CK) sm.uo.qs[cb][tc & 1][lane] = qs;
           } else
             kprod(pk, B.kh, 0, C.st[tc & 1], 0, lane);        // K_hat S
           const float4 bt4 = *reinterpret_cast<const float4*>(&B.beta[4 * g]);
