@@ -32,17 +32,20 @@
 //   waves 0-3  prep of block n+3: gate, cumulative products, scaled operands
 //              (hi/lo words) and the block's v tile into a triple-buffered LDS
 //              slot, with the next block's HBM inputs loaded a step ahead
-//   wave 4     A^T of block n+2 (kept in registers), s Q_hat S of block n+1
-//              from the chain's LDS copy of the state, and O = s Q_hat S + A U
-//              of block n with U handed over by the chain, then the o stores
+//   wave 4     A^T of block n+2 (kept in registers) and O = s Q_hat S + A U of
+//              block n with Q_hat S and U handed over by the chain, then the
+//              o stores (K not a multiple of 32: it forms s Q_hat S of block
+//              n+1 itself from the chain's LDS copy of the state)
 //   wave 5     R of block n+2 (MFMA), then (I + R)^{-1} = X_d - X_d N X_d
 //              (X_d: the two 8x8 diagonal inverses by substitution, N: the
 //              lower-left 8x8 block of R), on fp32 MFMA
 //   waves 6-7  the state chain of block n+1, one 16-wide value column block
 //              each, with that column block of the fp32 state held in
-//              registers for the whole sequence: diag(gamma) S, K_hat S, Ebar,
-//              U and the state update; U goes to wave 4 and a hi/lo copy of
-//              the new state to a double-buffered LDS slot
+//              registers for the whole sequence: diag(gamma) S, K_hat S and
+//              Q_hat S (from the hi/lo state in its registers), Ebar, U and the
+//              state update; Q_hat S and U go to wave 4 (K not a multiple of
+//              32: K_hat S against a hi/lo copy of the state in a
+//              double-buffered LDS slot, which wave 4 also reads)
 // Issue priority: the chain waves win their SIMD's arbitration from K_hat S
 // to U and yield it for the state update and its split, which only the next
 // step needs; wave 4 wins it over the prep wave on its SIMD.
@@ -743,8 +746,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
     // bf16 inputs: the A wave also forms the outputs, one step behind the
     // chain: O = s Q_hat S + A U for the block whose U the chain produced last
     // step.  A is computed as A^T = (k / E)(q E)^T, whose accumulator layout is
-    // A's MFMA operand layout, and stays in registers; Q_hat S reads the
-    // chain's LDS copy of the state; U arrives from the chain through LDS.
+    // A's MFMA operand layout, and stays in registers; Q_hat S (formed by the
+    // chain when K is a multiple of 32, else here from the chain's LDS copy
+    // of the state) and U arrive from the chain through LDS.
     bf16x4 ah_n = {}, al_n = {}, ah_o = {}, al_o = {};  // A of blocks it-2 (n), it-3 (o)
     bool skip_n = true, skip_o = true;  // block absent or run token by token
     f32x4 qsv[NCB];
