@@ -19,10 +19,11 @@
 // sequence for the last two), and under GVA sums of dq, dk over the value
 // heads that share a query/key head.
 //
-// Schedule, three launches after the zero fill:
-//  1. the fused chunk kernel in checkpoint mode (kda_chunk.hip) writes the
-//     state entering every 16-token segment and U_t = beta_t r_t of every
-//     token, on its fp32 path whatever the input type, and once per
+// Schedule, three launches:
+//  1. the fused chunk kernel in checkpoint mode (kda_chunk.hip) zeroes the
+//     outputs the later kernels accumulate into, writes the state entering
+//     every 16-token segment and U_t = beta_t r_t of every token, on its fp32
+//     path whatever the input type, and once per
 //     (sequence, value head, segment) E and the matrices below that do not
 //     depend on the value tile;
 //  2. bwd_segment_kernel: one workgroup per (sequence, value head, 16-wide
@@ -979,7 +980,7 @@ hipError_t launch_chunk_ckpt(const void* q, const void* k, const void* v, int bf
                              const float* beta, const float* A_log, const float* dt_bias, int kind,
                              int per_head, float lower_bound, const float* S0, float* ckpt,
                              float* u_out, float* eseg, float* ops, int* segbad, int B, int T, int H,
-                             int HV, int K, hipStream_t stream);
+                             int HV, int K, float* const zero[6], hipStream_t stream);
 
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -1049,14 +1050,17 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, int bf16, con
   hipError_t e;
   const int gK = per_head ? 1 : K;  // gate values per (token, value head)
   const long nq = (long)B * T * H * K, ng = (long)B * T * HV * gK;
-  const ZeroList zl{{dq, dk, dbeta, dg_raw, dA_log, ddt_bias},
-                    {nq, nq, (long)B * T * HV, ng, (long)HV, (long)HV * gK}};
-  if ((e = zero(zl, stream)) != hipSuccess) return e;
   if (T > 0) {
-    // the forward in checkpoint mode: every segment's entry state and U, no o
+    // the forward in checkpoint mode: every segment's entry state and U, no
+    // o; it also zeroes the outputs the later kernels accumulate into
+    float* const zero[6] = {dq, dk, dbeta, dg_raw, dA_log, ddt_bias};
     e = launch_chunk_ckpt(q, k, v, bf16, g_raw, beta, A_log, dt_bias, kind, per_head, lower_bound, S0,
-                          ckpt, u, eseg, ops, segbad, B, T, H, HV, K, stream);
+                          ckpt, u, eseg, ops, segbad, B, T, H, HV, K, zero, stream);
     if (e != hipSuccess) return e;
+  } else {  // no tokens: only the per-head sums exist, and they are zero
+    const ZeroList zl{{dq, dk, dbeta, dg_raw, dA_log, ddt_bias},
+                      {nq, nq, (long)B * T * HV, ng, (long)HV, (long)HV * gK}};
+    if ((e = zero(zl, stream)) != hipSuccess) return e;
   }
   BwdParams p{q, k, v, g_raw, beta, A_log, dt_bias, dout, dST, ckpt, u, ops, eseg, segbad, dq, dk, dv, dbeta,
               dg_raw, dS0, dA_log, ddt_bias, B, T, H, HV, NC, per_head, lower_bound};

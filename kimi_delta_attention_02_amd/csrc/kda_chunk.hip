@@ -97,6 +97,13 @@ struct ChunkParams {
   int B, T, H, HV, kind;
   int G;  // value heads per XCD group (a divisor of HV / H)
   float lower_bound;
+  // checkpoint mode, also: the backward's summed gradients, zeroed here so
+  // that no separate launch has to (each may be null): dq, dk [B, T, H, K],
+  // dbeta [B, T, HV], dg [B, T, HV, K] ([B, T, HV] with a per-head gate),
+  // dA_log [HV], ddt_bias [HV, K] ([HV] per head).  The workgroup of each
+  // head's first value tile zeroes its rows, that of the first value head of
+  // a query/key group the dq and dk rows.
+  float *zdq, *zdk, *zdb, *zdg, *zdA, *zddt;
 };
 
 constexpr int kTok = 16;      // tokens per block
@@ -683,6 +690,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
   #pragma unroll
               for (int j = 0; j < 2; ++j)
                 *reinterpret_cast<float4*>(eb + (2 * tp + j) * K) = float4{E[j][0], E[j][1], E[j][2], E[j][3]};
+              // and zeroes the gradient rows of its tokens and channels
+              const float4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  #pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                const long t = t0 + 2 * tp + j;
+                if (t < T_) {
+                  if (!GS && p.zdg) *reinterpret_cast<float4*>(p.zdg + ((b * T_ + t) * HV + hv) * (long)K + c0) = z4;
+                  if (hv % (HV / H) == 0) {
+                    const long qo = ((b * T_ + t) * H + h) * (long)K + c0;
+                    if (p.zdq) *reinterpret_cast<float4*>(p.zdq + qo) = z4;
+                    if (p.zdk) *reinterpret_cast<float4*>(p.zdk + qo) = z4;
+                  }
+                }
+              }
             }
           }
           float ke[2][4];
@@ -723,6 +744,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(ChunkParams p) {
             B.vT[vc + 1][vtt] = (uint16_t)(x >> 16);
           }
           if (tid < kTok) B.beta[tid] = it * kTok + tid < T_ ? cur.beta : 0.0f;
+          if constexpr (CK) {  // the backward's per-token gradients, zeroed (see ChunkParams)
+            if (v0 == 0 && tid < kTok && it * kTok + tid < T_) {
+              const long row = (b * T_ + it * kTok + tid) * HV + hv;
+              if (p.zdb) p.zdb[row] = 0.0f;
+              if (GS && p.zdg) p.zdg[row] = 0.0f;
+            }
+            if (v0 == 0 && it == 0) {  // and the per-head sums (every sequence writes the same zeros)
+              if (p.zddt && tid < GKD) p.zddt[(long)hv * GKD + tid] = 0.0f;
+              if (p.zdA && tid == 0) p.zdA[hv] = 0.0f;
+            }
+          }
         }
         if (prep_thread) {
           if ((it + 1) * kTok <= T_) prep_block(std::true_type{});
@@ -1207,10 +1239,10 @@ hipError_t launch_chunk_ckpt(const void* q, const void* k, const void* v, int bf
                              const float* beta, const float* A_log, const float* dt_bias, int kind,
                              int per_head, float lower_bound, const float* S0, float* ckpt,
                              float* u_out, float* eseg, float* ops, int* segbad, int B, int T, int H,
-                             int HV, int K, hipStream_t stream) {
+                             int HV, int K, float* const zero[6], hipStream_t stream) {
   ChunkParams p{q, k, v, g_raw, beta, A_log, dt_bias, S0, nullptr, nullptr, ckpt, u_out, eseg, ops,
                 segbad, B, T, H, HV,
-                kind, 1, lower_bound};
+                kind, 1, lower_bound, zero[0], zero[1], zero[2], zero[3], zero[4], zero[5]};
   const int Gq = HV / H;
   p.G = (B * HV / Gq) % 8 == 0 ? Gq : 1;
 #define KDA_CKPT_GS(KK, TT, GG)                                            \
