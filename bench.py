@@ -550,7 +550,7 @@ def main():
                          "launch_ms": bwd_ms,
                          "kernel": "kda_bwd, whole call (checkpoint-mode chunk forward, "
                                    "bwd_segment_kernel<128, bf16, safe gate>, "
-                                   "gate and zero-fill kernels)"}}
+                                   "gate kernel; the outputs zeroed by the first)"}}
         del gb, dout, wsb
 
     if args.copy_calibration_mib:
